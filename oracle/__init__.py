@@ -1,0 +1,20 @@
+"""CPU oracle for absorbed MLA decode — TEST INFRASTRUCTURE, not product code.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import or run anything in this package.  The HIP path never
+does, and this package imports nothing from the HIP path: the two share no
+code.  Inputs come from ``deepseek_mla_latent_amd.inputs`` (random draws
+only), passed in by the caller as numpy arrays.
+
+Modules:
+
+* ``mla_decode`` — fp64 numpy reference of the decode path, written the
+  non-absorbed way (K and V up-projected per head), plus the plain
+  definitions of the three library calls.
+* ``flops`` — the pages' FLOP convention and the three computation orders of
+  both absorptions, counted step by step from index extents; byte counts.
+
+Every function is pinned by ``tests/test_oracle.py`` / ``tests/test_flops.py``
+against what the pages print and against closed forms, special cases and
+library routines (see each test's docstring).
+"""
