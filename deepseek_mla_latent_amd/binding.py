@@ -1,0 +1,182 @@
+"""ctypes binding of ``libmla_latent.so`` (declared in ``include/mla_latent.h``).
+
+Argument marshalling only: every step of the decode path runs in the library's HIP
+kernels.  Functions keep the C names; tensor arguments are torch tensors on the GPU
+(torch provides device memory and the current stream), or raw integer device pointers.
+There is no fallback: if the library is missing the import of this module still works,
+but every call raises ``MlaLibraryMissing``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmla_latent.so")
+
+MLA_F32 = 0
+MLA_BF16 = 1
+
+STATUS = {
+    0: "MLA_OK", -1: "MLA_ERR_NULL", -2: "MLA_ERR_SHAPE", -3: "MLA_ERR_DTYPE", -4: "MLA_ERR_ALIGN",
+    -5: "MLA_ERR_WORKSPACE", -6: "MLA_ERR_UNSUPPORTED", -7: "MLA_ERR_LAUNCH", -8: "MLA_ERR_DEVICE",
+}
+EXPORTS = ("mla_absorb_q", "mla_decode_workspace_bytes", "mla_decode_num_splits", "mla_decode_attn",
+           "mla_out_proj", "mla_status_str")
+
+
+class MlaLibraryMissing(RuntimeError):
+    pass
+
+
+class MlaError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {mla_status_str(code)} ({code})")
+
+
+class mla_params(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("q_len", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+        ("kv_lora_rank", ctypes.c_int32), ("rope_dim", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float), ("causal", ctypes.c_int32), ("dtype", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None):
+    """Load the shared library once; raise MlaLibraryMissing if it is not built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise MlaLibraryMissing(f"{p} is not built; run `python -m deepseek_mla_latent_amd.build`")
+    lib = ctypes.CDLL(p)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    pp = ctypes.POINTER(mla_params)
+    lib.mla_absorb_q.argtypes = [vp, vp, vp, pp, vp]
+    lib.mla_absorb_q.restype = i32
+    lib.mla_decode_workspace_bytes.argtypes = [pp, i32]
+    lib.mla_decode_workspace_bytes.restype = sz
+    lib.mla_decode_num_splits.argtypes = [pp, i32]
+    lib.mla_decode_num_splits.restype = i32
+    lib.mla_decode_attn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i32, pp, vp]
+    lib.mla_decode_attn.restype = i32
+    lib.mla_out_proj.argtypes = [vp, vp, vp, pp, vp]
+    lib.mla_out_proj.restype = i32
+    lib.mla_status_str.argtypes = [i32]
+    lib.mla_status_str.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def make_params(*, batch: int, q_len: int, max_seq_len: int, max_pages_per_seq: Optional[int] = None,
+                softmax_scale: Optional[float] = None, causal: bool = True, dtype: int = MLA_BF16,
+                num_heads: int = 128, kv_lora_rank: int = 512, rope_dim: int = 64, head_dim: int = 128,
+                page_size: int = 64) -> mla_params:
+    if max_pages_per_seq is None:
+        max_pages_per_seq = max(1, -(-max_seq_len // page_size))
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(head_dim + rope_dim)
+    return mla_params(batch, q_len, num_heads, kv_lora_rank, rope_dim, head_dim, page_size, max_pages_per_seq,
+                      max_seq_len, softmax_scale, 1 if causal else 0, dtype)
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if not x.is_cuda:
+        raise ValueError("tensor arguments must be on the GPU")
+    if not x.is_contiguous():
+        raise ValueError("tensor arguments must be contiguous")
+    return x.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(code: int, where: str):
+    if code != 0:
+        raise MlaError(code, where)
+
+
+def mla_status_str(code: int) -> str:
+    try:
+        return load_library().mla_status_str(code).decode()
+    except MlaLibraryMissing:
+        return STATUS.get(code, "unknown")
+
+
+def mla_absorb_q(q_nope, w_uk, q_lat, params: mla_params, stream=None) -> None:
+    lib = load_library()
+    _check(lib.mla_absorb_q(_ptr(q_nope), _ptr(w_uk), _ptr(q_lat), ctypes.byref(params), _stream(stream)),
+           "mla_absorb_q")
+
+
+def mla_decode_workspace_bytes(params: mla_params, num_splits: int = 0) -> int:
+    return int(load_library().mla_decode_workspace_bytes(ctypes.byref(params), num_splits))
+
+
+def mla_decode_num_splits(params: mla_params, num_splits: int = 0) -> int:
+    r = int(load_library().mla_decode_num_splits(ctypes.byref(params), num_splits))
+    _check(min(r, 0), "mla_decode_num_splits")
+    return r
+
+
+def mla_decode_attn(q_lat, q_pe, kv_pool, block_table, seq_lens, o_lat, lse, workspace, num_splits: int,
+                    params: mla_params, stream=None, workspace_bytes: Optional[int] = None) -> None:
+    lib = load_library()
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None or isinstance(workspace, int) else \
+            workspace.numel() * workspace.element_size()
+    _check(lib.mla_decode_attn(_ptr(q_lat), _ptr(q_pe), _ptr(kv_pool), _ptr(block_table), _ptr(seq_lens),
+                               _ptr(o_lat), _ptr(lse), _ptr(workspace), workspace_bytes, num_splits,
+                               ctypes.byref(params), _stream(stream)), "mla_decode_attn")
+
+
+def mla_out_proj(o_lat, w_uv, out, params: mla_params, stream=None) -> None:
+    lib = load_library()
+    _check(lib.mla_out_proj(_ptr(o_lat), _ptr(w_uv), _ptr(out), ctypes.byref(params), _stream(stream)),
+           "mla_out_proj")
+
+
+class DecodeBuffers:
+    """Device tensors for one decode step: intermediates, outputs and workspace (torch-allocated).
+
+    Allocation happens here, once, outside the calls; ``run`` only enqueues the three library
+    calls, so it can be captured in a HIP graph and replayed.
+    """
+
+    def __init__(self, params: mla_params, num_splits: int = 0, device="cuda"):
+        import torch
+        self.params = params
+        self.num_splits = num_splits
+        B, S, H = params.batch, params.q_len, params.num_heads
+        dt = torch.bfloat16 if params.dtype == MLA_BF16 else torch.float32
+        self.q_lat = torch.empty((B, S, H, params.kv_lora_rank), dtype=dt, device=device)
+        self.o_lat = torch.empty((B, S, H, params.kv_lora_rank), dtype=torch.float32, device=device)
+        self.lse = torch.empty((B, S, H), dtype=torch.float32, device=device)
+        self.out = torch.empty((B, S, H, params.head_dim), dtype=dt, device=device)
+        ws = mla_decode_workspace_bytes(params, num_splits)
+        self.workspace = torch.empty(max(ws, 16) // 4 + 4, dtype=torch.float32, device=device) if ws else None
+
+    def run(self, q_nope, q_pe, w_uk, w_uv, kv_pool, block_table, seq_lens, stream=None):
+        p = self.params
+        mla_absorb_q(q_nope, w_uk, self.q_lat, p, stream)
+        mla_decode_attn(self.q_lat, q_pe, kv_pool, block_table, seq_lens, self.o_lat, self.lse, self.workspace,
+                        self.num_splits, p, stream)
+        mla_out_proj(self.o_lat, w_uv, self.out, p, stream)
+        return self.out

@@ -1,0 +1,52 @@
+// Shared device-side definitions for the gfx950 MLA decode kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace mla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+#define MLA_LDS __attribute__((address_space(3)))
+#define MLA_GLOBAL __attribute__((address_space(1)))
+
+// D(32x32) += A(32x16) * B(16x32), bf16 in, fp32 accumulate.
+// Lane l holds A[l%32][8*(l/32) .. +7], B[8*(l/32) .. +7][l%32];
+// D element i of lane l is D[(i/4)*8 + (l/32)*4 + i%4][l%32].
+__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// D(32x32) += A(32x2) * B(2x32), fp32. Lane l holds A[l%32][l/32], B[l/32][l%32]; D as above.
+__device__ __forceinline__ f32x16 mfma32x32x2f32(float a, float b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// bf16 <-> fp32 (round to nearest even; inputs here are finite).
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup w -> XCD w % 8), each XCD
+// with its own L2. Renumber so that consecutive logical ids run on the same XCD: logical ids
+// [0, n0) go to XCD 0, the next block to XCD 1, ... A bijection on [0, n).
+__device__ __forceinline__ int xcd_remap(int w, int n) {
+  const int q = n >> 3, r = n & 7;
+  const int xcd = w & 7, local = w >> 3;
+  return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+}
+
+}  // namespace mla

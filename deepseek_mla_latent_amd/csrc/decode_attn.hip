@@ -1,0 +1,414 @@
+// Latent-space attention for absorbed MLA decode, gfx950.
+//
+// For every (sequence b, query token i, head h):
+//   z_j   = scale * (q_lat[b,i,h,:] . c_j + q_pe[b,i,h,:] . k_pe_j)   over the visible cached tokens j
+//   o_lat = sum_j softmax(z)_j c_j ,  lse = log sum_j exp(z_j)
+// The latent c_j serves as key (with the shared RoPE key k_pe_j added to the score) and as value
+// for all 128 heads: "DeepSeek-V2的推理成本如何计算？" (izhida.com), answers "DeepSeek" (512-d
+// latent + 64-d RoPE inner product, 512-d weighted sum per head and cached token) and "专家"
+// (RoPE as a shared-key MQA whose score is added). Scores and the weighted sum are steps 3 and 1
+// of order 2 in "【笔记】MLA矩阵吸收分析" §二.2 and §三.2.
+//
+// bf16 kernel layout (one workgroup = 4 waves = 128 heads of one (b, i), one contiguous range of
+// cache pages):
+//   * each 64-token page is copied HBM -> LDS by direct-to-LDS loads (16 B per lane, no register
+//     staging) into one of two buffers, so page t+1 streams in while page t is computed;
+//   * the LDS tile is XOR-swizzled in 16-byte units so both read patterns below are spread over
+//     the banks;
+//   * scores are computed transposed, S^T = tile * Q^T, on 32x32x16 bf16 MFMAs: the tile is the
+//     A operand (ds_read_b128), the wave's 32 heads' [q_lat | q_pe] stay in registers as the B
+//     operand.  The accumulator layout then gives every lane one head and 16 tokens, which is
+//     already the B-operand layout of the next product (no cross-lane shuffle for P);
+//   * O^T (latent x heads) += tile^T * P^T reuses the same LDS tile as the value; its transposed
+//     A operand comes from ds_read_b64_tr_b16 (4 tokens x 1 latent column per lane per read);
+//   * online softmax in base 2 with the scale folded in; the running max is only raised (and O
+//     rescaled) when a tile's max exceeds it by more than 2^8, which keeps exp2 arguments <= 8
+//     and skips almost every rescale of the 256 accumulator registers.
+// Long contexts are split into page ranges (split-K over tokens); each range writes a normalised
+// partial (o_k, lse_k) and mla_lse_merge combines them.
+#include "common.h"
+#include "kernels.h"
+
+namespace mla {
+
+constexpr int kTile = kPage;                          // tokens per LDS tile = one cache page
+constexpr int kUnitsA = kDc / 8;                      // 16-byte units of c_KV per token (64)
+constexpr int kUnitsB = kDr / 8;                      // 16-byte units of k_pe per token (8)
+constexpr int kRegionA = kTile * kUnitsA * 16;        // 65536 B: c_KV part of a tile
+constexpr int kBufBytes = kRegionA + kTile * kUnitsB * 16;  // 73728 B per tile buffer
+constexpr float kRescaleSlack = 8.0f;                 // log2 units
+
+// Swizzle: 16-byte unit u of token t is stored at unit (u ^ swz(t)) of the token's LDS row.
+// Region A (64 units per row): bit-rotated low 4 bits of t, so 16 consecutive tokens at one unit
+// (the score A-operand read) and 8 tokens x 4 units (the transposed read) both spread over banks.
+__device__ __forceinline__ int swz_a(int t) { return ((t & 3) << 2) | ((t >> 2) & 3); }
+__device__ __forceinline__ int swz_b(int t) { return (t >> 1) & 7; }
+__device__ __forceinline__ int off_a(int t, int u) { return (t * kUnitsA + (u ^ swz_a(t))) * 16; }
+__device__ __forceinline__ int off_b(int t, int u) { return kRegionA + (t * kUnitsB + (u ^ swz_b(t))) * 16; }
+
+// Copy one page (cnt valid tokens, 1..64) into an LDS tile buffer.  Each direct-to-LDS load
+// writes 64 lanes x 16 B contiguously, so each instruction fills one token's 1 KiB c_KV row
+// (region A) or the 128 B k_pe rows of 8 tokens (region B); a lane fetches the global unit that
+// belongs at its swizzled slot.  Tokens past cnt re-read token 0 (always valid), so LDS never
+// holds bytes from outside the sequence; their scores are masked.
+__device__ __forceinline__ void issue_tile(MLA_LDS char* buf, const uint16_t* page_base, int cnt, int wave,
+                                           int lane) {
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int t = wave * 16 + k;
+    const int ts = t < cnt ? t : 0;
+    const int u = lane ^ swz_a(t);
+    const uint16_t* src = page_base + ts * kRow + u * 8;
+    __builtin_amdgcn_global_load_lds((const MLA_GLOBAL void*)src, (MLA_LDS void*)(buf + t * 1024), 16, 0, 0);
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int j = wave * 2 + k;
+    const int t = j * 8 + (lane >> 3);
+    const int ts = t < cnt ? t : 0;
+    const int u = (lane & 7) ^ swz_b(t);
+    const uint16_t* src = page_base + ts * kRow + kDc + u * 8;
+    __builtin_amdgcn_global_load_lds((const MLA_GLOBAL void*)src, (MLA_LDS void*)(buf + kRegionA + j * 1024), 16,
+                                     0, 0);
+  }
+}
+
+// The 256 O accumulators live in AGPRs and are otherwise only touched by MFMAs.  The two VALU
+// uses (rare rescale, final normalisation) go through inline asm that reads/writes the AGPRs
+// directly; written as plain C++, the register allocator moves all of O into VGPRs and spills.
+// Inline asm is opaque to the hazard recognizer, so the first access waits out the MFMA
+// write-to-read latency explicitly (s_nop 15 + s_nop 3 >= the 16-pass XDL requirement).
+__device__ __forceinline__ void acc_wait_mfma() { asm volatile("s_nop 15\n\ts_nop 3" ::); }
+
+__device__ __forceinline__ void acc_scale(f32x16& acc, float alpha) {
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    float x = acc[e];
+    float tmp;
+    asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                 : "+a"(x), "=&v"(tmp)
+                 : "v"(alpha));
+    acc[e] = x;
+  }
+}
+
+__device__ __forceinline__ float acc_read_scaled(float x, float scale) {
+  float tmp;
+  asm volatile("v_accvgpr_read_b32 %0, %1\n\tv_mul_f32 %0, %0, %2" : "=&v"(tmp) : "a"(x), "v"(scale));
+  return tmp;
+}
+
+__device__ __forceinline__ bf16x8 lds_read_b128(const MLA_LDS char* p) { return *(const MLA_LDS bf16x8*)p; }
+
+__device__ __forceinline__ bf16x8 lds_read_tr_pair(const MLA_LDS char* lo, const MLA_LDS char* hi) {
+  i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)lo);
+  i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)hi);
+  i16x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// Token range and output slots of one workgroup; shared by both dtypes.
+struct WorkItem {
+  int b, i, split;
+  int tok_begin, tok_end;  // [tok_begin, tok_end) of sequence b, page aligned at tok_begin
+  size_t out_row;          // index of (head 0) in the o/lse output rows
+};
+
+__device__ __forceinline__ WorkItem make_work(const AttnArgs& a, int id) {
+  WorkItem w;
+  w.i = id % a.S;
+  const int rest = id / a.S;
+  w.split = rest % a.num_splits;
+  w.b = rest / a.num_splits;
+  const int L = a.seq_lens[w.b];
+  int n = a.causal ? L - a.S + w.i + 1 : L;
+  n = n < 0 ? 0 : (n > L ? L : n);
+  const int p_begin = w.split * a.pages_per_split;
+  const int pages_L = (L + kPage - 1) / kPage;
+  int p_end = p_begin + a.pages_per_split;
+  p_end = p_end < pages_L ? p_end : pages_L;
+  w.tok_begin = p_begin * kPage;
+  const int e = p_end * kPage;
+  w.tok_end = e < n ? e : n;
+  const size_t bi = (size_t)w.b * a.S + w.i;
+  w.out_row = a.final_out ? bi * kHeads : (bi * a.num_splits + w.split) * kHeads;
+  return w;
+}
+
+__global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * kBufBytes];
+  MLA_LDS char* smem = (MLA_LDS char*)smem_raw;
+
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  const WorkItem w = make_work(a, id);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int h = wave * 32 + l32;
+
+  float* o_ptr = a.o_out + (w.out_row + h) * kDc + 4 * hf;
+  float* lse_ptr = a.lse_out ? a.lse_out + w.out_row + h : nullptr;
+
+  const int ntok = w.tok_end - w.tok_begin;
+  if (ntok <= 0) {  // empty key range: o = 0, lse = -inf
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int cb = 0; cb < 16; ++cb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) *(f32x4*)(o_ptr + 32 * cb + 8 * g) = z;
+    if (hf == 0 && lse_ptr) *lse_ptr = -INFINITY;
+    return;
+  }
+  const int ntiles = (ntok + kTile - 1) / kTile;
+  const int32_t* bt = a.block_table + (size_t)w.b * a.max_pages + w.tok_begin / kPage;
+  const uint16_t* pool = (const uint16_t*)a.pool;
+
+  issue_tile(smem, pool + (size_t)bt[0] * kPage * kRow, ntok < kTile ? ntok : kTile, wave, lane);
+
+  // This lane's head, as the B operand of the score MFMA: q[ks] = [q_lat | q_pe][16 ks + 8 hf .. +7].
+  bf16x8 q[36];
+  {
+    const size_t qrow = ((size_t)w.b * a.S + w.i) * kHeads + h;
+    const bf16x8* ql = (const bf16x8*)((const uint16_t*)a.q_lat + qrow * kDc + 8 * hf);
+    const bf16x8* qp = (const bf16x8*)((const uint16_t*)a.q_pe + qrow * kDr + 8 * hf);
+#pragma unroll
+    for (int ks = 0; ks < 32; ++ks) q[ks] = ql[2 * ks];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) q[32 + ks] = qp[2 * ks];
+  }
+
+  // Per-lane LDS byte offsets (within a tile buffer) of the swizzled reads; see the loops below.
+  int qk_a[8], qk_b[4], pv_lo[4], pv_hi[4];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) qk_a[k] = off_a(l32, 2 * k + hf);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) qk_b[k] = off_b(l32, 2 * k + hf);
+  {
+    const int r4 = (lane >> 2) & 3;
+    const int colq = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const int tb = 4 * hf + r4;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c = 32 * k + colq;
+      pv_lo[k] = off_a(tb, c >> 3) + (c & 7) * 2;
+      pv_hi[k] = off_a(tb + 8, c >> 3) + (c & 7) * 2;
+    }
+  }
+
+  f32x16 o[16];
+#pragma unroll
+  for (int cb = 0; cb < 16; ++cb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[cb][e] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  for (int t = 0; t < ntiles; ++t) {
+    __syncthreads();  // tile t has landed; every wave is done with the other buffer
+    const int tile_tok = t * kTile;
+    if (t + 1 < ntiles) {
+      // The per-lane DMA addresses are loop-invariant; recomputing them (a few VALU ops) is far
+      // cheaper than the registers LICM would pin across the loop, so hide the lane id from it.
+      int lane_v = lane;
+      asm volatile("" : "+v"(lane_v));
+      const int rem = ntok - tile_tok - kTile;
+      issue_tile(smem + ((t + 1) & 1) * kBufBytes, pool + (size_t)bt[t + 1] * kPage * kRow,
+                 rem < kTile ? rem : kTile, wave, lane_v);
+    }
+    const MLA_LDS char* buf = smem + (t & 1) * kBufBytes;
+    const int cnt = ntok - tile_tok < kTile ? ntok - tile_tok : kTile;
+
+    // The tile is processed as two 32-token halves st: scores, softmax, then the weighted sum.
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      // ---- scores S^T (32 tokens x 32 heads).  Address of (token 32 st + l32, unit 2 ks + hf) =
+      // qk_a[ks % 8] + 256 (ks / 8) + 32768 st (region A), qk_b[ks] + 4096 st (region B): the
+      // swizzle only touches the low 4 unit bits.
+      f32x16 sc;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sc[e] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 32; ++ks)
+        sc = mfma32x32x16(lds_read_b128(buf + qk_a[ks & 7] + 256 * (ks >> 3) + 32768 * st), q[ks], sc);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) sc = mfma32x32x16(lds_read_b128(buf + qk_b[ks] + 4096 * st), q[32 + ks], sc);
+      __builtin_amdgcn_sched_barrier(0);
+
+      // ---- online softmax (base 2); element e of sc is token 32 st + (e/4)*8 + 4 hf + e%4
+      float mt = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int tok = 32 * st + (e >> 2) * 8 + 4 * hf + (e & 3);
+        const float x = tok < cnt ? sc[e] * a.scale_log2 : -INFINITY;
+        sc[e] = x;
+        mt = fmaxf(mt, x);
+      }
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      if (__any(mt > m_run + kRescaleSlack)) {
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+        acc_wait_mfma();
+#pragma unroll
+        for (int cb = 0; cb < 16; ++cb) acc_scale(o[cb], alpha);
+        asm volatile("s_nop 4" ::);
+        m_run = m_new;
+      }
+      bf16x8 pk[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        uint32_t w4[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float p0 = __builtin_amdgcn_exp2f(sc[8 * kk + 2 * j] - m_run);
+          const float p1 = __builtin_amdgcn_exp2f(sc[8 * kk + 2 * j + 1] - m_run);
+          l_run += p0 + p1;
+          w4[j] = pack_bf16x2(p0, p1);
+        }
+        u32x4 v = {w4[0], w4[1], w4[2], w4[3]};
+        pk[kk] = __builtin_bit_cast(bf16x8, v);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+
+      // ---- O^T (latent x heads) += tile^T * P^T.  k slot j of lane half hf in step kk is token
+      // 32 st + 16 kk + (j/4)*8 + 4 hf + j%4; the transposed read gives lane l latent column l%32
+      // of 4 such tokens (source lane s of each 16-lane group supplies token row s/4, columns
+      // 4(s%4)..+3).  Address = pv_lo/hi[cb % 4] + 256 (cb / 4) + 32768 st + 16384 kk.
+#pragma unroll
+      for (int cb = 0; cb < 16; ++cb)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const int imm = 256 * (cb >> 2) + 32768 * st + 16384 * kk;
+          const bf16x8 av = lds_read_tr_pair(buf + pv_lo[cb & 3] + imm, buf + pv_hi[cb & 3] + imm);
+          o[cb] = mfma32x32x16(av, pk[kk], o[cb]);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = 1.0f / l_tot;
+  acc_wait_mfma();
+#pragma unroll
+  for (int cb = 0; cb < 16; ++cb)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      f32x4 v = {acc_read_scaled(o[cb][4 * g], inv), acc_read_scaled(o[cb][4 * g + 1], inv),
+                 acc_read_scaled(o[cb][4 * g + 2], inv), acc_read_scaled(o[cb][4 * g + 3], inv)};
+      *(f32x4*)(o_ptr + 32 * cb + 8 * g) = v;
+    }
+  if (hf == 0 && lse_ptr) *lse_ptr = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
+}
+
+// fp32 path: one workgroup per (b, i, split, head); 256 threads.  Logits one token per thread,
+// block-wide max/sum, then each thread accumulates two latent columns over the chunk's tokens.
+// Natural-exp online softmax with the exact rescale at every 256-token chunk.
+__global__ __launch_bounds__(256) void decode_attn_f32_kernel(AttnArgs a) {
+  __shared__ float qs[kRow];
+  __shared__ float ps[256];
+  __shared__ float red[8];
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int h = id % kHeads;
+  const WorkItem w = make_work(a, id / kHeads);
+  const int tid = threadIdx.x;
+  const float* pool = (const float*)a.pool;
+
+  const size_t qrow = ((size_t)w.b * a.S + w.i) * kHeads + h;
+  for (int c = tid; c < kDc; c += 256) qs[c] = ((const float*)a.q_lat)[qrow * kDc + c];
+  if (tid < kDr) qs[kDc + tid] = ((const float*)a.q_pe)[qrow * kDr + tid];
+  __syncthreads();
+
+  const int32_t* bt = a.block_table + (size_t)w.b * a.max_pages;
+  float m_run = -INFINITY, l_run = 0.f, acc0 = 0.f, acc1 = 0.f;
+  for (int start = w.tok_begin; start < w.tok_end; start += 256) {
+    const int tkn = start + tid;
+    float z = -INFINITY;
+    if (tkn < w.tok_end) {
+      const float* row = pool + ((size_t)bt[tkn / kPage] * kPage + tkn % kPage) * kRow;
+      float d = 0.f;
+      for (int c = 0; c < kRow; ++c) d = fmaf(qs[c], row[c], d);
+      z = d * a.scale;
+    }
+    float m = z;
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if ((tid & 63) == 0) red[tid >> 6] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float m_new = fmaxf(m_run, m);
+    const float alpha = expf(m_run - m_new);
+    const float p = tkn < w.tok_end ? expf(z - m_new) : 0.f;
+    ps[tid] = p;
+    float sm = p;
+    for (int off = 32; off > 0; off >>= 1) sm += __shfl_xor(sm, off);
+    __syncthreads();
+    if ((tid & 63) == 0) red[4 + (tid >> 6)] = sm;
+    __syncthreads();
+    l_run = l_run * alpha + (red[4] + red[5] + red[6] + red[7]);
+    acc0 *= alpha;
+    acc1 *= alpha;
+    const int cnt = w.tok_end - start < 256 ? w.tok_end - start : 256;
+    for (int j = 0; j < cnt; ++j) {
+      const int tj = start + j;
+      const float* row = pool + ((size_t)bt[tj / kPage] * kPage + tj % kPage) * kRow;
+      acc0 = fmaf(ps[j], row[tid], acc0);
+      acc1 = fmaf(ps[j], row[tid + 256], acc1);
+    }
+    m_run = m_new;
+    __syncthreads();
+  }
+  float* o_ptr = a.o_out + (w.out_row + h) * kDc;
+  const bool empty = w.tok_end <= w.tok_begin;
+  o_ptr[tid] = empty ? 0.f : acc0 / l_run;
+  o_ptr[tid + 256] = empty ? 0.f : acc1 / l_run;
+  if (tid == 0 && a.lse_out) a.lse_out[w.out_row + h] = empty ? -INFINITY : m_run + logf(l_run);
+}
+
+// Merge the per-split partials of every (b, i, h): lse = log sum_k e^{lse_k},
+// o = sum_k e^{lse_k - lse} o_k.  Empty splits carry lse_k = -inf and weight 0.
+// One workgroup per (row = b*S+i, group of 16 heads); thread = (head, 32-column slice).
+__global__ __launch_bounds__(256) void lse_merge_kernel(const float* __restrict__ o_part,
+                                                        const float* __restrict__ lse_part, float* __restrict__ o_lat,
+                                                        float* __restrict__ lse, int num_splits) {
+  const int row = blockIdx.x >> 3, hg = blockIdx.x & 7;
+  const int h = hg * 16 + (threadIdx.x >> 4);
+  const int c0 = (threadIdx.x & 15) * 32;
+  const size_t base = (size_t)row * num_splits * kHeads + h;  // split k at base + k * kHeads
+  float m = -INFINITY;
+  for (int k = 0; k < num_splits; ++k) m = fmaxf(m, lse_part[base + (size_t)k * kHeads]);
+  f32x4 acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float sum = 0.f;
+  if (m != -INFINITY) {
+    for (int k = 0; k < num_splits; ++k) {
+      const float wk = expf(lse_part[base + (size_t)k * kHeads] - m);
+      if (wk == 0.f) continue;
+      sum += wk;
+      const f32x4* src = (const f32x4*)(o_part + (base + (size_t)k * kHeads) * kDc + c0);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] += wk * src[j];
+    }
+  }
+  const float inv = sum > 0.f ? 1.0f / sum : 0.f;
+  f32x4* dst = (f32x4*)(o_lat + ((size_t)row * kHeads + h) * kDc + c0);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) dst[j] = acc[j] * inv;
+  if ((threadIdx.x & 15) == 0 && lse) lse[(size_t)row * kHeads + h] = m == -INFINITY ? -INFINITY : m + logf(sum);
+}
+
+hipError_t launch_decode_attn(const AttnArgs& a, int rows, hipStream_t stream) {
+  const int nwg = rows * a.num_splits;
+  if (a.dtype_bf16)
+    hipLaunchKernelGGL(decode_attn_bf16_kernel, dim3(nwg), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(decode_attn_f32_kernel, dim3(nwg * kHeads), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_lse_merge(const float* o_part, const float* lse_part, float* o_lat, float* lse, int rows,
+                            int num_splits, hipStream_t stream) {
+  hipLaunchKernelGGL(lse_merge_kernel, dim3(rows * 8), dim3(256), 0, stream, o_part, lse_part, o_lat, lse,
+                     num_splits);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,43 @@
+// Launch interface between the C-ABI host layer and the HIP kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+// Fixed head geometry of the DeepSeek-V2/V3 MLA layer the kernels are specialised for.
+constexpr int kHeads = 128;   // query heads: the M dimension of the attention MFMAs
+constexpr int kDc = 512;      // latent width (kv_lora_rank)
+constexpr int kDr = 64;       // shared RoPE key width
+constexpr int kRow = 576;     // cached row: [c_KV | k_pe]
+constexpr int kDh = 128;      // no-RoPE head dim = value head dim
+constexpr int kPage = 64;     // tokens per cache page
+
+struct AttnArgs {
+  const void* q_lat;           // (B,S,H,512) bf16 or fp32
+  const void* q_pe;            // (B,S,H,64)
+  const void* pool;            // (P,64,576)
+  const int32_t* block_table;  // (B,max_pages)
+  const int32_t* seq_lens;     // (B)
+  float* o_out;                // final o_lat (B,S,H,512), or partials (B*S, splits, H, 512)
+  float* lse_out;              // final lse (B,S,H) (may be null), or partial lse (B*S, splits, H)
+  int B, S, max_pages, pages_per_split, num_splits, causal, final_out, dtype_bf16;
+  float scale;       // softmax scale
+  float scale_log2;  // softmax scale * log2(e)
+};
+
+// decode attention over rows = B*S (b, i) pairs x num_splits page ranges
+hipError_t launch_decode_attn(const AttnArgs& a, int rows, hipStream_t stream);
+// merge of (rows, splits, H) partials into o_lat (rows, H, 512) and lse (rows, H) (lse may be null)
+hipError_t launch_lse_merge(const float* o_part, const float* lse_part, float* o_lat, float* lse, int rows,
+                            int num_splits, hipStream_t stream);
+// q_lat[n,h,:] = W_UK[h] q_nope[n,h,:] for n < tokens
+hipError_t launch_absorb_q(const void* q_nope, const void* w_uk, void* q_lat, int tokens, bool bf16,
+                           hipStream_t stream);
+// out[n,h,:] = W_UV[h]^T o_lat[n,h,:] for n < tokens
+hipError_t launch_out_proj(const float* o_lat, const void* w_uv, void* out, int tokens, bool bf16,
+                           hipStream_t stream);
+
+}  // namespace mla

@@ -1,0 +1,193 @@
+// C-ABI host layer: argument checks (all before any launch), key-split planning, workspace
+// sizing and kernel dispatch.  Allocates nothing, never synchronises.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+
+#include "../../include/mla_latent.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];  // 0 = not queried yet (a cache, not state)
+
+int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+  if (dev < kMaxDevices) {
+    const int cached = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (cached > 0) return cached;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return -1;
+  if (dev < kMaxDevices) g_cu_count[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+mla_status check_params(const mla_params* p) {
+  if (!p) return MLA_ERR_NULL;
+  if (p->dtype != MLA_F32 && p->dtype != MLA_BF16) return MLA_ERR_DTYPE;
+  if (p->num_heads != mla::kHeads || p->kv_lora_rank != mla::kDc || p->rope_dim != mla::kDr ||
+      p->head_dim != mla::kDh || p->page_size != mla::kPage)
+    return MLA_ERR_UNSUPPORTED;
+  if (p->batch < 0 || p->q_len < 1 || p->max_seq_len < 0 || p->max_pages_per_seq < 0) return MLA_ERR_SHAPE;
+  if ((int64_t)p->batch * p->q_len > (int64_t)(1 << 24)) return MLA_ERR_SHAPE;
+  return MLA_OK;
+}
+
+int64_t tokens_of(const mla_params* p) { return (int64_t)p->batch * p->q_len; }
+
+// Split planning: one workgroup per (b, i, split); aim for about one workgroup per compute unit
+// (each holds a CU: 128 heads of accumulators and two 72 KiB LDS tiles) with page-aligned,
+// equal page ranges and no trailing empty split.
+struct SplitPlan {
+  int splits, pages_per_split;
+};
+
+SplitPlan plan_splits(const mla_params* p, int requested, int cus) {
+  const int max_pages = (p->max_seq_len + mla::kPage - 1) / mla::kPage;
+  const int64_t rows = tokens_of(p);
+  int s = requested;
+  if (s <= 0) {
+    if (max_pages <= 1 || rows <= 0) {
+      s = 1;
+    } else {
+      const int64_t want = (cus + rows - 1) / rows;
+      s = (int)(want < max_pages ? want : max_pages);
+      if (s < 1) s = 1;
+    }
+  }
+  if (max_pages == 0) return {1, 1};
+  if (s > max_pages) s = max_pages;
+  const int pps = (max_pages + s - 1) / s;
+  s = (max_pages + pps - 1) / pps;
+  return {s, pps};
+}
+
+size_t workspace_for(const mla_params* p, int splits) {
+  if (splits <= 1) return 0;
+  const size_t n = (size_t)tokens_of(p) * splits * mla::kHeads;
+  return n * mla::kDc * sizeof(float) + n * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_str(mla_status s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_NULL: return "MLA_ERR_NULL: a required pointer is NULL";
+    case MLA_ERR_SHAPE: return "MLA_ERR_SHAPE: a size is out of range";
+    case MLA_ERR_DTYPE: return "MLA_ERR_DTYPE: dtype must be MLA_F32 or MLA_BF16";
+    case MLA_ERR_ALIGN: return "MLA_ERR_ALIGN: pointers must be 16-byte aligned";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace too small";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: only H=128, d_c=512, d_R=64, d_h=128, page 64";
+    case MLA_ERR_LAUNCH: return "MLA_ERR_LAUNCH: kernel launch failed";
+    case MLA_ERR_DEVICE: return "MLA_ERR_DEVICE: no usable HIP device";
+  }
+  return "unknown mla_status";
+}
+
+mla_status mla_absorb_q(const void* q_nope, const void* w_uk, void* q_lat, const mla_params* p, void* stream) {
+  mla_status st = check_params(p);
+  if (st != MLA_OK) return st;
+  if (tokens_of(p) == 0) return MLA_OK;
+  if (!q_nope || !w_uk || !q_lat) return MLA_ERR_NULL;
+  if (!aligned16(q_nope) || !aligned16(w_uk) || !aligned16(q_lat)) return MLA_ERR_ALIGN;
+  if (mla::launch_absorb_q(q_nope, w_uk, q_lat, (int)tokens_of(p), p->dtype == MLA_BF16, (hipStream_t)stream) !=
+      hipSuccess)
+    return MLA_ERR_LAUNCH;
+  return MLA_OK;
+}
+
+int32_t mla_decode_num_splits(const mla_params* p, int32_t num_splits) {
+  mla_status st = check_params(p);
+  if (st != MLA_OK) return st;
+  if (num_splits < 0) return MLA_ERR_SHAPE;
+  const int cus = num_splits > 0 ? 1 : cu_count();
+  if (cus <= 0) return MLA_ERR_DEVICE;
+  return plan_splits(p, num_splits, cus).splits;
+}
+
+size_t mla_decode_workspace_bytes(const mla_params* p, int32_t num_splits) {
+  const int32_t s = mla_decode_num_splits(p, num_splits);
+  return s > 0 ? workspace_for(p, s) : 0;
+}
+
+mla_status mla_decode_attn(const void* q_lat, const void* q_pe, const void* kv_pool, const int32_t* block_table,
+                           const int32_t* seq_lens, float* o_lat, float* lse, void* workspace,
+                           size_t workspace_bytes, int32_t num_splits, const mla_params* p, void* stream) {
+  mla_status st = check_params(p);
+  if (st != MLA_OK) return st;
+  if (num_splits < 0) return MLA_ERR_SHAPE;
+  const int max_pages = (p->max_seq_len + mla::kPage - 1) / mla::kPage;
+  if (p->max_pages_per_seq < max_pages) return MLA_ERR_SHAPE;
+  if (tokens_of(p) == 0) return MLA_OK;
+  if (!q_lat || !q_pe || !seq_lens || !o_lat) return MLA_ERR_NULL;
+  if (max_pages > 0 && (!kv_pool || !block_table)) return MLA_ERR_NULL;
+  if (!aligned16(q_lat) || !aligned16(q_pe) || !aligned16(kv_pool) || !aligned16(o_lat)) return MLA_ERR_ALIGN;
+  if (!std::isfinite(p->softmax_scale)) return MLA_ERR_SHAPE;
+  const int cus = num_splits > 0 ? 1 : cu_count();
+  if (cus <= 0) return MLA_ERR_DEVICE;
+  const SplitPlan plan = plan_splits(p, num_splits, cus);
+  const int64_t grid = tokens_of(p) * plan.splits * (p->dtype == MLA_BF16 ? 1 : mla::kHeads);
+  if (grid > 0x7fffffffLL) return MLA_ERR_SHAPE;
+  const size_t need = workspace_for(p, plan.splits);
+  if (need > 0) {
+    if (!workspace) return MLA_ERR_NULL;
+    if (workspace_bytes < need) return MLA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MLA_ERR_ALIGN;
+  }
+
+  mla::AttnArgs a;
+  a.q_lat = q_lat;
+  a.q_pe = q_pe;
+  a.pool = kv_pool;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.B = p->batch;
+  a.S = p->q_len;
+  a.max_pages = p->max_pages_per_seq;
+  a.pages_per_split = plan.pages_per_split;
+  a.num_splits = plan.splits;
+  a.causal = p->causal ? 1 : 0;
+  a.dtype_bf16 = p->dtype == MLA_BF16;
+  a.scale = p->softmax_scale;
+  a.scale_log2 = (float)((double)p->softmax_scale * 1.4426950408889634);
+  const int rows = (int)tokens_of(p);
+  hipStream_t s = (hipStream_t)stream;
+  if (plan.splits == 1) {
+    a.o_out = o_lat;
+    a.lse_out = lse;
+    a.final_out = 1;
+    if (mla::launch_decode_attn(a, rows, s) != hipSuccess) return MLA_ERR_LAUNCH;
+    return MLA_OK;
+  }
+  float* o_part = (float*)workspace;
+  float* lse_part = o_part + (size_t)rows * plan.splits * mla::kHeads * mla::kDc;
+  a.o_out = o_part;
+  a.lse_out = lse_part;
+  a.final_out = 0;
+  if (mla::launch_decode_attn(a, rows, s) != hipSuccess) return MLA_ERR_LAUNCH;
+  if (mla::launch_lse_merge(o_part, lse_part, o_lat, lse, rows, plan.splits, s) != hipSuccess) return MLA_ERR_LAUNCH;
+  return MLA_OK;
+}
+
+mla_status mla_out_proj(const float* o_lat, const void* w_uv, void* out, const mla_params* p, void* stream) {
+  mla_status st = check_params(p);
+  if (st != MLA_OK) return st;
+  if (tokens_of(p) == 0) return MLA_OK;
+  if (!o_lat || !w_uv || !out) return MLA_ERR_NULL;
+  if (!aligned16(o_lat) || !aligned16(w_uv) || !aligned16(out)) return MLA_ERR_ALIGN;
+  if (mla::launch_out_proj(o_lat, w_uv, out, (int)tokens_of(p), p->dtype == MLA_BF16, (hipStream_t)stream) !=
+      hipSuccess)
+    return MLA_ERR_LAUNCH;
+  return MLA_OK;
+}
+
+}  // extern "C"

@@ -221,3 +221,17 @@ def small_workload(batch: int, q_len: int, cache_len=None, *, dtype: str = "bf16
     """A reduced-size workload with the real head dims (for parity at oracle-friendly sizes)."""
     return DecodeWorkload(name, batch=batch, q_len=q_len, cache_len=cache_len, dtype=dtype, paged=paged,
                           ragged=ragged)
+
+
+def generate_latent(w: DecodeWorkload, seed: int):
+    """Stand-alone inputs for the attention and output-projection calls.
+
+    Returns (q_lat, o_lat): q_lat (B,S,H,d_c) with the variance an absorbed query has
+    (d_h · 1/d_c = 1/4), rounded to the workload dtype; o_lat (B,S,H,d_c) fp32 N(0,1),
+    the latent output the projection consumes.  Drawn from ``default_rng(seed)``.
+    """
+    rng = np.random.default_rng(seed)
+    shape = (w.batch, w.q_len, w.heads, w.kv_lora_rank)
+    q_lat = rng.standard_normal(shape, dtype=np.float32) * np.float32(math.sqrt(w.head_dim / w.kv_lora_rank))
+    o_lat = rng.standard_normal(shape, dtype=np.float32)
+    return _cast(q_lat, w.dtype), o_lat

@@ -1,0 +1,146 @@
+/*
+ * mla_latent.h — absorbed Multi-head Latent Attention (MLA) decode on MI355X (gfx950).
+ *
+ * One decode step of one MLA layer, as three enqueue-only calls:
+ *
+ *   mla_absorb_q     q_lat = W_UK^T q_nope   per head (the no-RoPE query moved into the
+ *                    512-d latent space, so per-head keys are never built)
+ *   mla_decode_attn  softmax over the cached context of scale*(q_lat.c_j + q_pe.k_pe_j),
+ *                    reduced to a latent output o_lat = sum_j p_j c_j, plus its log-sum-exp
+ *   mla_out_proj     out = W_UV^T o_lat      per head (values are never built)
+ *
+ * The method: "DeepSeek-V2的推理成本如何计算？" (izhida.com), answer "专家" — W_K is applied
+ * transposed to q and W_V after the latent attention-weighted average, so neither K nor V is
+ * computed; RoPE is a separate key shared by all heads whose score is added to the latent
+ * score. Shapes and computation order: "【笔记】MLA矩阵吸收分析" (wkq9411.github.io), §二.2
+ * (order 2: (b,s,h,k) query, (b,h,s,t) scores) and §三.2 (order 2: (b,h,s,k) latent output,
+ * then W_UV). The three calls are the BMM -> Attn -> BMM span of the decode stages listed in
+ * "Lower latency and higher throughput with multi-node DeepSeek deployment" (Perplexity),
+ * section "Наложение вычислений и взаимодействия", with kv_b_proj split into a K part and a
+ * V part (section "Слой MLA") and a paged cache addressed through a page table (same
+ * section).
+ *
+ * Conventions for every call
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library allocates and
+ *     frees nothing, never synchronises, and keeps no mutable global state (it caches the
+ *     device's compute-unit count once per device). Each call only enqueues kernels on
+ *     `stream` (a hipStream_t; NULL = the default stream), so calls are thread-safe and can be
+ *     captured into a HIP graph.
+ *   - Layouts are dense row-major with the last index fastest, exactly as the comments give.
+ *   - Every condition the host can check is checked BEFORE any launch; on failure the call
+ *     returns a negative mla_status, enqueues nothing and writes nothing.
+ *   - Supported dims: num_heads 128, kv_lora_rank 512, rope_dim 64, head_dim 128,
+ *     page_size 64. Other values give MLA_ERR_UNSUPPORTED.
+ *   - Pointers must be 16-byte aligned (MLA_ERR_ALIGN).
+ *   - Device-side preconditions (not checked; violating them is undefined behaviour):
+ *     0 <= seq_lens[b] <= max_seq_len; block_table[b][p] in [0, num_pages) for every page p
+ *     that holds one of the first seq_lens[b] tokens. With causal and q_len S, query i sees
+ *     the first seq_lens[b] - S + i + 1 tokens (fewer than one: an empty set).
+ *   - An empty key set yields o_lat = 0 and lse = -inf.
+ */
+#ifndef MLA_LATENT_H_
+#define MLA_LATENT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL = -1,        /* a required pointer is NULL */
+  MLA_ERR_SHAPE = -2,       /* a size is out of range (batch < 0, q_len < 1, tables too small ...) */
+  MLA_ERR_DTYPE = -3,       /* dtype is not MLA_F32 or MLA_BF16 */
+  MLA_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
+  MLA_ERR_WORKSPACE = -5,   /* workspace smaller than mla_decode_workspace_bytes() */
+  MLA_ERR_UNSUPPORTED = -6, /* head dims / page size other than the supported set */
+  MLA_ERR_LAUNCH = -7,      /* the HIP runtime rejected a launch */
+  MLA_ERR_DEVICE = -8       /* no usable HIP device */
+} mla_status;
+
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
+
+typedef struct {
+  int32_t batch;             /* B >= 0 sequences */
+  int32_t q_len;             /* S >= 1 query tokens per sequence (2 = MTP / speculative verify) */
+  int32_t num_heads;         /* H = 128 */
+  int32_t kv_lora_rank;      /* d_c = 512: latent width */
+  int32_t rope_dim;          /* d_R = 64: shared RoPE key width */
+  int32_t head_dim;          /* d_h = 128: no-RoPE query/key width and value width */
+  int32_t page_size;         /* 64 tokens per cache page */
+  int32_t max_pages_per_seq; /* row stride of block_table (>= ceil(max_seq_len / page_size)) */
+  int32_t max_seq_len;       /* host-known upper bound on seq_lens[]: sizes the grid, no D2H copy */
+  float softmax_scale;       /* multiplies the whole logit (latent + RoPE parts), e.g. 1/sqrt(192) */
+  int32_t causal;            /* 1: query i of S sees seq_lens[b] - S + i + 1 keys; 0: all keys */
+  mla_dtype dtype;           /* of q_nope, q_pe, q_lat, cache, W_UK, W_UV, out; accumulation is fp32 */
+} mla_params;
+
+/*
+ * q_lat[b,s,h,c] = sum_d W_UK[h,c,d] * q_nope[b,s,h,d]
+ *   q_nope (B,S,H,d_h)  dtype         — no-RoPE query
+ *   w_uk   (H,d_c,d_h)  dtype         — key up-projection, head-major
+ *   q_lat  (B,S,H,d_c)  dtype (out)   — absorbed query; fp32 accumulation, rounded once
+ * Cites: izhida answer "专家" (W_K applied transposed to q); absorption note §二.2 step 2.
+ */
+mla_status mla_absorb_q(const void* q_nope, const void* w_uk, void* q_lat, const mla_params* p,
+                        void* stream);
+
+/*
+ * Bytes of scratch memory mla_decode_attn needs for `num_splits` (0 = the library's choice),
+ * 0 when the call needs none. Returns 0 as well for an invalid `p` (the call will reject it).
+ */
+size_t mla_decode_workspace_bytes(const mla_params* p, int32_t num_splits);
+
+/*
+ * Number of key splits mla_decode_attn uses for `num_splits` (0 = the library's choice);
+ * returns a negative mla_status for an invalid `p`.
+ */
+int32_t mla_decode_num_splits(const mla_params* p, int32_t num_splits);
+
+/*
+ * Latent-space attention over a paged cache.
+ *   q_lat       (B,S,H,d_c)        dtype   absorbed query (from mla_absorb_q)
+ *   q_pe        (B,S,H,d_R)        dtype   RoPE query, already rotated
+ *   kv_pool     (P,page,d_c+d_R)   dtype   cache pages; row = [c_KV (d_c) | k_pe (d_R)]
+ *   block_table (B,max_pages_per_seq) int32  token j of sequence b lives in page
+ *                                         block_table[b][j / page] at slot j % page
+ *   seq_lens    (B)                int32   L_b = cached tokens of sequence b (the S new ones included)
+ *   o_lat       (B,S,H,d_c)        fp32 (out)  sum_j p_j c_j
+ *   lse         (B,S,H)            fp32 (out, may be NULL)  natural-log log-sum-exp of the
+ *                                         scaled logits
+ *   workspace / workspace_bytes           scratch of at least mla_decode_workspace_bytes()
+ *                                         (may be NULL when that is 0); contents are scratch
+ *   num_splits                            0 = library's choice; k > 0 splits every sequence's
+ *                                         keys into k contiguous page ranges, each reduced
+ *                                         separately and merged by log-sum-exp. Results for a
+ *                                         fixed split count are bitwise reproducible.
+ * Cites: izhida answer "DeepSeek" (per head a 512-d latent and a 64-d RoPE inner product and a
+ * weighted sum over the 512-d latent, per cached token) and answer "专家"; cache row of 576
+ * per layer (same answer; Perplexity post, section "Одноузловое против многоузлового").
+ */
+mla_status mla_decode_attn(const void* q_lat, const void* q_pe, const void* kv_pool,
+                           const int32_t* block_table, const int32_t* seq_lens, float* o_lat,
+                           float* lse, void* workspace, size_t workspace_bytes, int32_t num_splits,
+                           const mla_params* p, void* stream);
+
+/*
+ * out[b,s,h,v] = sum_c o_lat[b,s,h,c] * W_UV[h,c,v]
+ *   o_lat (B,S,H,d_c)  fp32          — latent attention output (from mla_decode_attn)
+ *   w_uv  (H,d_c,d_h)  dtype         — value up-projection, head-major
+ *   out   (B,S,H,d_h)  dtype (out)   — per-head attention output (before W_O)
+ * Cites: izhida answer "专家" (W_V applied after the latent average) and the same answer's
+ * batched GEMV whose cost is reading W_V; absorption note §三.2 step 2.
+ */
+mla_status mla_out_proj(const float* o_lat, const void* w_uv, void* out, const mla_params* p,
+                        void* stream);
+
+/* Static string for a status code (never NULL). */
+const char* mla_status_str(mla_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_LATENT_H_ */

@@ -1,0 +1,65 @@
+"""Shared test helpers: device upload of generated inputs, error metric, header parsing."""
+import os
+import re
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_latent.h")
+
+BF16_TOL = 2e-2  # max |gpu - ref| / max |ref|, bf16 inputs with fp32 accumulation
+F32_TOL = 1e-4   # same metric, fp32 inputs
+
+
+def declared_functions(path: str = HEADER):
+    """Names of the functions the C header declares."""
+    src = open(path).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(mla_[a-z_0-9]+)\s*\(", src,
+                                 flags=re.M)))
+
+
+def rel_err(gpu, ref) -> float:
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
+    den = np.max(np.abs(ref)) if ref.size else 1.0
+    return float(np.max(np.abs(gpu - ref)) / max(den, 1e-30)) if ref.size else 0.0
+
+
+def tol_for(x) -> float:
+    return BF16_TOL if x.is_bf16 else F32_TOL
+
+
+def to_device(x, device="cuda"):
+    """Upload a DecodeInputs batch (bf16 as bit-exact torch.bfloat16)."""
+    import torch
+
+    def conv(a):
+        if x.is_bf16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+    return dict(q_nope=conv(x.q_nope), q_pe=conv(x.q_pe), w_uk=conv(x.w_uk), w_uv=conv(x.w_uv),
+                pool=conv(x.pool), block_table=torch.from_numpy(x.block_table).to(device),
+                seq_lens=torch.from_numpy(x.seq_lens).to(device))
+
+
+def device_array(x, dtype_bf16: bool, device="cuda"):
+    import torch
+    if dtype_bf16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
+
+
+def to_host(t) -> np.ndarray:
+    return t.float().cpu().numpy()
+
+
+def params_for(x, **kw):
+    from deepseek_mla_latent_amd import binding
+    w = x.workload
+    return binding.make_params(batch=w.batch, q_len=w.q_len, max_seq_len=x.max_seq_len,
+                               max_pages_per_seq=x.block_table.shape[1], softmax_scale=w.softmax_scale,
+                               causal=kw.get("causal", True),
+                               dtype=binding.MLA_BF16 if x.is_bf16 else binding.MLA_F32)
