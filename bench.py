@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Absorbed-MLA decode throughput on one MI355X.
+
+One step = one pass of the whole decode path over one batch: mla_absorb_q -> mla_decode_attn
+(split-K attention + log-sum-exp merge) -> mla_out_proj, for one layer.  Default workload: batch 32
+sequences x 1 query token, 128 heads, d_c 512, d_R 64, d_h 128, 4096 cached tokens each (bf16,
+contiguous cache = identity page table).  Inputs are seeded synthetic data already resident in HBM.
+
+Timing: the three calls of each step are captured in a HIP graph (one graph per input replica);
+`--warmup` untimed replays, then `--steps` timed replays bracketed by torch.cuda.synchronize().
+Replicas rotate so consecutive steps touch disjoint buffers whose total exceeds twice the 256 MB
+Infinity Cache, so cache rows really come from HBM.  Separately, the same steps run eagerly with
+HIP events around each call (on the stream the kernels are launched on) to give per-call launch
+durations; the dominant call's algorithmic bytes over that duration is the roofline figure.
+
+Prints one JSON line.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_attn_b32_t4096_hbm_counters.json")
+ATTN_SOURCE = os.path.join(ROOT, "deepseek_mla_latent_amd", "csrc", "decode_attn.hip")
+METRIC = "MLA absorbed-decode tokens/s per layer + % of HBM/MFMA roofline, 1 GPU"
+MALL_BYTES = 256 * 2 ** 20
+
+
+def _rank_env():
+    return int(os.environ.get("WORLD_SIZE", "1")), int(os.environ.get("RANK", "0"))
+
+
+def _source_hash() -> str:
+    return hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(launch_bytes_key: str):
+    """HBM bytes per launch from committed rocprofv3 counters, if taken on the current kernel source."""
+    try:
+        rec = json.load(open(COUNTERS_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != _source_hash():
+        return None
+    return rec.get(launch_bytes_key)
+
+
+def cpu_baseline(x, target_seconds: float):
+    """The fp64 oracle (non-absorbed route) on a bounded sample: the first n sequences, all heads."""
+    import numpy as np
+    from oracle import mla_decode as ref
+
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"] or [cores])
+    except Exception:
+        pass
+    w = x.workload
+    q_nope, q_pe, w_uk, w_uv = x.f32("q_nope"), x.f32("q_pe"), x.f32("w_uk"), x.f32("w_uv")
+    pool = x.f32("pool")
+    t0 = time.perf_counter()
+    n = 0
+    while n < w.batch:
+        ref.mla_decode_nonabsorbed(q_nope, q_pe, w_uk, w_uv, pool, x.block_table, x.seq_lens,
+                                   softmax_scale=w.softmax_scale, seqs=[n])
+        n += 1
+        el = time.perf_counter() - t0
+        if el * (n + 1) / n > target_seconds:
+            break
+    el = time.perf_counter() - t0
+    return {"value": n * w.q_len / el, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n} of {w.batch} sequences x all {w.heads} heads x {w.q_len} query token(s) at "
+                      f"{int(x.seq_lens[0])} cached tokens, fp64 non-absorbed numpy, {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="b32_t4096")
+    ap.add_argument("--num-splits", type=int, default=0, help="0 = library's choice")
+    ap.add_argument("--replicas", type=int, default=0, help="0 = enough to exceed 2x the 256 MB MALL")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one device copy of this size first (counter calibration under rocprofv3)")
+    args = ap.parse_args()
+
+    world, rank = _rank_env()
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this decode path has no multi-GPU mode "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from deepseek_mla_latent_amd import accounting, binding
+    from deepseek_mla_latent_amd import inputs as gen
+
+    binding.load_library()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    w = gen.WORKLOADS[args.workload]
+    x = gen.generate_named(args.workload)
+    dt = "bf16" if x.is_bf16 else "f32"
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if x.is_bf16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    costs = accounting.path_costs(x.seq_lens, w.q_len, dt)
+    per_replica = sum(c.bytes for c in costs)
+    R = args.replicas or max(2, math.ceil(2 * MALL_BYTES / per_replica) + 1)
+
+    if args.copy_probe_mib:
+        src = torch.empty(args.copy_probe_mib * 2 ** 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    params = binding.make_params(batch=w.batch, q_len=w.q_len, max_seq_len=x.max_seq_len,
+                                 max_pages_per_seq=x.block_table.shape[1], softmax_scale=w.softmax_scale,
+                                 dtype=binding.MLA_BF16 if x.is_bf16 else binding.MLA_F32)
+    splits = binding.mla_decode_num_splits(params, args.num_splits)
+    reps = []
+    for _ in range(R):
+        d = dict(q_nope=up(x.q_nope), q_pe=up(x.q_pe), w_uk=up(x.w_uk), w_uv=up(x.w_uv), pool=up(x.pool),
+                 bt=torch.from_numpy(x.block_table).to(dev), lens=torch.from_numpy(x.seq_lens).to(dev))
+        d["bufs"] = binding.DecodeBuffers(params, args.num_splits, device=dev)
+        reps.append(d)
+
+    def run(d, stream=None):
+        d["bufs"].run(d["q_nope"], d["q_pe"], d["w_uk"], d["w_uv"], d["pool"], d["bt"], d["lens"], stream)
+
+    # graphs: one per replica, captured after an eager warm-up on a side stream
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for d in reps:
+            run(d)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for d in reps:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run(d)
+        graphs.append(g)
+
+    for k in range(args.warmup):
+        graphs[k % R].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        graphs[k % R].replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    # per-call launch durations: eager steps with HIP events on the launch stream
+    stream = torch.cuda.current_stream()
+    n_ev = max(20, min(args.steps, 200))
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_ev)]
+    for k in range(min(R, 4)):
+        run(reps[k % R])
+    torch.cuda.synchronize()
+    for k in range(n_ev):
+        d = reps[k % R]
+        p = d["bufs"]
+        e = evs[k]
+        e[0].record(stream)
+        binding.mla_absorb_q(d["q_nope"], d["w_uk"], p.q_lat, params)
+        e[1].record(stream)
+        binding.mla_decode_attn(p.q_lat, d["q_pe"], d["pool"], d["bt"], d["lens"], p.o_lat, p.lse, p.workspace,
+                                args.num_splits, params)
+        e[2].record(stream)
+        binding.mla_out_proj(p.o_lat, d["w_uv"], p.out, params)
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    call_us = [float(np.mean([evs[k][j].elapsed_time(evs[k][j + 1]) for k in range(n_ev)])) * 1e3 for j in range(3)]
+
+    tokens = w.batch * w.q_len
+    attn = costs[1]
+    attn_s = call_us[1] * 1e-6
+    achieved = attn.bytes / attn_s / 1e9
+    traffic = measured_traffic("hbm_bytes_per_launch")
+    t_roof = sum(c.roof_seconds(dt) for c in costs)
+    rec = {
+        "metric": METRIC,
+        "value": tokens / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic (seeded N(0,1) cache and queries, N(0,1/512) weights)",
+        "config": {"workload": args.workload, "batch": w.batch, "q_len": w.q_len,
+                   "cache_len": int(x.seq_lens.max()), "heads": w.heads, "kv_lora_rank": w.kv_lora_rank,
+                   "rope_dim": w.rope_dim, "head_dim": w.head_dim, "page_size": w.page_size,
+                   "num_splits": splits, "replicas": R, "graph_replay": True},
+        "roofline": {"kernel": "mla_decode_attn (split attention + LSE merge)", "bound": attn.bound(dt),
+                     "achieved": achieved, "peak": accounting.HBM_PEAK_BYTES_S / 1e9, "unit": "GB/s",
+                     "frac": achieved * 1e9 / accounting.HBM_PEAK_BYTES_S, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": attn.bytes, "launch_us": call_us[1]},
+        "path_roofline": {"t_roof_us": t_roof * 1e6, "t_step_us": ms_per_step * 1e3,
+                          "frac": t_roof / (ms_per_step * 1e-3),
+                          "calls_us": dict(zip([c.name for c in costs], call_us)),
+                          "calls_roof_us": {c.name: c.roof_seconds(dt) * 1e6 for c in costs}},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(gen.generate_named(args.workload), args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

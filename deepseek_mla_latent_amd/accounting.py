@@ -1,0 +1,61 @@
+"""Algorithmic bytes and FLOPs of the three decode calls, and MI355X roofline times.
+
+"Algorithmic" means what the method itself must move and compute: every cached row read once,
+weights read once, inputs read and outputs written once.  Implementation overhead (split-K
+partials, LDS re-reads, redundant loads) is excluded on purpose, so achieved/peak is an honest
+fraction of the hardware limit.
+
+* absorb_q:  W_UK + q_nope + q_lat;  2·T·H·d_c·d_h FLOPs (T = B·S tokens)
+* decode_attn: cache L_b·(d_c+d_R)·e for every sequence, q_lat + q_pe, block-table entries of the
+  used pages + lengths (int32), o_lat + lse written in fp32;  2·H·(d_c + d_R + d_c) FLOPs per
+  visible (query, key) pair — twice the per-token multiply-accumulate count of the izhida answer
+  "DeepSeek" ("DeepSeek-V2的推理成本如何计算？": 128×(512+64+512) per cached token).
+* out_proj:  W_UV + o_lat (fp32) + out;  2·T·H·d_c·d_h FLOPs.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Sequence
+
+HBM_PEAK_BYTES_S = 8.0e12  # MI355X HBM3E
+MFMA_PEAK_FLOPS = {"bf16": 2.5e15, "f32": 157.3e12}  # dense MFMA
+
+
+@dataclass
+class CallCost:
+    name: str
+    bytes: int
+    flops: int
+
+    def roof_seconds(self, dtype: str) -> float:
+        return max(self.bytes / HBM_PEAK_BYTES_S, self.flops / MFMA_PEAK_FLOPS[dtype])
+
+    def bound(self, dtype: str) -> str:
+        return "hbm" if self.bytes / HBM_PEAK_BYTES_S >= self.flops / MFMA_PEAK_FLOPS[dtype] else "mfma"
+
+
+def visible_pairs(seq_lens: Sequence[int], q_len: int, causal: bool = True) -> int:
+    pairs = 0
+    for L in seq_lens:
+        L = int(L)
+        for i in range(q_len):
+            n = L - q_len + i + 1 if causal else L
+            pairs += max(0, min(L, n))
+    return pairs
+
+
+def path_costs(seq_lens: Sequence[int], q_len: int, dtype: str, *, heads: int = 128, d_c: int = 512,
+               d_r: int = 64, d_h: int = 128, page: int = 64, causal: bool = True):
+    e = 2 if dtype == "bf16" else 4
+    B = len(seq_lens)
+    T = B * q_len
+    absorb = CallCost("mla_absorb_q", heads * d_c * d_h * e + T * heads * (d_h + d_c) * e,
+                      2 * T * heads * d_c * d_h)
+    cache = sum(int(L) for L in seq_lens) * (d_c + d_r) * e
+    tables = sum(-(-int(L) // page) for L in seq_lens) * 4 + B * 4
+    attn = CallCost("mla_decode_attn",
+                    cache + T * heads * (d_c + d_r) * e + tables + T * heads * (d_c + 1) * 4,
+                    2 * heads * (d_c + d_r + d_c) * visible_pairs(seq_lens, q_len, causal))
+    out = CallCost("mla_out_proj", heads * d_c * d_h * e + T * heads * d_c * 4 + T * heads * d_h * e,
+                   2 * T * heads * d_c * d_h)
+    return [absorb, attn, out]

@@ -9,12 +9,12 @@
 // (RoPE as a shared-key MQA whose score is added). Scores and the weighted sum are steps 3 and 1
 // of order 2 in "【笔记】MLA矩阵吸收分析" §二.2 and §三.2.
 //
-// bf16 kernel layout (one workgroup = 4 waves = 128 heads of one (b, i), one contiguous range of
-// cache pages):
-//   * each 64-token page is copied HBM -> LDS by direct-to-LDS loads (16 B per lane, no register
-//     staging) into one of two buffers, so page t+1 streams in while page t is computed;
-//   * the LDS tile is XOR-swizzled in 16-byte units so both read patterns below are spread over
-//     the banks;
+// bf16 kernel (one workgroup = 4 waves = 128 heads of one (b, i), one contiguous page range):
+//   * the key range is walked in tiles of 32 tokens (half a page).  Tiles stream HBM -> LDS by
+//     direct-to-LDS loads (16 B per lane, no register staging) into a ring of 4 LDS buffers,
+//     three tiles ahead of the one being computed, so about 100 KiB per CU are in flight;
+//   * each LDS tile is XOR-swizzled in 16-byte units so both read patterns below are free of
+//     bank conflicts;
 //   * scores are computed transposed, S^T = tile * Q^T, on 32x32x16 bf16 MFMAs: the tile is the
 //     A operand (ds_read_b128), the wave's 32 heads' [q_lat | q_pe] stay in registers as the B
 //     operand.  The accumulator layout then gives every lane one head and 16 tokens, which is
@@ -25,18 +25,23 @@
 //     rescaled) when a tile's max exceeds it by more than 2^8, which keeps exp2 arguments <= 8
 //     and skips almost every rescale of the 256 accumulator registers.
 // Long contexts are split into page ranges (split-K over tokens); each range writes a normalised
-// partial (o_k, lse_k) and mla_lse_merge combines them.
+// partial (o_k, lse_k) and lse_merge_kernel combines them.
 #include "common.h"
 #include "kernels.h"
 
 namespace mla {
 
-constexpr int kTile = kPage;                          // tokens per LDS tile = one cache page
+constexpr int kTile = 32;                             // tokens per LDS tile (half a page)
 constexpr int kUnitsA = kDc / 8;                      // 16-byte units of c_KV per token (64)
 constexpr int kUnitsB = kDr / 8;                      // 16-byte units of k_pe per token (8)
-constexpr int kRegionA = kTile * kUnitsA * 16;        // 65536 B: c_KV part of a tile
-constexpr int kBufBytes = kRegionA + kTile * kUnitsB * 16;  // 73728 B per tile buffer
+constexpr int kRegionA = kTile * kUnitsA * 16;        // 32768 B: c_KV part of a tile
+constexpr int kBufBytes = kRegionA + kTile * kUnitsB * 16;  // 36864 B per tile buffer
+constexpr int kNumBufs = 4;                           // LDS ring: tile t lives in buffer t % 4
+constexpr int kAhead = kNumBufs - 1;                  // tiles in flight ahead of the computed one
+constexpr int kDmaPerTile = 9;                        // direct-to-LDS loads per wave per tile
 constexpr float kRescaleSlack = 8.0f;                 // log2 units
+
+__device__ __forceinline__ uint32_t lds_addr(const MLA_LDS char* p) { return (uint32_t)(uintptr_t)p; }
 
 // Swizzle: 16-byte unit u of token t is stored at unit (u ^ swz(t)) of the token's LDS row.
 // Region A (64 units per row): bit-rotated low 4 bits of t, so 16 consecutive tokens at one unit
@@ -46,31 +51,24 @@ __device__ __forceinline__ int swz_b(int t) { return (t >> 1) & 7; }
 __device__ __forceinline__ int off_a(int t, int u) { return (t * kUnitsA + (u ^ swz_a(t))) * 16; }
 __device__ __forceinline__ int off_b(int t, int u) { return kRegionA + (t * kUnitsB + (u ^ swz_b(t))) * 16; }
 
-// Copy one page (cnt valid tokens, 1..64) into an LDS tile buffer.  Each direct-to-LDS load
-// writes 64 lanes x 16 B contiguously, so each instruction fills one token's 1 KiB c_KV row
-// (region A) or the 128 B k_pe rows of 8 tokens (region B); a lane fetches the global unit that
-// belongs at its swizzled slot.  Tokens past cnt re-read token 0 (always valid), so LDS never
-// holds bytes from outside the sequence; their scores are masked.
-__device__ __forceinline__ void issue_tile(MLA_LDS char* buf, const uint16_t* page_base, int cnt, int wave,
-                                           int lane) {
-#pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const int t = wave * 16 + k;
-    const int ts = t < cnt ? t : 0;
-    const int u = lane ^ swz_a(t);
-    const uint16_t* src = page_base + ts * kRow + u * 8;
-    __builtin_amdgcn_global_load_lds((const MLA_GLOBAL void*)src, (MLA_LDS void*)(buf + t * 1024), 16, 0, 0);
-  }
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int j = wave * 2 + k;
-    const int t = j * 8 + (lane >> 3);
-    const int ts = t < cnt ? t : 0;
-    const int u = (lane & 7) ^ swz_b(t);
-    const uint16_t* src = page_base + ts * kRow + kDc + u * 8;
-    __builtin_amdgcn_global_load_lds((const MLA_GLOBAL void*)src, (MLA_LDS void*)(buf + kRegionA + j * 1024), 16,
-                                     0, 0);
-  }
+// Direct-to-LDS load of 16 bytes per lane: lane l's bytes land at LDS address lds + 16 l.
+// Issued from asm: the compiler models this instruction as pending in the LDS counter as well,
+// which would turn every LDS operand wait of the tile computed meanwhile into a full drain.  It
+// has no register outputs; completion is awaited explicitly (dma_wait_tiles) before the barrier
+// that publishes a tile.  M0 is not otherwise used by this kernel.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory");
+}
+// Wait until at most `younger` tiles' loads (kDmaPerTile each) of this wave are still in flight.
+// Vector-memory loads complete in order, so this retires every older tile; loads the compiler
+// issues itself only ever make the wait stricter.
+__device__ __forceinline__ void dma_wait_tiles(int younger) {
+  if (younger >= 2)
+    asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+  else if (younger == 1)
+    asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // The 256 O accumulators live in AGPRs and are otherwise only touched by MFMAs.  The two VALU
@@ -97,6 +95,28 @@ __device__ __forceinline__ float acc_read_scaled(float x, float scale) {
   asm volatile("v_accvgpr_read_b32 %0, %1\n\tv_mul_f32 %0, %0, %2" : "=&v"(tmp) : "a"(x), "v"(scale));
   return tmp;
 }
+
+// MFMAs of the main loop are issued from asm volatile statements with a memory clobber: the
+// compiler keeps them in program order and cannot move the LDS operand loads (ordinary builtins,
+// whose waits it still inserts exactly) across them, so the software pipeline below is executed
+// as written.  Being opaque, these statements also hide hazards from the compiler; the few that
+// matter are handled explicitly:
+//   * VALU write -> MFMA source read needs 2 wait states: the first score MFMA takes SrcC = 0
+//     (no VALU zeroing) and P goes through pin_after_valu() before use;
+//   * MFMA result -> VALU read needs more than 11 wait states: scores go through
+//     wait_mfma_result(), O through acc_wait_mfma();
+//   * dependent accumulation chains (same SrcC/Dst) need none.
+__device__ __forceinline__ void mfma_first_v(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b) : "memory");
+}
+__device__ __forceinline__ void mfma_acc_v(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b) : "memory");
+}
+__device__ __forceinline__ void mfma_acc_a(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b) : "memory");
+}
+__device__ __forceinline__ void wait_mfma_result(f32x16& d) { asm volatile("s_nop 15\n\ts_nop 3" : "+v"(d)); }
+__device__ __forceinline__ void pin_after_valu(bf16x8& x, bf16x8& y) { asm volatile("s_nop 1" : "+v"(x), "+v"(y)); }
 
 __device__ __forceinline__ bf16x8 lds_read_b128(const MLA_LDS char* p) { return *(const MLA_LDS bf16x8*)p; }
 
@@ -136,8 +156,9 @@ __device__ __forceinline__ WorkItem make_work(const AttnArgs& a, int id) {
 }
 
 __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * kBufBytes];
-  MLA_LDS char* smem = (MLA_LDS char*)smem_raw;
+  __shared__ __attribute__((aligned(1024))) char lds_raw[kNumBufs * kBufBytes];
+  __shared__ int lds_pages[kMaxSplitPages];
+  MLA_LDS char* const smem = (MLA_LDS char*)lds_raw;
 
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   const WorkItem w = make_work(a, id);
@@ -163,7 +184,42 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
   const int32_t* bt = a.block_table + (size_t)w.b * a.max_pages + w.tok_begin / kPage;
   const uint16_t* pool = (const uint16_t*)a.pool;
 
-  issue_tile(smem, pool + (size_t)bt[0] * kPage * kRow, ntok < kTile ? ntok : kTile, wave, lane);
+  // The range's page ids are staged in LDS once (at most kMaxSplitPages; the host sizes splits
+  // accordingly), so the loop reads them with ds_read + readfirstlane.  A global load in the
+  // loop would make the compiler drain the vector-memory counter, i.e. wait for the tiles in
+  // flight; a scalar load would share the LDS counter and make every operand wait a full drain.
+  const int npages = (ntok + kPage - 1) / kPage;
+  for (int j = threadIdx.x; j < npages; j += 256) lds_pages[j] = bt[j];
+  __syncthreads();
+  auto tile_src = [&](int t) -> const uint16_t* {  // first token row of tile t (t < ntiles)
+    const int page = __builtin_amdgcn_readfirstlane(lds_pages[t >> 1]);
+    return pool + ((size_t)page * kPage + (t & 1) * kTile) * kRow;
+  };
+  auto tile_count = [&](int t) { return ntok - t * kTile < kTile ? ntok - t * kTile : kTile; };
+
+  // One step of copying tile `t` (cnt valid tokens, rows from `src`) into LDS buffer `dst`:
+  // steps 0-7 fill this wave's 8 tokens' 1 KiB c_KV rows (region A), step 8 the 128 B k_pe rows
+  // of 8 tokens (region B).  Tokens past cnt re-read token 0 (always valid), so LDS never holds
+  // bytes from outside the sequence; their scores are masked.
+  auto dma_step = [&](const uint16_t* src, int cnt, uint32_t dst, int k, int lane_v) {
+    if (k < 8) {
+      const int t = wave * 8 + k;
+      const int ts = t < cnt ? t : 0;
+      dma16(src + ts * kRow + (lane_v ^ swz_a(t)) * 8, dst + t * 1024);
+    } else {
+      const int t = wave * 8 + (lane_v >> 3);
+      const int ts = t < cnt ? t : 0;
+      dma16(src + ts * kRow + kDc + ((lane_v & 7) ^ swz_b(t)) * 8, dst + kRegionA + wave * 1024);
+    }
+  };
+  // Prologue: tiles 0 .. kAhead-1.
+  for (int t = 0; t < kAhead && t < ntiles; ++t) {
+    const uint16_t* src = tile_src(t);
+    const int cnt = tile_count(t);
+    const uint32_t dst = lds_addr(smem) + t * kBufBytes;
+#pragma unroll
+    for (int k = 0; k < kDmaPerTile; ++k) dma_step(src, cnt, dst, k, lane);
+  }
 
   // This lane's head, as the B operand of the score MFMA: q[ks] = [q_lat | q_pe][16 ks + 8 hf .. +7].
   bf16x8 q[36];
@@ -175,14 +231,22 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
     for (int ks = 0; ks < 32; ++ks) q[ks] = ql[2 * ks];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) q[32 + ks] = qp[2 * ks];
+    // Wait for q here, once: otherwise the loop inherits "q may be in flight" and carries
+    // vector-memory waits that the in-flight tile loads would then trip.
+#pragma unroll
+    for (int ks = 0; ks < 36; ++ks) asm volatile("" ::"v"(q[ks]));
   }
 
-  // Per-lane LDS byte offsets (within a tile buffer) of the swizzled reads; see the loops below.
+  // Per-lane LDS byte offsets of the swizzled reads in the current tile's buffer; advanced by one
+  // buffer per tile.  score step r (r < 32): qk_a[r % 8] + 256 (r / 8); (r >= 32): qk_b[r - 32].
+  // sum step m: latent block cb = m / 2, token step kk = m % 2 -> pv_lo/hi[cb % 4] + 256 (cb / 4)
+  // + 16384 kk.  All immediates stay below 64 KiB.
+  const int base0 = 0;  // offsets are relative to smem
   int qk_a[8], qk_b[4], pv_lo[4], pv_hi[4];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) qk_a[k] = off_a(l32, 2 * k + hf);
+  for (int k = 0; k < 8; ++k) qk_a[k] = base0 + off_a(l32, 2 * k + hf);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) qk_b[k] = off_b(l32, 2 * k + hf);
+  for (int k = 0; k < 4; ++k) qk_b[k] = base0 + off_b(l32, 2 * k + hf);
   {
     const int r4 = (lane >> 2) & 3;
     const int colq = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
@@ -190,10 +254,18 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int c = 32 * k + colq;
-      pv_lo[k] = off_a(tb, c >> 3) + (c & 7) * 2;
-      pv_hi[k] = off_a(tb + 8, c >> 3) + (c & 7) * 2;
+      pv_lo[k] = base0 + off_a(tb, c >> 3) + (c & 7) * 2;
+      pv_hi[k] = base0 + off_a(tb + 8, c >> 3) + (c & 7) * 2;
     }
   }
+  auto read_op = [&](int g) -> bf16x8 {  // A operand of MFMA g of the tile (0..67)
+    const MLA_LDS char* z = smem;
+    if (g < 32) return lds_read_b128(z + qk_a[g & 7] + 256 * (g >> 3));
+    if (g < 36) return lds_read_b128(z + qk_b[g - 32]);
+    const int m = g - 36, cb = m >> 1, kk = m & 1;
+    const int imm = 256 * (cb >> 2) + 16384 * kk;
+    return lds_read_tr_pair(z + pv_lo[cb & 3] + imm, z + pv_hi[cb & 3] + imm);
+  };
 
   f32x16 o[16];
 #pragma unroll
@@ -201,87 +273,112 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[cb][e] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
+  bool started = false;  // wave-uniform: a first key has been seen (m_run finite)
+  // Consume every scalar kernel argument the loop uses here, so no scalar load is still in
+  // flight inside the loop (it would share the LDS counter and force full drains there).
+  const float scale_log2 = a.scale_log2;
+  asm volatile("" ::"s"(scale_log2), "s"(ntiles), "s"(ntok));
 
   for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();  // tile t has landed; every wave is done with the other buffer
-    const int tile_tok = t * kTile;
-    if (t + 1 < ntiles) {
-      // The per-lane DMA addresses are loop-invariant; recomputing them (a few VALU ops) is far
-      // cheaper than the registers LICM would pin across the loop, so hide the lane id from it.
-      int lane_v = lane;
-      asm volatile("" : "+v"(lane_v));
-      const int rem = ntok - tile_tok - kTile;
-      issue_tile(smem + ((t + 1) & 1) * kBufBytes, pool + (size_t)bt[t + 1] * kPage * kRow,
-                 rem < kTile ? rem : kTile, wave, lane_v);
+    {  // tile t is in LDS for every wave; every wave is done with tile t-1's buffer
+      const int younger = ntiles - 1 - t;
+      dma_wait_tiles(younger < kAhead - 1 ? younger : kAhead - 1);
     }
-    const MLA_LDS char* buf = smem + (t & 1) * kBufBytes;
-    const int cnt = ntok - tile_tok < kTile ? ntok - tile_tok : kTile;
+    __syncthreads();
+    const int cnt = tile_count(t);
+    // The next tile to stream in goes to the buffer tile t-1 used.
+    const int tn = t + kAhead;
+    const bool more = tn < ntiles;
+    const uint16_t* nsrc = more ? tile_src(tn) : pool;
+    const int ncnt = more ? tile_count(tn) : 0;
+    const uint32_t ndst = lds_addr(smem) + (tn % kNumBufs) * kBufBytes;
+    // The per-lane DMA addresses are loop-invariant; recomputing them (a few VALU ops) is far
+    // cheaper than the registers LICM would pin across the loop, so hide the lane id from it.
+    int lane_v = lane;
+    asm volatile("" : "+v"(lane_v));
 
-    // The tile is processed as two 32-token halves st: scores, softmax, then the weighted sum.
+    // One stream of 68 MFMAs: 36 for the scores (K = 512 latent + 64 RoPE in steps of 16), then
+    // 32 for the weighted sum (16 latent blocks x 2 token steps).  Their A operands come from LDS
+    // through a 4-deep register ring: the read for MFMA g + 4 is issued right after MFMA g, so
+    // LDS latency hides behind MFMAs; the score tail already fetches the first weighted-sum
+    // operands (they do not depend on the softmax), which land while the softmax runs.  The next
+    // tile's 9 load instructions are spread over the score MFMAs, at the same slots in all four
+    // waves (staggering them across waves measured half again slower).
+    bf16x8 ring[4];
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      // ---- scores S^T (32 tokens x 32 heads).  Address of (token 32 st + l32, unit 2 ks + hf) =
-      // qk_a[ks % 8] + 256 (ks / 8) + 32768 st (region A), qk_b[ks] + 4096 st (region B): the
-      // swizzle only touches the low 4 unit bits.
-      f32x16 sc;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sc[e] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < 32; ++ks)
-        sc = mfma32x32x16(lds_read_b128(buf + qk_a[ks & 7] + 256 * (ks >> 3) + 32768 * st), q[ks], sc);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) sc = mfma32x32x16(lds_read_b128(buf + qk_b[ks] + 4096 * st), q[32 + ks], sc);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int g = 0; g < 4; ++g) ring[g] = read_op(g);
 
-      // ---- online softmax (base 2); element e of sc is token 32 st + (e/4)*8 + 4 hf + e%4
-      float mt = -INFINITY;
+    // ---- raw scores S^T (32 tokens x 32 heads)
+    f32x16 sc;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int tok = 32 * st + (e >> 2) * 8 + 4 * hf + (e & 3);
-        const float x = tok < cnt ? sc[e] * a.scale_log2 : -INFINITY;
-        sc[e] = x;
-        mt = fmaxf(mt, x);
-      }
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      if (__any(mt > m_run + kRescaleSlack)) {
-        const float m_new = fmaxf(m_run, mt);
+    for (int ks = 0; ks < 36; ++ks) {
+      if (ks == 0)
+        mfma_first_v(sc, ring[0], q[0]);
+      else
+        mfma_acc_v(sc, ring[ks & 3], q[ks]);
+      ring[ks & 3] = read_op(ks + 4);
+      if ((ks & 3) == 1 && more) dma_step(nsrc, ncnt, ndst, ks >> 2, lane_v);
+    }
+    wait_mfma_result(sc);
+
+    // ---- online softmax in base 2 (scale folded into the exponent's FMA); element e of sc is
+    // token (e/4)*8 + 4 hf + e%4 of the tile.  Masked keys get a raw score of -inf.
+    if (cnt < kTile) {  // wave-uniform: only the last tile of a range can be partial
+      const int lim = cnt - 4 * hf;  // element e is valid iff (e/4)*8 + e%4 < lim
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if ((e >> 2) * 8 + (e & 3) >= lim) sc[e] = -INFINITY;
+    }
+    float mt = sc[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mt = fmaxf(mt, sc[e]);
+    {  // lanes l and l^32 hold the same head
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+      mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
+    }
+    if (__any(mt > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, mt);
+      if (started) {  // O and l hold something: rescale them to the new reference
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
         acc_wait_mfma();
 #pragma unroll
         for (int cb = 0; cb < 16; ++cb) acc_scale(o[cb], alpha);
-        asm volatile("s_nop 4" ::);
-        m_run = m_new;
+        asm volatile("s_nop 4" ::: "memory");
       }
-      bf16x8 pk[2];
+      m_run = m_new;
+      started = true;
+    }
+    bf16x8 pk[2];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        uint32_t w4[4];
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float p0 = __builtin_amdgcn_exp2f(sc[8 * kk + 2 * j] - m_run);
-          const float p1 = __builtin_amdgcn_exp2f(sc[8 * kk + 2 * j + 1] - m_run);
-          l_run += p0 + p1;
-          w4[j] = pack_bf16x2(p0, p1);
-        }
-        u32x4 v = {w4[0], w4[1], w4[2], w4[3]};
-        pk[kk] = __builtin_bit_cast(bf16x8, v);
+      for (int j = 0; j < 8; ++j) {
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * kk + j], scale_log2, -m_run));
+        l_run += pv;
+        pk[kk][j] = (__bf16)pv;
       }
-      __builtin_amdgcn_sched_barrier(0);
+    pin_after_valu(pk[0], pk[1]);
 
-      // ---- O^T (latent x heads) += tile^T * P^T.  k slot j of lane half hf in step kk is token
-      // 32 st + 16 kk + (j/4)*8 + 4 hf + j%4; the transposed read gives lane l latent column l%32
-      // of 4 such tokens (source lane s of each 16-lane group supplies token row s/4, columns
-      // 4(s%4)..+3).  Address = pv_lo/hi[cb % 4] + 256 (cb / 4) + 32768 st + 16384 kk.
+    // ---- O^T (latent x heads) += tile^T * P^T.  k slot j of lane half hf in token step kk is
+    // token 16 kk + (j/4)*8 + 4 hf + j%4; the transposed read gives lane l latent column l%32 of
+    // 4 such tokens (source lane s of each 16-lane group supplies token row s/4, columns
+    // 4(s%4)..+3).
 #pragma unroll
-      for (int cb = 0; cb < 16; ++cb)
+    for (int m = 0; m < 32; ++m) {
+      mfma_acc_a(o[m >> 1], ring[m & 3], pk[m & 1]);
+      if (m + 4 < 32) ring[m & 3] = read_op(36 + m + 4);
+    }
+
+    // advance the read offsets to the next tile's buffer
+    const int step = (t % kNumBufs) == kNumBufs - 1 ? -(kNumBufs - 1) * kBufBytes : kBufBytes;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const int imm = 256 * (cb >> 2) + 32768 * st + 16384 * kk;
-          const bf16x8 av = lds_read_tr_pair(buf + pv_lo[cb & 3] + imm, buf + pv_hi[cb & 3] + imm);
-          o[cb] = mfma32x32x16(av, pk[kk], o[cb]);
-        }
-      __builtin_amdgcn_sched_barrier(0);
+    for (int k = 0; k < 8; ++k) qk_a[k] += step;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      qk_b[k] += step;
+      pv_lo[k] += step;
+      pv_hi[k] += step;
     }
   }
 

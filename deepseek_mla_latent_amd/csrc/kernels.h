@@ -14,6 +14,7 @@ constexpr int kDr = 64;       // shared RoPE key width
 constexpr int kRow = 576;     // cached row: [c_KV | k_pe]
 constexpr int kDh = 128;      // no-RoPE head dim = value head dim
 constexpr int kPage = 64;     // tokens per cache page
+constexpr int kMaxSplitPages = 2048;  // pages one attention workgroup may walk (131072 tokens)
 
 struct AttnArgs {
   const void* q_lat;           // (B,S,H,512) bf16 or fp32

@@ -63,6 +63,9 @@ SplitPlan plan_splits(const mla_params* p, int requested, int cus) {
   }
   if (max_pages == 0) return {1, 1};
   if (s > max_pages) s = max_pages;
+  // a workgroup stages its range's page ids in LDS: at most kMaxSplitPages pages per split
+  const int min_splits = (max_pages + mla::kMaxSplitPages - 1) / mla::kMaxSplitPages;
+  if (s < min_splits) s = min_splits;
   const int pps = (max_pages + s - 1) / s;
   s = (max_pages + pps - 1) / pps;
   return {s, pps};
