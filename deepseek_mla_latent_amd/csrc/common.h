@@ -29,15 +29,12 @@ __device__ __forceinline__ f32x16 mfma32x32x2f32(float a, float b, const f32x16&
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
-// bf16 <-> fp32 (round to nearest even; inputs here are finite).
+// bf16 <-> fp32.  The narrowing casts compile to v_cvt_pk_bf16_f32 (round to nearest even).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
-}
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup w -> XCD w % 8), each XCD

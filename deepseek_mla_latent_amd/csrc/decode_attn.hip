@@ -460,36 +460,69 @@ __global__ __launch_bounds__(256) void decode_attn_f32_kernel(AttnArgs a) {
 }
 
 // Merge the per-split partials of every (b, i, h): lse = log sum_k e^{lse_k},
-// o = sum_k e^{lse_k - lse} o_k.  Empty splits carry lse_k = -inf and weight 0.
-// One workgroup per (row = b*S+i, group of 16 heads); thread = (head, 32-column slice).
+// o = sum_k e^{lse_k - lse} o_k.  Empty splits carry lse_k = -inf, o_k = 0 and weight 0.
+// One wave per (row = b*S+i, head); lane l owns latent columns [8 l, 8 l + 8).  The split lse
+// values are read one per lane (64 splits per load) and their weights broadcast with readlane;
+// the partial rows are taken eight splits at a time with all sixteen loads issued before the
+// first use.  Workgroup ids go through the same XCD renumbering as the attention grid, so row b
+// is merged on the XCD whose L2 received its partials.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
 __global__ __launch_bounds__(256) void lse_merge_kernel(const float* __restrict__ o_part,
                                                         const float* __restrict__ lse_part, float* __restrict__ o_lat,
                                                         float* __restrict__ lse, int num_splits) {
-  const int row = blockIdx.x >> 3, hg = blockIdx.x & 7;
-  const int h = hg * 16 + (threadIdx.x >> 4);
-  const int c0 = (threadIdx.x & 15) * 32;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int rh = xcd_remap(blockIdx.x, gridDim.x) * 4 + wave;  // row * kHeads + h
+  const int row = rh / kHeads, h = rh % kHeads;
   const size_t base = (size_t)row * num_splits * kHeads + h;  // split k at base + k * kHeads
-  float m = -INFINITY;
-  for (int k = 0; k < num_splits; ++k) m = fmaxf(m, lse_part[base + (size_t)k * kHeads]);
-  f32x4 acc[8];
+  const float* lp = lse_part + base;
+  const float* op = o_part + base * kDc + 8 * lane;
+  constexpr float kLog2e = 1.4426950408889634f;
+  auto lse_of = [&](int k) { return k < num_splits ? lp[(size_t)k * kHeads] : -INFINITY; };
+
+  f32x4 x0[8], x1[8];
+  auto load_batch = [&](int kb) {  // splits kb .. kb+7 (clamped to the last one)
 #pragma unroll
-  for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float sum = 0.f;
-  if (m != -INFINITY) {
-    for (int k = 0; k < num_splits; ++k) {
-      const float wk = expf(lse_part[base + (size_t)k * kHeads] - m);
-      if (wk == 0.f) continue;
-      sum += wk;
-      const f32x4* src = (const f32x4*)(o_part + (base + (size_t)k * kHeads) * kDc + c0);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] += wk * src[j];
+    for (int j = 0; j < 8; ++j) {
+      const int k = kb + j < num_splits ? kb + j : num_splits - 1;
+      const f32x4* src = (const f32x4*)(op + (size_t)k * kHeads * kDc);
+      x0[j] = src[0];
+      x1[j] = src[1];
     }
+  };
+  load_batch(0);  // does not depend on the weights: in flight while they are formed
+  const float lse0 = lse_of(lane);
+  float m = lse0;
+  for (int k0 = 64; k0 < num_splits; k0 += 64) m = fmaxf(m, lse_of(k0 + lane));
+  m = wave_max(m);
+  const float m_ref = m == -INFINITY ? 0.f : m;  // all splits empty: every weight is 0
+
+  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+  float sum = 0.f, w_lane = 0.f;
+  for (int kb = 0; kb < num_splits; kb += 8) {
+    if ((kb & 63) == 0)  // weights of splits kb .. kb+63, one per lane (0 past the end)
+      w_lane = __builtin_amdgcn_exp2f(((kb == 0 ? lse0 : lse_of(kb + lane)) - m_ref) * kLog2e);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float w = kb + j < num_splits
+                          ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_lane), (kb & 63) + j))
+                          : 0.f;
+      sum += w;
+      a0 += w * x0[j];
+      a1 += w * x1[j];
+    }
+    if (kb + 8 < num_splits) load_batch(kb + 8);
   }
   const float inv = sum > 0.f ? 1.0f / sum : 0.f;
-  f32x4* dst = (f32x4*)(o_lat + ((size_t)row * kHeads + h) * kDc + c0);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) dst[j] = acc[j] * inv;
-  if ((threadIdx.x & 15) == 0 && lse) lse[(size_t)row * kHeads + h] = m == -INFINITY ? -INFINITY : m + logf(sum);
+  f32x4* dst = (f32x4*)(o_lat + (size_t)rh * kDc + 8 * lane);
+  dst[0] = a0 * inv;
+  dst[1] = a1 * inv;
+  if (lane == 0 && lse) lse[rh] = m == -INFINITY ? -INFINITY : m + logf(sum);
 }
 
 hipError_t launch_decode_attn(const AttnArgs& a, int rows, hipStream_t stream) {
@@ -503,8 +536,8 @@ hipError_t launch_decode_attn(const AttnArgs& a, int rows, hipStream_t stream) {
 
 hipError_t launch_lse_merge(const float* o_part, const float* lse_part, float* o_lat, float* lse, int rows,
                             int num_splits, hipStream_t stream) {
-  hipLaunchKernelGGL(lse_merge_kernel, dim3(rows * 8), dim3(256), 0, stream, o_part, lse_part, o_lat, lse,
-                     num_splits);
+  hipLaunchKernelGGL(lse_merge_kernel, dim3(rows * (kHeads / 4)), dim3(256), 0, stream, o_part, lse_part, o_lat,
+                     lse, num_splits);
   return hipGetLastError();
 }
 

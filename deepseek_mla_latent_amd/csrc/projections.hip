@@ -7,16 +7,26 @@
 // never formed: "DeepSeek-V2的推理成本如何计算？" (izhida.com), answer "专家"; "【笔记】MLA矩阵吸收分析"
 // §二.2 step 2 and §三.2 step 2.  Both are batched GEMVs / thin GEMMs (M = tokens = B*S) whose
 // cost is reading the 128 x 512 x 128 weight once (the same izhida answer notes that the main
-// cost of the W_V product is reading W_V), so they are HBM-bound: every workgroup streams its
-// weight slice exactly once and loops over the token blocks with it held in registers / LDS.
+// cost of the W_V product is reading W_V), so they are HBM-bound.  Each workgroup streams its
+// weight slice exactly once, and every wave issues all the loads of a step before its first
+// use, so a launch costs about one memory round trip plus the transfer.
 #include "common.h"
 #include "kernels.h"
 
 namespace mla {
 
+// Forces the values to be complete here: every load producing them is issued before this point,
+// and the compiler cannot trickle them out one MFMA at a time.
+template <typename T>
+__device__ __forceinline__ void settle(const T& x) {
+  asm volatile("" ::"v"(x));
+}
+
 // ---------------------------------------------------------------------------------------------
 // absorb: grid (4 latent blocks of 128, 128 heads), 4 waves; wave w owns 32 latent rows
-// c in [128 bx + 32 w, +32).  D(c x tokens) = W_UK[h] rows (A, straight from global) x q_nope^T (B).
+// c in [128 bx + 32 w, +32).  D(c x tokens) = W_UK[h] rows (A, straight from global) x q_nope^T
+// (B).  Columns of D belong to single tokens, so a token slot past the end reads a valid row
+// (token 0) and its column is simply not stored.
 template <bool BF16>
 __global__ __launch_bounds__(256) void absorb_q_kernel(const void* __restrict__ q_nope,
                                                        const void* __restrict__ w_uk, void* __restrict__ q_lat,
@@ -35,15 +45,16 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(const void* __restrict__ 
       const int n = 32 * nb + l32;
       const bool ok = n < tokens;
       const bf16x8* Q = (const bf16x8*)((const uint16_t*)q_nope + ((size_t)(ok ? n : 0) * kHeads + h) * kDh + 8 * hf);
+      bf16x8 bq[8];
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) bq[ks] = Q[2 * ks];
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) settle(bq[ks]);
       f32x16 acc;
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[e] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        bf16x8 bq = Q[2 * ks];
-        if (!ok) bq = bf16x8{};
-        acc = mfma32x32x16(aw[ks], bq, acc);
-      }
+      for (int ks = 0; ks < 8; ++ks) acc = mfma32x32x16(aw[ks], bq[ks], acc);
       if (ok) {  // element e: latent c_base + (e/4)*8 + 4 hf + e%4 of token n
         uint16_t* dst = (uint16_t*)q_lat + ((size_t)n * kHeads + h) * kDc + c_base + 4 * hf;
 #pragma unroll
@@ -63,16 +74,18 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(const void* __restrict__ 
       const int n = 32 * nb + l32;
       const bool ok = n < tokens;
       const f32x4* Q = (const f32x4*)((const float*)q_nope + ((size_t)(ok ? n : 0) * kHeads + h) * kDh + 4 * hf);
+      f32x4 bq[16];
+#pragma unroll
+      for (int m = 0; m < 16; ++m) bq[m] = Q[2 * m];
+#pragma unroll
+      for (int m = 0; m < 16; ++m) settle(bq[m]);
       f32x16 acc;
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[e] = 0.f;
 #pragma unroll
-      for (int m = 0; m < 16; ++m) {
-        f32x4 bq = Q[2 * m];
-        if (!ok) bq = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int m = 0; m < 16; ++m)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc = mfma32x32x2f32(aw[m][j], bq[j], acc);
-      }
+        for (int j = 0; j < 4; ++j) acc = mfma32x32x2f32(aw[m][j], bq[m][j], acc);
       if (ok) {
         float* dst = (float*)q_lat + ((size_t)n * kHeads + h) * kDc + c_base + 4 * hf;
 #pragma unroll
@@ -84,28 +97,160 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(const void* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------------------------
-// out-proj: grid (2 value halves of 64, 128 heads), 4 waves.  The workgroup stages
-// W_UV[h][:, 64 bx .. +64) (all 512 latent rows) in LDS once, then computes
-// D(v x tokens) = W_UV^T (A, transposed LDS read) x o_lat^T (B, from global) for every
-// (32-value block, 32-token block) pair, round-robin over the waves.  bf16: o_lat is split into
-// hi + lo bf16 parts (two MFMAs) so the fp32 latent output loses no precision worth noting.
-template <bool BF16>
-__global__ __launch_bounds__(256) void out_proj_kernel(const float* __restrict__ o_lat,
-                                                       const void* __restrict__ w_uv, void* __restrict__ out,
-                                                       int tokens) {
-  constexpr int kEl = BF16 ? 2 : 4;
-  constexpr int kRowBytes = 64 * kEl;  // one latent row of the staged slice
-  __shared__ __attribute__((aligned(16))) char wl_raw[kDc * kRowBytes];
-  MLA_LDS char* wl = (MLA_LDS char*)wl_raw;
+// out-proj, bf16: one workgroup per (head h, value half vh); logical ids 2h, 2h+1 run on the
+// same XCD, so the second read of o_lat[., h, .] can come from that XCD's L2.
+//
+// Wave w owns latent rows [128 w, +128): it copies W_UV[h][those rows][64 vh .. +64) into LDS
+// with direct-to-LDS loads (the only rows it ever reads, so no barrier is needed) and loads the
+// matching o_lat slice of a 32-token block into registers, all before the first MFMA.  Per token
+// block it computes the partial D(64 values x 32 tokens) over its 128 latent rows: A = W_UV^T by
+// transposed LDS reads, B = o_lat^T split into hi + lo bf16 parts (two MFMAs, so the fp32
+// latent input keeps about 16 mantissa bits).  The four partials are summed through LDS.
+constexpr int kOpRowBytes = 128;  // one latent row of the 64-value slice
+// 16-byte unit u of latent row c is stored at unit u ^ op_swz(c): the transposed reads touch
+// 4 consecutive rows x 64 B, which this spreads over all 64 banks.
+__device__ __forceinline__ int op_swz(int c) { return ((c >> 1) & 1) << 2; }
+
+__global__ __launch_bounds__(256, 1) void out_proj_bf16_kernel(const float* __restrict__ o_lat,
+                                                               const uint16_t* __restrict__ w_uv,
+                                                               uint16_t* __restrict__ out, int tokens) {
+  __shared__ __attribute__((aligned(1024))) char wl_raw[kDc * kOpRowBytes];  // 64 KiB
+  __shared__ float red[4 * 2 * 16 * 64];                                     // 32 KiB
+  MLA_LDS char* const wl = (MLA_LDS char*)wl_raw;
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int h = id >> 1, vh = id & 1;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, l32 = lane & 31, hf = lane >> 5;
+  const int c0 = 128 * wave;
+
+  {  // W slice rows [c0, c0 + 128): 16 loads of 8 rows x 128 B
+    const char* src = (const char*)(w_uv + (size_t)h * kDc * kDh + 64 * vh);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int c = c0 + 8 * i + (lane >> 3);
+      const int u = (lane & 7) ^ op_swz(c);
+      __builtin_amdgcn_global_load_lds((const MLA_GLOBAL void*)(src + (size_t)c * kDh * 2 + u * 16),
+                                       (MLA_LDS void*)(wl + (c0 + 8 * i) * kOpRowBytes), 16, 0, 0);
+    }
+  }
+  // B operand of k step ks for lane (token 32 nb + l32, half hf): latent c0 + 16 ks + 8 hf + j.
+  f32x4 x[16];
+  auto load_o = [&](int nb) {
+    int n = 32 * nb + l32;
+    n = n < tokens ? n : 0;
+    const f32x4* p = (const f32x4*)(o_lat + ((size_t)n * kHeads + h) * kDc + c0 + 8 * hf);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      x[2 * ks] = p[4 * ks];
+      x[2 * ks + 1] = p[4 * ks + 1];
+    }
+  };
+  load_o(0);
+#pragma unroll
+  for (int k = 0; k < 16; ++k) settle(x[k]);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's LDS rows have landed
+
+  // Transposed A read (32 values x 8 latent rows per pair): in each 16-lane group, source lane
+  // s supplies latent row c + s/4 and value columns 4 (s%4) .. +3 of the group's 16 columns.
+  const int r4 = (lane >> 2) & 3, g1 = (lane >> 4) & 1, q4 = lane & 3;
+  const int sw = (r4 >> 1) & 1;  // op_swz of the row, as a flip of the value block bit
+  const MLA_LDS char* a_base[2];
+#pragma unroll
+  for (int vb = 0; vb < 2; ++vb)
+    a_base[vb] = wl + (c0 + 8 * hf + r4) * kOpRowBytes + 64 * (vb ^ sw) + 16 * (2 * g1 + (q4 >> 1)) + 8 * (q4 & 1);
+
+  const int nblocks = (tokens + 31) / 32;
+  for (int nb = 0; nb < nblocks; ++nb) {
+    bf16x8 bh[8], bl[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const f32x4 a = x[2 * ks], b = x[2 * ks + 1];
+      const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+      u32x4 hw, lw;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        hw[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
+        const float r0 = v[2 * j] - __uint_as_float(hw[j] << 16);
+        const float r1 = v[2 * j + 1] - __uint_as_float(hw[j] & 0xffff0000u);
+        lw[j] = pack_bf16x2(r0, r1);
+      }
+      bh[ks] = __builtin_bit_cast(bf16x8, hw);
+      bl[ks] = __builtin_bit_cast(bf16x8, lw);
+    }
+    if (nb + 1 < nblocks) load_o(nb + 1);  // in flight during this block's MFMAs
+
+    f32x16 acc[2];
+#pragma unroll
+    for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[vb][e] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int vb = 0; vb < 2; ++vb) {
+        const MLA_LDS char* p = a_base[vb] + ks * 16 * kOpRowBytes;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)p);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(p + 4 * kOpRowBytes));
+        const i16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const bf16x8 av = __builtin_bit_cast(bf16x8, a8);
+        acc[vb] = mfma32x32x16(av, bh[ks], acc[vb]);
+        acc[vb] = mfma32x32x16(av, bl[ks], acc[vb]);
+      }
+
+    // Sum the four waves' partials.  red[((w * 2 + vb) * 16 + e) * 64 + lane]; element e of
+    // lane l is value 32 vb + (e/4)*8 + 4 (l/32) + e%4 of token l%32.
+    if (nb > 0) __syncthreads();  // the previous block's sums have been read
+#pragma unroll
+    for (int vb = 0; vb < 2; ++vb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) red[((wave * 2 + vb) * 16 + e) * 64 + lane] = acc[vb][e];
+    __syncthreads();
+    {
+      const int vb = wave >> 1;
+      const int n = 32 * nb + l32;
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg) {
+        const int g = 2 * (wave & 1) + gg;
+        float s[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = 4 * g + i;
+          s[i] = red[((0 * 2 + vb) * 16 + e) * 64 + lane] + red[((1 * 2 + vb) * 16 + e) * 64 + lane] +
+                 red[((2 * 2 + vb) * 16 + e) * 64 + lane] + red[((3 * 2 + vb) * 16 + e) * 64 + lane];
+        }
+        if (n < tokens) {
+          const int v = 64 * vh + 32 * vb + 8 * g + 4 * hf;
+          const uint2 pk = {pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
+          *(uint2*)(out + ((size_t)n * kHeads + h) * kDh + v) = pk;
+        }
+      }
+    }
+  }
+}
+
+// out-proj, fp32: grid (2 value halves of 64, 128 heads), 4 waves.  The workgroup stages
+// W_UV[h][:, 64 bx .. +64) in LDS, then computes D(v x tokens) = W_UV^T x o_lat^T with the fp32
+// MFMA for every (32-value block, 32-token block) pair, round-robin over the waves.
+__global__ __launch_bounds__(256) void out_proj_f32_kernel(const float* __restrict__ o_lat,
+                                                           const float* __restrict__ w_uv, float* __restrict__ out,
+                                                           int tokens) {
+  __shared__ float wl[kDc * 64];  // 128 KiB
   const int h = blockIdx.y, vh = blockIdx.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hf = lane >> 5;
-
-  {  // stage: row c of the slice is 64 values at W_UV[h][c][64 vh]
-    const char* src = (const char*)w_uv + ((size_t)h * kDc * kDh + 64 * vh) * kEl;
-    constexpr int kUnitsPerRow = kRowBytes / 16;
-    for (int u = threadIdx.x; u < kDc * kUnitsPerRow; u += 256) {
-      const int c = u / kUnitsPerRow, k = u % kUnitsPerRow;
-      *(MLA_LDS u32x4*)(wl + c * kRowBytes + k * 16) = *(const u32x4*)(src + (size_t)c * kDh * kEl + k * 16);
+  {
+    const float* src = w_uv + (size_t)h * kDc * kDh + 64 * vh;
+    for (int u0 = 0; u0 < kDc * 16; u0 += 256 * 8) {
+      f32x4 t[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int u = u0 + threadIdx.x + 256 * k;
+        t[k] = *(const f32x4*)(src + (size_t)(u >> 4) * kDh + (u & 15) * 4);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int u = u0 + threadIdx.x + 256 * k;
+        *(f32x4*)(wl + (u >> 4) * 64 + (u & 15) * 4) = t[k];
+      }
     }
   }
   __syncthreads();
@@ -119,61 +264,26 @@ __global__ __launch_bounds__(256) void out_proj_kernel(const float* __restrict__
     f32x16 acc;
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[e] = 0.f;
-    if constexpr (BF16) {
-      // A lane l: value column 32 vb + l%32, latent rows 16 ks + 8 hf + j.  Transposed read:
-      // source lane s of each 16-lane group supplies latent row (s/4) (+4 for the second read)
-      // and value columns 4 (s%4) .. +3 of the group's 16-column half.
-      const int r4 = (lane >> 2) & 3;
-      const int col = 32 * vb + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-#pragma unroll 4
-      for (int ks = 0; ks < 32; ++ks) {
-        const int c = 16 * ks + 8 * hf + r4;
-        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(wl + c * kRowBytes + col * 2));
-        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(wl + (c + 4) * kRowBytes + col * 2));
-        i16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        const bf16x8 av = __builtin_bit_cast(bf16x8, a8);
-        const f32x4 x0 = ok ? *(const f32x4*)(O + 16 * ks + 8 * hf) : f32x4{0.f, 0.f, 0.f, 0.f};
-        const f32x4 x1 = ok ? *(const f32x4*)(O + 16 * ks + 8 * hf + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
-        const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-        uint32_t hw[4], lw[4];
+    // k step (m, j) pairs lane half hf with latent row c = 8 m + 4 hf + j.
+    for (int m0 = 0; m0 < 64; m0 += 16) {
+      f32x4 xb[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) xb[k] = *(const f32x4*)(O + 8 * (m0 + k) + 4 * hf);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) settle(xb[k]);
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const uint16_t h0 = f32_to_bf16(x[2 * j]), h1 = f32_to_bf16(x[2 * j + 1]);
-          hw[j] = uint32_t(h0) | (uint32_t(h1) << 16);
-          lw[j] = pack_bf16x2(x[2 * j] - bf16_to_f32(h0), x[2 * j + 1] - bf16_to_f32(h1));
+          const int c = 8 * (m0 + k) + 4 * hf + j;
+          acc = mfma32x32x2f32(wl[c * 64 + 32 * vb + l32], xb[k][j], acc);
         }
-        const u32x4 hv = {hw[0], hw[1], hw[2], hw[3]}, lv = {lw[0], lw[1], lw[2], lw[3]};
-        acc = mfma32x32x16(av, __builtin_bit_cast(bf16x8, hv), acc);
-        acc = mfma32x32x16(av, __builtin_bit_cast(bf16x8, lv), acc);
-      }
-    } else {
-      // fp32: k step (m, j) pairs lane half hf with latent row c = 8 m + 4 hf + j.
-      const MLA_LDS float* wf = (const MLA_LDS float*)wl;
-#pragma unroll 2
-      for (int m = 0; m < 64; ++m) {
-        const f32x4 xb = ok ? *(const f32x4*)(O + 8 * m + 4 * hf) : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int c = 8 * m + 4 * hf + j;
-          acc = mfma32x32x2f32(wf[c * 64 + 32 * vb + l32], xb[j], acc);
-        }
-      }
     }
     if (ok) {  // element e: value 32 vb + (e/4)*8 + 4 hf + e%4 of token n
-      const int v0 = 64 * vh + 32 * vb + 4 * hf;
-      if constexpr (BF16) {
-        uint16_t* dst = (uint16_t*)out + ((size_t)n * kHeads + h) * kDh + v0;
+      float* dst = out + ((size_t)n * kHeads + h) * kDh + 64 * vh + 32 * vb + 4 * hf;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          uint2 v = {pack_bf16x2(acc[4 * g], acc[4 * g + 1]), pack_bf16x2(acc[4 * g + 2], acc[4 * g + 3])};
-          *(uint2*)(dst + 8 * g) = v;
-        }
-      } else {
-        float* dst = (float*)out + ((size_t)n * kHeads + h) * kDh + v0;
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          *(f32x4*)(dst + 8 * g) = f32x4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
-      }
+      for (int g = 0; g < 4; ++g)
+        *(f32x4*)(dst + 8 * g) = f32x4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
     }
   }
 }
@@ -190,11 +300,12 @@ hipError_t launch_absorb_q(const void* q_nope, const void* w_uk, void* q_lat, in
 
 hipError_t launch_out_proj(const float* o_lat, const void* w_uv, void* out, int tokens, bool bf16,
                            hipStream_t stream) {
-  const dim3 grid(2, kHeads);
   if (bf16)
-    hipLaunchKernelGGL(out_proj_kernel<true>, grid, dim3(256), 0, stream, o_lat, w_uv, out, tokens);
+    hipLaunchKernelGGL(out_proj_bf16_kernel, dim3(2 * kHeads), dim3(256), 0, stream, o_lat,
+                       (const uint16_t*)w_uv, (uint16_t*)out, tokens);
   else
-    hipLaunchKernelGGL(out_proj_kernel<false>, grid, dim3(256), 0, stream, o_lat, w_uv, out, tokens);
+    hipLaunchKernelGGL(out_proj_f32_kernel, dim3(2, kHeads), dim3(256), 0, stream, o_lat, (const float*)w_uv,
+                       (float*)out, tokens);
   return hipGetLastError();
 }
 
