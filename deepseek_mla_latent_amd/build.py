@@ -17,10 +17,13 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = ["mla_api.cpp", "decode_attn.hip", "projections.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-# gfx950 only; packed-fp32 VALU ops are disabled (plain fp32 code is scalar fp32).
+# gfx950 only; packed-fp32 VALU ops are disabled (plain fp32 code is scalar fp32).  The attention
+# kernel's MFMA stream is written as fully unrolled loops whose bodies exceed the default size
+# limit of "#pragma unroll"; partially unrolled, its register arrays would be indexed at run time.
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-pragma-unroll-threshold=1000000",
     "-Wall", "-Wno-unused-result",
 ]
 

@@ -37,7 +37,6 @@ constexpr int kUnitsB = kDr / 8;                      // 16-byte units of k_pe p
 constexpr int kRegionA = kTile * kUnitsA * 16;        // 32768 B: c_KV part of a tile
 constexpr int kBufBytes = kRegionA + kTile * kUnitsB * 16;  // 36864 B per tile buffer
 constexpr int kNumBufs = 4;                           // LDS ring: tile t lives in buffer t % 4
-constexpr int kAhead = kNumBufs - 1;                  // tiles in flight ahead of the computed one
 constexpr int kDmaPerTile = 9;                        // direct-to-LDS loads per wave per tile
 constexpr float kRescaleSlack = 8.0f;                 // log2 units
 
@@ -58,6 +57,11 @@ __device__ __forceinline__ int off_b(int t, int u) { return kRegionA + (t * kUni
 // that publishes a tile.  M0 is not otherwise used by this kernel.
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory");
+}
+// The same from a wave-uniform base plus a 32-bit per-lane byte offset (no 64-bit vector math).
+__device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+               : "memory");
 }
 // Wait until at most `younger` tiles' loads (kDmaPerTile each) of this wave are still in flight.
 // Vector-memory loads complete in order, so this retires every older tile; loads the compiler
@@ -103,8 +107,8 @@ __device__ __forceinline__ float acc_read_scaled(float x, float scale) {
 // matter are handled explicitly:
 //   * VALU write -> MFMA source read needs 2 wait states: the first score MFMA takes SrcC = 0
 //     (no VALU zeroing) and P goes through pin_after_valu() before use;
-//   * MFMA result -> VALU read needs more than 11 wait states: scores go through
-//     wait_mfma_result(), O through acc_wait_mfma();
+//   * MFMA result -> VALU read needs 18 wait states (16-pass XDL op): the last score MFMA of a
+//     chain carries them (mfma_acc_v_last), O goes through acc_wait_mfma();
 //   * dependent accumulation chains (same SrcC/Dst) need none.
 __device__ __forceinline__ void mfma_first_v(f32x16& d, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b) : "memory");
@@ -115,10 +119,21 @@ __device__ __forceinline__ void mfma_acc_v(f32x16& d, const bf16x8& a, const bf1
 __device__ __forceinline__ void mfma_acc_a(f32x16& d, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b) : "memory");
 }
-__device__ __forceinline__ void wait_mfma_result(f32x16& d) { asm volatile("s_nop 15\n\ts_nop 3" : "+v"(d)); }
+// Last MFMA of a chain whose result the VALU reads: the wait is part of the same statement, so
+// no copy the compiler places after it (it cannot see the MFMA) can read the result too early.
+__device__ __forceinline__ void mfma_acc_v_last(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 15\n\ts_nop 3" : "+v"(d) : "v"(a), "v"(b) : "memory");
+}
 __device__ __forceinline__ void pin_after_valu(bf16x8& x, bf16x8& y) { asm volatile("s_nop 1" : "+v"(x), "+v"(y)); }
 
 __device__ __forceinline__ bf16x8 lds_read_b128(const MLA_LDS char* p) { return *(const MLA_LDS bf16x8*)p; }
+
+// max of three (no NaN canonicalisation: inputs are scores or -inf)
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 
 __device__ __forceinline__ bf16x8 lds_read_tr_pair(const MLA_LDS char* lo, const MLA_LDS char* hi) {
   i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)lo);
@@ -167,16 +182,34 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
   const int l32 = lane & 31, hf = lane >> 5;
   const int h = wave * 32 + l32;
 
-  float* o_ptr = a.o_out + (w.out_row + h) * kDc + 4 * hf;
-  float* lse_ptr = a.lse_out ? a.lse_out + w.out_row + h : nullptr;
+  // Output slots of this lane (head h, latent columns 8 g + 4 hf + 32 cb ..).  Computed where
+  // they are used: held across the loop they would cost two 64-bit registers.
+  // Final outputs are fp32; split partials are bf16 (the merge widens them again).
+  auto out_ptrs = [&](int ln, size_t& o_idx, float*& lse_ptr) {
+    const int hh = wave * 32 + (ln & 31);
+    o_idx = (w.out_row + hh) * kDc + 4 * (ln >> 5);
+    lse_ptr = a.lse_out ? a.lse_out + w.out_row + hh : nullptr;
+  };
+  // Element e of the 4 at (cb, g): latent column 32 cb + 8 g + 4 hf + e.
+  auto store4 = [&](size_t o_idx, int cb, int g, const f32x4& v) {
+    if (a.final_out) {
+      *(f32x4*)((float*)a.o_out + o_idx + 32 * cb + 8 * g) = v;
+    } else {
+      const uint2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      *(uint2*)((uint16_t*)a.o_out + o_idx + 32 * cb + 8 * g) = pk;
+    }
+  };
 
   const int ntok = w.tok_end - w.tok_begin;
   if (ntok <= 0) {  // empty key range: o = 0, lse = -inf
+    size_t o_idx;
+    float* lse_ptr;
+    out_ptrs(lane, o_idx, lse_ptr);
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int cb = 0; cb < 16; ++cb)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) *(f32x4*)(o_ptr + 32 * cb + 8 * g) = z;
+      for (int g = 0; g < 4; ++g) store4(o_idx, cb, g, z);
     if (hf == 0 && lse_ptr) *lse_ptr = -INFINITY;
     return;
   }
@@ -191,38 +224,33 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
   const int npages = (ntok + kPage - 1) / kPage;
   for (int j = threadIdx.x; j < npages; j += 256) lds_pages[j] = bt[j];
   __syncthreads();
-  auto tile_src = [&](int t) -> const uint16_t* {  // first token row of tile t (t < ntiles)
-    const int page = __builtin_amdgcn_readfirstlane(lds_pages[t >> 1]);
+  auto row_of = [&](int t, int page) -> const uint16_t* {  // first token row of tile t
     return pool + ((size_t)page * kPage + (t & 1) * kTile) * kRow;
   };
   auto tile_count = [&](int t) { return ntok - t * kTile < kTile ? ntok - t * kTile : kTile; };
 
-  // One step of copying tile `t` (cnt valid tokens, rows from `src`) into LDS buffer `dst`:
+  // One step of copying a tile (cnt valid tokens, rows from `src`) into LDS buffer `dst`:
   // steps 0-7 fill this wave's 8 tokens' 1 KiB c_KV rows (region A), step 8 the 128 B k_pe rows
   // of 8 tokens (region B).  Tokens past cnt re-read token 0 (always valid), so LDS never holds
   // bytes from outside the sequence; their scores are masked.
-  auto dma_step = [&](const uint16_t* src, int cnt, uint32_t dst, int k, int lane_v) {
+  // lane16 = 16 * lane: the per-lane part of every address is one XOR with a wave-uniform value.
+  auto dma_step = [&](const uint16_t* src, int cnt, uint32_t dst, int k, uint32_t lane16) {
+    const char* base = (const char*)src;
     if (k < 8) {
-      const int t = wave * 8 + k;
+      const int t = wave * 8 + k;  // wave-uniform
       const int ts = t < cnt ? t : 0;
-      dma16(src + ts * kRow + (lane_v ^ swz_a(t)) * 8, dst + t * 1024);
+      dma16_s(base + ts * (kRow * 2), lane16 ^ (swz_a(t) * 16), dst + t * 1024);
     } else {
-      const int t = wave * 8 + (lane_v >> 3);
+      const int t = wave * 8 + (int)(lane16 >> 7);
       const int ts = t < cnt ? t : 0;
-      dma16(src + ts * kRow + kDc + ((lane_v & 7) ^ swz_b(t)) * 8, dst + kRegionA + wave * 1024);
+      const uint32_t u = ((lane16 >> 4) & 7) ^ swz_b(t);
+      dma16_s(base, ts * (kRow * 2) + kDc * 2 + u * 16, dst + kRegionA + wave * 1024);
     }
   };
-  // Prologue: tiles 0 .. kAhead-1.
-  for (int t = 0; t < kAhead && t < ntiles; ++t) {
-    const uint16_t* src = tile_src(t);
-    const int cnt = tile_count(t);
-    const uint32_t dst = lds_addr(smem) + t * kBufBytes;
-#pragma unroll
-    for (int k = 0; k < kDmaPerTile; ++k) dma_step(src, cnt, dst, k, lane);
-  }
-
-  // This lane's head, as the B operand of the score MFMA: q[ks] = [q_lat | q_pe][16 ks + 8 hf .. +7].
-  bf16x8 q[36];
+  // Prologue.  The query loads go first and tile 0 right behind them; the compiler's wait for q
+  // (it cannot see the asm loads, so it waits for everything) then also covers tile 0, which is
+  // needed first anyway.  Tiles 1 and 2 start streaming after that wait.
+  bf16x8 q[36];  // this lane's head as the score B operand: [q_lat | q_pe][16 ks + 8 hf .. +7]
   {
     const size_t qrow = ((size_t)w.b * a.S + w.i) * kHeads + h;
     const bf16x8* ql = (const bf16x8*)((const uint16_t*)a.q_lat + qrow * kDc + 8 * hf);
@@ -231,22 +259,32 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
     for (int ks = 0; ks < 32; ++ks) q[ks] = ql[2 * ks];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) q[32 + ks] = qp[2 * ks];
-    // Wait for q here, once: otherwise the loop inherits "q may be in flight" and carries
-    // vector-memory waits that the in-flight tile loads would then trip.
-#pragma unroll
-    for (int ks = 0; ks < 36; ++ks) asm volatile("" ::"v"(q[ks]));
   }
+  auto prologue_tile = [&](int t) {
+    const uint16_t* src = row_of(t, __builtin_amdgcn_readfirstlane(lds_pages[t >> 1]));
+    const int cnt = tile_count(t);
+    const uint32_t dst = lds_addr(smem) + t * kBufBytes;
+#pragma unroll
+    for (int k = 0; k < kDmaPerTile; ++k) dma_step(src, cnt, dst, k, lane * 16);
+  };
+  prologue_tile(0);
+  // Wait for q here, once: otherwise the loop inherits "q may be in flight" and carries
+  // vector-memory waits that the in-flight tile loads would then trip.
+#pragma unroll
+  for (int ks = 0; ks < 36; ++ks) asm volatile("" ::"v"(q[ks]));
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  for (int t = 1; t < kNumBufs - 1 && t < ntiles; ++t) prologue_tile(t);
 
-  // Per-lane LDS byte offsets of the swizzled reads in the current tile's buffer; advanced by one
-  // buffer per tile.  score step r (r < 32): qk_a[r % 8] + 256 (r / 8); (r >= 32): qk_b[r - 32].
+  // Per-lane LDS byte offsets of the swizzled reads, relative to smem; the score offsets follow
+  // the tile being scored, the sum offsets the (previous) tile being summed, one buffer per tile.
+  // score step r (r < 32): qk_a[r % 8] + 256 (r / 8); (r >= 32): qk_b[r - 32].
   // sum step m: latent block cb = m / 2, token step kk = m % 2 -> pv_lo/hi[cb % 4] + 256 (cb / 4)
   // + 16384 kk.  All immediates stay below 64 KiB.
-  const int base0 = 0;  // offsets are relative to smem
   int qk_a[8], qk_b[4], pv_lo[4], pv_hi[4];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) qk_a[k] = base0 + off_a(l32, 2 * k + hf);
+  for (int k = 0; k < 8; ++k) qk_a[k] = off_a(l32, 2 * k + hf);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) qk_b[k] = base0 + off_b(l32, 2 * k + hf);
+  for (int k = 0; k < 4; ++k) qk_b[k] = off_b(l32, 2 * k + hf);
   {
     const int r4 = (lane >> 2) & 3;
     const int colq = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
@@ -254,17 +292,34 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int c = 32 * k + colq;
-      pv_lo[k] = base0 + off_a(tb, c >> 3) + (c & 7) * 2;
-      pv_hi[k] = base0 + off_a(tb + 8, c >> 3) + (c & 7) * 2;
+      pv_lo[k] = off_a(tb, c >> 3) + (c & 7) * 2;
+      pv_hi[k] = off_a(tb + 8, c >> 3) + (c & 7) * 2;
     }
   }
-  auto read_op = [&](int g) -> bf16x8 {  // A operand of MFMA g of the tile (0..67)
-    const MLA_LDS char* z = smem;
-    if (g < 32) return lds_read_b128(z + qk_a[g & 7] + 256 * (g >> 3));
-    if (g < 36) return lds_read_b128(z + qk_b[g - 32]);
-    const int m = g - 36, cb = m >> 1, kk = m & 1;
+  auto read_qk = [&](int g) -> bf16x8 {  // A operand of score MFMA g (0..35)
+    if (g < 32) return lds_read_b128(smem + qk_a[g & 7] + 256 * (g >> 3));
+    return lds_read_b128(smem + qk_b[g - 32]);
+  };
+  auto read_pv = [&](int m) -> bf16x8 {  // A operand of sum MFMA m (0..31)
+    const int cb = m >> 1, kk = m & 1;
     const int imm = 256 * (cb >> 2) + 16384 * kk;
-    return lds_read_tr_pair(z + pv_lo[cb & 3] + imm, z + pv_hi[cb & 3] + imm);
+    return lds_read_tr_pair(smem + pv_lo[cb & 3] + imm, smem + pv_hi[cb & 3] + imm);
+  };
+  auto step_of = [](int t) { return (t % kNumBufs) == kNumBufs - 1 ? -(kNumBufs - 1) * kBufBytes : kBufBytes; };
+  auto advance_qk = [&](int t) {  // from tile t's buffer to tile t+1's
+    const int s = step_of(t);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) qk_a[k] += s;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) qk_b[k] += s;
+  };
+  auto advance_pv = [&](int t) {
+    const int s = step_of(t);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      pv_lo[k] += s;
+      pv_hi[k] += s;
+    }
   };
 
   f32x16 o[16];
@@ -279,120 +334,192 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
   const float scale_log2 = a.scale_log2;
   asm volatile("" ::"s"(scale_log2), "s"(ntiles), "s"(ntok));
 
-  for (int t = 0; t < ntiles; ++t) {
-    {  // tile t is in LDS for every wave; every wave is done with tile t-1's buffer
-      const int younger = ntiles - 1 - t;
-      dma_wait_tiles(younger < kAhead - 1 ? younger : kAhead - 1);
+  // ---- online softmax of one tile's raw scores sc (element e = token (e/4)*8 + 4 hf + e%4 of
+  // the tile), in base 2 with the scale folded into the exponent's FMA, cut into stages so that
+  // its instructions can ride between the MFMAs of the next tile's scores.  Masked keys get a raw
+  // score of -inf.  Output: P in bf16 (pk), already in the B layout of the weighted sum.
+  bf16x8 pk[2];
+  float mx[5], mt = 0.f, alpha = 1.f;
+  bool rescale = false;  // wave-uniform
+  // Stage s runs in score slot s: 0-2 the tile max and the new reference, then one probability in
+  // every second slot (3, 5, .., 33), so no slot holds more VALU work than one MFMA's duration.
+  auto softmax_stage = [&](int s, int cnt, f32x16& sc) {
+    if (s == 0) {
+      if (cnt < kTile) {  // wave-uniform: only the last tile of a range can be partial
+        const int lim = cnt - 4 * hf;  // element e is valid iff (e/4)*8 + e%4 < lim
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if ((e >> 2) * 8 + (e & 3) >= lim) sc[e] = -INFINITY;
+      }
+#pragma unroll
+      for (int i = 0; i < 5; ++i) mx[i] = max3(sc[3 * i], sc[3 * i + 1], sc[3 * i + 2]);
+    } else if (s == 1) {  // lanes l and l^32 hold the same head
+      mt = fmaxf(max3(mx[0], mx[1], mx[2]), max3(mx[3], mx[4], sc[15]));
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+      mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
+    } else if (s == 2) {
+      // Branch-free on purpose: a branch here lets the compiler duplicate the rest of the score
+      // chain per outcome.  O itself is rescaled right before the sum, outside the chain.
+      const bool raise = __any(mt > m_run + kRescaleSlack);  // wave-uniform
+      const float m_new = raise ? fmaxf(m_run, mt) : m_run;
+      rescale = raise && started;  // O and l hold something: rescale them to the new reference
+      alpha = rescale ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+      l_run *= alpha;
+      m_run = m_new;
+      started = started || raise;
+    } else if (s >= 3 && s < 35 && (s & 1)) {
+      const int e = (s - 3) >> 1;
+      const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], scale_log2, -m_run));
+      l_run += pv;
+      pk[e >> 3][e & 7] = (__bf16)pv;
+      // keep this stage here: without the pin the compiler sinks all of them to the first use
+      asm volatile("" : "+v"(pk[e >> 3]), "+v"(l_run));
     }
-    __syncthreads();
+  };
+  constexpr int kSoftmaxStages = 35;
+
+  // ---- scores of tile 0 (nothing to overlap yet); every wave's part of it has landed
+  __builtin_amdgcn_s_barrier();
+  bf16x8 ring[4];
+  f32x16 sa, sb;  // raw scores: the two buffers swap roles every tile (no copy between them)
+#pragma unroll
+  for (int g = 0; g < 4; ++g) ring[g] = read_qk(g);
+#pragma unroll
+  for (int ks = 0; ks < 36; ++ks) {
+    if (ks == 0)
+      mfma_first_v(sa, ring[0], q[0]);
+    else if (ks < 35)
+      mfma_acc_v(sa, ring[ks & 3], q[ks]);
+    else
+      mfma_acc_v_last(sa, ring[ks & 3], q[ks]);
+    if (ks + 4 < 36) ring[ks & 3] = read_qk(ks + 4);
+  }
+  if (ntiles > 1) {  // tile 1 has landed everywhere; start its operand reads
+    dma_wait_tiles(ntiles > 2 ? 1 : 0);
+    __builtin_amdgcn_s_barrier();
+    advance_qk(0);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) ring[g] = read_qk(g);
+  }
+  // page id of tile 3 (the first one the loop streams in)
+  int page_ahead = ntiles > 3 ? __builtin_amdgcn_readfirstlane(lds_pages[3 >> 1]) : 0;
+
+  // ---- steady state, iteration t: scores of tile t+1 with the softmax of tile t riding in the
+  // gaps of that MFMA chain, then the weighted sum of tile t.  Tile t+3 streams in meanwhile, into
+  // the buffer tile t-1 used.  One barrier per tile sits four MFMAs before the end of the sum: by
+  // then every read of tile t has completed and tile t+2 has landed, so the operand reads of tile
+  // t+2's scores start while the last four sum MFMAs execute.
+  // The last iteration scores a stale buffer (its result is never used) to keep a single copy of
+  // the softmax and the sum in the code.
+  auto iteration = [&](int t, f32x16& sc, f32x16& sn) {
     const int cnt = tile_count(t);
-    // The next tile to stream in goes to the buffer tile t-1 used.
-    const int tn = t + kAhead;
+    const int tn = t + kNumBufs - 1;
+    // Past the last tile the nine loads still issue (a branch per load in the MFMA stream costs
+    // more than the load), but every lane then reads the same 16 bytes at the start of the pool,
+    // into the buffer of tile t-1, which nothing reads again.
     const bool more = tn < ntiles;
-    const uint16_t* nsrc = more ? tile_src(tn) : pool;
+    const uint16_t* nsrc = more ? row_of(tn, page_ahead) : pool;
     const int ncnt = more ? tile_count(tn) : 0;
     const uint32_t ndst = lds_addr(smem) + (tn % kNumBufs) * kBufBytes;
-    // The per-lane DMA addresses are loop-invariant; recomputing them (a few VALU ops) is far
-    // cheaper than the registers LICM would pin across the loop, so hide the lane id from it.
-    int lane_v = lane;
-    asm volatile("" : "+v"(lane_v));
+    // The per-lane DMA offsets are loop-invariant; recomputing them (one XOR each) is cheaper than
+    // the registers LICM would pin across the loop, so hide the lane id from it.
+    uint32_t lane16 = lane * 16;
+    asm volatile("" : "+v"(lane16));
+    lane16 = more ? lane16 : 0u;
 
-    // One stream of 68 MFMAs: 36 for the scores (K = 512 latent + 64 RoPE in steps of 16), then
-    // 32 for the weighted sum (16 latent blocks x 2 token steps).  Their A operands come from LDS
-    // through a 4-deep register ring: the read for MFMA g + 4 is issued right after MFMA g, so
-    // LDS latency hides behind MFMAs; the score tail already fetches the first weighted-sum
-    // operands (they do not depend on the softmax), which land while the softmax runs.  The next
-    // tile's 9 load instructions are spread over the score MFMAs, at the same slots in all four
-    // waves (staggering them across waves measured half again slower).
-    bf16x8 ring[4];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) ring[g] = read_op(g);
-
-    // ---- raw scores S^T (32 tokens x 32 heads)
-    f32x16 sc;
+    int pid_v = 0;
 #pragma unroll
     for (int ks = 0; ks < 36; ++ks) {
       if (ks == 0)
-        mfma_first_v(sc, ring[0], q[0]);
+        mfma_first_v(sn, ring[0], q[0]);
+      else if (ks < 35)
+        mfma_acc_v(sn, ring[ks & 3], q[ks]);
       else
-        mfma_acc_v(sc, ring[ks & 3], q[ks]);
-      ring[ks & 3] = read_op(ks + 4);
-      if ((ks & 3) == 1 && more) dma_step(nsrc, ncnt, ndst, ks >> 2, lane_v);
+        mfma_acc_v_last(sn, ring[ks & 3], q[ks]);
+      ring[ks & 3] = ks + 4 < 36 ? read_qk(ks + 4) : read_pv(ks + 4 - 36);
+      if ((ks & 3) == 1) dma_step(nsrc, ncnt, ndst, ks >> 2, lane16);
+      if (ks < kSoftmaxStages) softmax_stage(ks, cnt, sc);
+      if (ks == 12) pid_v = lds_pages[((t + kNumBufs) >> 1) < npages ? (t + kNumBufs) >> 1 : 0];
+      __builtin_amdgcn_sched_barrier(0);
     }
-    wait_mfma_result(sc);
-
-    // ---- online softmax in base 2 (scale folded into the exponent's FMA); element e of sc is
-    // token (e/4)*8 + 4 hf + e%4 of the tile.  Masked keys get a raw score of -inf.
-    if (cnt < kTile) {  // wave-uniform: only the last tile of a range can be partial
-      const int lim = cnt - 4 * hf;  // element e is valid iff (e/4)*8 + e%4 < lim
+    if (rescale) {
+      acc_wait_mfma();
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if ((e >> 2) * 8 + (e & 3) >= lim) sc[e] = -INFINITY;
+      for (int cb = 0; cb < 16; ++cb) acc_scale(o[cb], alpha);
+      asm volatile("s_nop 4" ::: "memory");
     }
-    float mt = sc[0];
-#pragma unroll
-    for (int e = 1; e < 16; ++e) mt = fmaxf(mt, sc[e]);
-    {  // lanes l and l^32 hold the same head
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
-      mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
-    }
-    if (__any(mt > m_run + kRescaleSlack)) {
-      const float m_new = fmaxf(m_run, mt);
-      if (started) {  // O and l hold something: rescale them to the new reference
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-        acc_wait_mfma();
-#pragma unroll
-        for (int cb = 0; cb < 16; ++cb) acc_scale(o[cb], alpha);
-        asm volatile("s_nop 4" ::: "memory");
-      }
-      m_run = m_new;
-      started = true;
-    }
-    bf16x8 pk[2];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * kk + j], scale_log2, -m_run));
-        l_run += pv;
-        pk[kk][j] = (__bf16)pv;
-      }
     pin_after_valu(pk[0], pk[1]);
 
-    // ---- O^T (latent x heads) += tile^T * P^T.  k slot j of lane half hf in token step kk is
-    // token 16 kk + (j/4)*8 + 4 hf + j%4; the transposed read gives lane l latent column l%32 of
-    // 4 such tokens (source lane s of each 16-lane group supplies token row s/4, columns
-    // 4(s%4)..+3).
 #pragma unroll
     for (int m = 0; m < 32; ++m) {
       mfma_acc_a(o[m >> 1], ring[m & 3], pk[m & 1]);
-      if (m + 4 < 32) ring[m & 3] = read_op(36 + m + 4);
+      if (m + 4 < 32) {
+        ring[m & 3] = read_pv(m + 4);
+      } else if (t + 2 < ntiles) {
+        // Every iteration issues exactly nine loads, so "all but the youngest nine have landed"
+        // means tile t+2 is in.
+        if (m == 28) {  // every read of tile t done, tile t+2 landed: publish
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          dma_wait_tiles(1);
+          __builtin_amdgcn_s_barrier();
+          advance_qk(t + 1);
+        }
+        ring[m & 3] = read_qk(m - 28);
+      }
+      if (m == 8) page_ahead = __builtin_amdgcn_readfirstlane(pid_v);
+      __builtin_amdgcn_sched_barrier(0);
     }
-
-    // advance the read offsets to the next tile's buffer
-    const int step = (t % kNumBufs) == kNumBufs - 1 ? -(kNumBufs - 1) * kBufBytes : kBufBytes;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) qk_a[k] += step;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      qk_b[k] += step;
-      pv_lo[k] += step;
-      pv_hi[k] += step;
-    }
+    advance_pv(t);
+  };
+  // Unrolled twice so that the two score buffers alternate: a loop-carried copy of an MFMA result
+  // (which the compiler cannot see being written) could be placed before the write completes.
+  for (int t = 0; t < ntiles; t += 2) {
+    iteration(t, sa, sb);
+    if (t + 1 < ntiles) iteration(t + 1, sb, sa);
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.0f / l_tot;
+  size_t o_idx;
+  float* lse_ptr;
+  {
+    int lane_e = lane;
+    asm volatile("" : "+v"(lane_e));
+    out_ptrs(lane_e, o_idx, lse_ptr);
+  }
+  // The last loads (stale prefetches) land in LDS before the staging below reuses it, and every
+  // wave has finished reading the tile buffers.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
   acc_wait_mfma();
+  if (a.final_out) {
 #pragma unroll
-  for (int cb = 0; cb < 16; ++cb)
+    for (int cb = 0; cb < 16; ++cb)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      f32x4 v = {acc_read_scaled(o[cb][4 * g], inv), acc_read_scaled(o[cb][4 * g + 1], inv),
-                 acc_read_scaled(o[cb][4 * g + 2], inv), acc_read_scaled(o[cb][4 * g + 3], inv)};
-      *(f32x4*)(o_ptr + 32 * cb + 8 * g) = v;
-    }
+      for (int g = 0; g < 4; ++g) {
+        f32x4 v = {acc_read_scaled(o[cb][4 * g], inv), acc_read_scaled(o[cb][4 * g + 1], inv),
+                   acc_read_scaled(o[cb][4 * g + 2], inv), acc_read_scaled(o[cb][4 * g + 3], inv)};
+        store4(o_idx, cb, g, v);
+      }
+  } else {
+    // bf16 partial rows go out through LDS: each lane holds 4-value pieces of one head's row, so
+    // direct stores would write 32 rows x 16 B per instruction; staged, one store writes one
+    // whole 1 KiB row.  Rows are 1040 B apart in LDS (2-way bank conflicts on the writes).
+    constexpr int kStageRow = kDc * 2 + 16;
+    MLA_LDS char* stage = smem + wave * (32 * kStageRow);
+#pragma unroll
+    for (int cb = 0; cb < 16; ++cb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const u32x2 v = {pack_bf16x2(acc_read_scaled(o[cb][4 * g], inv), acc_read_scaled(o[cb][4 * g + 1], inv)),
+                         pack_bf16x2(acc_read_scaled(o[cb][4 * g + 2], inv), acc_read_scaled(o[cb][4 * g + 3], inv))};
+        *(MLA_LDS u32x2*)(stage + l32 * kStageRow + (32 * cb + 8 * g + 4 * hf) * 2) = v;
+      }
+    uint16_t* rows = (uint16_t*)a.o_out + (w.out_row + wave * 32) * kDc + 8 * lane;
+#pragma unroll 8
+    for (int r = 0; r < 32; ++r)
+      *(u32x4*)(rows + (size_t)r * kDc) = *(const MLA_LDS u32x4*)(stage + r * kStageRow + 16 * lane);
+  }
   if (hf == 0 && lse_ptr) *lse_ptr = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
 }
 
@@ -452,7 +579,7 @@ __global__ __launch_bounds__(256) void decode_attn_f32_kernel(AttnArgs a) {
     m_run = m_new;
     __syncthreads();
   }
-  float* o_ptr = a.o_out + (w.out_row + h) * kDc;
+  float* o_ptr = (float*)a.o_out + (w.out_row + h) * kDc;
   const bool empty = w.tok_end <= w.tok_begin;
   o_ptr[tid] = empty ? 0.f : acc0 / l_run;
   o_ptr[tid + 256] = empty ? 0.f : acc1 / l_run;
@@ -472,7 +599,21 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-__global__ __launch_bounds__(256) void lse_merge_kernel(const float* __restrict__ o_part,
+// Lane l's 8 partial values of split k (latent columns 8 l .. 8 l + 7), widened to fp32.
+__device__ __forceinline__ void load_part8(const float* p, f32x4& x0, f32x4& x1) {
+  x0 = ((const f32x4*)p)[0];
+  x1 = ((const f32x4*)p)[1];
+}
+__device__ __forceinline__ void load_part8(const uint16_t* p, f32x4& x0, f32x4& x1) {
+  const u32x4 u = *(const u32x4*)p;
+  x0 = f32x4{__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xffff0000u), __uint_as_float(u[1] << 16),
+             __uint_as_float(u[1] & 0xffff0000u)};
+  x1 = f32x4{__uint_as_float(u[2] << 16), __uint_as_float(u[2] & 0xffff0000u), __uint_as_float(u[3] << 16),
+             __uint_as_float(u[3] & 0xffff0000u)};
+}
+
+template <typename PartT>
+__global__ __launch_bounds__(256) void lse_merge_kernel(const PartT* __restrict__ o_part,
                                                         const float* __restrict__ lse_part, float* __restrict__ o_lat,
                                                         float* __restrict__ lse, int num_splits) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -481,7 +622,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const float* __restrict_
   const int row = rh / kHeads, h = rh % kHeads;
   const size_t base = (size_t)row * num_splits * kHeads + h;  // split k at base + k * kHeads
   const float* lp = lse_part + base;
-  const float* op = o_part + base * kDc + 8 * lane;
+  const PartT* op = o_part + base * kDc + 8 * lane;
   constexpr float kLog2e = 1.4426950408889634f;
   auto lse_of = [&](int k) { return k < num_splits ? lp[(size_t)k * kHeads] : -INFINITY; };
 
@@ -490,9 +631,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const float* __restrict_
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int k = kb + j < num_splits ? kb + j : num_splits - 1;
-      const f32x4* src = (const f32x4*)(op + (size_t)k * kHeads * kDc);
-      x0[j] = src[0];
-      x1[j] = src[1];
+      load_part8(op + (size_t)k * kHeads * kDc, x0[j], x1[j]);
     }
   };
   load_batch(0);  // does not depend on the weights: in flight while they are formed
@@ -534,10 +673,15 @@ hipError_t launch_decode_attn(const AttnArgs& a, int rows, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_lse_merge(const float* o_part, const float* lse_part, float* o_lat, float* lse, int rows,
-                            int num_splits, hipStream_t stream) {
-  hipLaunchKernelGGL(lse_merge_kernel, dim3(rows * (kHeads / 4)), dim3(256), 0, stream, o_part, lse_part, o_lat,
-                     lse, num_splits);
+hipError_t launch_lse_merge(const void* o_part, bool part_bf16, const float* lse_part, float* o_lat, float* lse,
+                            int rows, int num_splits, hipStream_t stream) {
+  const dim3 grid(rows * (kHeads / 4));
+  if (part_bf16)
+    hipLaunchKernelGGL(lse_merge_kernel<uint16_t>, grid, dim3(256), 0, stream, (const uint16_t*)o_part, lse_part,
+                       o_lat, lse, num_splits);
+  else
+    hipLaunchKernelGGL(lse_merge_kernel<float>, grid, dim3(256), 0, stream, (const float*)o_part, lse_part, o_lat,
+                       lse, num_splits);
   return hipGetLastError();
 }
 

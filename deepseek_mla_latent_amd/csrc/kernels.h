@@ -22,7 +22,8 @@ struct AttnArgs {
   const void* pool;            // (P,64,576)
   const int32_t* block_table;  // (B,max_pages)
   const int32_t* seq_lens;     // (B)
-  float* o_out;                // final o_lat (B,S,H,512), or partials (B*S, splits, H, 512)
+  void* o_out;                 // final o_lat (B,S,H,512) fp32, or partials (B*S, splits, H, 512):
+                               // bf16 for the bf16 kernel, fp32 for the fp32 kernel
   float* lse_out;              // final lse (B,S,H) (may be null), or partial lse (B*S, splits, H)
   int B, S, max_pages, pages_per_split, num_splits, causal, final_out, dtype_bf16;
   float scale;       // softmax scale
@@ -31,9 +32,10 @@ struct AttnArgs {
 
 // decode attention over rows = B*S (b, i) pairs x num_splits page ranges
 hipError_t launch_decode_attn(const AttnArgs& a, int rows, hipStream_t stream);
-// merge of (rows, splits, H) partials into o_lat (rows, H, 512) and lse (rows, H) (lse may be null)
-hipError_t launch_lse_merge(const float* o_part, const float* lse_part, float* o_lat, float* lse, int rows,
-                            int num_splits, hipStream_t stream);
+// merge of (rows, splits, H) partials (bf16 or fp32) into o_lat (rows, H, 512) and lse (rows, H)
+// (lse may be null)
+hipError_t launch_lse_merge(const void* o_part, bool part_bf16, const float* lse_part, float* o_lat, float* lse,
+                            int rows, int num_splits, hipStream_t stream);
 // q_lat[n,h,:] = W_UK[h] q_nope[n,h,:] for n < tokens
 hipError_t launch_absorb_q(const void* q_nope, const void* w_uk, void* q_lat, int tokens, bool bf16,
                            hipStream_t stream);

@@ -71,10 +71,15 @@ SplitPlan plan_splits(const mla_params* p, int requested, int cus) {
   return {s, pps};
 }
 
+// Split partials: o (rows, splits, H, d_c) in the input dtype (bf16 partials carry 8 mantissa bits,
+// far inside the bf16 tolerance; they halve the bytes written and merged), then lse (rows, splits, H)
+// fp32.  The o block is a multiple of 16 bytes, so lse stays aligned.
+size_t part_elem_bytes(const mla_params* p) { return p->dtype == MLA_BF16 ? 2 : 4; }
+
 size_t workspace_for(const mla_params* p, int splits) {
   if (splits <= 1) return 0;
   const size_t n = (size_t)tokens_of(p) * splits * mla::kHeads;
-  return n * mla::kDc * sizeof(float) + n * sizeof(float);
+  return n * mla::kDc * part_elem_bytes(p) + n * sizeof(float);
 }
 
 }  // namespace
@@ -171,13 +176,14 @@ mla_status mla_decode_attn(const void* q_lat, const void* q_pe, const void* kv_p
     if (mla::launch_decode_attn(a, rows, s) != hipSuccess) return MLA_ERR_LAUNCH;
     return MLA_OK;
   }
-  float* o_part = (float*)workspace;
-  float* lse_part = o_part + (size_t)rows * plan.splits * mla::kHeads * mla::kDc;
+  char* o_part = (char*)workspace;
+  float* lse_part = (float*)(o_part + (size_t)rows * plan.splits * mla::kHeads * mla::kDc * part_elem_bytes(p));
   a.o_out = o_part;
   a.lse_out = lse_part;
   a.final_out = 0;
   if (mla::launch_decode_attn(a, rows, s) != hipSuccess) return MLA_ERR_LAUNCH;
-  if (mla::launch_lse_merge(o_part, lse_part, o_lat, lse, rows, plan.splits, s) != hipSuccess) return MLA_ERR_LAUNCH;
+  if (mla::launch_lse_merge(o_part, p->dtype == MLA_BF16, lse_part, o_lat, lse, rows, plan.splits, s) != hipSuccess)
+    return MLA_ERR_LAUNCH;
   return MLA_OK;
 }
 

@@ -76,7 +76,8 @@ def test_attention_errors():
     assert _attn(P(softmax_scale=float("inf"))) == -2
     # explicit split count: workspace size is host-computable, no device query
     need = lib.mla_decode_workspace_bytes(ctypes.byref(P()), 2)
-    assert need == 2 * 1 * 2 * 128 * (512 + 1) * 4
+    assert need == 2 * 1 * 2 * 128 * (512 * 2 + 4)  # bf16 partials + fp32 lse
+    assert lib.mla_decode_workspace_bytes(ctypes.byref(P(dtype=binding.MLA_F32)), 2) == 2 * 1 * 2 * 128 * (512 + 1) * 4
     assert _attn(P(), ws=None, ws_bytes=0, splits=2) == -1
     assert _attn(P(), ws=FAKE, ws_bytes=need - 4, splits=2) == -5
     assert _attn(P(), ws=MISALIGNED, ws_bytes=need, splits=2) == -4
