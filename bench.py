@@ -28,7 +28,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_attn_b32_t4096_hbm_counters.json")
-ATTN_SOURCE = os.path.join(ROOT, "deepseek_mla_latent_amd", "csrc", "decode_attn.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "deepseek_mla_latent_amd", "csrc", f) for f in ("decode_attn.hip", "common.h")]
 METRIC = "MLA absorbed-decode tokens/s per layer + % of HBM/MFMA roofline, 1 GPU"
 MALL_BYTES = 256 * 2 ** 20
 
@@ -38,7 +38,10 @@ def _rank_env():
 
 
 def _source_hash() -> str:
-    return hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(launch_bytes_key: str):

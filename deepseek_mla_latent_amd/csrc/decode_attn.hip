@@ -437,7 +437,7 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
       else
         mfma_acc_v_last(sn, ring[ks & 3], q[ks]);
       ring[ks & 3] = ks + 4 < 36 ? read_qk(ks + 4) : read_pv(ks + 4 - 36);
-      if ((ks & 3) == 1) dma_step(nsrc, ncnt, ndst, ks >> 2, lane16);
+      if (ks % 7 == 2) dma_step(nsrc, ncnt, ndst, ks / 7, lane16);  // loads 0-4 (slots 2, 9, .., 30)
       if (ks < kSoftmaxStages) softmax_stage(ks, cnt, sc);
       if (ks == 12) pid_v = lds_pages[((t + kNumBufs) >> 1) < npages ? (t + kNumBufs) >> 1 : 0];
       __builtin_amdgcn_sched_barrier(0);
@@ -466,6 +466,7 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
         }
         ring[m & 3] = read_qk(m - 28);
       }
+      if (m % 7 == 3 && m < 28) dma_step(nsrc, ncnt, ndst, 5 + m / 7, lane16);  // loads 5-8 (slots 3, .., 24)
       if (m == 8) page_ahead = __builtin_amdgcn_readfirstlane(pid_v);
       __builtin_amdgcn_sched_barrier(0);
     }

@@ -220,8 +220,8 @@ __global__ __launch_bounds__(256, 1) void out_proj_bf16_kernel(const float* __re
         }
         if (n < tokens) {
           const int v = 64 * vh + 32 * vb + 8 * g + 4 * hf;
-          const uint2 pk = {pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
-          *(uint2*)(out + ((size_t)n * kHeads + h) * kDh + v) = pk;
+          const u32x2 pk = {pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
+          *(u32x2*)(out + ((size_t)n * kHeads + h) * kDh + v) = pk;
         }
       }
     }

@@ -168,6 +168,23 @@ def test_attention_page_permutation_is_bitwise_invisible():
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
+def test_attention_rescale_path():
+    """Later tiles score far above earlier ones, so the running max is raised (and O rescaled) many
+    times: rows of tile t are scaled by 1 + t before rounding to bf16."""
+    say("attn rescale path")
+    w = gen.small_workload(2, 1, ragged=(290, 330), dtype="bf16", paged=True)
+    x = gen.generate(w, 27, poison_unused=True)
+    pool = gen.bf16_bits_to_f32(x.pool).copy()
+    for b in range(w.batch):
+        for j in range(int(x.seq_lens[b])):
+            page, slot = x.block_table[b, j // 64], j % 64
+            pool[page, slot] *= np.float32(1 + j // 32)
+    x = gen.DecodeInputs(w, x.seq_lens, x.block_table, gen.round_to_bf16_bits(pool), x.q_nope, x.q_pe, x.w_uk,
+                         x.w_uv)
+    for splits in (1, 2):
+        _attn_case(x, 28, splits)
+
+
 # ------------------------------------------------------------------------------------ end to end
 def _end_to_end(x, seqs, heads, splits=0):
     """GPU q_nope -> q_lat -> (o_lat, lse) -> out against the non-absorbed oracle on sampled (b, h)."""
