@@ -600,18 +600,33 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// Lane l's 8 partial values of split k (latent columns 8 l .. 8 l + 7), widened to fp32.
-__device__ __forceinline__ void load_part8(const float* p, f32x4& x0, f32x4& x1) {
-  x0 = ((const f32x4*)p)[0];
-  x1 = ((const f32x4*)p)[1];
-}
-__device__ __forceinline__ void load_part8(const uint16_t* p, f32x4& x0, f32x4& x1) {
-  const u32x4 u = *(const u32x4*)p;
-  x0 = f32x4{__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xffff0000u), __uint_as_float(u[1] << 16),
-             __uint_as_float(u[1] & 0xffff0000u)};
-  x1 = f32x4{__uint_as_float(u[2] << 16), __uint_as_float(u[2] & 0xffff0000u), __uint_as_float(u[3] << 16),
-             __uint_as_float(u[3] & 0xffff0000u)};
-}
+// Lane l's 8 partial values of one split (latent columns 8 l .. 8 l + 7), kept as loaded (bf16
+// words stay packed until use: the register count decides how many merge waves fit on a CU).
+template <typename PartT>
+struct PartRow;
+template <>
+struct PartRow<float> {
+  f32x4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = ((const f32x4*)p)[0];
+    b = ((const f32x4*)p)[1];
+  }
+  __device__ __forceinline__ f32x4 lo() const { return a; }
+  __device__ __forceinline__ f32x4 hi() const { return b; }
+};
+template <>
+struct PartRow<uint16_t> {
+  u32x4 u;
+  __device__ __forceinline__ void load(const uint16_t* p) { u = *(const u32x4*)p; }
+  __device__ __forceinline__ f32x4 lo() const {
+    return f32x4{__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xffff0000u), __uint_as_float(u[1] << 16),
+                 __uint_as_float(u[1] & 0xffff0000u)};
+  }
+  __device__ __forceinline__ f32x4 hi() const {
+    return f32x4{__uint_as_float(u[2] << 16), __uint_as_float(u[2] & 0xffff0000u), __uint_as_float(u[3] << 16),
+                 __uint_as_float(u[3] & 0xffff0000u)};
+  }
+};
 
 template <typename PartT>
 __global__ __launch_bounds__(256) void lse_merge_kernel(const PartT* __restrict__ o_part,
@@ -627,12 +642,12 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const PartT* __restrict_
   constexpr float kLog2e = 1.4426950408889634f;
   auto lse_of = [&](int k) { return k < num_splits ? lp[(size_t)k * kHeads] : -INFINITY; };
 
-  f32x4 x0[8], x1[8];
+  PartRow<PartT> x[8];
   auto load_batch = [&](int kb) {  // splits kb .. kb+7 (clamped to the last one)
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int k = kb + j < num_splits ? kb + j : num_splits - 1;
-      load_part8(op + (size_t)k * kHeads * kDc, x0[j], x1[j]);
+      x[j].load(op + (size_t)k * kHeads * kDc);
     }
   };
   load_batch(0);  // does not depend on the weights: in flight while they are formed
@@ -653,8 +668,8 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const PartT* __restrict_
                           ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_lane), (kb & 63) + j))
                           : 0.f;
       sum += w;
-      a0 += w * x0[j];
-      a1 += w * x1[j];
+      a0 += w * x[j].lo();
+      a1 += w * x[j].hi();
     }
     if (kb + 8 < num_splits) load_batch(kb + 8);
   }

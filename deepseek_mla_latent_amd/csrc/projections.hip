@@ -101,27 +101,33 @@ __global__ __launch_bounds__(256) void absorb_q_kernel(const void* __restrict__ 
 // same XCD, so the second read of o_lat[., h, .] can come from that XCD's L2.
 //
 // Wave w owns latent rows [128 w, +128): it copies W_UV[h][those rows][64 vh .. +64) into LDS
-// with direct-to-LDS loads (the only rows it ever reads, so no barrier is needed) and loads the
-// matching o_lat slice of a 32-token block into registers, all before the first MFMA.  Per token
-// block it computes the partial D(64 values x 32 tokens) over its 128 latent rows: A = W_UV^T by
-// transposed LDS reads, B = o_lat^T split into hi + lo bf16 parts (two MFMAs, so the fp32
-// latent input keeps about 16 mantissa bits).  The four partials are summed through LDS.
+// and, per 32-token block, the matching o_lat slices (512 B per token, two tokens per 1 KiB
+// direct-to-LDS load), so every global read is a whole 1 KiB.  Per token block it computes the
+// partial D(64 values x 32 tokens) over its 128 latent rows: A = W_UV^T by transposed LDS reads,
+// B = o_lat^T split into hi + lo bf16 parts (two MFMAs, so the fp32 latent input keeps about 16
+// mantissa bits).  The four partials are summed through LDS.  A wave only ever reads the LDS rows
+// it loaded itself, so only the sums need barriers.
 constexpr int kOpRowBytes = 128;  // one latent row of the 64-value slice
 // 16-byte unit u of latent row c is stored at unit u ^ op_swz(c): the transposed reads touch
 // 4 consecutive rows x 64 B, which this spreads over all 64 banks.
 __device__ __forceinline__ int op_swz(int c) { return ((c >> 1) & 1) << 2; }
+// o_lat staging: token n's 512 B slice as 32 units of 16 B, unit u stored at u ^ (n & 15), so the
+// 32 tokens' B-operand reads at one column hit 16 different bank groups (2-way at most).
+constexpr int kOStageBytes = 32 * 512;  // per wave
 
 __global__ __launch_bounds__(256, 1) void out_proj_bf16_kernel(const float* __restrict__ o_lat,
                                                                const uint16_t* __restrict__ w_uv,
                                                                uint16_t* __restrict__ out, int tokens) {
   __shared__ __attribute__((aligned(1024))) char wl_raw[kDc * kOpRowBytes];  // 64 KiB
-  __shared__ float red[4 * 2 * 16 * 64];                                     // 32 KiB
+  __shared__ __attribute__((aligned(1024))) char os_raw[4 * kOStageBytes];    // 64 KiB, then the sums
   MLA_LDS char* const wl = (MLA_LDS char*)wl_raw;
+  MLA_LDS char* const os = (MLA_LDS char*)os_raw;
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   const int h = id >> 1, vh = id & 1;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, l32 = lane & 31, hf = lane >> 5;
   const int c0 = 128 * wave;
+  MLA_LDS char* const ow = os + wave * kOStageBytes;
 
   {  // W slice rows [c0, c0 + 128): 16 loads of 8 rows x 128 B
     const char* src = (const char*)(w_uv + (size_t)h * kDc * kDh + 64 * vh);
@@ -133,22 +139,19 @@ __global__ __launch_bounds__(256, 1) void out_proj_bf16_kernel(const float* __re
                                        (MLA_LDS void*)(wl + (c0 + 8 * i) * kOpRowBytes), 16, 0, 0);
     }
   }
-  // B operand of k step ks for lane (token 32 nb + l32, half hf): latent c0 + 16 ks + 8 hf + j.
-  f32x4 x[16];
+  // o_lat slices of block nb: load i covers tokens 2i, 2i+1 (lane halves); a token past the end
+  // reads token 0 (its column is not stored).
   auto load_o = [&](int nb) {
-    int n = 32 * nb + l32;
-    n = n < tokens ? n : 0;
-    const f32x4* p = (const f32x4*)(o_lat + ((size_t)n * kHeads + h) * kDc + c0 + 8 * hf);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      x[2 * ks] = p[4 * ks];
-      x[2 * ks + 1] = p[4 * ks + 1];
+    for (int i = 0; i < 16; ++i) {
+      const int t = 2 * i + hf;
+      int n = 32 * nb + t;
+      n = n < tokens ? n : 0;
+      const int u = l32 ^ (t & 15);
+      const char* src = (const char*)(o_lat + ((size_t)n * kHeads + h) * kDc + c0) + u * 16;
+      __builtin_amdgcn_global_load_lds((const MLA_GLOBAL void*)src, (MLA_LDS void*)(ow + i * 1024), 16, 0, 0);
     }
   };
-  load_o(0);
-#pragma unroll
-  for (int k = 0; k < 16; ++k) settle(x[k]);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's LDS rows have landed
 
   // Transposed A read (32 values x 8 latent rows per pair): in each 16-lane group, source lane
   // s supplies latent row c + s/4 and value columns 4 (s%4) .. +3 of the group's 16 columns.
@@ -161,10 +164,17 @@ __global__ __launch_bounds__(256, 1) void out_proj_bf16_kernel(const float* __re
 
   const int nblocks = (tokens + 31) / 32;
   for (int nb = 0; nb < nblocks; ++nb) {
+    load_o(nb);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's W rows and o slices have landed
+    // B operand of k step ks for lane (token l32, half hf): latent c0 + 16 ks + 8 hf + j, i.e.
+    // units 4 ks + 2 hf and 4 ks + 2 hf + 1 of the token's slice.
     bf16x8 bh[8], bl[8];
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const f32x4 a = x[2 * ks], b = x[2 * ks + 1];
+      const MLA_LDS char* row = ow + (l32 >> 1) * 1024 + (l32 & 1) * 512;
+      const int u0 = (4 * ks + 2 * hf) ^ (l32 & 15);
+      const f32x4 a = *(const MLA_LDS f32x4*)(row + u0 * 16);
+      const f32x4 b = *(const MLA_LDS f32x4*)(row + (u0 ^ 1) * 16);
       const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
       u32x4 hw, lw;
 #pragma unroll
@@ -177,7 +187,6 @@ __global__ __launch_bounds__(256, 1) void out_proj_bf16_kernel(const float* __re
       bh[ks] = __builtin_bit_cast(bf16x8, hw);
       bl[ks] = __builtin_bit_cast(bf16x8, lw);
     }
-    if (nb + 1 < nblocks) load_o(nb + 1);  // in flight during this block's MFMAs
 
     f32x16 acc[2];
 #pragma unroll
@@ -197,9 +206,10 @@ __global__ __launch_bounds__(256, 1) void out_proj_bf16_kernel(const float* __re
         acc[vb] = mfma32x32x16(av, bl[ks], acc[vb]);
       }
 
-    // Sum the four waves' partials.  red[((w * 2 + vb) * 16 + e) * 64 + lane]; element e of
-    // lane l is value 32 vb + (e/4)*8 + 4 (l/32) + e%4 of token l%32.
-    if (nb > 0) __syncthreads();  // the previous block's sums have been read
+    // Sum the four waves' partials in the staging area: red[((w * 2 + vb) * 16 + e) * 64 + lane];
+    // element e of lane l is value 32 vb + (e/4)*8 + 4 (l/32) + e%4 of token l%32.
+    __syncthreads();  // every wave has read its o slices
+    MLA_LDS float* red = (MLA_LDS float*)os;
 #pragma unroll
     for (int vb = 0; vb < 2; ++vb)
 #pragma unroll
@@ -225,6 +235,7 @@ __global__ __launch_bounds__(256, 1) void out_proj_bf16_kernel(const float* __re
         }
       }
     }
+    __syncthreads();  // the sums are read before the next block's slices land in the area
   }
 }
 
