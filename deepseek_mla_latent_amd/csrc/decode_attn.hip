@@ -247,19 +247,30 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
       dma16_s(base, ts * (kRow * 2) + kDc * 2 + u * 16, dst + kRegionA + wave * 1024);
     }
   };
-  // Prologue.  The query loads go first and tile 0 right behind them; the compiler's wait for q
-  // (it cannot see the asm loads, so it waits for everything) then also covers tile 0, which is
-  // needed first anyway.  Tiles 1 and 2 start streaming after that wait.
+  // Prologue.  The query rows come in first, through LDS: each wave copies its 32 heads' q_lat
+  // rows (1 KiB each, one load per row, 16-byte unit u of row r stored at u ^ (r & 15)) into the
+  // tile buffers, which are still free, and reads its B operands from there; q_pe (4 loads) comes
+  // straight from memory.  Then tiles 0-2 start streaming into the buffers.
   bf16x8 q[36];  // this lane's head as the score B operand: [q_lat | q_pe][16 ks + 8 hf .. +7]
   {
-    const size_t qrow = ((size_t)w.b * a.S + w.i) * kHeads + h;
-    const bf16x8* ql = (const bf16x8*)((const uint16_t*)a.q_lat + qrow * kDc + 8 * hf);
-    const bf16x8* qp = (const bf16x8*)((const uint16_t*)a.q_pe + qrow * kDr + 8 * hf);
+    const size_t qrow0 = ((size_t)w.b * a.S + w.i) * kHeads + wave * 32;
+    const char* qsrc = (const char*)((const uint16_t*)a.q_lat + qrow0 * kDc);
+    const uint32_t qdst = lds_addr(smem) + wave * 32 * 1024;
 #pragma unroll
-    for (int ks = 0; ks < 32; ++ks) q[ks] = ql[2 * ks];
+    for (int r = 0; r < 32; ++r) dma16_s(qsrc + r * 1024, (uint32_t)((lane ^ (r & 15)) * 16), qdst + r * 1024);
+    const bf16x8* qp = (const bf16x8*)((const uint16_t*)a.q_pe + (qrow0 + l32) * kDr + 8 * hf);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) q[32 + ks] = qp[2 * ks];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) asm volatile("" ::"v"(q[32 + ks]));
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const MLA_LDS char* qrowp = smem + wave * 32 * 1024 + l32 * 1024;
+#pragma unroll
+    for (int ks = 0; ks < 32; ++ks) q[ks] = lds_read_b128(qrowp + (((2 * ks + hf) ^ (l32 & 15)) * 16));
+#pragma unroll
+    for (int ks = 0; ks < 32; ++ks) asm volatile("" ::"v"(q[ks]));
   }
+  __syncthreads();  // every wave has its q: the buffers take the tiles now
   auto prologue_tile = [&](int t) {
     const uint16_t* src = row_of(t, __builtin_amdgcn_readfirstlane(lds_pages[t >> 1]));
     const int cnt = tile_count(t);
@@ -267,13 +278,8 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int k = 0; k < kDmaPerTile; ++k) dma_step(src, cnt, dst, k, lane * 16);
   };
-  prologue_tile(0);
-  // Wait for q here, once: otherwise the loop inherits "q may be in flight" and carries
-  // vector-memory waits that the in-flight tile loads would then trip.
-#pragma unroll
-  for (int ks = 0; ks < 36; ++ks) asm volatile("" ::"v"(q[ks]));
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  for (int t = 1; t < kNumBufs - 1 && t < ntiles; ++t) prologue_tile(t);
+  for (int t = 0; t < kNumBufs - 1 && t < ntiles; ++t) prologue_tile(t);
+  dma_wait_tiles(ntiles - 1 < 2 ? ntiles - 1 : 2);  // tile 0 has landed (this wave's part)
 
   // Per-lane LDS byte offsets of the swizzled reads, relative to smem; the score offsets follow
   // the tile being scored, the sum offsets the (previous) tile being summed, one buffer per tile.
@@ -378,8 +384,8 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
   };
   constexpr int kSoftmaxStages = 35;
 
-  // ---- scores of tile 0 (nothing to overlap yet); every wave's part of it has landed
-  __builtin_amdgcn_s_barrier();
+  // ---- scores of tile 0 (nothing to overlap yet)
+  __builtin_amdgcn_s_barrier();  // every wave's part of tile 0 has landed
   bf16x8 ring[4];
   f32x16 sa, sb;  // raw scores: the two buffers swap roles every tile (no copy between them)
 #pragma unroll
