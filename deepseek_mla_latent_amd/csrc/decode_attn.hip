@@ -412,9 +412,9 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
 
   // ---- steady state, iteration t: scores of tile t+1 with the softmax of tile t riding in the
   // gaps of that MFMA chain, then the weighted sum of tile t.  Tile t+3 streams in meanwhile, into
-  // the buffer tile t-1 used.  One barrier per tile sits four MFMAs before the end of the sum: by
-  // then every read of tile t has completed and tile t+2 has landed, so the operand reads of tile
-  // t+2's scores start while the last four sum MFMAs execute.
+  // the buffer tile t-1 used.  One barrier per tile follows the sum: every read of tile t has
+  // completed (the sum MFMAs consumed them) and tile t+2 has landed; then the first operand reads
+  // of tile t+2's scores are issued.
   // The last iteration scores a stale buffer (its result is never used) to keep a single copy of
   // the softmax and the sum in the code.
   auto iteration = [&](int t, f32x16& sc, f32x16& sn) {
@@ -438,10 +438,8 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
     for (int ks = 0; ks < 36; ++ks) {
       if (ks == 0)
         mfma_first_v(sn, ring[0], q[0]);
-      else if (ks < 35)
-        mfma_acc_v(sn, ring[ks & 3], q[ks]);
       else
-        mfma_acc_v_last(sn, ring[ks & 3], q[ks]);
+        mfma_acc_v(sn, ring[ks & 3], q[ks]);
       ring[ks & 3] = ks + 4 < 36 ? read_qk(ks + 4) : read_pv(ks + 4 - 36);
       if (ks % 7 == 2) dma_step(nsrc, ncnt, ndst, ks / 7, lane16);  // loads 0-4 (slots 2, 9, .., 30)
       if (ks < kSoftmaxStages) softmax_stage(ks, cnt, sc);
@@ -459,22 +457,17 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int m = 0; m < 32; ++m) {
       mfma_acc_a(o[m >> 1], ring[m & 3], pk[m & 1]);
-      if (m + 4 < 32) {
-        ring[m & 3] = read_pv(m + 4);
-      } else if (t + 2 < ntiles) {
-        // Every iteration issues exactly nine loads, so "all but the youngest nine have landed"
-        // means tile t+2 is in.
-        if (m == 28) {  // every read of tile t done, tile t+2 landed: publish
-          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-          dma_wait_tiles(1);
-          __builtin_amdgcn_s_barrier();
-          advance_qk(t + 1);
-        }
-        ring[m & 3] = read_qk(m - 28);
-      }
+      if (m + 4 < 32) ring[m & 3] = read_pv(m + 4);
       if (m % 7 == 3 && m < 28) dma_step(nsrc, ncnt, ndst, 5 + m / 7, lane16);  // loads 5-8 (slots 3, .., 24)
       if (m == 8) page_ahead = __builtin_amdgcn_readfirstlane(pid_v);
       __builtin_amdgcn_sched_barrier(0);
+    }
+    if (t + 2 < ntiles) {  // every read of tile t done, tile t+2 landed: publish, then prefetch
+      dma_wait_tiles(1);
+      __builtin_amdgcn_s_barrier();
+      advance_qk(t + 1);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) ring[g] = read_qk(g);
     }
     advance_pv(t);
   };
