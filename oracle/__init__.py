@@ -11,10 +11,13 @@ Modules:
 * ``mla_decode`` — fp64 numpy reference of the decode path, written the
   non-absorbed way (K and V up-projected per head), plus the plain
   definitions of the three library calls.
+* ``mla_prefill`` — fp64 reference of prefill in multi-head form (order 1): K/V
+  up-projection of every cached token, then per-head attention over them.
 * ``flops`` — the pages' FLOP convention and the three computation orders of
   both absorptions, counted step by step from index extents; byte counts.
 
-Every function is pinned by ``tests/test_oracle.py`` / ``tests/test_flops.py``
+Every function is pinned by ``tests/test_oracle.py``, ``tests/test_oracle_prefill.py`` and
+``tests/test_flops.py``
 against what the pages print and against closed forms, special cases and
 library routines (see each test's docstring).
 """
