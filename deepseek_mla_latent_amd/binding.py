@@ -24,7 +24,7 @@ STATUS = {
     -5: "MLA_ERR_WORKSPACE", -6: "MLA_ERR_UNSUPPORTED", -7: "MLA_ERR_LAUNCH", -8: "MLA_ERR_DEVICE",
 }
 EXPORTS = ("mla_absorb_q", "mla_decode_workspace_bytes", "mla_decode_num_splits", "mla_decode_attn",
-           "mla_out_proj", "mla_status_str")
+           "mla_out_proj", "mla_prefill_kv_bytes", "mla_prefill_kv_up", "mla_prefill_attn", "mla_status_str")
 
 
 class MlaLibraryMissing(RuntimeError):
@@ -70,6 +70,12 @@ def load_library(path: Optional[str] = None):
     lib.mla_decode_attn.restype = i32
     lib.mla_out_proj.argtypes = [vp, vp, vp, pp, vp]
     lib.mla_out_proj.restype = i32
+    lib.mla_prefill_kv_bytes.argtypes = [pp]
+    lib.mla_prefill_kv_bytes.restype = sz
+    lib.mla_prefill_kv_up.argtypes = [vp, vp, vp, vp, vp, vp, sz, pp, vp]
+    lib.mla_prefill_kv_up.restype = i32
+    lib.mla_prefill_attn.argtypes = [vp, vp, vp, sz, vp, vp, vp, pp, vp]
+    lib.mla_prefill_attn.restype = i32
     lib.mla_status_str.argtypes = [i32]
     lib.mla_status_str.restype = ctypes.c_char_p
     if path is None:
@@ -151,6 +157,30 @@ def mla_out_proj(o_lat, w_uv, out, params: mla_params, stream=None) -> None:
     lib = load_library()
     _check(lib.mla_out_proj(_ptr(o_lat), _ptr(w_uv), _ptr(out), ctypes.byref(params), _stream(stream)),
            "mla_out_proj")
+
+
+def _nbytes(x, given: Optional[int]) -> int:
+    if given is not None:
+        return given
+    return 0 if x is None or isinstance(x, int) else x.numel() * x.element_size()
+
+
+def mla_prefill_kv_bytes(params: mla_params) -> int:
+    return int(load_library().mla_prefill_kv_bytes(ctypes.byref(params)))
+
+
+def mla_prefill_kv_up(kv_pool, block_table, seq_lens, w_uk, w_uv, kv, params: mla_params, stream=None,
+                      kv_bytes: Optional[int] = None) -> None:
+    lib = load_library()
+    _check(lib.mla_prefill_kv_up(_ptr(kv_pool), _ptr(block_table), _ptr(seq_lens), _ptr(w_uk), _ptr(w_uv), _ptr(kv),
+                                 _nbytes(kv, kv_bytes), ctypes.byref(params), _stream(stream)), "mla_prefill_kv_up")
+
+
+def mla_prefill_attn(q_nope, q_pe, kv, seq_lens, out, lse, params: mla_params, stream=None,
+                     kv_bytes: Optional[int] = None) -> None:
+    lib = load_library()
+    _check(lib.mla_prefill_attn(_ptr(q_nope), _ptr(q_pe), _ptr(kv), _nbytes(kv, kv_bytes), _ptr(seq_lens), _ptr(out),
+                                _ptr(lse), ctypes.byref(params), _stream(stream)), "mla_prefill_attn")
 
 
 class DecodeBuffers:

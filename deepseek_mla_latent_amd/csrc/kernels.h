@@ -43,4 +43,25 @@ hipError_t launch_absorb_q(const void* q_nope, const void* w_uk, void* q_lat, in
 hipError_t launch_out_proj(const float* o_lat, const void* w_uv, void* out, int tokens, bool bf16,
                            hipStream_t stream);
 
+// Prefill in multi-head form (bf16).  kv (B,H,Lp,256) = [K_nope | V] per head and token and
+// kpe (B,Lp,64) = the shared RoPE key, Lp = max_pages * 64; rows from seq_lens[b] up to the end of
+// its last page are zeros.
+// Grid: batch x 128 heads x tiles (two pages each); max_pages is the block-table row stride.
+hipError_t launch_kv_up_grid(const void* pool, const int32_t* block_table, const int32_t* seq_lens,
+                             const void* w_uk, const void* w_uv, void* kv, void* kpe, int batch, int max_pages,
+                             int tiles, hipStream_t stream);
+
+struct PrefillArgs {
+  const void* q_nope;  // (B,S,H,128) bf16
+  const void* q_pe;    // (B,S,H,64) bf16
+  const void* kv;      // (B,H,Lp,256) bf16
+  const void* kpe;     // (B,Lp,64) bf16
+  const int32_t* seq_lens;
+  void* out;           // (B,S,H,128) bf16
+  float* lse;          // (B,S,H) or null
+  int B, S, Lp, nqb, causal;
+  float scale_log2;    // softmax scale * log2(e)
+};
+hipError_t launch_prefill_attn(const PrefillArgs& a, hipStream_t stream);
+
 }  // namespace mla

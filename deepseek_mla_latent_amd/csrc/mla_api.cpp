@@ -82,6 +82,21 @@ size_t workspace_for(const mla_params* p, int splits) {
   return n * mla::kDc * part_elem_bytes(p) + n * sizeof(float);
 }
 
+// Prefill buffer: [K_nope | V] (B, H, Lp, 256) then k_pe (B, Lp, 64), bf16, Lp = max_pages * page.
+size_t prefill_kv_bytes(const mla_params* p) {
+  const size_t Lp = (size_t)p->max_pages_per_seq * mla::kPage;
+  return (size_t)p->batch * Lp * ((size_t)mla::kHeads * 2 * mla::kDh + mla::kDr) * 2;
+}
+
+mla_status check_prefill(const mla_params* p) {
+  mla_status st = check_params(p);
+  if (st != MLA_OK) return st;
+  if (p->dtype != MLA_BF16) return MLA_ERR_DTYPE;
+  const int max_pages = (p->max_seq_len + mla::kPage - 1) / mla::kPage;
+  if (p->max_pages_per_seq < max_pages) return MLA_ERR_SHAPE;
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -196,6 +211,61 @@ mla_status mla_out_proj(const float* o_lat, const void* w_uv, void* out, const m
   if (mla::launch_out_proj(o_lat, w_uv, out, (int)tokens_of(p), p->dtype == MLA_BF16, (hipStream_t)stream) !=
       hipSuccess)
     return MLA_ERR_LAUNCH;
+  return MLA_OK;
+}
+
+size_t mla_prefill_kv_bytes(const mla_params* p) {
+  if (check_prefill(p) != MLA_OK) return 0;
+  return prefill_kv_bytes(p);
+}
+
+mla_status mla_prefill_kv_up(const void* kv_pool, const int32_t* block_table, const int32_t* seq_lens,
+                             const void* w_uk, const void* w_uv, void* kv, size_t kv_bytes, const mla_params* p,
+                             void* stream) {
+  mla_status st = check_prefill(p);
+  if (st != MLA_OK) return st;
+  const int pages = (p->max_seq_len + mla::kPage - 1) / mla::kPage;
+  if (p->batch == 0 || pages == 0) return MLA_OK;
+  if (!kv_pool || !block_table || !seq_lens || !w_uk || !w_uv || !kv) return MLA_ERR_NULL;
+  if (!aligned16(kv_pool) || !aligned16(w_uk) || !aligned16(w_uv) || !aligned16(kv)) return MLA_ERR_ALIGN;
+  if (kv_bytes < prefill_kv_bytes(p)) return MLA_ERR_WORKSPACE;
+  if ((int64_t)p->batch * mla::kHeads * ((pages + 1) / 2) > 0x7fffffffLL) return MLA_ERR_SHAPE;
+  char* kpe = (char*)kv + (size_t)p->batch * mla::kHeads * p->max_pages_per_seq * mla::kPage * 2 * mla::kDh * 2;
+  // the grid covers the pages max_seq_len needs; rows are laid out with the table's page stride
+  if (mla::launch_kv_up_grid(kv_pool, block_table, seq_lens, w_uk, w_uv, kv, kpe, p->batch, p->max_pages_per_seq,
+                             (pages + 1) / 2, (hipStream_t)stream) != hipSuccess)
+    return MLA_ERR_LAUNCH;
+  return MLA_OK;
+}
+
+mla_status mla_prefill_attn(const void* q_nope, const void* q_pe, const void* kv, size_t kv_bytes,
+                            const int32_t* seq_lens, void* out, float* lse, const mla_params* p, void* stream) {
+  mla_status st = check_prefill(p);
+  if (st != MLA_OK) return st;
+  if (tokens_of(p) == 0) return MLA_OK;
+  if (!q_nope || !q_pe || !seq_lens || !out) return MLA_ERR_NULL;
+  if (p->max_seq_len > 0 && !kv) return MLA_ERR_NULL;
+  if (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(kv) || !aligned16(out)) return MLA_ERR_ALIGN;
+  if (!std::isfinite(p->softmax_scale)) return MLA_ERR_SHAPE;
+  if (p->max_seq_len > 0 && kv_bytes < prefill_kv_bytes(p)) return MLA_ERR_WORKSPACE;
+  const int nqb = (p->q_len + 127) / 128;
+  if ((int64_t)p->batch * mla::kHeads * nqb > 0x7fffffffLL) return MLA_ERR_SHAPE;
+  mla::PrefillArgs a;
+  a.q_nope = q_nope;
+  a.q_pe = q_pe;
+  a.kv = kv;
+  a.kpe = kv ? (const char*)kv + (size_t)p->batch * mla::kHeads * p->max_pages_per_seq * mla::kPage * 2 * mla::kDh * 2
+             : nullptr;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.lse = lse;
+  a.B = p->batch;
+  a.S = p->q_len;
+  a.Lp = p->max_pages_per_seq * mla::kPage;
+  a.nqb = nqb;
+  a.causal = p->causal ? 1 : 0;
+  a.scale_log2 = (float)((double)p->softmax_scale * 1.4426950408889634);
+  if (mla::launch_prefill_attn(a, (hipStream_t)stream) != hipSuccess) return MLA_ERR_LAUNCH;
   return MLA_OK;
 }
 

@@ -88,6 +88,14 @@ WORKLOADS = {
 }
 WORKLOAD_SEEDS = {name: i + 1 for i, name in enumerate(WORKLOADS)}
 
+# Prefill of a whole prompt in multi-head form: one 4096-token prompt (the 4K context of the
+# DeepSeek-V2 cost estimate), every token a query (S = L), causal, paged cache.
+PREFILL_WORKLOADS = {
+    "prefill_b1_s4096": DecodeWorkload("prefill_b1_s4096", batch=1, q_len=4096, cache_len=4096, dtype="bf16",
+                                       paged=True),
+}
+WORKLOAD_SEEDS.update({name: 101 + i for i, name in enumerate(PREFILL_WORKLOADS)})
+
 
 def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """fp32 -> bf16 bit patterns (uint16), round-to-nearest-even; NaN stays NaN."""
@@ -212,8 +220,9 @@ def generate(w: DecodeWorkload, seed: int, *, poison_unused: bool = False,
 
 
 def generate_named(name: str, *, poison_unused: bool = False) -> DecodeInputs:
-    """The batch for one of the five named workloads, with its fixed seed."""
-    return generate(WORKLOADS[name], WORKLOAD_SEEDS[name], poison_unused=poison_unused)
+    """The batch for one of the named workloads (decode or prefill), with its fixed seed."""
+    w = WORKLOADS[name] if name in WORKLOADS else PREFILL_WORKLOADS[name]
+    return generate(w, WORKLOAD_SEEDS[name], poison_unused=poison_unused)
 
 
 def small_workload(batch: int, q_len: int, cache_len=None, *, dtype: str = "bf16", paged: bool = True,

@@ -1,5 +1,6 @@
 /*
- * mla_latent.h — absorbed Multi-head Latent Attention (MLA) decode on MI355X (gfx950).
+ * mla_latent.h — Multi-head Latent Attention (MLA) on MI355X (gfx950): absorbed decode, and
+ * prefill in multi-head form.
  *
  * One decode step of one MLA layer, as three enqueue-only calls:
  *
@@ -52,9 +53,9 @@ typedef enum {
   MLA_OK = 0,
   MLA_ERR_NULL = -1,        /* a required pointer is NULL */
   MLA_ERR_SHAPE = -2,       /* a size is out of range (batch < 0, q_len < 1, tables too small ...) */
-  MLA_ERR_DTYPE = -3,       /* dtype is not MLA_F32 or MLA_BF16 */
+  MLA_ERR_DTYPE = -3,       /* dtype is not MLA_F32 or MLA_BF16 (prefill: not MLA_BF16) */
   MLA_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
-  MLA_ERR_WORKSPACE = -5,   /* workspace smaller than mla_decode_workspace_bytes() */
+  MLA_ERR_WORKSPACE = -5,   /* workspace / kv buffer smaller than its _bytes() query */
   MLA_ERR_UNSUPPORTED = -6, /* head dims / page size other than the supported set */
   MLA_ERR_LAUNCH = -7,      /* the HIP runtime rejected a launch */
   MLA_ERR_DEVICE = -8       /* no usable HIP device */
@@ -135,6 +136,58 @@ mla_status mla_decode_attn(const void* q_lat, const void* q_pe, const void* kv_p
  */
 mla_status mla_out_proj(const float* o_lat, const void* w_uv, void* out, const mla_params* p,
                         void* stream);
+
+/*
+ * ---- Prefill in multi-head form ("order 1") --------------------------------------------------
+ * When the query tokens are the prompt itself (t = s), up-projecting K and V from the latent and
+ * attending per head costs fewer FLOPs than the absorbed route: "【笔记】MLA矩阵吸收分析" §二.4.1
+ * (order 1 minus order 2 is negative at t = s), with the order-1 steps of §二.1 and §三.1; the
+ * Perplexity post plans the same for its prefill (section "Будущая работа": project the latent
+ * into K/V space, then compute in MHA form). Two calls, bf16 only (MLA_F32 gives MLA_ERR_DTYPE):
+ *
+ *   mla_prefill_kv_up   K_nope and V of every cached token, per head, from the paged latent cache
+ *   mla_prefill_attn    attention per head over those keys/values with the shared RoPE key
+ *
+ * q_len S is the number of new (query) tokens per sequence; they are the last S of the
+ * seq_lens[b] cached tokens, with the same causal rule as decode (S = seq_lens[b]: a whole prompt).
+ */
+
+/*
+ * Bytes of the K/V buffer the two prefill calls exchange (0 for an invalid `p`):
+ * B * Lp * (H * 256 + 64) * 2 with Lp = max_pages_per_seq * page_size. Layout: [K_nope | V]
+ * (B, H, Lp, 256) bf16, then k_pe (B, Lp, 64) bf16.
+ */
+size_t mla_prefill_kv_bytes(const mla_params* p);
+
+/*
+ * K_nope[b,h,j,:] = sum_c c_j[c] W_UK[h,c,:] and V[b,h,j,:] = sum_c c_j[c] W_UV[h,c,:] for
+ * every cached token j < seq_lens[b] (page lookup as in mla_decode_attn), and a dense copy of
+ * k_pe_j. Rows from seq_lens[b] to the end of that sequence's last page are written as zeros;
+ * rows after that are not written.
+ *   kv_pool, block_table, seq_lens  as for mla_decode_attn
+ *   w_uk, w_uv (H,d_c,d_h) bf16
+ *   kv / kv_bytes                   the buffer above (at least mla_prefill_kv_bytes(p) bytes)
+ * Cites: absorption note §二.1 step 2 ((b,t,h,d) keys) and §三.1 step 1 ((b,t,h,v) values).
+ */
+mla_status mla_prefill_kv_up(const void* kv_pool, const int32_t* block_table, const int32_t* seq_lens,
+                             const void* w_uk, const void* w_uv, void* kv, size_t kv_bytes,
+                             const mla_params* p, void* stream);
+
+/*
+ * out[b,i,h,:] = sum_j p_j V[b,h,j,:] with p = softmax over the visible keys j of
+ * scale * (q_nope[b,i,h,:] . K_nope[b,h,j,:] + q_pe[b,i,h,:] . k_pe_j); lse as in
+ * mla_decode_attn.
+ *   q_nope (B,S,H,d_h), q_pe (B,S,H,d_R) bf16   query (q_pe already rotated)
+ *   kv / kv_bytes                               written by mla_prefill_kv_up with the same p
+ *   out    (B,S,H,d_h) bf16 (out)               per-head attention output (before W_O)
+ *   lse    (B,S,H) fp32 (out, may be NULL)
+ * Equal (up to rounding) to mla_absorb_q + mla_decode_attn + mla_out_proj on the same inputs.
+ * Cites: absorption note §二.1 step 3 and §三.1 step 2; izhida answer "专家" (the RoPE part is
+ * a key shared by all heads whose score is added).
+ */
+mla_status mla_prefill_attn(const void* q_nope, const void* q_pe, const void* kv, size_t kv_bytes,
+                            const int32_t* seq_lens, void* out, float* lse, const mla_params* p,
+                            void* stream);
 
 /* Static string for a status code (never NULL). */
 const char* mla_status_str(mla_status s);

@@ -92,3 +92,44 @@ def test_split_planning_is_page_aligned():
         assert got == want, (L, req, got)
     assert lib.mla_decode_workspace_bytes(ctypes.byref(P(max_seq_len=64)), 4) == 0  # one split: no workspace
     assert lib.mla_decode_num_splits(ctypes.byref(P(head_dim=1)), 2) == -6
+
+
+def _kv_up(params, ptrs=None, kv_bytes=None):
+    p = dict(pool=FAKE, bt=FAKE, lens=FAKE, wk=FAKE, wv=FAKE, kv=FAKE)
+    p.update(ptrs or {})
+    if kv_bytes is None:
+        kv_bytes = lib.mla_prefill_kv_bytes(ctypes.byref(params))
+    return lib.mla_prefill_kv_up(p["pool"], p["bt"], p["lens"], p["wk"], p["wv"], p["kv"], kv_bytes,
+                                 ctypes.byref(params), None)
+
+
+def _pf_attn(params, ptrs=None, kv_bytes=None):
+    p = dict(qn=FAKE, qp=FAKE, kv=FAKE, lens=FAKE, out=FAKE, lse=FAKE)
+    p.update(ptrs or {})
+    if kv_bytes is None:
+        kv_bytes = lib.mla_prefill_kv_bytes(ctypes.byref(params))
+    return lib.mla_prefill_attn(p["qn"], p["qp"], p["kv"], kv_bytes, p["lens"], p["out"], p["lse"],
+                                ctypes.byref(params), None)
+
+
+def test_prefill_kv_bytes():
+    # [K_nope | V] (B, H, Lp, 256) + k_pe (B, Lp, 64), bf16; Lp = 5 pages * 64 for 300 tokens
+    assert lib.mla_prefill_kv_bytes(ctypes.byref(P(q_len=300))) == 2 * 320 * (128 * 256 + 64) * 2
+    assert lib.mla_prefill_kv_bytes(ctypes.byref(P(q_len=300, max_pages_per_seq=8))) == 2 * 512 * (128 * 256 + 64) * 2
+    assert lib.mla_prefill_kv_bytes(ctypes.byref(P(dtype=binding.MLA_F32))) == 0
+    assert lib.mla_prefill_kv_bytes(ctypes.byref(P(head_dim=64))) == 0
+
+
+@pytest.mark.parametrize("fn", [_kv_up, _pf_attn])
+def test_prefill_errors(fn):
+    first = "pool" if fn is _kv_up else "qn"
+    assert fn(P(q_len=300), {first: None}) == -1
+    assert fn(P(q_len=300), {"lens": None}) == -1
+    assert fn(P(q_len=300), {first: MISALIGNED}) == -4
+    assert fn(P(q_len=300, dtype=binding.MLA_F32), kv_bytes=1 << 30) == -3  # bf16 only
+    assert fn(P(q_len=300, num_heads=64), kv_bytes=1 << 30) == -6
+    assert fn(P(q_len=300, max_pages_per_seq=2), kv_bytes=1 << 30) == -2
+    need = lib.mla_prefill_kv_bytes(ctypes.byref(P(q_len=300)))
+    assert fn(P(q_len=300), kv_bytes=need - 2) == -5
+    assert fn(P(q_len=300, batch=0), kv_bytes=0) == 0
+    assert lib.mla_prefill_kv_up(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None, None) == -1
