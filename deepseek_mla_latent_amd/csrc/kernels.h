@@ -46,10 +46,11 @@ hipError_t launch_out_proj(const float* o_lat, const void* w_uv, void* out, int 
 // Prefill in multi-head form (bf16).  kv (B,H,Lp,256) = [K_nope | V] per head and token and
 // kpe (B,Lp,64) = the shared RoPE key, Lp = max_pages * 64; rows from seq_lens[b] up to the end of
 // its last page are zeros.
-// Grid: batch x 128 heads x tiles (two pages each); max_pages is the block-table row stride.
+// One workgroup per (head, K or V) walks pages [0, pages_max) of every sequence; max_pages is the
+// block-table row stride.
 hipError_t launch_kv_up_grid(const void* pool, const int32_t* block_table, const int32_t* seq_lens,
                              const void* w_uk, const void* w_uv, void* kv, void* kpe, int batch, int max_pages,
-                             int tiles, hipStream_t stream);
+                             int pages_max, hipStream_t stream);
 
 struct PrefillArgs {
   const void* q_nope;  // (B,S,H,128) bf16

@@ -229,11 +229,11 @@ mla_status mla_prefill_kv_up(const void* kv_pool, const int32_t* block_table, co
   if (!kv_pool || !block_table || !seq_lens || !w_uk || !w_uv || !kv) return MLA_ERR_NULL;
   if (!aligned16(kv_pool) || !aligned16(w_uk) || !aligned16(w_uv) || !aligned16(kv)) return MLA_ERR_ALIGN;
   if (kv_bytes < prefill_kv_bytes(p)) return MLA_ERR_WORKSPACE;
-  if ((int64_t)p->batch * mla::kHeads * ((pages + 1) / 2) > 0x7fffffffLL) return MLA_ERR_SHAPE;
+  if ((int64_t)p->batch * pages > 0x7fffffffLL) return MLA_ERR_SHAPE;
   char* kpe = (char*)kv + (size_t)p->batch * mla::kHeads * p->max_pages_per_seq * mla::kPage * 2 * mla::kDh * 2;
-  // the grid covers the pages max_seq_len needs; rows are laid out with the table's page stride
+  // the walk covers the pages max_seq_len needs; rows are laid out with the table's page stride
   if (mla::launch_kv_up_grid(kv_pool, block_table, seq_lens, w_uk, w_uv, kv, kpe, p->batch, p->max_pages_per_seq,
-                             (pages + 1) / 2, (hipStream_t)stream) != hipSuccess)
+                             pages, (hipStream_t)stream) != hipSuccess)
     return MLA_ERR_LAUNCH;
   return MLA_OK;
 }
@@ -248,7 +248,7 @@ mla_status mla_prefill_attn(const void* q_nope, const void* q_pe, const void* kv
   if (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(kv) || !aligned16(out)) return MLA_ERR_ALIGN;
   if (!std::isfinite(p->softmax_scale)) return MLA_ERR_SHAPE;
   if (p->max_seq_len > 0 && kv_bytes < prefill_kv_bytes(p)) return MLA_ERR_WORKSPACE;
-  const int nqb = (p->q_len + 127) / 128;
+  const int nqb = (p->q_len + 255) / 256;  // 256 queries per workgroup
   if ((int64_t)p->batch * mla::kHeads * nqb > 0x7fffffffLL) return MLA_ERR_SHAPE;
   mla::PrefillArgs a;
   a.q_nope = q_nope;

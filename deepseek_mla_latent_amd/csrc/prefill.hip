@@ -23,11 +23,8 @@ namespace mla {
 namespace {
 
 constexpr int kKvRow = 2 * kDh;             // 256 elements per (head, token): [K_nope | V]
-constexpr int kUpChunk = 64;                 // W rows (latent index k) per LDS chunk
-constexpr int kUpMatBytes = kUpChunk * kDh * 2;  // 16 KiB: one chunk of W_UK[h] or W_UV[h]
-constexpr int kUpBufBytes = 2 * kUpMatBytes;     // both matrices
 
-constexpr int kPfQueries = 128;              // queries per attention workgroup (4 waves x 32)
+constexpr int kPfQueries = 256;              // queries per attention workgroup (8 waves x 32)
 constexpr int kPfKeys = kPage;               // keys per LDS tile
 constexpr int kPfKvBytes = kPfKeys * kKvRow * 2;          // 32 KiB: [K_nope | V] rows
 constexpr int kPfBufBytes = kPfKvBytes + kPfKeys * kDr * 2;  // + 8 KiB of k_pe rows
@@ -45,9 +42,15 @@ __device__ __forceinline__ bf16x8 lds_tr_pair(const MLA_LDS char* lo, const MLA_
 }
 
 // Direct-to-LDS load of 16 bytes per lane (lane l's bytes land at lds + 16 l) from a wave-uniform
-// base plus a per-lane byte offset.  Completion is awaited with an explicit vmcnt wait.
+// base plus a per-lane byte offset.  Completion is awaited with an explicit vmcnt wait.  The base
+// goes through readfirstlane so that it is always held in scalar registers (the instruction's
+// scalar-address form), whatever the compiler's uniformity analysis concluded.
 __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+  const uint64_t a = (uint64_t)(uintptr_t)sbase;
+  const uint64_t base = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base),
+               "s"(__builtin_amdgcn_readfirstlane(lds))
                : "memory");
 }
 __device__ __forceinline__ uint32_t lds_u32(const MLA_LDS char* p) { return (uint32_t)(uintptr_t)p; }
@@ -63,178 +66,252 @@ __device__ __forceinline__ u32x2 pack4(float a, float b, float c, float d) {
 }  // namespace
 
 // ------------------------------------------------------------------------------------------------
-// K/V up-projection.  Workgroup = (sequence b, head h, 128-token tile); wave (wm, wn) computes the
-// transposed product out^T[n][token] = sum_k W[k][n] c[token][k] for the 64 tokens of page wm and
-// the 128 columns of matrix wn (0: W_UK -> K_nope, 1: W_UV -> V).  W^T is the A operand, read
-// transposed from LDS (64-row chunks shared by the two page waves); c^T is the B operand, whose
-// 8 consecutive k per lane are 16 contiguous bytes of a cache row, loaded straight from the pool.
-// The accumulator layout gives each lane 4 consecutive n of one token: 8-byte bf16 stores.
+// K/V up-projection.  Workgroup = (head h, half of the pages); 256 workgroups.  Wave w owns 64
+// output columns: matrix m = w / 2 (0: W_UK -> K_nope, 1: W_UV -> V), columns 64 (w % 2) ..
+// +63.  Its slice of W (512 x 64) is held in registers for the whole walk as 64 MFMA A operands
+// (W^T rows = output columns), read once through LDS with transposed reads.  The cached pages then
+// stream through LDS (two 64 KiB buffers, one page ahead) by direct-to-LDS loads of whole 1 KiB
+// latent rows, and each wave computes out^T[n][token] = sum_k W[k][n] c[token][k] for its 64
+// columns and the page's 64 tokens: the B operand (8 consecutive k of one token per lane) is a
+// ds_read_b128 of the staged row.  The page's output rows ([K_nope | V] of 64 consecutive tokens,
+// one contiguous 32 KiB block) are assembled in LDS and written with 1 KiB-contiguous stores one
+// page late.  Roles keep store latency out of the page waits: wave 0 issues every page load and
+// waits for it (a vector-memory wait covers all of a wave's outstanding loads and stores), waves
+// 1-3 issue every store and never wait on vector memory.  The shared RoPE key is copied by
+// kpe_copy_kernel.
 //
-// W chunk layout in LDS: matrix m, row r (k), 16-byte unit u stored at unit u ^ ((r & 3) << 2),
-// so the 4 rows x 4 units of a transposed read fall on 16 distinct units (all 64 banks).
-__global__ __launch_bounds__(256, 2) void kv_up_kernel(const uint16_t* __restrict__ pool,
+// LDS layouts: W staging row k (256 B), unit u at u ^ ((k & 3) << 2) (transposed reads of 4 rows
+// x 4 units hit 16 distinct units); page row t (1 KiB) and output row t (512 B), unit u at
+// u ^ (t & 15) (16 tokens at one unit hit 16 distinct units).
+__global__ __launch_bounds__(256, 1) void kv_up_kernel(const uint16_t* __restrict__ pool,
                                                        const int32_t* __restrict__ block_table,
                                                        const int32_t* __restrict__ seq_lens,
                                                        const uint16_t* __restrict__ w_uk,
                                                        const uint16_t* __restrict__ w_uv, uint16_t* __restrict__ kv,
-                                                       uint16_t* __restrict__ kpe, int max_pages, int tiles_per_seq) {
-  __shared__ __attribute__((aligned(16))) char lds_raw[2 * kUpBufBytes];
+                                                       int batch, int max_pages, int pages_max) {
+  constexpr int kPageBytes = kPage * kDc * 2;     // 64 KiB: the latent rows of one page
+  constexpr int kOutBytes = kPage * kKvRow * 2;   // 32 KiB: the page's [K_nope | V] rows
+  __shared__ __attribute__((aligned(16))) char lds_raw[2 * kPageBytes + kOutBytes];
   MLA_LDS char* lds = (MLA_LDS char*)lds_raw;
 
-  const int id = xcd_remap(blockIdx.x, gridDim.x);  // one XCD walks all tiles of a few heads
-  const int tt = id % tiles_per_seq;
-  const int h = (id / tiles_per_seq) % kHeads;
-  const int b = id / (tiles_per_seq * kHeads);
-  const int L = seq_lens[b];
-  const int npages = (L + kPage - 1) / kPage;
-  if (tt * 2 >= npages) return;  // whole workgroup: no page of this tile holds a token
-
+  const int h = blockIdx.x >> 1, part = blockIdx.x & 1;  // workgroups of one part share an XCD parity
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
-  const int wm = wave & 1, wn = wave >> 1;
-  const int page = tt * 2 + wm;
-  const bool page_ok = page < npages;
-  const int valid = page_ok ? min(kPage, L - page * kPage) : 0;  // tokens of this page
-  const int pid = page_ok ? block_table[(size_t)b * max_pages + page] : 0;
-  const uint16_t* prow = pool + (size_t)pid * kPage * kRow;
+  const int m = wave >> 1, n0 = 64 * (wave & 1);
   const size_t Lp = (size_t)max_pages * kPage;
 
-  // W chunks stream into LDS by direct-to-LDS loads: 32 pieces of 1 KiB (4 rows of one matrix)
-  // per chunk, 8 per wave; LDS position p of row r receives source unit p ^ ((r & 3) << 2).
-  const char* wsrc[2] = {(const char*)(w_uk + (size_t)h * kDc * kDh), (const char*)(w_uv + (size_t)h * kDc * kDh)};
-  auto issue_chunk = [&](int c, int buf) {
+  // W slice -> registers: two rounds (W_UK, then W_UV) of 128 KiB through both page buffers.
+  bf16x8 wf[32][2];
+  {
+    const int tr_row = 8 * hf + ((lane >> 2) & 3);
+    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    auto tr_off = [&](int r, int n) { return r * 256 + ((((n >> 3) ^ ((r & 3) << 2))) << 4) + (n & 7) * 2; };
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int pc = wave * 8 + j;
-      const int m = pc >> 4, r = 4 * (pc & 15) + (lane >> 4), p = lane & 15;
-      const int u = p ^ ((r & 3) << 2);
-      dma16(wsrc[m], (uint32_t)((c * kUpChunk + r) * kDh * 2 + u * 16),
-            lds_u32(lds + buf * kUpBufBytes + m * kUpMatBytes + (pc & 15) * 1024));
-    }
-  };
-
-  // B operand (c^T) for k-step ks (16 latent indices) and token block tb: 16 B of the cache row.
-  // Always loaded (a row of this page, or of pool page 0 for a page past the sequence) and
-  // zeroed for tokens past the sequence end, so every wave issues the same number of loads.
-  const bool tok_ok[2] = {l32 < valid, 32 + l32 < valid};
-  auto load_c = [&](int ks, int tb) -> bf16x8 {
-    const bf16x8 v = *(const bf16x8*)(prow + (size_t)(tb * 32 + l32) * kRow + ks * 16 + hf * 8);
-    return tok_ok[tb] ? v : bf16x8{};
-  };
-
-  // A operand (W^T) addresses: rows k = 16 ks' + 8 hf + (lane >> 2 & 3) (+4 for the high half),
-  // columns n = 32 nb + 16 ((lane >> 4) & 1) + 4 (lane & 3).
-  const int tr_row = 8 * hf + ((lane >> 2) & 3);
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  auto tr_off = [&](int r, int n) { return r * 256 + ((((n >> 3) ^ ((r & 3) << 2))) << 4) + (n & 7) * 2; };
-
-  f32x16 acc[4][2];
+    for (int round = 0; round < 2; ++round) {
+      const char* w = (const char*)((round ? w_uv : w_uk) + (size_t)h * kDc * kDh);
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb) acc[nb][tb] = f32x16{};
-
-  constexpr int kChunks = kDc / kUpChunk;  // 8
-  bf16x8 cf[4][2], cn[4][2];
-  issue_chunk(0, 0);
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb) cf[ks][tb] = load_c(ks, tb);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-
-  for (int c = 0; c < kChunks; ++c) {
-    // next chunk's W (into the other buffer, last read before the previous barrier) and c rows
-    if (c + 1 < kChunks) {
-      issue_chunk(c + 1, (c + 1) & 1);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) cn[ks][tb] = load_c((c + 1) * 4 + ks, tb);
-    }
-    const MLA_LDS char* wbuf = lds + (c & 1) * kUpBufBytes + wn * kUpMatBytes;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      bf16x8 af[4];
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int r = ks * 16 + tr_row, n = nb * 32 + tr_col;
-        af[nb] = lds_tr_pair(wbuf + tr_off(r, n), wbuf + tr_off(r + 4, n));
+      for (int j = 0; j < 32; ++j) {
+        const int pc = wave * 32 + j;
+        const int r = 4 * pc + (lane >> 4), p = lane & 15;
+        dma16(w, (uint32_t)(r * kDh * 2 + ((p ^ ((r & 3) << 2)) << 4)), lds_u32(lds + pc * 1024));
       }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (m == round) {
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
+        for (int ks = 0; ks < 32; ++ks)
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) acc[nb][tb] = mfma32x32x16(af[nb], cf[ks][tb], acc[nb][tb]);
+          for (int nb = 0; nb < 2; ++nb) {
+            const int r = ks * 16 + tr_row, n = n0 + nb * 32 + tr_col;
+            wf[ks][nb] = lds_tr_pair(lds + tr_off(r, n), lds + tr_off(r + 4, n));
+          }
+      }
+      __syncthreads();  // reads done before the buffers are reused
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) cf[ks][tb] = cn[ks][tb];
   }
 
-  // Stores: element e of block (nb, tb) is out^T[32 nb + 8 (e/4) + 4 hf + e%4][32 tb + l32].
-  if (page_ok) {
-    uint16_t* dst = kv + (((size_t)b * kHeads + h) * Lp + (size_t)page * kPage) * kKvRow + wn * kDh;
+  // pages of this part: virtual pages v = b * pages_max + p with v % 2 == part, walked from a
+  // start that depends on the head (so that at any moment the workgroups write to different
+  // addresses of the output rather than to the same page offset of 128 heads' rows) and wrapping
+  const int nv = batch * pages_max;
+  const int count = (nv - part + 1) / 2;  // virtual pages of this part
+  const int j0 = count ? (int)(((long long)h * count) / kHeads) : 0;
+  struct Page {
+    int jj, v, valid;  // jj: position in the walk (count = done)
+    const uint16_t* rows;
+  };
+  // (wave-uniform values; read with readfirstlane so that the page base is a scalar address)
+  auto find = [&](int jj) -> Page {  // first page at or after walk position jj that holds tokens
+    for (; jj < count; ++jj) {
+      int j = j0 + jj;
+      j = j >= count ? j - count : j;
+      const int v = __builtin_amdgcn_readfirstlane(part + 2 * j);
+      const int b = v / pages_max, p = v - b * pages_max;
+      const int L = seq_lens[b];  // uniform address: a scalar load, no vector-memory wait
+      if (p * kPage < L) {
+        const int pid = __builtin_amdgcn_readfirstlane(block_table[(size_t)b * max_pages + p]);
+        return {jj, v, min(kPage, L - p * kPage), pool + (size_t)pid * kPage * kRow};
+      }
+    }
+    return {count, nv, 0, pool};
+  };
+  // one page: 64 latent rows of 1 KiB, all issued by wave 0; LDS position q of row t gets unit
+  // q ^ (t & 15)
+  auto issue_page = [&](const Page& pg, int buf) {
+#pragma unroll
+    for (int t = 0; t < kPage; ++t)
+      dma16(pg.rows, (uint32_t)(t * kRow * 2 + ((lane ^ (t & 15)) << 4)), lds_u32(lds + buf * kPageBytes + t * 1024));
+  };
+  const int b_off[2] = {(l32 * 1024), ((32 + l32) * 1024)};  // this lane's token rows (tb = 0, 1)
+
+  MLA_LDS char* ostage = lds + 2 * kPageBytes;
+  f32x16 acc[2][2];
+  // results -> output staging: element e of block (nb, tb) is out^T[32 nb + 8 (e/4) + 4 hf + e%4]
+  // [32 tb + l32]; rows past the sequence end (to the page end) are zeros
+  auto stage_out = [&](int valid) {
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
       const int tok = tb * 32 + l32;
-      const bool ok = tok < valid;  // rows past the sequence end are written as zeros
+      const bool ok = tok < valid;
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
+      for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const f32x16& d = acc[nb][tb];
-          u32x2 v = ok ? pack4(d[4 * g], d[4 * g + 1], d[4 * g + 2], d[4 * g + 3]) : u32x2{0u, 0u};
-          *(u32x2*)(dst + (size_t)tok * kKvRow + nb * 32 + g * 8 + hf * 4) = v;
+          const f32x16& x = acc[nb][tb];
+          const u32x2 v = ok ? pack4(x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]) : u32x2{0u, 0u};
+          const int u = (m * kDh + n0 + nb * 32 + g * 8) >> 3;  // 16-byte unit of the row
+          *(MLA_LDS u32x2*)(ostage + tok * 512 + (((u & 16) | ((u & 15) ^ (tok & 15))) << 4) + hf * 8) = v;
         }
     }
-    // the shared RoPE key: head-0 workgroups copy it densely, zeros past the sequence end
-    if (h == 0 && wn == 0) {
-      uint16_t* kdst = kpe + ((size_t)b * Lp + (size_t)page * kPage) * kDr;
-#pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int q = it * 64 + lane, row = q >> 3, u = q & 7;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (row < valid) v = *(const u32x4*)(prow + (size_t)row * kRow + kDc + u * 8);
-        *(u32x4*)(kdst + (size_t)row * kDr + u * 8) = v;
-      }
+  };
+  // staged rows -> HBM (waves 1-3): the page's 32 KiB block, 1 KiB per instruction
+  auto write_out = [&](const Page& pg) {
+    const int b = pg.v / pages_max, p = pg.v - b * pages_max;
+    char* dst = (char*)(kv + (((size_t)b * kHeads + h) * Lp + (size_t)p * kPage) * kKvRow);
+    for (int piece = wave - 1; piece < 32; piece += 3) {
+      const int row = 2 * piece + (lane >> 5), u = lane & 31;
+      const u32x4 v = *(const MLA_LDS u32x4*)(ostage + row * 512 + (((u & 16) | ((u & 15) ^ (row & 15))) << 4));
+      *(u32x4*)(dst + row * 512 + u * 16) = v;
     }
+  };
+
+  Page cur = find(0), prev = {count, nv, 0, pool};
+  if (wave == 0 && cur.jj < count) issue_page(cur, 0);
+  for (int idx = 0; cur.jj < count; ++idx) {
+    if (wave == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this page (wave 0 stores nothing)
+    __syncthreads();  // page in LDS; the other buffer is free; the previous results are staged
+    const Page next = find(cur.jj + 1);
+    if (wave == 0) {
+      if (next.jj < count) issue_page(next, (idx + 1) & 1);
+    } else if (prev.jj < count) {
+      write_out(prev);
+    }
+    const MLA_LDS char* pg = lds + (idx & 1) * kPageBytes;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) acc[nb][tb] = f32x16{};
+    // B operands stream through a ring three k-steps deep: the reads for step ks + 2 are issued
+    // (and pinned there by a scheduling barrier) before the MFMAs of step ks
+    auto read_b = [&](int ks, bf16x8 (&bf)[2]) {
+      const int u = 2 * ks + hf;
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) bf[tb] = lds_b128(pg + b_off[tb] + ((u ^ (l32 & 15)) << 4));
+    };
+    bf16x8 ring[3][2];
+    read_b(0, ring[0]);
+    read_b(1, ring[1]);
+#pragma unroll
+    for (int ks = 0; ks < 32; ++ks) {
+      if (ks + 2 < 32) read_b(ks + 2, ring[(ks + 2) % 3]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) acc[nb][tb] = mfma32x32x16(wf[ks][nb], ring[ks % 3][tb], acc[nb][tb]);
+    }
+    __syncthreads();  // every wave has read the staged rows of the previous page
+    stage_out(cur.valid);
+    prev = cur;
+    cur = next;
+  }
+  if (prev.jj < count) {
+    __syncthreads();
+    if (wave != 0) write_out(prev);
+  }
+}
+
+// The shared RoPE key of every cached token, copied densely: kpe[b, j] = k_pe_j for j < seq_lens[b],
+// zeros to the end of the last page.  One 64-lane workgroup per (b, page).
+__global__ __launch_bounds__(64) void kpe_copy_kernel(const uint16_t* __restrict__ pool,
+                                                      const int32_t* __restrict__ block_table,
+                                                      const int32_t* __restrict__ seq_lens, uint16_t* __restrict__ kpe,
+                                                      int max_pages, int pages_max) {
+  const int b = blockIdx.x / pages_max, p = blockIdx.x % pages_max;
+  const int valid = min(kPage, seq_lens[b] - p * kPage);
+  if (valid <= 0) return;
+  const uint16_t* rows = pool + (size_t)block_table[(size_t)b * max_pages + p] * kPage * kRow;
+  uint16_t* dst = kpe + ((size_t)b * max_pages + p) * kPage * kDr;
+  const int lane = threadIdx.x;
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int q = it * 64 + lane, row = q >> 3, u = q & 7;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (row < valid) v = *(const u32x4*)(rows + (size_t)row * kRow + kDc + u * 8);
+    *(u32x4*)(dst + (size_t)row * kDr + u * 8) = v;
   }
 }
 
 hipError_t launch_kv_up_grid(const void* pool, const int32_t* block_table, const int32_t* seq_lens,
                              const void* w_uk, const void* w_uv, void* kv, void* kpe, int batch, int max_pages,
-                             int tiles, hipStream_t stream) {
-  const int64_t grid = (int64_t)batch * kHeads * tiles;
-  if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(kv_up_kernel, dim3((unsigned)grid), dim3(256), 0, stream, (const uint16_t*)pool, block_table,
-                     seq_lens, (const uint16_t*)w_uk, (const uint16_t*)w_uv, (uint16_t*)kv, (uint16_t*)kpe,
-                     max_pages, tiles);
+                             int pages_max, hipStream_t stream) {
+  if (batch == 0 || pages_max == 0) return hipSuccess;
+  hipLaunchKernelGGL(kv_up_kernel, dim3(2 * kHeads), dim3(256), 0, stream, (const uint16_t*)pool, block_table,
+                     seq_lens, (const uint16_t*)w_uk, (const uint16_t*)w_uv, (uint16_t*)kv, batch, max_pages,
+                     pages_max);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kpe_copy_kernel, dim3((unsigned)(batch * pages_max)), dim3(64), 0, stream, (const uint16_t*)pool,
+                     block_table, seq_lens, (uint16_t*)kpe, max_pages, pages_max);
   return hipGetLastError();
 }
 
 // ------------------------------------------------------------------------------------------------
-// Causal multi-head attention over the up-projected keys.  Workgroup = (b, h, 128-query block);
-// wave w owns 32 queries.  Per 64-key tile:
-//   S^T (keys x queries) = [K_nope | k_pe] Q^T: 2 key blocks x 12 MFMAs, keys as the A operand
+// Causal multi-head attention over the up-projected keys.  Workgroup = (b, h, 256-query block),
+// 8 waves (two per SIMD); wave w owns 32 queries.  Per 64-key tile:
+//   S^T (keys x queries) = [K_nope | k_pe] Q^T: 2 key blocks x 12 k-steps, keys as the A operand
 //   (ds_read_b128 rows), the wave's queries as the B operand held in registers for the whole walk;
 //   online softmax per query column (the lane pair l, l^32 holds one query);
-//   O^T (dv x queries) += V^T P^T: 4 dv blocks x 4 MFMAs, V^T read transposed from the same tile.
+//   O^T (dv x queries) += V^T P^T: 4 dv blocks x 4 key steps, V^T read transposed from the tile.
 // The accumulator layout of S^T is the B-operand layout of P^T when the 16 keys of an MFMA step
 // are taken in the order the accumulator holds them; the V^T reads use the same key order.
+// Software pipeline across tiles, so that the matrix cores are not idle during the softmax:
+//   scores(t)  ->  [sum(t-1) | softmax(t)]
+// where "[x | y]" issues the MFMAs of x interleaved with the VALU work of y.
 // Tile layout: key row r of [K_nope | V] (32 units of 16 B), unit u at u ^ swz(r) (low 4 bits),
 // k_pe row r (8 units) at u ^ ((r >> 1) & 7): both read patterns hit 16 distinct units per
-// 16 lanes.  Tiles stream in by direct-to-LDS loads, one tile ahead (two buffers).
-// The running max is only raised when a tile's max exceeds it by more than 2^8 (log2 units).
+// 16 lanes.  Tiles stream in by direct-to-LDS loads into a ring of 4 buffers, two tiles ahead
+// (tile t - 1 is still read during tile t).  A wave stops computing at the first tile past its
+// last query's keys (it still takes part in loads and barriers).  The running max is only raised
+// when a tile's max exceeds it by more than 2^8 (log2 units).
 __device__ __forceinline__ int pf_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 __device__ __forceinline__ int pf_swz_pe(int r) { return (r >> 1) & 7; }
 
-__global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds_raw[2 * kPfBufBytes];
+constexpr int kPfWaves = 8;
+constexpr int kPfRing = 4;
+constexpr int kPfAhead = 2;  // tiles in flight beyond the one being computed
+
+// wait until at most `younger` tiles' loads (5 per wave each) are in flight (loads retire in order)
+__device__ __forceinline__ void pf_wait_tiles(int younger) {
+  if (younger >= 1)
+    asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+__global__ __launch_bounds__(64 * kPfWaves, 1) void prefill_attn_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds_raw[kPfRing * kPfBufBytes];  // 160 KiB
   MLA_LDS char* lds = (MLA_LDS char*)lds_raw;
 
   const int nbh = a.B * kHeads;
@@ -248,141 +325,221 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillArgs a) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
-  const int q0 = qb * kPfQueries;
-  const int qi = q0 + wave * 32 + l32;    // this lane's query (column)
-  const int qc = min(qi, S - 1);           // padding queries behave like the last one
+  const int q0 = qb * kPfQueries, qw = q0 + wave * 32;  // first query of the block / of the wave
+  const int qi = qw + l32;                              // this lane's query (column)
   auto visible = [&](int q) { return a.causal ? max(0, min(L, L - S + q + 1)) : L; };
-  const int vis = visible(qc);
-  const int kend = visible(min(S - 1, q0 + kPfQueries - 1));  // keys any query of the block sees
+  const int vis = visible(min(qi, S - 1));             // padding queries behave like the last one
+  const int kend = visible(min(S - 1, q0 + kPfQueries - 1));  // keys any query of the workgroup sees
   const int ntiles = (kend + kPfKeys - 1) / kPfKeys;
-  const int wave_vis = visible(min(S - 1, q0 + wave * 32));   // fewest keys a query of the wave sees
+  const int wave_vis_lo = visible(min(S - 1, qw));       // fewest keys a query of the wave sees
+  const int wave_vis_hi = visible(min(S - 1, qw + 31));  // most
 
   const size_t Lp = (size_t)a.Lp;
   const char* kv_seq = (const char*)a.kv + ((size_t)b * kHeads + h) * Lp * kKvRow * 2;
   const char* pe_seq = (const char*)a.kpe + (size_t)b * Lp * kDr * 2;
 
-  // tile DMA: 32 KiB of [K_nope | V] rows (8 loads per wave) + 8 KiB of k_pe rows (2 per wave)
-  auto issue_tile = [&](int t, int buf) {
-    MLA_LDS char* dst = lds + buf * kPfBufBytes;
+  // tile DMA: 32 KiB of [K_nope | V] rows + 8 KiB of k_pe rows, 5 loads of 1 KiB per wave
+  auto issue_tile = [&](int t) {
+    MLA_LDS char* dst = lds + (t % kPfRing) * kPfBufBytes;
     const char* kv_t = kv_seq + (size_t)t * kPfKeys * kKvRow * 2;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int c = wave * 8 + j;             // 1 KiB piece: rows 2c, 2c+1
+    for (int j = 0; j < 4; ++j) {
+      const int c = wave * 4 + j;             // 1 KiB piece: rows 2c, 2c+1
       const int r = 2 * c + (lane >> 5), p = lane & 31;
       const int u = (p & 16) | ((p & 15) ^ pf_swz(r));
       dma16(kv_t, (uint32_t)(r * kKvRow * 2 + u * 16), lds_u32(dst + c * 1024));
     }
-    const char* pe_t = pe_seq + (size_t)t * kPfKeys * kDr * 2;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int c = wave * 2 + j;             // rows 8c .. 8c+7
-      const int r = 8 * c + (lane >> 3), p = lane & 7;
-      const int u = p ^ pf_swz_pe(r);
-      dma16(pe_t, (uint32_t)(r * kDr * 2 + u * 16), lds_u32(dst + kPfKvBytes + c * 1024));
-    }
+    const int r = 8 * wave + (lane >> 3), p = lane & 7;  // rows 8 wave .. 8 wave + 7
+    dma16(pe_seq + (size_t)t * kPfKeys * kDr * 2, (uint32_t)(r * kDr * 2 + ((p ^ pf_swz_pe(r)) << 4)),
+          lds_u32(dst + kPfKvBytes + wave * 1024));
   };
+  for (int t = 0; t < kPfAhead && t < ntiles; ++t) issue_tile(t);
 
-  if (ntiles > 0) issue_tile(0, 0);
-
-  // queries as B operands: k-steps 0..7 from q_nope, 8..11 from q_pe
+  // queries as B operands: k-steps 0..7 from q_nope, 8..11 from q_pe.  Loaded after the first
+  // tiles are requested and consumed by an empty asm statement before the loop: the wait for
+  // them happens here, once, and no load the compiler tracks is pending inside the loop (its
+  // waits there would otherwise also drain the tile loads in flight).
   bf16x8 qf[12];
   {
+    const int qc = min(qi, S - 1);
     const uint16_t* qn = (const uint16_t*)a.q_nope + (((size_t)b * S + qc) * kHeads + h) * kDh;
     const uint16_t* qp = (const uint16_t*)a.q_pe + (((size_t)b * S + qc) * kHeads + h) * kDr;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qf[ks] = *(const bf16x8*)(qn + ks * 16 + hf * 8);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qf[8 + ks] = *(const bf16x8*)(qp + ks * 16 + hf * 8);
+#pragma unroll
+    for (int ks = 0; ks < 12; ++ks) asm volatile("" ::"v"(qf[ks]));
   }
 
-  // per-lane operand offsets within a tile buffer
-  int k_off[2][12];
+  // Operand addresses: a few per-lane bases, the rest immediates.  Key operand (k-step ks, key
+  // block kb): row 32 kb + l32 has the swizzle of row l32, so kb only adds 32 rows.  Value
+  // operand (key step kk, dv block cb): rows 16 kk + 4 hf + (lane >> 2 & 3) (+8 for the high
+  // half) have swizzles independent of kk, so kk only adds 16 rows; dv columns
+  // 32 cb + 16 ((lane >> 4) & 1) + 4 (lane & 3).
+  int kofs[12];
+  {
+    const int sw_kv = pf_swz(l32), sw_pe = pf_swz_pe(l32);
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const int r = kb * 32 + l32;
+    for (int ks = 0; ks < 8; ++ks) kofs[ks] = l32 * kKvRow * 2 + (((2 * ks + hf) ^ sw_kv) << 4);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) k_off[kb][ks] = r * kKvRow * 2 + (((2 * ks + hf) ^ pf_swz(r)) << 4);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) k_off[kb][8 + ks] = kPfKvBytes + r * kDr * 2 + (((2 * ks + hf) ^ pf_swz_pe(r)) << 4);
+    for (int ks = 0; ks < 4; ++ks) kofs[8 + ks] = kPfKvBytes + l32 * kDr * 2 + (((2 * ks + hf) ^ sw_pe) << 4);
   }
-  // V^T reads: key rows 16 kk + 4 hf + (lane >> 2 & 3) (+8 for the high half), dv columns
-  // 32 cb + 16 ((lane >> 4) & 1) + 4 (lane & 3)
-  const int vr = 4 * hf + ((lane >> 2) & 3);
-  const int vc = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  auto v_off = [&](int r, int dv) {
-    const int u = 16 + (dv >> 3);
-    return r * kKvRow * 2 + (((u & 16) | ((u & 15) ^ pf_swz(r))) << 4) + (dv & 7) * 2;
+  auto k_imm = [](int kb, int ks) { return kb * 32 * (ks < 8 ? kKvRow * 2 : kDr * 2); };
+  int vofs[4][2];
+  {
+    const int vr = 4 * hf + ((lane >> 2) & 3);
+    const int vc = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int hi = 0; hi < 2; ++hi) {
+        const int r = vr + 8 * hi, dv = cb * 32 + vc, u = 16 + (dv >> 3);
+        vofs[cb][hi] = r * kKvRow * 2 + (((u & 16) | ((u & 15) ^ pf_swz(r))) << 4) + (dv & 7) * 2;
+      }
+  }
+  auto read_v = [&](const MLA_LDS char* tile, int i) {  // operand i = 4 kk + cb
+    const int kk = i >> 2, cb = i & 3, imm = kk * 16 * kKvRow * 2;
+    return lds_tr_pair(tile + vofs[cb][0] + imm, tile + vofs[cb][1] + imm);
   };
 
   f32x16 o[4];
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) o[cb] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY, l_run = 0.f, alpha = 1.f;
+  bool rescale = false;
   const float sl2 = a.scale_log2;
+  f32x16 s[2];     // scores of the current tile, per key block
+  bf16x8 pk[4];    // P^T operands of the tile being summed, per key step
+  bf16x8 pn[4];    // P^T operands being produced for the current tile
 
-  for (int t = 0; t < ntiles; ++t) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (t + 1 < ntiles) issue_tile(t + 1, (t + 1) & 1);
-    const MLA_LDS char* tile = lds + (t & 1) * kPfBufBytes;
-
-    f32x16 s[2] = {f32x16{}, f32x16{}};
+  // Softmax of the current tile, cut into 18 stages spread over the 16 MFMA slots of the sum:
+  // stage 0 masks, stage 1 takes the max, combines the lane pair and decides the rescale
+  // (branch-free), stages 2..17 compute two probabilities each.
+  auto sm_stage = [&](int st, int key0, bool need_mask) {
+    if (st == 0) {
+      if (need_mask) {
 #pragma unroll
-    for (int ks = 0; ks < 12; ++ks)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32x32x16(lds_b128(tile + k_off[kb][ks]), qf[ks], s[kb]);
-
-    // scaled logits in log2 units; keys past this query's visible count are -inf
-    const int key0 = t * kPfKeys;
-    const bool need_mask = key0 + kPfKeys > wave_vis;
-    float mt = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float x = s[kb][e] * sl2;
-        if (need_mask) {
-          const int key = key0 + kb * 32 + (e >> 2) * 8 + hf * 4 + (e & 3);
-          x = key < vis ? x : -INFINITY;
-        }
-        s[kb][e] = x;
-        mt = fmaxf(mt, x);
+          for (int e = 0; e < 16; ++e) {
+            const int key = key0 + kb * 32 + (e >> 2) * 8 + hf * 4 + (e & 3);
+            s[kb][e] = key < vis ? s[kb][e] : -INFINITY;
+          }
       }
-    {
+    } else if (st == 1) {
+      float mt = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) mt = fmaxf(mt, fmaxf(s[kb][e], s[kb][e + 1]));
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
-      mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    }
-    if (__any(mt > m_run + 8.0f)) {  // wave-uniform: raise the reference, rescale O and l
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sl2;
+      const bool raise = __any(mt > m_run + 8.0f);  // wave-uniform
+      const float m_new = raise ? fmaxf(m_run, mt) : m_run;
+      rescale = raise && m_run != -INFINITY;  // O and l hold something: bring them to m_new
+      alpha = rescale ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
       l_run *= alpha;
+      m_run = m_new;
+    } else {
+      const float msub = m_run == -INFINITY ? 0.f : m_run;  // no visible key yet: every p is 0
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int e = (st - 2) * 2 + q;  // 0..31
+        const int kb = e >> 4, ee = e & 15;
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][ee], sl2, -msub));
+        l_run += p;
+        pn[kb * 2 + (ee >> 3)][ee & 7] = (__bf16)p;
+      }
+    }
+  };
+  // [sum of the previous tile (operands pk) | softmax of the current tile (stages over the slots)]
+  auto sum_with_softmax = [&](const MLA_LDS char* tile, int key0, bool need_mask, bool do_sm) {
+    bf16x8 vr3[3];
+    vr3[0] = read_v(tile, 0);
+    vr3[1] = read_v(tile, 1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i + 2 < 16) vr3[(i + 2) % 3] = read_v(tile, i + 2);
+      if (do_sm) {  // stages 0, 1 at the first slot, 2..16 at slots 1..15, 17 at the last
+        sm_stage(i == 0 ? 0 : i + 1, key0, need_mask);
+        if (i == 0) sm_stage(1, key0, need_mask);
+        if (i == 15) sm_stage(17, key0, need_mask);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      o[i & 3] = mfma32x32x16(vr3[i % 3], pk[i >> 2], o[i & 3]);
+    }
+  };
+  // O is brought to the reference max of the tile whose probabilities are summed next; the
+  // decision was taken in that tile's softmax
+  bool pending_rescale = false;
+  float pending_alpha = 1.f;
+  auto scale_o = [&]() {
+    if (pending_rescale) {
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) o[cb][e] *= alpha;
-      m_run = m_new;
+        for (int e = 0; e < 16; ++e) o[cb][e] *= pending_alpha;
     }
-    const float msub = m_run == -INFINITY ? 0.f : m_run;  // no visible key yet: every p is 0
-    bf16x8 pk[4];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = __builtin_amdgcn_exp2f(s[kb][e] - msub);
-        l_run += p;
-        pk[kb * 2 + (e >> 3)][e & 7] = (__bf16)p;
-      }
+  };
 
+  // Before the first tile, "the sum over the previous tile" runs over a zeroed buffer with P = 0,
+  // so the loop body has no first-iteration special case.
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int r = kk * 16 + vr;
+  for (int kk = 0; kk < 4; ++kk) pk[kk] = bf16x8{};
+  {
+    MLA_LDS char* z = lds + (kPfRing - 1) * kPfBufBytes;
+    for (int i = tid; i < kPfBufBytes / 16; i += 64 * kPfWaves) *(MLA_LDS u32x4*)(z + i * 16) = u32x4{0u, 0u, 0u, 0u};
+  }
+
+  bool done = false;  // this wave's queries see no key of this tile, nor of any later one
+  for (int t = 0; t < ntiles; ++t) {
+    pf_wait_tiles(min(ntiles - 1 - t, kPfAhead - 1));
+    __syncthreads();  // tile t is in LDS; every wave is done with tile t - 2's buffer
+    if (t + kPfAhead < ntiles) issue_tile(t + kPfAhead);
+    if (done) continue;
+    const int key0 = t * kPfKeys;
+    const MLA_LDS char* tile = lds + (t % kPfRing) * kPfBufBytes;
+    const MLA_LDS char* prev = lds + ((t + kPfRing - 1) % kPfRing) * kPfBufBytes;
+    if (key0 >= wave_vis_hi) {  // wave-uniform: finish the sum over the previous tile
+      scale_o();
+      sum_with_softmax(prev, 0, false, false);
+      done = true;
+      continue;
+    }
+
+    // scores: the key operands stream through a ring two k-steps ahead of their MFMAs
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+    {
+      bf16x8 kr[3][2];
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const int dv = cb * 32 + vc;
-        const bf16x8 vf = lds_tr_pair(tile + v_off(r, dv), tile + v_off(r + 8, dv));
-        o[cb] = mfma32x32x16(vf, pk[kk], o[cb]);
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) kr[ks][kb] = lds_b128(tile + kofs[ks] + k_imm(kb, ks));
+#pragma unroll
+      for (int ks = 0; ks < 12; ++ks) {
+        if (ks + 2 < 12) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) kr[(ks + 2) % 3][kb] = lds_b128(tile + kofs[ks + 2] + k_imm(kb, ks + 2));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32x32x16(kr[ks % 3][kb], qf[ks], s[kb]);
       }
     }
+
+    // [sum(t-1) | softmax(t)]
+    scale_o();
+    sum_with_softmax(prev, key0, key0 + kPfKeys > wave_vis_lo, true);
+    pending_rescale = rescale;
+    pending_alpha = alpha;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) pk[kk] = pn[kk];
+  }
+  if (!done && ntiles > 0) {
+    scale_o();
+    sum_with_softmax(lds + ((ntiles - 1) % kPfRing) * kPfBufBytes, 0, false, false);
   }
 
   // normalise and store: element e of block cb is O^T[32 cb + 8 (e/4) + 4 hf + e%4][query]
@@ -410,7 +567,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillArgs a) {
 hipError_t launch_prefill_attn(const PrefillArgs& a, hipStream_t stream) {
   const int64_t grid = (int64_t)a.B * kHeads * a.nqb;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(prefill_attn_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(prefill_attn_kernel, dim3((unsigned)grid), dim3(64 * kPfWaves), 0, stream, a);
   return hipGetLastError();
 }
 
