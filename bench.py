@@ -13,6 +13,10 @@ Infinity Cache, so cache rows really come from HBM.  Separately, the same steps 
 HIP events around each call (on the stream the kernels are launched on) to give per-call launch
 durations; the dominant call's algorithmic bytes over that duration is the roofline figure.
 
+Prefill workloads (``--workload prefill_b1_s4096``): one step = mla_prefill_kv_up ->
+mla_prefill_attn over one batch of whole prompts (multi-head form), reported as prompt tokens/s
+against the MFMA roofline of the attention call.
+
 Prints one JSON line.
 """
 import argparse
@@ -30,6 +34,7 @@ if ROOT not in sys.path:
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_attn_b32_t4096_hbm_counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "deepseek_mla_latent_amd", "csrc", f) for f in ("decode_attn.hip", "common.h")]
 METRIC = "MLA absorbed-decode tokens/s per layer + % of HBM/MFMA roofline, 1 GPU"
+PREFILL_METRIC = "MLA prefill (multi-head form) prompt tokens/s per layer + % of MFMA roofline, 1 GPU"
 MALL_BYTES = 256 * 2 ** 20
 
 
@@ -44,15 +49,29 @@ def _source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(launch_bytes_key: str):
-    """HBM bytes per launch from committed rocprofv3 counters, if taken on the current kernel source."""
+def measured_traffic(launch_bytes_key: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counters, if taken on this workload and on the
+    current kernel source."""
     try:
         rec = json.load(open(COUNTERS_FILE))
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256_16") != _source_hash():
+    if rec.get("kernel_source_sha256_16") != _source_hash() or rec.get("workload") != workload:
         return None
     return rec.get(launch_bytes_key)
+
+
+def roofline_entry(kernel: str, call, dt: str, seconds: float, traffic=None) -> dict:
+    """Achieved rate of one call against the MI355X peak of the resource that bounds it."""
+    from deepseek_mla_latent_amd import accounting
+    bound = call.bound(dt)
+    if bound == "hbm":
+        achieved, peak, unit = call.bytes / seconds / 1e9, accounting.HBM_PEAK_BYTES_S / 1e9, "GB/s"
+    else:
+        achieved, peak, unit = call.flops / seconds / 1e12, accounting.MFMA_PEAK_FLOPS[dt] / 1e12, "TFLOP/s"
+    return {"kernel": kernel, "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+            "frac": achieved / peak, "traffic": traffic, "algorithmic_bytes_per_launch": call.bytes,
+            "algorithmic_flops_per_launch": call.flops, "launch_us": seconds * 1e6}
 
 
 def cpu_baseline(x, target_seconds: float):
@@ -85,6 +104,143 @@ def cpu_baseline(x, target_seconds: float):
                       f"token(s) at {int(x.seq_lens[0])} cached tokens, fp64 non-absorbed numpy, {el:.1f} s"}
 
 
+def prefill_cpu_baseline(x, target_seconds: float):
+    """The fp64 oracle of the two prefill calls on a bounded sample: whole heads (all prompt tokens
+    of the first sequence), one after another, for about target_seconds; scaled to tokens/s as the
+    fraction of the 128 heads done."""
+    import numpy as np
+    from oracle import mla_prefill as ref
+
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"] or [cores])
+    except Exception:
+        pass
+    w = x.workload
+    pool, w_uk, w_uv = x.f32("pool"), x.f32("w_uk"), x.f32("w_uv")
+    q_nope, q_pe = x.f32("q_nope")[:1], x.f32("q_pe")[:1]
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        h = n % w.heads
+        K, V, kpe = ref.kv_up_reference(pool, x.block_table[:1], x.seq_lens[:1], w_uk, w_uv, heads=[h])
+        ref.mha_attention_reference(q_nope, q_pe, K, V, kpe, x.seq_lens[:1], softmax_scale=w.softmax_scale,
+                                    heads=[h])
+        n += 1
+        el = time.perf_counter() - t0
+        if el * (n + 1) / n > target_seconds:
+            break
+    el = time.perf_counter() - t0
+    return {"value": (n / w.heads) * w.q_len / el, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n} of {w.heads} heads x all {w.q_len} prompt tokens of one sequence ({int(x.seq_lens[0])} "
+                      f"keys), fp64 numpy K/V up-projection + per-head attention, {el:.1f} s"}
+
+
+def run_prefill(args, dev):
+    import numpy as np
+    import torch
+
+    from deepseek_mla_latent_amd import accounting, binding
+    from deepseek_mla_latent_amd import inputs as gen
+
+    w = gen.PREFILL_WORKLOADS[args.workload]
+    x = gen.generate_named(args.workload)
+    dt = "bf16"
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    costs = accounting.prefill_costs(x.seq_lens, w.q_len, dt)
+    per_replica = sum(c.bytes for c in costs)
+    R = args.replicas or max(2, math.ceil(2 * MALL_BYTES / per_replica) + 1)
+    params = binding.make_params(batch=w.batch, q_len=w.q_len, max_seq_len=x.max_seq_len,
+                                 max_pages_per_seq=x.block_table.shape[1], softmax_scale=w.softmax_scale,
+                                 dtype=binding.MLA_BF16)
+    kv_bytes = binding.mla_prefill_kv_bytes(params)
+    reps = []
+    for _ in range(R):
+        d = dict(q_nope=up(x.q_nope), q_pe=up(x.q_pe), w_uk=up(x.w_uk), w_uv=up(x.w_uv), pool=up(x.pool),
+                 bt=torch.from_numpy(x.block_table).to(dev), lens=torch.from_numpy(x.seq_lens).to(dev))
+        d["kv"] = torch.empty(kv_bytes // 2, dtype=torch.bfloat16, device=dev)
+        d["out"] = torch.empty((w.batch, w.q_len, w.heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+        d["lse"] = torch.empty((w.batch, w.q_len, w.heads), dtype=torch.float32, device=dev)
+        reps.append(d)
+
+    def kv_up(d):
+        binding.mla_prefill_kv_up(d["pool"], d["bt"], d["lens"], d["w_uk"], d["w_uv"], d["kv"], params)
+
+    def attn(d):
+        binding.mla_prefill_attn(d["q_nope"], d["q_pe"], d["kv"], d["lens"], d["out"], d["lse"], params)
+
+    def run(d):
+        kv_up(d)
+        attn(d)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for d in reps:
+            run(d)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for d in reps:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run(d)
+        graphs.append(g)
+    for k in range(args.warmup):
+        graphs[k % R].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        graphs[k % R].replay()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    stream = torch.cuda.current_stream()
+    n_ev = max(10, min(args.steps, 50))
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_ev)]
+    for k in range(n_ev):
+        d = reps[k % R]
+        evs[k][0].record(stream)
+        kv_up(d)
+        evs[k][1].record(stream)
+        attn(d)
+        evs[k][2].record(stream)
+    torch.cuda.synchronize()
+    call_us = [float(np.mean([evs[k][j].elapsed_time(evs[k][j + 1]) for k in range(n_ev)])) * 1e3 for j in range(2)]
+    t_roof = sum(c.roof_seconds(dt) for c in costs)
+    rec = {
+        "metric": PREFILL_METRIC,
+        "value": w.batch * w.q_len / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic (seeded N(0,1) cache and queries, N(0,1/512) weights)",
+        "config": {"workload": args.workload, "batch": w.batch, "prompt_len": w.q_len,
+                   "cache_len": int(x.seq_lens.max()), "heads": w.heads, "kv_lora_rank": w.kv_lora_rank,
+                   "rope_dim": w.rope_dim, "head_dim": w.head_dim, "page_size": w.page_size, "causal": True,
+                   "replicas": R, "graph_replay": True},
+        "roofline": roofline_entry("mla_prefill_attn", costs[1], dt, call_us[1] * 1e-6),
+        "path_roofline": {"t_roof_us": t_roof * 1e6, "t_step_us": ms_per_step * 1e3,
+                          "frac": t_roof / (ms_per_step * 1e-3),
+                          "calls_us": dict(zip([c.name for c in costs], call_us)),
+                          "calls_roof_us": {c.name: c.roof_seconds(dt) * 1e6 for c in costs},
+                          "calls_frac": {c.name: c.roof_seconds(dt) / (u * 1e-6) for c, u in zip(costs, call_us)}},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = prefill_cpu_baseline(x, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -115,6 +271,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload in gen.PREFILL_WORKLOADS:
+        return run_prefill(args, dev)
 
     w = gen.WORKLOADS[args.workload]
     x = gen.generate_named(args.workload)
@@ -201,8 +359,7 @@ def main():
     tokens = w.batch * w.q_len
     attn = costs[1]
     attn_s = call_us[1] * 1e-6
-    achieved = attn.bytes / attn_s / 1e9
-    traffic = measured_traffic("hbm_bytes_per_launch")
+    traffic = measured_traffic("hbm_bytes_per_launch", args.workload)
     t_roof = sum(c.roof_seconds(dt) for c in costs)
     rec = {
         "metric": METRIC,
@@ -221,10 +378,7 @@ def main():
                    "cache_len": int(x.seq_lens.max()), "heads": w.heads, "kv_lora_rank": w.kv_lora_rank,
                    "rope_dim": w.rope_dim, "head_dim": w.head_dim, "page_size": w.page_size,
                    "num_splits": splits, "replicas": R, "graph_replay": True},
-        "roofline": {"kernel": "mla_decode_attn (split attention + LSE merge)", "bound": attn.bound(dt),
-                     "achieved": achieved, "peak": accounting.HBM_PEAK_BYTES_S / 1e9, "unit": "GB/s",
-                     "frac": achieved * 1e9 / accounting.HBM_PEAK_BYTES_S, "traffic": traffic,
-                     "algorithmic_bytes_per_launch": attn.bytes, "launch_us": call_us[1]},
+        "roofline": roofline_entry("mla_decode_attn (split attention + LSE merge)", attn, dt, attn_s, traffic),
         "path_roofline": {"t_roof_us": t_roof * 1e6, "t_step_us": ms_per_step * 1e3,
                           "frac": t_roof / (ms_per_step * 1e-3),
                           "calls_us": dict(zip([c.name for c in costs], call_us)),

@@ -11,6 +11,13 @@ fraction of the hardware limit.
   visible (query, key) pair — twice the per-token multiply-accumulate count of the izhida answer
   "DeepSeek" ("DeepSeek-V2的推理成本如何计算？": 128×(512+64+512) per cached token).
 * out_proj:  W_UV + o_lat (fp32) + out;  2·T·H·d_c·d_h FLOPs.
+
+Prefill in multi-head form (two calls):
+
+* prefill_kv_up: latent rows and k_pe read once, W_UK + W_UV, [K_nope | V] of every cached token
+  and head plus the dense k_pe written;  2·L·H·d_c·2d_h FLOPs (L = all cached tokens).
+* prefill_attn: q_nope + q_pe, [K_nope | V] + k_pe read once, out + lse written;
+  2·H·(d_h + d_R + d_h) FLOPs per visible (query, key) pair.
 """
 from __future__ import annotations
 
@@ -59,3 +66,17 @@ def path_costs(seq_lens: Sequence[int], q_len: int, dtype: str, *, heads: int = 
     out = CallCost("mla_out_proj", heads * d_c * d_h * e + T * heads * d_c * 4 + T * heads * d_h * e,
                    2 * T * heads * d_c * d_h)
     return [absorb, attn, out]
+
+
+def prefill_costs(seq_lens: Sequence[int], q_len: int, dtype: str = "bf16", *, heads: int = 128, d_c: int = 512,
+                  d_r: int = 64, d_h: int = 128, causal: bool = True):
+    e = 2 if dtype == "bf16" else 4
+    L = sum(int(n) for n in seq_lens)
+    T = len(seq_lens) * q_len
+    up = CallCost("mla_prefill_kv_up",
+                  L * (d_c + d_r) * e + 2 * heads * d_c * d_h * e + L * heads * 2 * d_h * e + L * d_r * e,
+                  2 * L * heads * d_c * 2 * d_h)
+    attn = CallCost("mla_prefill_attn",
+                    T * heads * (d_h + d_r) * e + L * heads * 2 * d_h * e + L * d_r * e + T * heads * (d_h * e + 4),
+                    2 * heads * (d_h + d_r + d_h) * visible_pairs(seq_lens, q_len, causal))
+    return [up, attn]
