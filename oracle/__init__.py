@@ -13,11 +13,13 @@ Modules:
   definitions of the three library calls.
 * ``mla_prefill`` — fp64 reference of prefill in multi-head form (order 1): K/V
   up-projection of every cached token, then per-head attention over them.
+* ``mla_prepare`` — fp64 reference of the step before the path: the fused a-projection (a plain
+  matmul), rotary position embedding, and the AppendKV scatter into the paged cache.
 * ``flops`` — the pages' FLOP convention and the three computation orders of
   both absorptions, counted step by step from index extents; byte counts.
 
-Every function is pinned by ``tests/test_oracle.py``, ``tests/test_oracle_prefill.py`` and
-``tests/test_flops.py``
+Every function is pinned by ``tests/test_oracle.py``, ``tests/test_oracle_prefill.py``,
+``tests/test_oracle_prepare.py`` and ``tests/test_flops.py``
 against what the pages print and against closed forms, special cases and
 library routines (see each test's docstring).
 """
