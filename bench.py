@@ -13,6 +13,10 @@ Infinity Cache, so cache rows really come from HBM.  Separately, the same steps 
 HIP events around each call (on the stream the kernels are launched on) to give per-call launch
 durations; the dominant call's algorithmic bytes over that duration is the roofline figure.
 
+The step before attention (``--workload prepare_b32_t4096``): one step = mla_linear (the fused
+a-projection of 32 tokens, 7168 -> 1536 + 512 + 64) -> mla_rope_append into a 4096-token cache,
+reported as tokens/s against the HBM roofline of the projection (a weight stream).
+
 Prefill workloads (``--workload prefill_b1_s4096``): one step = mla_prefill_kv_up ->
 mla_prefill_attn over one batch of whole prompts (multi-head form), reported as prompt tokens/s
 against the MFMA roofline of the attention call.
@@ -35,6 +39,10 @@ COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_attn_b32_t4096_hbm_counte
 KERNEL_SOURCES = [os.path.join(ROOT, "deepseek_mla_latent_amd", "csrc", f) for f in ("decode_attn.hip", "common.h")]
 METRIC = "MLA absorbed-decode tokens/s per layer + % of HBM/MFMA roofline, 1 GPU"
 PREFILL_METRIC = "MLA prefill (multi-head form) prompt tokens/s per layer + % of MFMA roofline, 1 GPU"
+PREPARE_METRIC = "MLA step before attention (fused a-projection + RoPE + AppendKV) tokens/s per layer + % of HBM roofline, 1 GPU"
+# The step before attention at a decode batch: 32 tokens, hidden 7168 (DeepSeek-V3), fused projection to
+# q_lora_rank 1536 + kv_lora_rank 512 + rope 64 = 2112 columns, then RoPE + AppendKV into a 4096-token cache.
+PREPARE_WORKLOADS = {"prepare_b32_t4096": dict(batch=32, q_len=1, cache_len=4096, d_model=7168, q_lora_rank=1536)}
 MALL_BYTES = 256 * 2 ** 20
 
 
@@ -241,6 +249,149 @@ def run_prefill(args, dev):
     print(json.dumps(rec), flush=True)
 
 
+def run_prepare(args, dev):
+    import numpy as np
+    import torch
+
+    from deepseek_mla_latent_amd import accounting, binding
+    from deepseek_mla_latent_amd import inputs as gen
+
+    cfg = PREPARE_WORKLOADS[args.workload]
+    B, S, L, D, QR = cfg["batch"], cfg["q_len"], cfg["cache_len"], cfg["d_model"], cfg["q_lora_rank"]
+    N = QR + 512 + 64
+    M = B * S
+    w = gen.small_workload(B, S, cache_len=L, dtype="bf16", paged=False)
+    x = gen.generate(w, 301)
+    rng = np.random.default_rng(302)
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    hidden = gen.round_to_bf16_bits(rng.standard_normal((M, D), dtype=np.float32))
+    w_a = gen.round_to_bf16_bits(rng.standard_normal((D, N), dtype=np.float32) / np.float32(np.sqrt(D)))
+    e = 2
+    lin = accounting.CallCost("mla_linear", (M * D + D * N + M * N) * e, 2 * M * D * N)
+    rope = accounting.CallCost("mla_rope_append", M * (576 * e + 128 * 64 * e * 2 + 576 * e) + B * 8, 0)
+    per_replica = lin.bytes
+    R = args.replicas or max(2, int(np.ceil(2 * MALL_BYTES / per_replica)) + 1)
+    params = binding.make_params(batch=B, q_len=S, max_seq_len=L, max_pages_per_seq=x.block_table.shape[1],
+                                 softmax_scale=w.softmax_scale)
+    ws_bytes = binding.mla_linear_workspace_bytes(M, D, N)
+    reps = []
+    for _ in range(R):
+        d = dict(h=up(hidden), w=up(w_a), q_pe=up(x.q_pe), pool=up(x.pool),
+                 bt=torch.from_numpy(x.block_table).to(dev), lens=torch.from_numpy(x.seq_lens).to(dev))
+        d["y"] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        d["ws"] = torch.empty(max(ws_bytes, 16) // 4, dtype=torch.float32, device=dev) if ws_bytes else None
+        reps.append(d)
+
+    def linear(d):
+        binding.mla_linear(d["h"], d["w"], d["y"], M, D, N, d["ws"])
+
+    def rope_append(d):
+        binding.mla_rope_append(d["q_pe"], d["y"].data_ptr() + QR * 2, N, d["pool"], d["bt"], d["lens"], params)
+
+    def run(d):
+        linear(d)
+        rope_append(d)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for d in reps:
+            run(d)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for d in reps:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run(d)
+        graphs.append(g)
+    for k in range(args.warmup):
+        graphs[k % R].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        graphs[k % R].replay()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    stream = torch.cuda.current_stream()
+    n_ev = max(20, min(args.steps, 200))
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_ev)]
+    for k in range(n_ev):
+        d = reps[k % R]
+        evs[k][0].record(stream)
+        linear(d)
+        evs[k][1].record(stream)
+        rope_append(d)
+        evs[k][2].record(stream)
+    torch.cuda.synchronize()
+    call_us = [float(np.mean([evs[k][j].elapsed_time(evs[k][j + 1]) for k in range(n_ev)])) * 1e3 for j in range(2)]
+    costs = [lin, rope]
+    t_roof = sum(c.roof_seconds("bf16") for c in costs)
+    rec = {
+        "metric": PREPARE_METRIC,
+        "value": M / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) hidden states and cache, N(0,1/d_model) projection weights)",
+        "config": {"workload": args.workload, "batch": B, "q_len": S, "cache_len": L, "d_model": D,
+                   "projection_out": N, "linear_splits_workspace_bytes": ws_bytes, "replicas": R,
+                   "graph_replay": True},
+        "roofline": roofline_entry("mla_linear (fused a-projection)", lin, "bf16", call_us[0] * 1e-6),
+        "path_roofline": {"t_roof_us": t_roof * 1e6, "t_step_us": ms_per_step * 1e3,
+                          "frac": t_roof / (ms_per_step * 1e-3),
+                          "calls_us": dict(zip([c.name for c in costs], call_us)),
+                          "calls_roof_us": {c.name: c.roof_seconds("bf16") * 1e6 for c in costs}},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = prepare_cpu_baseline(hidden, w_a, x, QR, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+def prepare_cpu_baseline(hidden, w_a, x, q_lora_rank: int, target_seconds: float):
+    """The fp64 oracle of the step (projection, rotation, append) on the whole batch, repeated for
+    about target_seconds."""
+    import numpy as np
+    from deepseek_mla_latent_amd import inputs as gen
+    from oracle import mla_prepare as ref
+
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"] or [cores])
+    except Exception:
+        pass
+    h, w = gen.bf16_bits_to_f32(hidden), gen.bf16_bits_to_f32(w_a)
+    q_pe, pool = x.f32("q_pe"), x.f32("pool")
+    S = x.workload.q_len
+    pos = ref.new_token_positions(x.seq_lens, S)
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        y = ref.linear_reference(h, w)
+        kva = y[:, q_lora_rank:q_lora_rank + 576].reshape(len(x.seq_lens), S, 576)
+        ref.rope_reference(q_pe, pos)
+        ref.append_kv_reference(pool, x.block_table, x.seq_lens, kva[..., :512], ref.rope_reference(kva[..., 512:], pos))
+        n += 1
+        el = time.perf_counter() - t0
+        if el * (n + 1) / n > target_seconds:
+            break
+    el = time.perf_counter() - t0
+    return {"value": n * h.shape[0] / el, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n} passes over the whole batch ({h.shape[0]} tokens: fp64 projection {h.shape[1]}x{w.shape[1]}, "
+                      f"rotation, append into the cache copy), {el:.1f} s"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -273,6 +424,8 @@ def main():
     torch.cuda.set_device(dev)
     if args.workload in gen.PREFILL_WORKLOADS:
         return run_prefill(args, dev)
+    if args.workload in PREPARE_WORKLOADS:
+        return run_prepare(args, dev)
 
     w = gen.WORKLOADS[args.workload]
     x = gen.generate_named(args.workload)

@@ -24,7 +24,8 @@ STATUS = {
     -5: "MLA_ERR_WORKSPACE", -6: "MLA_ERR_UNSUPPORTED", -7: "MLA_ERR_LAUNCH", -8: "MLA_ERR_DEVICE",
 }
 EXPORTS = ("mla_absorb_q", "mla_decode_workspace_bytes", "mla_decode_num_splits", "mla_decode_attn",
-           "mla_out_proj", "mla_prefill_kv_bytes", "mla_prefill_kv_up", "mla_prefill_attn", "mla_status_str")
+           "mla_out_proj", "mla_prefill_kv_bytes", "mla_prefill_kv_up", "mla_prefill_attn",
+           "mla_linear_workspace_bytes", "mla_linear", "mla_rope_append", "mla_status_str")
 
 
 class MlaLibraryMissing(RuntimeError):
@@ -76,6 +77,12 @@ def load_library(path: Optional[str] = None):
     lib.mla_prefill_kv_up.restype = i32
     lib.mla_prefill_attn.argtypes = [vp, vp, vp, sz, vp, vp, vp, pp, vp]
     lib.mla_prefill_attn.restype = i32
+    lib.mla_linear_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.mla_linear_workspace_bytes.restype = sz
+    lib.mla_linear.argtypes = [vp, vp, vp, i32, i32, i32, vp, sz, vp]
+    lib.mla_linear.restype = i32
+    lib.mla_rope_append.argtypes = [vp, vp, i32, vp, vp, vp, ctypes.c_float, pp, vp]
+    lib.mla_rope_append.restype = i32
     lib.mla_status_str.argtypes = [i32]
     lib.mla_status_str.restype = ctypes.c_char_p
     if path is None:
@@ -181,6 +188,24 @@ def mla_prefill_attn(q_nope, q_pe, kv, seq_lens, out, lse, params: mla_params, s
     lib = load_library()
     _check(lib.mla_prefill_attn(_ptr(q_nope), _ptr(q_pe), _ptr(kv), _nbytes(kv, kv_bytes), _ptr(seq_lens), _ptr(out),
                                 _ptr(lse), ctypes.byref(params), _stream(stream)), "mla_prefill_attn")
+
+
+def mla_linear_workspace_bytes(m: int, k: int, n: int) -> int:
+    return int(load_library().mla_linear_workspace_bytes(m, k, n))
+
+
+def mla_linear(x, w, y, m: int, k: int, n: int, workspace=None, stream=None,
+               workspace_bytes: Optional[int] = None) -> None:
+    lib = load_library()
+    _check(lib.mla_linear(_ptr(x), _ptr(w), _ptr(y), m, k, n, _ptr(workspace), _nbytes(workspace, workspace_bytes),
+                          _stream(stream)), "mla_linear")
+
+
+def mla_rope_append(q_pe, kv_a, kv_a_stride: int, kv_pool, block_table, seq_lens, params: mla_params,
+                    rope_base: float = 10000.0, stream=None) -> None:
+    lib = load_library()
+    _check(lib.mla_rope_append(_ptr(q_pe), _ptr(kv_a), kv_a_stride, _ptr(kv_pool), _ptr(block_table), _ptr(seq_lens),
+                               rope_base, ctypes.byref(params), _stream(stream)), "mla_rope_append")
 
 
 class DecodeBuffers:

@@ -65,4 +65,15 @@ struct PrefillArgs {
 };
 hipError_t launch_prefill_attn(const PrefillArgs& a, hipStream_t stream);
 
+// y (M x N) = x (M x K) W (K x N), bf16 row-major, fp32 accumulation; K % 64 == 0, N % 64 == 0.
+// splits > 1 splits K (K / splits % 64 == 0) and needs partial = splits * M * N floats.
+int linear_splits(int M, int K, int N, int cus);
+hipError_t launch_linear(const void* x, const void* w, void* y, float* partial, int M, int K, int N, int splits,
+                         hipStream_t stream);
+// rotary embedding of q_pe (B,S,H,64, in place) and of the k_pe part of kv_a rows (stride
+// kv_stride elements, [c_KV 512 | k_pe 64] at the row start), and AppendKV of [c_KV | k_pe] into
+// the paged pool at positions seq_lens[b] - S + i.
+hipError_t launch_rope_append(void* q_pe, const void* kv_a, int kv_stride, void* pool, const int32_t* block_table,
+                              const int32_t* seq_lens, int B, int S, int max_pages, double base, hipStream_t stream);
+
 }  // namespace mla

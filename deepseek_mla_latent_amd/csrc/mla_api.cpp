@@ -97,6 +97,12 @@ mla_status check_prefill(const mla_params* p) {
   return MLA_OK;
 }
 
+mla_status check_linear(int32_t m, int32_t k, int32_t n) {
+  if (m < 0 || k <= 0 || n <= 0 || k % 64 != 0 || n % 64 != 0) return MLA_ERR_SHAPE;
+  if ((int64_t)m * k * 2 >= (int64_t)1 << 32 || (int64_t)k * n * 2 >= (int64_t)1 << 32) return MLA_ERR_SHAPE;
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -266,6 +272,53 @@ mla_status mla_prefill_attn(const void* q_nope, const void* q_pe, const void* kv
   a.causal = p->causal ? 1 : 0;
   a.scale_log2 = (float)((double)p->softmax_scale * 1.4426950408889634);
   if (mla::launch_prefill_attn(a, (hipStream_t)stream) != hipSuccess) return MLA_ERR_LAUNCH;
+  return MLA_OK;
+}
+
+size_t mla_linear_workspace_bytes(int32_t m, int32_t k, int32_t n) {
+  if (check_linear(m, k, n) != MLA_OK || m == 0) return 0;
+  const int cus = cu_count();
+  if (cus <= 0) return 0;
+  const int s = mla::linear_splits(m, k, n, cus);
+  return s > 1 ? (size_t)s * m * n * sizeof(float) : 0;
+}
+
+mla_status mla_linear(const void* x, const void* w, void* y, int32_t m, int32_t k, int32_t n, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  mla_status st = check_linear(m, k, n);
+  if (st != MLA_OK) return st;
+  if (m == 0) return MLA_OK;
+  if (!x || !w || !y) return MLA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return MLA_ERR_ALIGN;
+  const int cus = cu_count();
+  if (cus <= 0) return MLA_ERR_DEVICE;
+  const int splits = mla::linear_splits(m, k, n, cus);
+  if (splits > 1) {
+    if (!workspace) return MLA_ERR_NULL;
+    if (workspace_bytes < (size_t)splits * m * n * sizeof(float)) return MLA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MLA_ERR_ALIGN;
+  }
+  if (mla::launch_linear(x, w, y, (float*)workspace, m, k, n, splits, (hipStream_t)stream) != hipSuccess)
+    return MLA_ERR_LAUNCH;
+  return MLA_OK;
+}
+
+mla_status mla_rope_append(void* q_pe, const void* kv_a, int32_t kv_a_stride, void* kv_pool,
+                           const int32_t* block_table, const int32_t* seq_lens, float rope_base, const mla_params* p,
+                           void* stream) {
+  mla_status st = check_params(p);
+  if (st != MLA_OK) return st;
+  if (p->dtype != MLA_BF16) return MLA_ERR_DTYPE;
+  const int max_pages = (p->max_seq_len + mla::kPage - 1) / mla::kPage;
+  if (p->max_pages_per_seq < max_pages) return MLA_ERR_SHAPE;
+  if (kv_a_stride < mla::kRow || kv_a_stride % 8 != 0) return MLA_ERR_SHAPE;
+  if (!(rope_base > 0.f) || !std::isfinite(rope_base)) return MLA_ERR_SHAPE;
+  if (tokens_of(p) == 0) return MLA_OK;
+  if (!q_pe || !kv_a || !kv_pool || !block_table || !seq_lens) return MLA_ERR_NULL;
+  if (!aligned16(q_pe) || !aligned16(kv_a) || !aligned16(kv_pool)) return MLA_ERR_ALIGN;
+  if (mla::launch_rope_append(q_pe, kv_a, kv_a_stride, kv_pool, block_table, seq_lens, p->batch, p->q_len,
+                              p->max_pages_per_seq, (double)rope_base, (hipStream_t)stream) != hipSuccess)
+    return MLA_ERR_LAUNCH;
   return MLA_OK;
 }
 

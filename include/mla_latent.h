@@ -189,6 +189,58 @@ mla_status mla_prefill_attn(const void* q_nope, const void* q_pe, const void* kv
                             const int32_t* seq_lens, void* out, float* lse, const mla_params* p,
                             void* stream);
 
+/*
+ * ---- The step before the path -----------------------------------------------------------------
+ * The stage before attention is InputNorm, QKVProj, AppendKV, BMM (Perplexity post, section
+ * "Наложение вычислений и взаимодействия"), with q_a_proj and kv_a_proj fused into one projection
+ * (section "Слой MLA"). The absorption note (§二.1) gives the compressed widths. The
+ * normalisations are not part of these calls.
+ */
+
+/*
+ * Bytes of scratch memory mla_linear needs for an m x k by k x n product (0 when none, or for
+ * invalid sizes). It depends on the device's compute-unit count: query it on the device that
+ * will run the call.
+ */
+size_t mla_linear_workspace_bytes(int32_t m, int32_t k, int32_t n);
+
+/*
+ * y = x W: x (m, k) bf16, W (k, n) bf16, y (m, n) bf16 (out), all row-major; fp32 accumulation,
+ * rounded once. k and n must be multiples of 64. For a few rows the layer is a weight stream:
+ * the library splits k so the grid fills the chip, and sums the fp32 partials in a fixed order
+ * in `workspace` (at least mla_linear_workspace_bytes(); its contents are scratch). Results are
+ * bitwise reproducible on one device. Serves the fused a-projection
+ * (y = [c^Q | c^KV | k_pe before rotation], k = d_model, n = q_lora_rank + 512 + 64) and any
+ * other plain projection in the same form.
+ * Cites: Perplexity post, section "Слой MLA" (fused qkv_a_proj); absorption note §二.1 (widths).
+ */
+mla_status mla_linear(const void* x, const void* w, void* y, int32_t m, int32_t k, int32_t n,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Rotary position embedding, then AppendKV, for the S = q_len new tokens of each sequence. Token
+ * i of sequence b is at position pos = seq_lens[b] - S + i, so seq_lens already counts the new
+ * tokens.
+ *   q_pe    (B,S,H,64) bf16, rotated in place
+ *   kv_a    rows of kv_a_stride elements (>= 576, a multiple of 8), one per token (b, i), each
+ *           starting with [c_KV (512) | k_pe (64) before rotation]; e.g. the fused projection's
+ *           output at column offset q_lora_rank
+ *   kv_pool, block_table, seq_lens as for mla_decode_attn; the slot of pos receives
+ *           [c_KV | rotated k_pe]. A token at a negative position (seq_lens[b] < S) is rotated
+ *           but not written.
+ *   rope_base  the rotation base (10000)
+ * Rotation: each consecutive pair (x[2j], x[2j+1]) turns by pos * rope_base^(-2j/64) (the
+ * rotation of Su et al., RoFormer; the pages give no formula). Angles are formed in fp64; the
+ * rotation is done in fp32 and rounded once to bf16. c_KV is copied bit for bit.
+ * bf16 only (MLA_ERR_DTYPE otherwise).
+ * Cites: Perplexity post, sections "Наложение вычислений и взаимодействия" (AppendKV before
+ * attention) and "Слой MLA" (paged cache); izhida answer "专家" (the RoPE key is one per token,
+ * shared by the heads).
+ */
+mla_status mla_rope_append(void* q_pe, const void* kv_a, int32_t kv_a_stride, void* kv_pool,
+                           const int32_t* block_table, const int32_t* seq_lens, float rope_base,
+                           const mla_params* p, void* stream);
+
 /* Static string for a status code (never NULL). */
 const char* mla_status_str(mla_status s);
 

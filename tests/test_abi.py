@@ -133,3 +133,35 @@ def test_prefill_errors(fn):
     assert fn(P(q_len=300), kv_bytes=need - 2) == -5
     assert fn(P(q_len=300, batch=0), kv_bytes=0) == 0
     assert lib.mla_prefill_kv_up(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None, None) == -1
+
+
+def test_linear_errors():
+    def lin(m=32, k=128, n=64, x=FAKE, w=FAKE, y=FAKE):
+        return lib.mla_linear(x, w, y, m, k, n, None, 0, None)
+    assert lin(k=100) == -2  # k not a multiple of 64
+    assert lin(n=96) == -2   # n not a multiple of 64
+    assert lin(m=-1) == -2
+    assert lin(m=1 << 20, k=4096) == -2  # x larger than 4 GiB
+    assert lin(x=None) == -1
+    assert lin(y=MISALIGNED) == -4
+    assert lin(m=0) == 0
+    assert lib.mla_linear_workspace_bytes(32, 100, 64) == 0
+
+
+def test_rope_append_errors():
+    def ra(params, stride=576, base=10000.0, **ptrs):
+        p = dict(q=FAKE, kv=FAKE, pool=FAKE, bt=FAKE, lens=FAKE)
+        p.update(ptrs)
+        return lib.mla_rope_append(p["q"], p["kv"], stride, p["pool"], p["bt"], p["lens"], base, ctypes.byref(params),
+                                   None)
+    assert ra(P(dtype=binding.MLA_F32)) == -3
+    assert ra(P(), stride=512) == -2
+    assert ra(P(), stride=580) == -2   # rows must stay 16-byte aligned
+    assert ra(P(), base=0.0) == -2
+    assert ra(P(), base=float("nan")) == -2
+    assert ra(P(max_pages_per_seq=2)) == -2
+    assert ra(P(), q=None) == -1
+    assert ra(P(), pool=None) == -1
+    assert ra(P(), kv=MISALIGNED) == -4
+    assert ra(P(batch=0)) == 0
+    assert ra(P(num_heads=64)) == -6
