@@ -165,3 +165,16 @@ def latent_attention_reference(q_lat, q_pe, pool, block_table, seq_lens, *, soft
                 p, lse[b, i, h] = _softmax_stats(Z[:, h])
                 o_lat[b, i, h] = p @ C[:n] if n else 0.0
     return {"o_lat": o_lat, "lse": lse}
+
+
+def o_proj_reference(out, w_o):
+    """y[b,s,e] = sum over heads h and value dims v of out[b,s,h,v] W_O[h,v,e], fp64.
+
+    The output projection after the path: "【笔记】MLA矩阵吸收分析" §三.1 / §三.2, step 3 (W_O of shape
+    (n_heads x v_head_dim, dim) -> (h, v, e)), summed over the heads as the FLOP count 2bhsev of
+    the same steps implies.  ``w_o`` is (H, d_v, e).
+    """
+    o = np.asarray(out, dtype=np.float64)
+    B, S, H, V = o.shape
+    w = np.asarray(w_o, dtype=np.float64).reshape(H * V, -1)
+    return (o.reshape(B * S, H * V) @ w).reshape(B, S, -1)

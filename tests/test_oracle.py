@@ -254,3 +254,22 @@ def test_planted_mistakes_are_caught():
                                              softmax_scale=1 / math.sqrt(128))["out"]
     assert _rel(no_rope, good) > 1e-3
     assert _rel(wrong_scale, good) > 1e-3
+
+
+def test_three_orders_of_the_second_absorption_agree():
+    """[note] §三: W_O[score(W_UV c)] (order 1), W_O[W_UV(score c)] (order 2) and (W_O W_UV)(score c)
+    (order 3, the fused (h, k, e) weight formed with a library einsum) give the same output."""
+    t = _tiny(seed=21)
+    rng = np.random.default_rng(22)
+    H, Dc, Dv = t["w_uv"].shape
+    w_o = rng.standard_normal((H, Dv, 10)) / math.sqrt(H * Dv)
+    r = _nonabsorbed(t, 0.7)  # order 1: per-head V, then attention
+    y1 = ref.o_proj_reference(r["out"], w_o)
+    y2 = ref.o_proj_reference(ref.out_proj_reference(r["o_lat"], t["w_uv"]), w_o)  # order 2
+    w_ouv = torch.einsum("hkv,hve->hke", torch.from_numpy(t["w_uv"]), torch.from_numpy(w_o)).numpy()
+    y3 = torch.einsum("bshk,hke->bse", torch.from_numpy(r["o_lat"]), torch.from_numpy(w_ouv)).numpy()  # order 3
+    np.testing.assert_allclose(y1, y3, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(y2, y3, rtol=1e-11, atol=1e-12)
+    # a dropped head in the sum (a plausible indexing mistake) is caught
+    y_bad = ref.o_proj_reference(r["out"][:, :, 1:], w_o[1:])
+    assert not np.allclose(y_bad, y3, rtol=1e-6)
