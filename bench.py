@@ -17,6 +17,10 @@ The step before attention (``--workload prepare_b32_t4096``): one step = mla_lin
 a-projection of 32 tokens, 7168 -> 1536 + 512 + 64) -> mla_rope_append into a 4096-token cache,
 reported as tokens/s against the HBM roofline of the projection (a weight stream).
 
+The output projection after the path (``--workload oproj_b32``): one step = mla_linear of the
+per-head outputs of 32 tokens (128 x 128 = 16384 wide) by W_O (16384 x 7168), a 235 MB weight
+stream, against the HBM roofline.
+
 Prefill workloads (``--workload prefill_b1_s4096``): one step = mla_prefill_kv_up ->
 mla_prefill_attn over one batch of whole prompts (multi-head form), reported as prompt tokens/s
 against the MFMA roofline of the attention call.
@@ -43,6 +47,9 @@ PREPARE_METRIC = "MLA step before attention (fused a-projection + RoPE + AppendK
 # The step before attention at a decode batch: 32 tokens, hidden 7168 (DeepSeek-V3), fused projection to
 # q_lora_rank 1536 + kv_lora_rank 512 + rope 64 = 2112 columns, then RoPE + AppendKV into a 4096-token cache.
 PREPARE_WORKLOADS = {"prepare_b32_t4096": dict(batch=32, q_len=1, cache_len=4096, d_model=7168, q_lora_rank=1536)}
+OPROJ_METRIC = "MLA output projection W_O after the path, tokens/s per layer + % of HBM roofline, 1 GPU"
+# The output projection after the path at a decode batch: 32 tokens x (128 heads x 128) -> 7168.
+OPROJ_WORKLOADS = {"oproj_b32": dict(tokens=32, k=128 * 128, n=7168)}
 MALL_BYTES = 256 * 2 ** 20
 
 
@@ -392,6 +399,101 @@ def prepare_cpu_baseline(hidden, w_a, x, q_lora_rank: int, target_seconds: float
                       f"rotation, append into the cache copy), {el:.1f} s"}
 
 
+def run_oproj(args, dev):
+    import numpy as np
+    import torch
+
+    from deepseek_mla_latent_amd import accounting, binding
+    from deepseek_mla_latent_amd import inputs as gen
+
+    cfg = OPROJ_WORKLOADS[args.workload]
+    M, K, N = cfg["tokens"], cfg["k"], cfg["n"]
+    rng = np.random.default_rng(401)
+    x = gen.round_to_bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
+    w = gen.round_to_bf16_bits(rng.standard_normal((K, N), dtype=np.float32) / np.float32(np.sqrt(K)))
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    lin = accounting.CallCost("mla_linear", (M * K + K * N + M * N) * 2, 2 * M * K * N)
+    R = args.replicas or max(2, int(np.ceil(2 * MALL_BYTES / lin.bytes)) + 1)
+    ws_bytes = binding.mla_linear_workspace_bytes(M, K, N)
+    reps = []
+    for _ in range(R):
+        d = dict(x=up(x), w=up(w), y=torch.empty((M, N), dtype=torch.bfloat16, device=dev))
+        d["ws"] = torch.empty(max(ws_bytes, 16) // 4, dtype=torch.float32, device=dev) if ws_bytes else None
+        reps.append(d)
+
+    def run(d):
+        binding.mla_linear(d["x"], d["w"], d["y"], M, K, N, d["ws"])
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for d in reps:
+            run(d)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for d in reps:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run(d)
+        graphs.append(g)
+    for k in range(args.warmup):
+        graphs[k % R].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        graphs[k % R].replay()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    stream = torch.cuda.current_stream()
+    n_ev = max(20, min(args.steps, 100))
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_ev)]
+    for k in range(n_ev):
+        evs[k][0].record(stream)
+        run(reps[k % R])
+        evs[k][1].record(stream)
+    torch.cuda.synchronize()
+    call_us = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3
+    rec = {
+        "metric": OPROJ_METRIC,
+        "value": M / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) per-head outputs, N(0,1/16384) weights)",
+        "config": {"workload": args.workload, "tokens": M, "k": K, "n": N, "workspace_bytes": ws_bytes,
+                   "replicas": R, "graph_replay": True},
+        "roofline": roofline_entry("mla_linear (W_O)", lin, "bf16", call_us * 1e-6),
+        "path_roofline": {"t_roof_us": lin.roof_seconds("bf16") * 1e6, "t_step_us": ms_per_step * 1e3,
+                          "frac": lin.roof_seconds("bf16") / (ms_per_step * 1e-3)},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import mla_prepare as ref
+        xf, wf = gen.bf16_bits_to_f32(x), gen.bf16_bits_to_f32(w)
+        t0 = time.perf_counter()
+        n = 0
+        while True:
+            ref.linear_reference(xf, wf)
+            n += 1
+            el = time.perf_counter() - t0
+            if el * (n + 1) / n > args.cpu_seconds:
+                break
+        el = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": n * M / el, "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)),
+                               "kind": "oracle",
+                               "sample": f"{n} fp64 projections of all {M} tokens ({K}x{N}), {el:.1f} s"}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -426,6 +528,8 @@ def main():
         return run_prefill(args, dev)
     if args.workload in PREPARE_WORKLOADS:
         return run_prepare(args, dev)
+    if args.workload in OPROJ_WORKLOADS:
+        return run_oproj(args, dev)
 
     w = gen.WORKLOADS[args.workload]
     x = gen.generate_named(args.workload)

@@ -146,3 +146,30 @@ def test_prepared_inputs_feed_the_decode_path():
     err = rel_err(to_host(bufs.out), r["out"])
     say("  out rel err", err)
     assert err <= BF16_TOL
+
+
+def test_output_projection_after_the_decode_path():
+    """decode path out (B,S,H,128) -> W_O as a plain projection (16384 -> 7168) with mla_linear,
+    against the oracle's non-absorbed output followed by its output projection."""
+    import torch
+    say("decode -> W_O")
+    B, S, E = 4, 1, 7168
+    w = gen.small_workload(B, S, ragged=(60, 330), dtype="bf16", paged=True)
+    x = gen.generate(w, 91, poison_unused=True)
+    rng = np.random.default_rng(92)
+    w_o = gen.round_to_bf16_bits(rng.standard_normal((128 * 128, E), dtype=np.float32) / np.float32(128.0))
+    p = params_for(x)
+    d = to_device(x)
+    bufs = binding.DecodeBuffers(p, 0)
+    bufs.run(d["q_nope"], d["q_pe"], d["w_uk"], d["w_uv"], d["pool"], d["block_table"], d["seq_lens"])
+    y = torch.full((B * S, E), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ws_bytes = binding.mla_linear_workspace_bytes(B * S, 128 * 128, E)
+    ws = torch.empty(max(ws_bytes, 16) // 4, dtype=torch.float32, device="cuda") if ws_bytes else None
+    binding.mla_linear(bufs.out.reshape(B * S, 128 * 128), _bf16_dev(w_o), y, B * S, 128 * 128, E, ws)
+    torch.cuda.synchronize()
+    r = dec.mla_decode_nonabsorbed(x.f32("q_nope"), x.f32("q_pe"), x.f32("w_uk"), x.f32("w_uv"), x.f32("pool"),
+                                   x.block_table, x.seq_lens, softmax_scale=w.softmax_scale)
+    want = dec.o_proj_reference(r["out"], gen.bf16_bits_to_f32(w_o).reshape(128, 128, E)).reshape(B * S, E)
+    err = rel_err(to_host(y), want)
+    say("  rel err", err)
+    assert err <= BF16_TOL
