@@ -15,11 +15,13 @@ Modules:
   up-projection of every cached token, then per-head attention over them.
 * ``mla_prepare`` — fp64 reference of the step before the path: the fused a-projection (a plain
   matmul), rotary position embedding, and the AppendKV scatter into the paged cache.
+* ``fp8`` — E4M3 rounding and coding, block quantisation (128 x 128 weight blocks, 128-element
+  activation vectors) and the two per-head products in FP8.
 * ``flops`` — the pages' FLOP convention and the three computation orders of
   both absorptions, counted step by step from index extents; byte counts.
 
 Every function is pinned by ``tests/test_oracle.py``, ``tests/test_oracle_prefill.py``,
-``tests/test_oracle_prepare.py`` and ``tests/test_flops.py``
+``tests/test_oracle_prepare.py``, ``tests/test_oracle_fp8.py`` and ``tests/test_flops.py``
 against what the pages print and against closed forms, special cases and
 library routines (see each test's docstring).
 """
