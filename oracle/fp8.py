@@ -10,8 +10,9 @@ as an FP8 block-quantised batched matmul (section "Слой MLA").
 
 Readings (the pages name the scheme, not the format or the rounding; each listed in the design
 notes): FP8 is E4M3 (4 exponent bits, bias 7, 3 mantissa bits, no infinities, largest finite
-448); a block's scale is amax / 448 computed in fp32; a value x is coded as x / scale (an fp32
-division) rounded to the nearest E4M3 value, ties to even; an all-zero block has codes 0.
+448); a block's scale is amax / 448 computed in fp32; a value x is coded as x * (448 / amax)
+(the factor an fp32 division, the product an fp32 multiplication) rounded to the nearest E4M3
+value, ties to even; an all-zero block has codes 0.
 """
 from __future__ import annotations
 
@@ -70,9 +71,9 @@ def quantize(x, axis_blocks):
     red = tuple(2 * i + 1 for i in range(len(shape)))
     amax = np.max(np.abs(xr), axis=red, keepdims=True).astype(np.float32)
     scale = (amax / np.float32(E4M3_MAX)).astype(np.float32)
-    safe = np.where(scale > 0, scale, np.float32(1.0))
-    codes = e4m3_round((xr / safe).astype(np.float32))  # an fp32 division, then E4M3 rounding
-    codes = np.where(scale > 0, codes, np.float32(0.0))
+    factor = (np.float32(E4M3_MAX) / np.where(amax > 0, amax, np.float32(1.0))).astype(np.float32)
+    codes = e4m3_round((xr * factor).astype(np.float32))  # an fp32 product, then E4M3 rounding
+    codes = np.where(amax > 0, codes, np.float32(0.0))
     return codes.reshape(shape), np.squeeze(scale, axis=red).astype(np.float32)
 
 
