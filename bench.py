@@ -504,6 +504,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough to exceed 2x the 256 MB MALL")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fp8-projections", action="store_true",
+                    help="decode: run the two per-head projections FP8 block-quantised (bf16 workloads)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one device copy of this size first (counter calibration under rocprofv3)")
     args = ap.parse_args()
@@ -563,8 +565,20 @@ def main():
         d["bufs"] = binding.DecodeBuffers(params, args.num_splits, device=dev)
         reps.append(d)
 
+    fp8 = bool(args.fp8_projections)
+    if fp8:
+        assert x.is_bf16, "FP8 projections take bf16 activations"
+        for d in reps:  # static weight quantisation, once, outside the timed steps
+            pk_uk = torch.empty(binding.mla_fp8_weight_bytes(), dtype=torch.uint8, device=dev)
+            pk_uv = torch.empty_like(pk_uk)
+            binding.mla_quantize_w_uk_fp8(d["w_uk"], pk_uk, params)
+            binding.mla_quantize_w_uv_fp8(d["w_uv"], pk_uv, params)
+            d["w_uk"], d["w_uv"] = pk_uk, pk_uv
+        torch.cuda.synchronize()
+        costs = accounting.path_costs(x.seq_lens, w.q_len, dt, fp8_projections=True)
+
     def run(d, stream=None):
-        d["bufs"].run(d["q_nope"], d["q_pe"], d["w_uk"], d["w_uv"], d["pool"], d["bt"], d["lens"], stream)
+        d["bufs"].run(d["q_nope"], d["q_pe"], d["w_uk"], d["w_uv"], d["pool"], d["bt"], d["lens"], stream, fp8=fp8)
 
     # graphs: one per replica, captured after an eager warm-up on a side stream
     side = torch.cuda.Stream()
@@ -603,12 +617,12 @@ def main():
         p = d["bufs"]
         e = evs[k]
         e[0].record(stream)
-        binding.mla_absorb_q(d["q_nope"], d["w_uk"], p.q_lat, params)
+        (binding.mla_absorb_q_fp8 if fp8 else binding.mla_absorb_q)(d["q_nope"], d["w_uk"], p.q_lat, params)
         e[1].record(stream)
         binding.mla_decode_attn(p.q_lat, d["q_pe"], d["pool"], d["bt"], d["lens"], p.o_lat, p.lse, p.workspace,
                                 args.num_splits, params)
         e[2].record(stream)
-        binding.mla_out_proj(p.o_lat, d["w_uv"], p.out, params)
+        (binding.mla_out_proj_fp8 if fp8 else binding.mla_out_proj)(p.o_lat, d["w_uv"], p.out, params)
         e[3].record(stream)
     torch.cuda.synchronize()
     call_us = [float(np.mean([evs[k][j].elapsed_time(evs[k][j + 1]) for k in range(n_ev)])) * 1e3 for j in range(3)]
@@ -634,7 +648,8 @@ def main():
         "config": {"workload": args.workload, "batch": w.batch, "q_len": w.q_len,
                    "cache_len": int(x.seq_lens.max()), "heads": w.heads, "kv_lora_rank": w.kv_lora_rank,
                    "rope_dim": w.rope_dim, "head_dim": w.head_dim, "page_size": w.page_size,
-                   "num_splits": splits, "replicas": R, "graph_replay": True},
+                   "num_splits": splits, "replicas": R, "graph_replay": True,
+                   "projections": "fp8 block-quantised" if fp8 else dt},
         "roofline": roofline_entry("mla_decode_attn (split attention + LSE merge)", attn, dt, attn_s, traffic),
         "path_roofline": {"t_roof_us": t_roof * 1e6, "t_step_us": ms_per_step * 1e3,
                           "frac": t_roof / (ms_per_step * 1e-3),

@@ -52,18 +52,20 @@ def visible_pairs(seq_lens: Sequence[int], q_len: int, causal: bool = True) -> i
 
 
 def path_costs(seq_lens: Sequence[int], q_len: int, dtype: str, *, heads: int = 128, d_c: int = 512,
-               d_r: int = 64, d_h: int = 128, page: int = 64, causal: bool = True):
+               d_r: int = 64, d_h: int = 128, page: int = 64, causal: bool = True, fp8_projections: bool = False):
     e = 2 if dtype == "bf16" else 4
+    ew = 1 if fp8_projections else e  # weight element bytes (FP8 codes; scales added below)
+    wsc = heads * (d_c // 128) * 4 if fp8_projections else 0
     B = len(seq_lens)
     T = B * q_len
-    absorb = CallCost("mla_absorb_q", heads * d_c * d_h * e + T * heads * (d_h + d_c) * e,
+    absorb = CallCost("mla_absorb_q", heads * d_c * d_h * ew + wsc + T * heads * (d_h + d_c) * e,
                       2 * T * heads * d_c * d_h)
     cache = sum(int(L) for L in seq_lens) * (d_c + d_r) * e
     tables = sum(-(-int(L) // page) for L in seq_lens) * 4 + B * 4
     attn = CallCost("mla_decode_attn",
                     cache + T * heads * (d_c + d_r) * e + tables + T * heads * (d_c + 1) * 4,
                     2 * heads * (d_c + d_r + d_c) * visible_pairs(seq_lens, q_len, causal))
-    out = CallCost("mla_out_proj", heads * d_c * d_h * e + T * heads * d_c * 4 + T * heads * d_h * e,
+    out = CallCost("mla_out_proj", heads * d_c * d_h * ew + wsc + T * heads * d_c * 4 + T * heads * d_h * e,
                    2 * T * heads * d_c * d_h)
     return [absorb, attn, out]
 

@@ -25,7 +25,8 @@ STATUS = {
 }
 EXPORTS = ("mla_absorb_q", "mla_decode_workspace_bytes", "mla_decode_num_splits", "mla_decode_attn",
            "mla_out_proj", "mla_prefill_kv_bytes", "mla_prefill_kv_up", "mla_prefill_attn",
-           "mla_linear_workspace_bytes", "mla_linear", "mla_rope_append", "mla_status_str")
+           "mla_linear_workspace_bytes", "mla_linear", "mla_rope_append", "mla_fp8_weight_bytes",
+           "mla_quantize_w_uk_fp8", "mla_quantize_w_uv_fp8", "mla_absorb_q_fp8", "mla_out_proj_fp8", "mla_status_str")
 
 
 class MlaLibraryMissing(RuntimeError):
@@ -83,6 +84,14 @@ def load_library(path: Optional[str] = None):
     lib.mla_linear.restype = i32
     lib.mla_rope_append.argtypes = [vp, vp, i32, vp, vp, vp, ctypes.c_float, pp, vp]
     lib.mla_rope_append.restype = i32
+    lib.mla_fp8_weight_bytes.argtypes = []
+    lib.mla_fp8_weight_bytes.restype = sz
+    for name in ("mla_quantize_w_uk_fp8", "mla_quantize_w_uv_fp8"):
+        getattr(lib, name).argtypes = [vp, vp, sz, pp, vp]
+        getattr(lib, name).restype = i32
+    for name in ("mla_absorb_q_fp8", "mla_out_proj_fp8"):
+        getattr(lib, name).argtypes = [vp, vp, vp, pp, vp]
+        getattr(lib, name).restype = i32
     lib.mla_status_str.argtypes = [i32]
     lib.mla_status_str.restype = ctypes.c_char_p
     if path is None:
@@ -208,6 +217,30 @@ def mla_rope_append(q_pe, kv_a, kv_a_stride: int, kv_pool, block_table, seq_lens
                                rope_base, ctypes.byref(params), _stream(stream)), "mla_rope_append")
 
 
+def mla_fp8_weight_bytes() -> int:
+    return int(load_library().mla_fp8_weight_bytes())
+
+
+def mla_quantize_w_uk_fp8(w_uk, packed, params: mla_params, stream=None, packed_bytes: Optional[int] = None) -> None:
+    _check(load_library().mla_quantize_w_uk_fp8(_ptr(w_uk), _ptr(packed), _nbytes(packed, packed_bytes),
+                                                ctypes.byref(params), _stream(stream)), "mla_quantize_w_uk_fp8")
+
+
+def mla_quantize_w_uv_fp8(w_uv, packed, params: mla_params, stream=None, packed_bytes: Optional[int] = None) -> None:
+    _check(load_library().mla_quantize_w_uv_fp8(_ptr(w_uv), _ptr(packed), _nbytes(packed, packed_bytes),
+                                                ctypes.byref(params), _stream(stream)), "mla_quantize_w_uv_fp8")
+
+
+def mla_absorb_q_fp8(q_nope, w_uk_fp8, q_lat, params: mla_params, stream=None) -> None:
+    _check(load_library().mla_absorb_q_fp8(_ptr(q_nope), _ptr(w_uk_fp8), _ptr(q_lat), ctypes.byref(params),
+                                           _stream(stream)), "mla_absorb_q_fp8")
+
+
+def mla_out_proj_fp8(o_lat, w_uv_fp8, out, params: mla_params, stream=None) -> None:
+    _check(load_library().mla_out_proj_fp8(_ptr(o_lat), _ptr(w_uv_fp8), _ptr(out), ctypes.byref(params),
+                                           _stream(stream)), "mla_out_proj_fp8")
+
+
 class DecodeBuffers:
     """Device tensors for one decode step: intermediates, outputs and workspace (torch-allocated).
 
@@ -228,10 +261,12 @@ class DecodeBuffers:
         ws = mla_decode_workspace_bytes(params, num_splits)
         self.workspace = torch.empty(max(ws, 16) // 4 + 4, dtype=torch.float32, device=device) if ws else None
 
-    def run(self, q_nope, q_pe, w_uk, w_uv, kv_pool, block_table, seq_lens, stream=None):
+    def run(self, q_nope, q_pe, w_uk, w_uv, kv_pool, block_table, seq_lens, stream=None, fp8: bool = False):
+        """The three calls; with ``fp8`` the weights are packed FP8 weights and the two projections
+        run block-quantised (mla_absorb_q_fp8 / mla_out_proj_fp8)."""
         p = self.params
-        mla_absorb_q(q_nope, w_uk, self.q_lat, p, stream)
+        (mla_absorb_q_fp8 if fp8 else mla_absorb_q)(q_nope, w_uk, self.q_lat, p, stream)
         mla_decode_attn(self.q_lat, q_pe, kv_pool, block_table, seq_lens, self.o_lat, self.lse, self.workspace,
                         self.num_splits, p, stream)
-        mla_out_proj(self.o_lat, w_uv, self.out, p, stream)
+        (mla_out_proj_fp8 if fp8 else mla_out_proj)(self.o_lat, w_uv, self.out, p, stream)
         return self.out

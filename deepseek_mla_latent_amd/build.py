@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_NAME = "libmla_latent.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["mla_api.cpp", "decode_attn.hip", "projections.hip", "prefill.hip", "prepare.hip"]
+SOURCES = ["mla_api.cpp", "decode_attn.hip", "projections.hip", "prefill.hip", "prepare.hip", "fp8.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # gfx950 only; packed-fp32 VALU ops are disabled (plain fp32 code is scalar fp32).  The attention

@@ -1,0 +1,328 @@
+// FP8 block-quantised per-head products (k_b_proj / v_b_proj), gfx950.
+//
+// The Perplexity post ("Lower latency and higher throughput with multi-node DeepSeek deployment")
+// runs the W_UK and W_UV products as an FP8 block-quantised batched matmul (section "Слой MLA") with
+// the scheme of section "Квантование": weights quantised statically, one scale per 128 x 128 block;
+// activations quantised on the fly, one scale per 128-element vector along the reduction
+// dimension.  Format E4M3 (bias 7, 3 mantissa bits, no infinities, largest finite 448); a block's
+// scale is amax / 448 in fp32; a value is coded as x * (448 / amax) (one fp32 division per block,
+// fp32 products) rounded to the nearest E4M3 value, ties to even.
+//
+//   quantize_weight_fp8_kernel  W (H, 512, 128) bf16 -> codes + scales (H, 4); W_UV's codes are
+//                               stored transposed, (H, 128 v, 512 c), so both products read
+//                               8 consecutive k per lane from one row.
+//   absorb_q_fp8_kernel         q_lat = W_UK q_nope per head: K = 128 (one block per token/head)
+//   out_proj_fp8_kernel         out = W_UV^T o_lat per head: K = 512 (four blocks per token/head)
+// One workgroup per head.  Per block of 32 tokens the workgroup first codes the activations once,
+// cooperatively, into LDS (codes + per-vector scales); then each wave runs its 32x32x16 FP8
+// MFMAs with fp32 accumulation, the weight codes (loaded once per workgroup) as the A operand and
+// the activation codes from LDS as the B operand.  Each block's sum is scaled by its activation
+// scale (per token: a lane holds one token) times its weight scale.  Lane halves split each
+// 128-long k block: half hf holds k in [64 hf, 64 hf + 64), 8 per MFMA step, the same order for
+// the A and B operands.
+#include "common.h"
+#include "kernels.h"
+
+namespace mla {
+
+namespace {
+
+constexpr float kE4M3Max = 448.0f;
+
+// E4M3 code of v (|v| <= about 464): the nearest E4M3 value, ties to even, 448 at most.
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 31) << 7;
+  const float a = fabsf(v);
+  uint32_t E, M;
+  if (a >= 0.015625f) {  // normal: spacing 2^(e-3)
+    int e = (int)((__float_as_uint(a) >> 23) & 0xff) - 127;
+    uint32_t m = (uint32_t)rintf(ldexpf(a, 3 - e));  // 8 .. 16
+    if (m == 16) {
+      m = 8;
+      ++e;
+    }
+    E = (uint32_t)(e + 7);
+    M = m - 8;
+    if (E > 15 || (E == 15 && M == 7)) {  // above 448: saturate
+      E = 15;
+      M = 6;
+    }
+  } else {  // subnormal: spacing 2^-9
+    const uint32_t m = (uint32_t)rintf(a * 512.0f);  // 0 .. 8
+    E = m == 8 ? 1u : 0u;
+    M = m == 8 ? 0u : m;
+  }
+  return sign | (E << 3) | M;
+}
+
+// N values -> N codes (N/4 words, 4 codes per word, little-endian) of x * factor
+template <int N>
+__device__ __forceinline__ void code_n(const float (&x)[N], float factor, uint32_t (&w)[N / 4]) {
+#pragma unroll
+  for (int i = 0; i < N / 4; ++i) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) word |= e4m3_code(x[4 * i + j] * factor) << (8 * j);
+    w[i] = word;
+  }
+}
+__device__ __forceinline__ float code_factor(float amax) { return amax > 0.f ? kE4M3Max / amax : 0.f; }
+
+__device__ __forceinline__ f32x16 mfma_fp8(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, const f32x16& c) {
+  const long a = (long)(((uint64_t)a1 << 32) | a0), b = (long)(((uint64_t)b1 << 32) | b0);
+  return __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a, b, c, 0, 0, 0);
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------------------------------------
+// One workgroup (256 threads) per (head, 128-row block of the 512 latent rows): thread t holds
+// row r = t / 2, columns 64 (t % 2) .. +63 of the block.  amax over the block, then codes.
+__global__ __launch_bounds__(256) void quantize_weight_fp8_kernel(const uint16_t* __restrict__ w,
+                                                                  uint8_t* __restrict__ codes,
+                                                                  float* __restrict__ scales, int transpose) {
+  __shared__ float red[4];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[128 * 128];
+  const int h = blockIdx.y, cb = blockIdx.x, t = threadIdx.x;
+  const int r = t >> 1, c0 = 64 * (t & 1);
+  const uint16_t* src = w + ((size_t)h * kDc + cb * 128 + r) * kDh + c0;
+  float x[64];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const u32x4 v = *(const u32x4*)(src + u * 8);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[8 * u + 2 * j] = __uint_as_float(v[j] << 16);
+      x[8 * u + 2 * j + 1] = __uint_as_float(v[j] & 0xffff0000u);
+    }
+  }
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) m = fmaxf(m, fabsf(x[i]));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((t & 63) == 0) red[t >> 6] = m;
+  __syncthreads();
+  const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float scale = amax / kE4M3Max;
+  uint32_t wd[16];
+  code_n<64>(x, code_factor(amax), wd);
+  if (t == 0) scales[h * 4 + cb] = scale;
+  if (!transpose) {  // codes (H, 512, 128), row-major like W
+    uint8_t* dst = codes + ((size_t)h * kDc + cb * 128 + r) * kDh + c0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) *(u32x4*)(dst + 16 * u) = u32x4{wd[4 * u], wd[4 * u + 1], wd[4 * u + 2], wd[4 * u + 3]};
+    return;
+  }
+  // transposed: codes (H, 128, 512): row v, columns c; through LDS
+#pragma unroll
+  for (int u = 0; u < 16; ++u) *(uint32_t*)(tile + r * 128 + c0 + 4 * u) = wd[u];
+  __syncthreads();
+  const int v = t >> 1, k0 = 64 * (t & 1);  // this thread writes row v, latent rows k0 .. +63 of the block
+  uint32_t out[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) word |= (uint32_t)tile[(k0 + 4 * i + j) * 128 + v] << (8 * j);
+    out[i] = word;
+  }
+  uint8_t* dst = codes + ((size_t)h * kDh + v) * kDc + cb * 128 + k0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) *(u32x4*)(dst + 16 * u) = u32x4{out[4 * u], out[4 * u + 1], out[4 * u + 2], out[4 * u + 3]};
+}
+
+// ------------------------------------------------------------------------------------------------
+// Activation coding into LDS: token j (0..31) of the block, 128-long vector v of that token: the
+// 8 threads 8 (4 j + v') .. +7 (v' = vector index within the pass) take 16 values each; amax
+// over the 8 through lane shuffles.  Codes row j holds the token's vectors back to back; 16-byte
+// unit u of row j sits at u ^ (j & 7) within each 128-byte vector, so the 16 tokens a B-operand
+// read spans hit distinct units.
+template <int V>  // vectors (of 128) per token
+struct ActStage {
+  uint8_t codes[32 * V * 128];
+  float scale[32 * V];
+};
+
+__device__ __forceinline__ int act_off(int j, int vec, int V, int byte) {  // byte within the 128-byte vector
+  return (j * V + vec) * 128 + ((((byte >> 4) ^ (j & 7))) << 4) + (byte & 15);
+}
+
+// codes the token block's activations (fp32 or bf16 source); rows past `tokens` code token tokens-1
+template <int V, bool BF16>
+__device__ __forceinline__ void code_tokens(const void* src, size_t token_stride, int n0, int tokens, int tid,
+                                            ActStage<V>& st) {
+#pragma unroll
+  for (int pass = 0; pass < V; ++pass) {
+    const int g = pass * 256 + tid;       // 0 .. 256 V - 1
+    const int vecid = g >> 3, part = g & 7;  // vecid = j * V + vec
+    const int j = vecid / V, vec = vecid % V;
+    const int n = min(n0 + j, tokens - 1);
+    float x[16];
+    if (BF16) {
+      const uint16_t* p = (const uint16_t*)src + n * token_stride + vec * 128 + part * 16;
+      const u32x4 a = *(const u32x4*)p, b = *(const u32x4*)(p + 8);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[2 * k] = __uint_as_float(a[k] << 16), x[2 * k + 1] = __uint_as_float(a[k] & 0xffff0000u);
+        x[8 + 2 * k] = __uint_as_float(b[k] << 16), x[8 + 2 * k + 1] = __uint_as_float(b[k] & 0xffff0000u);
+      }
+    } else {
+      const float* p = (const float*)src + n * token_stride + vec * 128 + part * 16;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const f32x4 q = *(const f32x4*)(p + 4 * k);
+        x[4 * k] = q[0], x[4 * k + 1] = q[1], x[4 * k + 2] = q[2], x[4 * k + 3] = q[3];
+      }
+    }
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(x[i]));
+    m = fmaxf(m, __shfl_xor(m, 1));
+    m = fmaxf(m, __shfl_xor(m, 2));
+    m = fmaxf(m, __shfl_xor(m, 4));
+    uint32_t w[4];
+    code_n<16>(x, code_factor(m), w);
+    *(u32x4*)&st.codes[act_off(j, vec, V, part * 16)] = u32x4{w[0], w[1], w[2], w[3]};
+    if (part == 0) st.scale[vecid] = m / kE4M3Max;
+  }
+}
+
+// B operand of k-step ks (vector vec) for this lane's token l32 and k half hf: 8 bytes
+__device__ __forceinline__ uint64_t act_b(const uint8_t* codes, int l32, int hf, int vec, int V, int ks) {
+  return *(const uint64_t*)&codes[act_off(l32, vec, V, 64 * hf + 8 * ks)];
+}
+
+// absorb: one workgroup per head, 4 waves; wave w owns latent rows c = 128 w + 32 mb + l32
+// (mb = 0..3).  A = W_UK codes of those rows (the lane's k half: 64 bytes per row, loaded once).
+__global__ __launch_bounds__(256) void absorb_q_fp8_kernel(const uint16_t* __restrict__ q_nope,
+                                                           const uint8_t* __restrict__ codes,
+                                                           const float* __restrict__ scales,
+                                                           uint16_t* __restrict__ q_lat, int tokens) {
+  __shared__ __attribute__((aligned(16))) ActStage<1> st;
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  uint32_t aw[4][16];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    const uint8_t* src = codes + ((size_t)h * kDc + wave * 128 + mb * 32 + l32) * kDh + 64 * hf;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const u32x4 v = *(const u32x4*)(src + 16 * u);
+      aw[mb][4 * u] = v[0], aw[mb][4 * u + 1] = v[1], aw[mb][4 * u + 2] = v[2], aw[mb][4 * u + 3] = v[3];
+    }
+  }
+  const float sw = scales[h * 4 + wave];  // latent block of this wave's rows
+  for (int n0 = 0; n0 < tokens; n0 += 32) {
+    __syncthreads();  // the previous block's codes are consumed
+    code_tokens<1, true>(q_nope + (size_t)h * kDh, (size_t)kHeads * kDh, n0, tokens, tid, st);
+    __syncthreads();
+    uint64_t bq[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) bq[ks] = act_b(st.codes, l32, hf, 0, 1, ks);
+    const int n = n0 + l32;
+    const float s = st.scale[l32] * sw;  // this lane's token
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      f32x16 acc = {};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        acc = mfma_fp8(aw[mb][2 * ks], aw[mb][2 * ks + 1], (uint32_t)bq[ks], (uint32_t)(bq[ks] >> 32), acc);
+      if (n < tokens) {
+        uint16_t* dst = q_lat + ((size_t)n * kHeads + h) * kDc + wave * 128 + mb * 32 + 4 * hf;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          u32x2 v;
+          v[0] = pack_bf16x2(acc[4 * g] * s, acc[4 * g + 1] * s);
+          v[1] = pack_bf16x2(acc[4 * g + 2] * s, acc[4 * g + 3] * s);
+          *(u32x2*)(dst + 8 * g) = v;
+        }
+      }
+    }
+  }
+}
+
+// out-proj: one workgroup per head, 4 waves; wave w owns value rows v = 32 w + l32.  A = W_UV^T
+// codes of row v (the lane's k half of each of the 4 latent blocks: 4 x 64 bytes, loaded once).
+// Each latent block's MFMA sum is scaled by s_o[n][kb] * s_w[h][kb] and added in fp32.
+__global__ __launch_bounds__(256) void out_proj_fp8_kernel(const float* __restrict__ o_lat,
+                                                           const uint8_t* __restrict__ codes,
+                                                           const float* __restrict__ scales,
+                                                           uint16_t* __restrict__ out, int tokens) {
+  __shared__ __attribute__((aligned(16))) ActStage<4> st;
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int v = wave * 32 + l32;
+  uint32_t aw[4][16];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const uint8_t* src = codes + ((size_t)h * kDh + v) * kDc + kb * 128 + 64 * hf;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const u32x4 q = *(const u32x4*)(src + 16 * u);
+      aw[kb][4 * u] = q[0], aw[kb][4 * u + 1] = q[1], aw[kb][4 * u + 2] = q[2], aw[kb][4 * u + 3] = q[3];
+    }
+  }
+  float sw[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) sw[kb] = scales[h * 4 + kb];
+  for (int n0 = 0; n0 < tokens; n0 += 32) {
+    __syncthreads();
+    code_tokens<4, false>(o_lat + (size_t)h * kDc, (size_t)kHeads * kDc, n0, tokens, tid, st);
+    __syncthreads();
+    const int n = n0 + l32;
+    f32x16 acc = {};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      f32x16 part = {};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const uint64_t b = act_b(st.codes, l32, hf, kb, 4, ks);
+        part = mfma_fp8(aw[kb][2 * ks], aw[kb][2 * ks + 1], (uint32_t)b, (uint32_t)(b >> 32), part);
+      }
+      const float s = st.scale[l32 * 4 + kb] * sw[kb];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[e] += part[e] * s;
+    }
+    if (n < tokens) {
+      uint16_t* dst = out + ((size_t)n * kHeads + h) * kDh + wave * 32 + 4 * hf;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        u32x2 q;
+        q[0] = pack_bf16x2(acc[4 * g], acc[4 * g + 1]);
+        q[1] = pack_bf16x2(acc[4 * g + 2], acc[4 * g + 3]);
+        *(u32x2*)(dst + 8 * g) = q;
+      }
+    }
+  }
+}
+
+hipError_t launch_quantize_weight_fp8(const void* w, void* packed, bool transpose, hipStream_t stream) {
+  uint8_t* codes = (uint8_t*)packed;
+  float* scales = (float*)(codes + (size_t)kHeads * kDc * kDh);
+  hipLaunchKernelGGL(quantize_weight_fp8_kernel, dim3(4, kHeads), dim3(256), 0, stream, (const uint16_t*)w, codes,
+                     scales, transpose ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_absorb_q_fp8(const void* q_nope, const void* packed, void* q_lat, int tokens, hipStream_t stream) {
+  if (tokens == 0) return hipSuccess;
+  const uint8_t* codes = (const uint8_t*)packed;
+  const float* scales = (const float*)(codes + (size_t)kHeads * kDc * kDh);
+  hipLaunchKernelGGL(absorb_q_fp8_kernel, dim3(kHeads), dim3(256), 0, stream, (const uint16_t*)q_nope, codes,
+                     scales, (uint16_t*)q_lat, tokens);
+  return hipGetLastError();
+}
+
+hipError_t launch_out_proj_fp8(const float* o_lat, const void* packed, void* out, int tokens, hipStream_t stream) {
+  if (tokens == 0) return hipSuccess;
+  const uint8_t* codes = (const uint8_t*)packed;
+  const float* scales = (const float*)(codes + (size_t)kHeads * kDc * kDh);
+  hipLaunchKernelGGL(out_proj_fp8_kernel, dim3(kHeads), dim3(256), 0, stream, o_lat, codes, scales, (uint16_t*)out,
+                     tokens);
+  return hipGetLastError();
+}
+
+}  // namespace mla

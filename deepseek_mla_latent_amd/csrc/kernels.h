@@ -70,6 +70,11 @@ hipError_t launch_prefill_attn(const PrefillArgs& a, hipStream_t stream);
 int linear_splits(int M, int K, int N, int cus);
 hipError_t launch_linear(const void* x, const void* w, void* y, float* partial, int M, int K, int N, int splits,
                          hipStream_t stream);
+// FP8 block-quantised per-head products.  Packed weight = E4M3 codes (H x 512 x 128 bytes; W_UV's
+// stored transposed as (H, 128, 512)) followed by H x 4 fp32 scales (one per 128 x 128 block).
+hipError_t launch_quantize_weight_fp8(const void* w, void* packed, bool transpose, hipStream_t stream);
+hipError_t launch_absorb_q_fp8(const void* q_nope, const void* packed, void* q_lat, int tokens, hipStream_t stream);
+hipError_t launch_out_proj_fp8(const float* o_lat, const void* packed, void* out, int tokens, hipStream_t stream);
 // rotary embedding of q_pe (B,S,H,64, in place) and of the k_pe part of kv_a rows (stride
 // kv_stride elements, [c_KV 512 | k_pe 64] at the row start), and AppendKV of [c_KV | k_pe] into
 // the paged pool at positions seq_lens[b] - S + i.

@@ -322,4 +322,55 @@ mla_status mla_rope_append(void* q_pe, const void* kv_a, int32_t kv_a_stride, vo
   return MLA_OK;
 }
 
+size_t mla_fp8_weight_bytes(void) {
+  return (size_t)mla::kHeads * mla::kDc * mla::kDh + (size_t)mla::kHeads * 4 * sizeof(float);
+}
+
+static mla_status quantize_fp8(const void* w, void* packed, size_t packed_bytes, const mla_params* p, bool transpose,
+                               void* stream) {
+  mla_status st = check_params(p);
+  if (st != MLA_OK) return st;
+  if (p->dtype != MLA_BF16) return MLA_ERR_DTYPE;
+  if (!w || !packed) return MLA_ERR_NULL;
+  if (!aligned16(w) || !aligned16(packed)) return MLA_ERR_ALIGN;
+  if (packed_bytes < mla_fp8_weight_bytes()) return MLA_ERR_WORKSPACE;
+  if (mla::launch_quantize_weight_fp8(w, packed, transpose, (hipStream_t)stream) != hipSuccess) return MLA_ERR_LAUNCH;
+  return MLA_OK;
+}
+
+mla_status mla_quantize_w_uk_fp8(const void* w_uk, void* packed, size_t packed_bytes, const mla_params* p,
+                                 void* stream) {
+  return quantize_fp8(w_uk, packed, packed_bytes, p, false, stream);
+}
+
+mla_status mla_quantize_w_uv_fp8(const void* w_uv, void* packed, size_t packed_bytes, const mla_params* p,
+                                 void* stream) {
+  return quantize_fp8(w_uv, packed, packed_bytes, p, true, stream);
+}
+
+mla_status mla_absorb_q_fp8(const void* q_nope, const void* w_uk_fp8, void* q_lat, const mla_params* p,
+                            void* stream) {
+  mla_status st = check_params(p);
+  if (st != MLA_OK) return st;
+  if (p->dtype != MLA_BF16) return MLA_ERR_DTYPE;
+  if (tokens_of(p) == 0) return MLA_OK;
+  if (!q_nope || !w_uk_fp8 || !q_lat) return MLA_ERR_NULL;
+  if (!aligned16(q_nope) || !aligned16(w_uk_fp8) || !aligned16(q_lat)) return MLA_ERR_ALIGN;
+  if (mla::launch_absorb_q_fp8(q_nope, w_uk_fp8, q_lat, (int)tokens_of(p), (hipStream_t)stream) != hipSuccess)
+    return MLA_ERR_LAUNCH;
+  return MLA_OK;
+}
+
+mla_status mla_out_proj_fp8(const float* o_lat, const void* w_uv_fp8, void* out, const mla_params* p, void* stream) {
+  mla_status st = check_params(p);
+  if (st != MLA_OK) return st;
+  if (p->dtype != MLA_BF16) return MLA_ERR_DTYPE;
+  if (tokens_of(p) == 0) return MLA_OK;
+  if (!o_lat || !w_uv_fp8 || !out) return MLA_ERR_NULL;
+  if (!aligned16(o_lat) || !aligned16(w_uv_fp8) || !aligned16(out)) return MLA_ERR_ALIGN;
+  if (mla::launch_out_proj_fp8(o_lat, w_uv_fp8, out, (int)tokens_of(p), (hipStream_t)stream) != hipSuccess)
+    return MLA_ERR_LAUNCH;
+  return MLA_OK;
+}
+
 }  // extern "C"

@@ -241,6 +241,45 @@ mla_status mla_rope_append(void* q_pe, const void* kv_a, int32_t kv_a_stride, vo
                            const int32_t* block_table, const int32_t* seq_lens, float rope_base,
                            const mla_params* p, void* stream);
 
+/*
+ * ---- FP8 block-quantised per-head products ----------------------------------------------------
+ * The k_b_proj / v_b_proj products (W_UK, W_UV) as an FP8 block-quantised batched matmul
+ * (Perplexity post, section "Слой MLA"), with the scheme of section "Квантование": weights
+ * quantised statically, one scale per 128 x 128 block; activations on the fly, one scale per
+ * 128-element vector along the reduction dimension. Format E4M3 (bias 7, largest finite 448;
+ * the pages name no format). A block's scale is amax / 448 in fp32; a value is coded as
+ * x / scale (fp32 division) rounded to the nearest E4M3 value, ties to even. An all-zero block
+ * has codes 0. The products accumulate in fp32 per block, then scale. bf16 activations only.
+ *
+ * Packed weight (mla_fp8_weight_bytes() bytes, 16-byte aligned, owned by the caller): E4M3 codes,
+ * H x 512 x 128 bytes (W_UK: (H, 512 c, 128 d) as the weight; W_UV: transposed, (H, 128 v, 512 c)),
+ * then H x 4 fp32 scales (head h, latent block c / 128).
+ */
+size_t mla_fp8_weight_bytes(void);
+
+/* Static quantisation of W_UK (H,512,128) bf16 / W_UV (H,512,128) bf16 into a packed weight. */
+mla_status mla_quantize_w_uk_fp8(const void* w_uk, void* packed, size_t packed_bytes,
+                                 const mla_params* p, void* stream);
+mla_status mla_quantize_w_uv_fp8(const void* w_uv, void* packed, size_t packed_bytes,
+                                 const mla_params* p, void* stream);
+
+/*
+ * As mla_absorb_q, in FP8: q_nope (B,S,H,128) bf16 quantised per (token, head) vector;
+ * q_lat (B,S,H,512) bf16 = s_q * s_w[h][c/128] * sum_d code(q) code(W).
+ * Cites: Perplexity post, sections "Слой MLA" (FP8 block-quantised BMM for k_b_proj) and
+ * "Квантование" (128-element activation vectors, 128 x 128 weight blocks).
+ */
+mla_status mla_absorb_q_fp8(const void* q_nope, const void* w_uk_fp8, void* q_lat,
+                            const mla_params* p, void* stream);
+
+/*
+ * As mla_out_proj, in FP8: o_lat (B,S,H,512) fp32 quantised per 128-long latent block of each
+ * (token, head); out (B,S,H,128) bf16 = sum over the four blocks of s_o * s_w * sum code*code.
+ * Cites: as mla_absorb_q_fp8 (v_b_proj).
+ */
+mla_status mla_out_proj_fp8(const float* o_lat, const void* w_uv_fp8, void* out, const mla_params* p,
+                            void* stream);
+
 /* Static string for a status code (never NULL). */
 const char* mla_status_str(mla_status s);
 

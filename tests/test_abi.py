@@ -165,3 +165,18 @@ def test_rope_append_errors():
     assert ra(P(), kv=MISALIGNED) == -4
     assert ra(P(batch=0)) == 0
     assert ra(P(num_heads=64)) == -6
+
+
+def test_fp8_errors():
+    assert lib.mla_fp8_weight_bytes() == 128 * 512 * 128 + 128 * 4 * 4
+    nb = lib.mla_fp8_weight_bytes()
+    assert lib.mla_quantize_w_uk_fp8(FAKE, FAKE, nb, ctypes.byref(P(dtype=binding.MLA_F32)), None) == -3
+    assert lib.mla_quantize_w_uk_fp8(FAKE, FAKE, nb - 1, ctypes.byref(P()), None) == -5
+    assert lib.mla_quantize_w_uv_fp8(None, FAKE, nb, ctypes.byref(P()), None) == -1
+    assert lib.mla_quantize_w_uv_fp8(FAKE, MISALIGNED, nb, ctypes.byref(P()), None) == -4
+    for fn in (lib.mla_absorb_q_fp8, lib.mla_out_proj_fp8):
+        assert fn(FAKE, FAKE, FAKE, ctypes.byref(P(dtype=binding.MLA_F32)), None) == -3
+        assert fn(None, FAKE, FAKE, ctypes.byref(P()), None) == -1
+        assert fn(FAKE, FAKE, MISALIGNED, ctypes.byref(P()), None) == -4
+        assert fn(FAKE, FAKE, FAKE, ctypes.byref(P(head_dim=64)), None) == -6
+        assert fn(FAKE, FAKE, FAKE, ctypes.byref(P(batch=0)), None) == 0
