@@ -13,10 +13,11 @@
 //                               8 consecutive k per lane from one row.
 //   absorb_q_fp8_kernel         q_lat = W_UK q_nope per head: K = 128 (one block per token/head)
 //   out_proj_fp8_kernel         out = W_UV^T o_lat per head: K = 512 (four blocks per token/head)
-// One workgroup per head.  Per block of 32 tokens the workgroup first codes the activations once,
-// cooperatively, into LDS (codes + per-vector scales); then each wave runs its 32x32x16 FP8
-// MFMAs with fp32 accumulation, the weight codes (loaded once per workgroup) as the A operand and
-// the activation codes from LDS as the B operand.  Each block's sum is scaled by its activation
+// One workgroup (8 waves) per head.  Per block of 32 tokens the workgroup first codes the
+// activations once, cooperatively, into LDS (codes + per-vector scales); then each wave runs its
+// 32x32x16 FP8 MFMAs with fp32 accumulation, the weight codes (loaded once per workgroup) as the
+// A operand and the activation codes from LDS as the B operand; results go out through an LDS
+// tile as whole rows.  Each block's sum is scaled by its activation
 // scale (per token: a lane holds one token) times its weight scale.  Lane halves split each
 // 128-long k block: half hf holds k in [64 hf, 64 hf + 64), 8 per MFMA step, the same order for
 // the A and B operands.
@@ -133,13 +134,14 @@ __global__ __launch_bounds__(256) void quantize_weight_fp8_kernel(const uint16_t
 }
 
 // ------------------------------------------------------------------------------------------------
-// Activation coding into LDS: token j (0..31) of the block, 128-long vector v of that token: the
-// 8 threads 8 (4 j + v') .. +7 (v' = vector index within the pass) take 16 values each; amax
-// over the 8 through lane shuffles.  Codes row j holds the token's vectors back to back; 16-byte
-// unit u of row j sits at u ^ (j & 7) within each 128-byte vector, so the 16 tokens a B-operand
-// read spans hit distinct units.
+// Activation coding into LDS.  A block of 32 tokens, V vectors of 128 per token: groups of P
+// consecutive values, 128 / P groups per vector; thread tid takes groups tid, tid + NT, ...
+// (NT = workgroup size).  A vector's groups sit in consecutive lanes, so its amax is a few lane
+// shuffles.  All of a thread's loads are issued before any coding.  Codes row j holds token j's
+// vectors back to back; 16-byte unit u of a 128-byte vector of row j sits at u ^ (j & 7), so the
+// 16 tokens a B-operand read spans hit distinct units.  Rows past `tokens` code the last token.
 template <int V>  // vectors (of 128) per token
-struct ActStage {
+struct ActCodes {
   uint8_t codes[32 * V * 128];
   float scale[32 * V];
 };
@@ -148,42 +150,52 @@ __device__ __forceinline__ int act_off(int j, int vec, int V, int byte) {  // by
   return (j * V + vec) * 128 + ((((byte >> 4) ^ (j & 7))) << 4) + (byte & 15);
 }
 
-// codes the token block's activations (fp32 or bf16 source); rows past `tokens` code token tokens-1
-template <int V, bool BF16>
+template <int V, int P, int NT, bool BF16>
 __device__ __forceinline__ void code_tokens(const void* src, size_t token_stride, int n0, int tokens, int tid,
-                                            ActStage<V>& st) {
+                                            ActCodes<V>& st) {
+  constexpr int kParts = 128 / P, kPasses = 32 * V * kParts / NT;
+  static_assert(kPasses * NT == 32 * V * kParts, "whole passes");
+  float x[kPasses][P];
 #pragma unroll
-  for (int pass = 0; pass < V; ++pass) {
-    const int g = pass * 256 + tid;       // 0 .. 256 V - 1
-    const int vecid = g >> 3, part = g & 7;  // vecid = j * V + vec
+  for (int pass = 0; pass < kPasses; ++pass) {
+    const int g = pass * NT + tid, vecid = g / kParts, part = g % kParts;
     const int j = vecid / V, vec = vecid % V;
     const int n = min(n0 + j, tokens - 1);
-    float x[16];
     if (BF16) {
-      const uint16_t* p = (const uint16_t*)src + n * token_stride + vec * 128 + part * 16;
-      const u32x4 a = *(const u32x4*)p, b = *(const u32x4*)(p + 8);
+      const uint16_t* p = (const uint16_t*)src + n * token_stride + vec * 128 + part * P;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        x[2 * k] = __uint_as_float(a[k] << 16), x[2 * k + 1] = __uint_as_float(a[k] & 0xffff0000u);
-        x[8 + 2 * k] = __uint_as_float(b[k] << 16), x[8 + 2 * k + 1] = __uint_as_float(b[k] & 0xffff0000u);
+      for (int u = 0; u < P / 8; ++u) {
+        const u32x4 a = *(const u32x4*)(p + 8 * u);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          x[pass][8 * u + 2 * k] = __uint_as_float(a[k] << 16);
+          x[pass][8 * u + 2 * k + 1] = __uint_as_float(a[k] & 0xffff0000u);
+        }
       }
     } else {
-      const float* p = (const float*)src + n * token_stride + vec * 128 + part * 16;
+      const float* p = (const float*)src + n * token_stride + vec * 128 + part * P;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const f32x4 q = *(const f32x4*)(p + 4 * k);
-        x[4 * k] = q[0], x[4 * k + 1] = q[1], x[4 * k + 2] = q[2], x[4 * k + 3] = q[3];
+      for (int u = 0; u < P / 4; ++u) {
+        const f32x4 q = *(const f32x4*)(p + 4 * u);
+        x[pass][4 * u] = q[0], x[pass][4 * u + 1] = q[1], x[pass][4 * u + 2] = q[2], x[pass][4 * u + 3] = q[3];
       }
     }
+  }
+#pragma unroll
+  for (int pass = 0; pass < kPasses; ++pass) {
+    const int g = pass * NT + tid, vecid = g / kParts, part = g % kParts;
+    const int j = vecid / V, vec = vecid % V;
     float m = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(x[i]));
-    m = fmaxf(m, __shfl_xor(m, 1));
-    m = fmaxf(m, __shfl_xor(m, 2));
-    m = fmaxf(m, __shfl_xor(m, 4));
-    uint32_t w[4];
-    code_n<16>(x, code_factor(m), w);
-    *(u32x4*)&st.codes[act_off(j, vec, V, part * 16)] = u32x4{w[0], w[1], w[2], w[3]};
+    for (int i = 0; i < P; ++i) m = fmaxf(m, fabsf(x[pass][i]));
+#pragma unroll
+    for (int off = 1; off < kParts; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+    uint32_t w[P / 4];
+    code_n<P>(x[pass], code_factor(m), w);
+    if (P == 16)
+      *(u32x4*)&st.codes[act_off(j, vec, V, part * P)] = u32x4{w[0], w[1], w[2], w[3]};
+    else
+      *(u32x2*)&st.codes[act_off(j, vec, V, part * P)] = u32x2{w[0], w[1]};
     if (part == 0) st.scale[vecid] = m / kE4M3Max;
   }
 }
@@ -193,109 +205,142 @@ __device__ __forceinline__ uint64_t act_b(const uint8_t* codes, int l32, int hf,
   return *(const uint64_t*)&codes[act_off(l32, vec, V, 64 * hf + 8 * ks)];
 }
 
-// absorb: one workgroup per head, 4 waves; wave w owns latent rows c = 128 w + 32 mb + l32
-// (mb = 0..3).  A = W_UK codes of those rows (the lane's k half: 64 bytes per row, loaded once).
-__global__ __launch_bounds__(256) void absorb_q_fp8_kernel(const uint16_t* __restrict__ q_nope,
+// 8 bytes of output for token row `row` at byte `byte` of a staged tile of 16-byte units with
+// `units` units per row; unit u of row r sits at u ^ (r % units), so the 32 rows one
+// MFMA-fragment store spans hit distinct units.
+__device__ __forceinline__ int out_off(int row, int byte, int units) {
+  return row * units * 16 + ((((byte >> 4) ^ (row & (units - 1)))) << 4) + (byte & 15);
+}
+
+// fragment (32 x 32 D, this lane's column = token l32) -> bf16 into the staged tile at rows' byte
+// offset `byte0` (+ 16 g + 8 hf per 4-row group g), times `s`
+__device__ __forceinline__ void stage_fragment(uint8_t* tile, int units, int l32, int hf, int byte0,
+                                               const f32x16& acc, float s) {
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    u32x2 v;
+    v[0] = pack_bf16x2(acc[4 * g] * s, acc[4 * g + 1] * s);
+    v[1] = pack_bf16x2(acc[4 * g + 2] * s, acc[4 * g + 3] * s);
+    *(u32x2*)&tile[out_off(l32, byte0 + 16 * g + 8 * hf, units)] = v;
+  }
+}
+
+// staged tile (32 token rows of `units` 16-byte units) -> global rows dst + n * stride (bytes)
+template <int NT>
+__device__ __forceinline__ void store_tile(const uint8_t* tile, int units, uint8_t* dst, size_t stride, int n0,
+                                           int tokens, int tid) {
+#pragma unroll
+  for (int k = tid; k < 32 * units; k += NT) {
+    const int row = k / units, u = k % units;
+    if (n0 + row < tokens)
+      *(u32x4*)(dst + (size_t)(n0 + row) * stride + 16 * u) = *(const u32x4*)&tile[out_off(row, 16 * u, units)];
+  }
+}
+
+// absorb: one workgroup per head, 8 waves; wave w owns latent rows c = 64 w + 32 mb + l32
+// (mb = 0, 1).  A = W_UK codes of those rows (the lane's k half: 64 bytes per row, loaded once).
+// Output per token: 512 bf16 (1 KiB) staged in LDS, then stored as whole rows.
+__global__ __launch_bounds__(512) void absorb_q_fp8_kernel(const uint16_t* __restrict__ q_nope,
                                                            const uint8_t* __restrict__ codes,
                                                            const float* __restrict__ scales,
                                                            uint16_t* __restrict__ q_lat, int tokens) {
-  __shared__ __attribute__((aligned(16))) ActStage<1> st;
+  __shared__ __attribute__((aligned(16))) ActCodes<1> st;
+  __shared__ __attribute__((aligned(16))) uint8_t tile[32 * kDc * 2];
   const int h = blockIdx.x, tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
-  uint32_t aw[4][16];
+  uint32_t aw[2][16];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-    const uint8_t* src = codes + ((size_t)h * kDc + wave * 128 + mb * 32 + l32) * kDh + 64 * hf;
+  for (int mb = 0; mb < 2; ++mb) {
+    const uint8_t* src = codes + ((size_t)h * kDc + wave * 64 + mb * 32 + l32) * kDh + 64 * hf;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const u32x4 v = *(const u32x4*)(src + 16 * u);
       aw[mb][4 * u] = v[0], aw[mb][4 * u + 1] = v[1], aw[mb][4 * u + 2] = v[2], aw[mb][4 * u + 3] = v[3];
     }
   }
-  const float sw = scales[h * 4 + wave];  // latent block of this wave's rows
+  const float sw = scales[h * 4 + (wave >> 1)];  // latent block of this wave's rows
   for (int n0 = 0; n0 < tokens; n0 += 32) {
-    __syncthreads();  // the previous block's codes are consumed
-    code_tokens<1, true>(q_nope + (size_t)h * kDh, (size_t)kHeads * kDh, n0, tokens, tid, st);
+    __syncthreads();  // the previous block's codes and staged rows are consumed
+    code_tokens<1, 8, 512, true>(q_nope + (size_t)h * kDh, (size_t)kHeads * kDh, n0, tokens, tid, st);
     __syncthreads();
     uint64_t bq[8];
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) bq[ks] = act_b(st.codes, l32, hf, 0, 1, ks);
-    const int n = n0 + l32;
     const float s = st.scale[l32] * sw;  // this lane's token
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
+    for (int mb = 0; mb < 2; ++mb) {
       f32x16 acc = {};
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks)
         acc = mfma_fp8(aw[mb][2 * ks], aw[mb][2 * ks + 1], (uint32_t)bq[ks], (uint32_t)(bq[ks] >> 32), acc);
-      if (n < tokens) {
-        uint16_t* dst = q_lat + ((size_t)n * kHeads + h) * kDc + wave * 128 + mb * 32 + 4 * hf;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          u32x2 v;
-          v[0] = pack_bf16x2(acc[4 * g] * s, acc[4 * g + 1] * s);
-          v[1] = pack_bf16x2(acc[4 * g + 2] * s, acc[4 * g + 3] * s);
-          *(u32x2*)(dst + 8 * g) = v;
-        }
-      }
+      stage_fragment(tile, kDc * 2 / 16, l32, hf, 2 * (wave * 64 + mb * 32), acc, s);
     }
+    __syncthreads();
+    store_tile<512>(tile, kDc * 2 / 16, (uint8_t*)(q_lat + (size_t)h * kDc), (size_t)kHeads * kDc * 2, n0, tokens,
+                    tid);
   }
 }
 
-// out-proj: one workgroup per head, 4 waves; wave w owns value rows v = 32 w + l32.  A = W_UV^T
-// codes of row v (the lane's k half of each of the 4 latent blocks: 4 x 64 bytes, loaded once).
-// Each latent block's MFMA sum is scaled by s_o[n][kb] * s_w[h][kb] and added in fp32.
-__global__ __launch_bounds__(256) void out_proj_fp8_kernel(const float* __restrict__ o_lat,
+// out-proj: one workgroup per head, 8 waves; wave w owns value rows v = 32 (w & 3) + l32 and the
+// latent blocks kb = 2 (w >> 2), +1.  A = W_UV^T codes of row v (the lane's k half of each of its
+// two latent blocks: 2 x 64 bytes, loaded once).  Each latent block's MFMA sum is scaled by
+// s_o[n][kb] * s_w[h][kb]; waves 4..7 hand their fp32 sums to waves 0..3 through LDS, which add
+// them (blocks 0+1, then 2+3) and stage the bf16 rows (256 bytes per token) for whole-row stores.
+__global__ __launch_bounds__(512) void out_proj_fp8_kernel(const float* __restrict__ o_lat,
                                                            const uint8_t* __restrict__ codes,
                                                            const float* __restrict__ scales,
                                                            uint16_t* __restrict__ out, int tokens) {
-  __shared__ __attribute__((aligned(16))) ActStage<4> st;
+  __shared__ __attribute__((aligned(16))) ActCodes<4> st;
+  __shared__ __attribute__((aligned(16))) float red[4][16][64];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[32 * kDh * 2];
   const int h = blockIdx.x, tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int vb = wave & 3, kh = wave >> 2;
   const int lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
-  const int v = wave * 32 + l32;
-  uint32_t aw[4][16];
+  const int v = vb * 32 + l32;
+  uint32_t aw[2][16];
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    const uint8_t* src = codes + ((size_t)h * kDh + v) * kDc + kb * 128 + 64 * hf;
+  for (int k2 = 0; k2 < 2; ++k2) {
+    const uint8_t* src = codes + ((size_t)h * kDh + v) * kDc + (2 * kh + k2) * 128 + 64 * hf;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const u32x4 q = *(const u32x4*)(src + 16 * u);
-      aw[kb][4 * u] = q[0], aw[kb][4 * u + 1] = q[1], aw[kb][4 * u + 2] = q[2], aw[kb][4 * u + 3] = q[3];
+      aw[k2][4 * u] = q[0], aw[k2][4 * u + 1] = q[1], aw[k2][4 * u + 2] = q[2], aw[k2][4 * u + 3] = q[3];
     }
   }
-  float sw[4];
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) sw[kb] = scales[h * 4 + kb];
+  const float sw0 = scales[h * 4 + 2 * kh], sw1 = scales[h * 4 + 2 * kh + 1];
   for (int n0 = 0; n0 < tokens; n0 += 32) {
     __syncthreads();
-    code_tokens<4, false>(o_lat + (size_t)h * kDc, (size_t)kHeads * kDc, n0, tokens, tid, st);
+    code_tokens<4, 16, 512, false>(o_lat + (size_t)h * kDc, (size_t)kHeads * kDc, n0, tokens, tid, st);
     __syncthreads();
-    const int n = n0 + l32;
     f32x16 acc = {};
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const int kb = 2 * kh + k2;
       f32x16 part = {};
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         const uint64_t b = act_b(st.codes, l32, hf, kb, 4, ks);
-        part = mfma_fp8(aw[kb][2 * ks], aw[kb][2 * ks + 1], (uint32_t)b, (uint32_t)(b >> 32), part);
+        part = mfma_fp8(aw[k2][2 * ks], aw[k2][2 * ks + 1], (uint32_t)b, (uint32_t)(b >> 32), part);
       }
-      const float s = st.scale[l32 * 4 + kb] * sw[kb];
+      const float s = st.scale[l32 * 4 + kb] * (k2 ? sw1 : sw0);
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[e] += part[e] * s;
     }
-    if (n < tokens) {
-      uint16_t* dst = out + ((size_t)n * kHeads + h) * kDh + wave * 32 + 4 * hf;
+    if (kh == 1) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2 q;
-        q[0] = pack_bf16x2(acc[4 * g], acc[4 * g + 1]);
-        q[1] = pack_bf16x2(acc[4 * g + 2], acc[4 * g + 3]);
-        *(u32x2*)(dst + 8 * g) = q;
-      }
+      for (int e = 0; e < 16; ++e) red[vb][e][lane] = acc[e];
     }
+    __syncthreads();
+    if (kh == 0) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[e] += red[vb][e][lane];
+      stage_fragment(tile, kDh * 2 / 16, l32, hf, 2 * vb * 32, acc, 1.0f);
+    }
+    __syncthreads();
+    store_tile<512>(tile, kDh * 2 / 16, (uint8_t*)(out + (size_t)h * kDh), (size_t)kHeads * kDh * 2, n0, tokens,
+                    tid);
   }
 }
 
@@ -311,7 +356,7 @@ hipError_t launch_absorb_q_fp8(const void* q_nope, const void* packed, void* q_l
   if (tokens == 0) return hipSuccess;
   const uint8_t* codes = (const uint8_t*)packed;
   const float* scales = (const float*)(codes + (size_t)kHeads * kDc * kDh);
-  hipLaunchKernelGGL(absorb_q_fp8_kernel, dim3(kHeads), dim3(256), 0, stream, (const uint16_t*)q_nope, codes,
+  hipLaunchKernelGGL(absorb_q_fp8_kernel, dim3(kHeads), dim3(512), 0, stream, (const uint16_t*)q_nope, codes,
                      scales, (uint16_t*)q_lat, tokens);
   return hipGetLastError();
 }
@@ -320,7 +365,7 @@ hipError_t launch_out_proj_fp8(const float* o_lat, const void* packed, void* out
   if (tokens == 0) return hipSuccess;
   const uint8_t* codes = (const uint8_t*)packed;
   const float* scales = (const float*)(codes + (size_t)kHeads * kDc * kDh);
-  hipLaunchKernelGGL(out_proj_fp8_kernel, dim3(kHeads), dim3(256), 0, stream, o_lat, codes, scales, (uint16_t*)out,
+  hipLaunchKernelGGL(out_proj_fp8_kernel, dim3(kHeads), dim3(512), 0, stream, o_lat, codes, scales, (uint16_t*)out,
                      tokens);
   return hipGetLastError();
 }
