@@ -21,6 +21,13 @@ natural-exp softmax, ``lse`` in natural-log units of the scaled logits;
 q_pe / k_pe arrive already rotated; with S query tokens and L cached tokens
 (the S new ones included) query i sees keys j < L - S + i + 1 when causal;
 an empty key set gives o_lat = 0, out = 0, lse = -inf.
+
+Tree-masked verify (the Perplexity post, section "Будущая работа": EAGLE-style speculation
+predicts several tokens arranged as a tree): the S new tokens are the nodes of a draft tree,
+cached at positions L - S .. L - 1 in an order where every parent precedes its children;
+``parents[j]`` in [-1, j) names node j's parent (-1: a child of the last committed token).
+Query i sees the committed keys 0 .. L - S - 1 and the new keys of its ancestors and itself
+(a reading: the pages give no mask; a chain of parents j - 1 is the causal case).
 """
 from __future__ import annotations
 
@@ -49,6 +56,33 @@ def visible_keys(L: int, S: int, i: int, causal: bool) -> int:
     return max(0, min(L, n))
 
 
+def tree_ancestors(parents) -> np.ndarray:
+    """A[i, j] is true iff node j is node i or one of its ancestors, walking parent links."""
+    parents = np.asarray(parents, dtype=np.int64)
+    S = parents.shape[0]
+    A = np.zeros((S, S), dtype=bool)
+    for i in range(S):
+        j = i
+        while j >= 0:
+            A[i, j] = True
+            p = int(parents[j])
+            if not -1 <= p < j:
+                raise ValueError(f"parent of node {j} is {p}: must be in [-1, {j})")
+            j = p
+    return A
+
+
+def visible_key_index(L: int, S: int, i: int, causal: bool, ancestors: Optional[np.ndarray] = None) -> np.ndarray:
+    """Indices of the keys query token i of S sees.  Without a tree: the first
+    ``visible_keys`` ones.  With a tree (``ancestors`` from ``tree_ancestors``): the committed
+    keys and the new keys of node i's ancestors and itself."""
+    if ancestors is None:
+        return np.arange(visible_keys(L, S, i, causal))
+    base = L - S
+    new = [base + j for j in range(S) if ancestors[i, j] and base + j >= 0]
+    return np.concatenate([np.arange(max(base, 0)), np.asarray(new, dtype=np.int64)]).astype(np.int64)
+
+
 def _softmax_stats(z: np.ndarray):
     """Exact two-pass softmax of one logit row: (p, lse)."""
     if z.size == 0:
@@ -62,7 +96,7 @@ def _softmax_stats(z: np.ndarray):
 def mla_decode_nonabsorbed(q_nope, q_pe, w_uk, w_uv, pool, block_table, seq_lens, *, softmax_scale: float,
                            page_size: int = 64, causal: bool = True,
                            seqs: Optional[Iterable[int]] = None, heads: Optional[Iterable[int]] = None,
-                           return_probs: bool = False):
+                           return_probs: bool = False, tree=None):
     """Reference decode, non-absorbed order, fp64.
 
     Shapes: q_nope (B,S,H,d_h), q_pe (B,S,H,d_R), w_uk / w_uv (H,d_c,d_h),
@@ -73,8 +107,9 @@ def mla_decode_nonabsorbed(q_nope, q_pe, w_uk, w_uv, pool, block_table, seq_lens
     z_j = scale·(q_nope·K_j + q_pe·R_j) for the visible keys; exact softmax;
     out = Σ p_j V_j.  ``o_lat`` = Σ p_j C_j is the latent-space output the
     attention call returns (same p).  Entries outside ``seqs``×``heads`` stay
-    NaN.  Returns a dict with o_lat (B,S,H,d_c), lse (B,S,H), out (B,S,H,d_h)
-    and, if asked, probs[(b,i,h)] = p.
+    NaN.  ``tree`` (B,S) parent indices switch to the tree mask (``causal`` is
+    then ignored).  Returns a dict with o_lat (B,S,H,d_c), lse (B,S,H),
+    out (B,S,H,d_h) and, if asked, probs[(b,i,h)] = p.
     """
     q_nope = np.asarray(q_nope, dtype=np.float64)
     q_pe = np.asarray(q_pe, dtype=np.float64)
@@ -91,15 +126,17 @@ def mla_decode_nonabsorbed(q_nope, q_pe, w_uk, w_uv, pool, block_table, seq_lens
         L = int(seq_lens[b])
         rows = gather_rows(pool, block_table[b], L, page_size)
         C, R = rows[:, :Dc], rows[:, Dc:]
+        anc = None if tree is None else tree_ancestors(tree[b])
         for h in heads:
             K = C @ np.asarray(w_uk[h], dtype=np.float64)  # (L, d_h)  k_nope of every cached token
             V = C @ np.asarray(w_uv[h], dtype=np.float64)  # (L, d_h)  v of every cached token
             for i in range(S):
-                n = visible_keys(L, S, i, causal)
-                z = softmax_scale * (K[:n] @ q_nope[b, i, h] + R[:n] @ q_pe[b, i, h])
+                idx = visible_key_index(L, S, i, causal, anc)
+                n = idx.size
+                z = softmax_scale * (K[idx] @ q_nope[b, i, h] + R[idx] @ q_pe[b, i, h])
                 p, lse[b, i, h] = _softmax_stats(z)
-                out[b, i, h] = p @ V[:n] if n else 0.0
-                o_lat[b, i, h] = p @ C[:n] if n else 0.0
+                out[b, i, h] = p @ V[idx] if n else 0.0
+                o_lat[b, i, h] = p @ C[idx] if n else 0.0
                 if return_probs:
                     probs[(b, i, h)] = p
     res = {"o_lat": o_lat, "lse": lse, "out": out}
@@ -140,14 +177,15 @@ def out_proj_reference(o_lat, w_uv):
 
 def latent_attention_reference(q_lat, q_pe, pool, block_table, seq_lens, *, softmax_scale: float,
                                page_size: int = 64, causal: bool = True,
-                               seqs: Optional[Iterable[int]] = None):
+                               seqs: Optional[Iterable[int]] = None, tree=None):
     """What the attention call computes from an already-absorbed query, fp64.
 
     Logit of head h against cached token j: scale·(q_lat·c_j + q_pe·k_pe_j),
     the latent c_j serving as the key and (below) as the value of every head
     — izhida answer "DeepSeek" (each head takes a weighted sum over the
-    512-d latent; the RoPE inner product is 64-d) and answer "专家".  Returns
-    o_lat (B,S,H,d_c) = Σ_j p_j c_j and lse (B,S,H).
+    512-d latent; the RoPE inner product is 64-d) and answer "专家".  ``tree``
+    as in ``mla_decode_nonabsorbed``.  Returns o_lat (B,S,H,d_c) = Σ_j p_j c_j
+    and lse (B,S,H).
     """
     q_lat = np.asarray(q_lat, dtype=np.float64)
     q_pe = np.asarray(q_pe, dtype=np.float64)
@@ -158,12 +196,14 @@ def latent_attention_reference(q_lat, q_pe, pool, block_table, seq_lens, *, soft
         L = int(seq_lens[b])
         rows = gather_rows(pool, block_table[b], L, page_size)
         C, R = rows[:, :Dc], rows[:, Dc:]
+        anc = None if tree is None else tree_ancestors(tree[b])
         for i in range(S):
-            n = visible_keys(L, S, i, causal)
-            Z = softmax_scale * (C[:n] @ q_lat[b, i].T + R[:n] @ q_pe[b, i].T)  # (n, H): one column per head
+            idx = visible_key_index(L, S, i, causal, anc)
+            n = idx.size
+            Z = softmax_scale * (C[idx] @ q_lat[b, i].T + R[idx] @ q_pe[b, i].T)  # (n, H): one column per head
             for h in range(H):
                 p, lse[b, i, h] = _softmax_stats(Z[:, h])
-                o_lat[b, i, h] = p @ C[:n] if n else 0.0
+                o_lat[b, i, h] = p @ C[idx] if n else 0.0
     return {"o_lat": o_lat, "lse": lse}
 
 
