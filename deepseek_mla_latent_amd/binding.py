@@ -24,6 +24,7 @@ STATUS = {
     -5: "MLA_ERR_WORKSPACE", -6: "MLA_ERR_UNSUPPORTED", -7: "MLA_ERR_LAUNCH", -8: "MLA_ERR_DEVICE",
 }
 EXPORTS = ("mla_absorb_q", "mla_decode_workspace_bytes", "mla_decode_num_splits", "mla_decode_attn",
+           "mla_decode_attn_tree",
            "mla_out_proj", "mla_prefill_kv_bytes", "mla_prefill_kv_up", "mla_prefill_attn",
            "mla_linear_workspace_bytes", "mla_linear", "mla_rope_append", "mla_fp8_weight_bytes",
            "mla_quantize_w_uk_fp8", "mla_quantize_w_uv_fp8", "mla_absorb_q_fp8", "mla_out_proj_fp8", "mla_status_str")
@@ -51,15 +52,43 @@ class mla_params(ctypes.Structure):
 _lib = None
 
 
+class MlaRuntimeConflict(RuntimeError):
+    """More than one HIP runtime is mapped into the process."""
+
+
+def _hip_runtimes_mapped():
+    """Paths of the HIP runtime libraries mapped into this process (Linux)."""
+    try:
+        with open("/proc/self/maps") as f:
+            return sorted({line.split()[-1] for line in f if "libamdhip64" in line})
+    except OSError:
+        return []
+
+
 def load_library(path: Optional[str] = None):
-    """Load the shared library once; raise MlaLibraryMissing if it is not built."""
+    """Load the shared library once; raise MlaLibraryMissing if it is not built.
+
+    The library must run on the same HIP runtime as the framework that owns the device memory it
+    is handed.  torch ships its own copy of the runtime under the same soname, so torch is
+    imported first: the library's dependency then resolves to the copy already loaded.  Loaded the
+    other way round, the process would hold two runtimes (the library's launches going through one
+    while torch's memory and streams belong to the other); that state is refused.
+    """
     global _lib
     if _lib is not None and path is None:
         return _lib
     p = path or LIB_PATH
     if not os.path.exists(p):
         raise MlaLibraryMissing(f"{p} is not built; run `python -m deepseek_mla_latent_amd.build`")
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(p)
+    runtimes = _hip_runtimes_mapped()
+    if len(runtimes) > 1:
+        raise MlaRuntimeConflict(f"{p} was loaded next to another HIP runtime: {runtimes}; load it in a process "
+                                 "whose HIP runtime is already the one torch uses (import torch first)")
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     pp = ctypes.POINTER(mla_params)
     lib.mla_absorb_q.argtypes = [vp, vp, vp, pp, vp]
@@ -70,6 +99,8 @@ def load_library(path: Optional[str] = None):
     lib.mla_decode_num_splits.restype = i32
     lib.mla_decode_attn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i32, pp, vp]
     lib.mla_decode_attn.restype = i32
+    lib.mla_decode_attn_tree.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i32, pp, vp]
+    lib.mla_decode_attn_tree.restype = i32
     lib.mla_out_proj.argtypes = [vp, vp, vp, pp, vp]
     lib.mla_out_proj.restype = i32
     lib.mla_prefill_kv_bytes.argtypes = [pp]
@@ -167,6 +198,16 @@ def mla_decode_attn(q_lat, q_pe, kv_pool, block_table, seq_lens, o_lat, lse, wor
     _check(lib.mla_decode_attn(_ptr(q_lat), _ptr(q_pe), _ptr(kv_pool), _ptr(block_table), _ptr(seq_lens),
                                _ptr(o_lat), _ptr(lse), _ptr(workspace), workspace_bytes, num_splits,
                                ctypes.byref(params), _stream(stream)), "mla_decode_attn")
+
+
+def mla_decode_attn_tree(q_lat, q_pe, kv_pool, block_table, seq_lens, tree_parents, o_lat, lse, workspace,
+                         num_splits: int, params: mla_params, stream=None,
+                         workspace_bytes: Optional[int] = None) -> None:
+    lib = load_library()
+    _check(lib.mla_decode_attn_tree(_ptr(q_lat), _ptr(q_pe), _ptr(kv_pool), _ptr(block_table), _ptr(seq_lens),
+                                    _ptr(tree_parents), _ptr(o_lat), _ptr(lse), _ptr(workspace),
+                                    _nbytes(workspace, workspace_bytes), num_splits, ctypes.byref(params),
+                                    _stream(stream)), "mla_decode_attn_tree")
 
 
 def mla_out_proj(o_lat, w_uv, out, params: mla_params, stream=None) -> None:

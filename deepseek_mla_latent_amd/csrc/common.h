@@ -8,6 +8,11 @@
 
 namespace mla {
 
+// Launch helpers read the launch's status from the thread's last-error slot right after the
+// launch.  An error that an earlier, unrelated runtime call left there (the caller's own, or a
+// framework's) would then be reported as this launch's, so the slot is cleared first.
+inline void forget_stale_error() { (void)hipGetLastError(); }
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));

@@ -26,6 +26,11 @@
 //     and skips almost every rescale of the 256 accumulator registers.
 // Long contexts are split into page ranges (split-K over tokens); each range writes a normalised
 // partial (o_k, lse_k) and lse_merge_kernel combines them.
+// Tree-masked verify (EAGLE-style draft trees: the Perplexity post, section "Будущая работа"): the
+// S new tokens are tree nodes cached at positions L-S .. L-1, parents before children; query i
+// sees the committed keys and the keys of its ancestors and itself.  The row's visibility of the
+// S new keys is one 64-bit mask (S <= 64), built once per workgroup by walking parent links and
+// applied only to tiles that reach position L-S.
 #include "common.h"
 #include "kernels.h"
 
@@ -143,9 +148,28 @@ __device__ __forceinline__ bf16x8 lds_read_tr_pair(const MLA_LDS char* lo, const
 }
 
 // Token range and output slots of one workgroup; shared by both dtypes.
+// Visibility of the S new keys to query (b, i) under a draft tree (S <= 64), wave-uniform: bit j
+// set iff node j is node i or one of its ancestors.  Lane j loads node j's parent once; the walk
+// then follows parent links through readlane while they point strictly backwards, so it ends
+// after at most S steps whatever the table holds.
+__device__ __forceinline__ int tree_parent_of_lane(const int32_t* parents, int b, int S, int lane) {
+  return lane < S ? parents[(size_t)b * S + lane] : -1;
+}
+__device__ __forceinline__ uint64_t tree_walk(int par, int S, int i) {
+  uint64_t m = 0;
+  int j = i;
+  for (int step = 0; step < S && j >= 0; ++step) {
+    m |= 1ull << j;
+    const int pj = __builtin_amdgcn_readlane(par, j);
+    j = pj < j ? pj : -1;
+  }
+  return m;
+}
+
 struct WorkItem {
   int b, i, split;
   int tok_begin, tok_end;  // [tok_begin, tok_end) of sequence b, page aligned at tok_begin
+  int tail;                // L - S: position of the first new token (node 0 of a draft tree)
   size_t out_row;          // index of (head 0) in the o/lse output rows
 };
 
@@ -156,13 +180,14 @@ __device__ __forceinline__ WorkItem make_work(const AttnArgs& a, int id) {
   w.split = rest % a.num_splits;
   w.b = rest / a.num_splits;
   const int L = a.seq_lens[w.b];
-  int n = a.causal ? L - a.S + w.i + 1 : L;
+  int n = a.causal && !a.tree_parents ? L - a.S + w.i + 1 : L;
   n = n < 0 ? 0 : (n > L ? L : n);
   const int p_begin = w.split * a.pages_per_split;
   const int pages_L = (L + kPage - 1) / kPage;
   int p_end = p_begin + a.pages_per_split;
   p_end = p_end < pages_L ? p_end : pages_L;
   w.tok_begin = p_begin * kPage;
+  w.tail = L - a.S;
   const int e = p_end * kPage;
   w.tok_end = e < n ? e : n;
   const size_t bi = (size_t)w.b * a.S + w.i;
@@ -170,9 +195,16 @@ __device__ __forceinline__ WorkItem make_work(const AttnArgs& a, int id) {
   return w;
 }
 
+template <bool kTree>
 __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds_raw[kNumBufs * kBufBytes];
-  __shared__ int lds_pages[kMaxSplitPages];
+  // Page ids of the range, then 12 words for kTree: word 0 = the first tile of the range that
+  // reaches a draft-tree key; words 2-3 = zeros (no key of an earlier tile is masked); words 4-11
+  // = the masked-key windows of that tile and the next three, two per tile (lanes 0-31, lanes
+  // 32-63).  Read back per tile: held in registers across the loop they would not fit, and kept in
+  // the page-id array so that both are addressed from one base.
+  __shared__ __attribute__((aligned(16))) int lds_pages[kMaxSplitPages + 12];
+  int* const lds_tree = lds_pages + kMaxSplitPages;
   MLA_LDS char* const smem = (MLA_LDS char*)lds_raw;
 
   const int id = xcd_remap(blockIdx.x, gridDim.x);
@@ -181,6 +213,9 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
   const int lane = threadIdx.x & 63;
   const int l32 = lane & 31, hf = lane >> 5;
   const int h = wave * 32 + l32;
+  // kTree: node `lane`'s parent, loaded here and walked once the query prologue has waited for its
+  // loads
+  const int tpar = kTree ? tree_parent_of_lane(a.tree_parents, w.b, a.S, lane) : -1;
 
   // Output slots of this lane (head h, latent columns 8 g + 4 hf + 32 cb ..).  Computed where
   // they are used: held across the loop they would cost two 64-bit registers.
@@ -270,6 +305,25 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 32; ++ks) asm volatile("" ::"v"(q[ks]));
   }
+  if (kTree && wave == 0) {
+    // Window of tile t for lane half hf: bit k (k = (e/4)*8 + e%4 for element e) is the
+    // visibility of the key at kpos(t) + 4 hf + k, i.e. node j = kpos(t) - tail + 4 hf + k.  With
+    // E = [32 ones | the row's 64-bit mask | 32 zeros], E bit j + 32 is node j (negative:
+    // committed), so the window is E bits u .. u + 31 for u = kpos(t) - tail + 4 hf + 32.
+    const uint64_t m = tree_walk(tpar, a.S, w.i);
+    const int t_first = w.tail - w.tok_begin < kTile ? 0 : (w.tail - w.tok_begin) / kTile;
+    if (lane < 8) {
+      int u = w.tok_begin + (t_first + (lane >> 1)) * kTile - w.tail + 4 * (lane & 1) + 32;
+      u = u < 0 ? 0 : (u > 96 ? 96 : u);  // below 0: all committed; above 96: all past node 63
+      const int qw = u >> 5, r = u & 31;
+      const uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
+      const uint32_t lo_w = qw == 0 ? 0xffffffffu : (qw == 1 ? lo : (qw == 2 ? hi : 0u));
+      const uint32_t hi_w = qw == 0 ? lo : (qw == 1 ? hi : 0u);
+      lds_tree[4 + lane] = (int32_t)~__builtin_amdgcn_alignbit(hi_w, lo_w, r);  // 1 = masked
+    }
+    if (lane == 0) lds_tree[0] = t_first;
+    if (lane == 2 || lane == 3) lds_tree[lane] = 0;
+  }
   __syncthreads();  // every wave has its q: the buffers take the tiles now
   auto prologue_tile = [&](int t) {
     const uint16_t* src = row_of(t, __builtin_amdgcn_readfirstlane(lds_pages[t >> 1]));
@@ -333,12 +387,15 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
   for (int cb = 0; cb < 16; ++cb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[cb][e] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-  bool started = false;  // wave-uniform: a first key has been seen (m_run finite)
+  // The reference starts at the lowest finite float, so a tile whose keys are all masked (a draft
+  // tree can hide whole tiles, even the first of a range) gives exp2(-inf) = 0, never inf - inf.
+  float m_run = -3.402823466e38f, l_run = 0.f;
+  bool started = false;  // wave-uniform: a first visible key has been seen
   // Consume every scalar kernel argument the loop uses here, so no scalar load is still in
   // flight inside the loop (it would share the LDS counter and force full drains there).
   const float scale_log2 = a.scale_log2;
   asm volatile("" ::"s"(scale_log2), "s"(ntiles), "s"(ntok));
+
 
   // ---- online softmax of one tile's raw scores sc (element e = token (e/4)*8 + 4 hf + e%4 of
   // the tile), in base 2 with the scale folded into the exponent's FMA, cut into stages so that
@@ -384,6 +441,34 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
   };
   constexpr int kSoftmaxStages = 35;
 
+  // kTree: raw scores of tile t.  A key of a node that is neither the query's node nor one of its
+  // ancestors gets -inf; committed keys stay.  Tiles before the first one that reaches the tree
+  // keep everything; a range meets at most three such tiles (64 nodes), a fourth entry covers the
+  // stale tile scored past the end.
+  // Element e: a signed extract of its masked-key bit (0 or all ones) selects the score or -inf
+  // (an instruction literal), two temporaries at a time.  The kernel has no register to spare
+  // across the loop, so nothing here may be hoisted out of it: the LDS address and the lane half
+  // are hidden from loop-invariant code motion.
+  auto tree_mask_tile = [&](f32x16& sc, int t) {
+    int z = 0;  // an opaque zero in the addresses: a constant LDS address would be hoisted
+    asm volatile("" : "+s"(z));
+    int ci = t - __builtin_amdgcn_readfirstlane(lds_tree[z]);  // wave-uniform
+    ci = ci < -1 ? -1 : (ci > 3 ? 3 : ci);
+    int ln = lane;  // an opaque copy of the lane id (live anyway): its half is not hoisted either
+    asm volatile("" : "+v"(ln));
+    const uint32_t mwin = (uint32_t)lds_tree[z + 4 + 2 * ci + (ln >> 5)];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float x = sc[e];
+      uint32_t m, ninf;  // m = masked ? ~0 : 0; ninf = m & bits(-inf); x = m ? -inf : x
+      asm volatile(
+          "v_bfe_i32 %1, %3, %4, 1\n\tv_and_b32 %2, 0xff800000, %1\n\tv_bfi_b32 %0, %1, %2, %0"
+          : "+v"(x), "=&v"(m), "=&v"(ninf)
+          : "v"(mwin), "i"((e >> 2) * 8 + (e & 3)));
+      sc[e] = x;
+    }
+  };
+
   // ---- scores of tile 0 (nothing to overlap yet)
   __builtin_amdgcn_s_barrier();  // every wave's part of tile 0 has landed
   bf16x8 ring[4];
@@ -400,6 +485,7 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
       mfma_acc_v_last(sa, ring[ks & 3], q[ks]);
     if (ks + 4 < 36) ring[ks & 3] = read_qk(ks + 4);
   }
+  if constexpr (kTree) tree_mask_tile(sa, 0);
   if (ntiles > 1) {  // tile 1 has landed everywhere; start its operand reads
     dma_wait_tiles(ntiles > 2 ? 1 : 0);
     __builtin_amdgcn_s_barrier();
@@ -462,10 +548,18 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
       if (m == 8) page_ahead = __builtin_amdgcn_readfirstlane(pid_v);
       __builtin_amdgcn_sched_barrier(0);
     }
+    // kTree: mask the next tile's scores here, where the operand ring is dead (its registers are
+    // what the masking needs) and 32 MFMAs separate the last write of sn from these reads
+    if constexpr (kTree) tree_mask_tile(sn, t + 1);
     if (t + 2 < ntiles) {  // every read of tile t done, tile t+2 landed: publish, then prefetch
       dma_wait_tiles(1);
       __builtin_amdgcn_s_barrier();
       advance_qk(t + 1);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) ring[g] = read_qk(g);
+    } else if constexpr (kTree) {
+      // Past the last tile the ring keeps its spent values for the stale scores; refilled from the
+      // current buffer instead (any LDS bytes do), its old values die before the masking above.
 #pragma unroll
       for (int g = 0; g < 4; ++g) ring[g] = read_qk(g);
     }
@@ -479,7 +573,7 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = 1.0f / l_tot;
+  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;  // every key masked: o = 0, lse = -inf
   size_t o_idx;
   float* lse_ptr;
   {
@@ -542,11 +636,17 @@ __global__ __launch_bounds__(256) void decode_attn_f32_kernel(AttnArgs a) {
   __syncthreads();
 
   const int32_t* bt = a.block_table + (size_t)w.b * a.max_pages;
+  const uint64_t tmask =
+      a.tree_parents ? tree_walk(tree_parent_of_lane(a.tree_parents, w.b, a.S, tid & 63), a.S, w.i) : 0ull;
+  auto visible = [&](int tkn) {
+    const int j = tkn - w.tail;
+    return !a.tree_parents || j < 0 || (j < 64 && ((tmask >> j) & 1ull));
+  };
   float m_run = -INFINITY, l_run = 0.f, acc0 = 0.f, acc1 = 0.f;
   for (int start = w.tok_begin; start < w.tok_end; start += 256) {
     const int tkn = start + tid;
     float z = -INFINITY;
-    if (tkn < w.tok_end) {
+    if (tkn < w.tok_end && visible(tkn)) {
       const float* row = pool + ((size_t)bt[tkn / kPage] * kPage + tkn % kPage) * kRow;
       float d = 0.f;
       for (int c = 0; c < kRow; ++c) d = fmaf(qs[c], row[c], d);
@@ -558,8 +658,9 @@ __global__ __launch_bounds__(256) void decode_attn_f32_kernel(AttnArgs a) {
     __syncthreads();
     m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     const float m_new = fmaxf(m_run, m);
-    const float alpha = expf(m_run - m_new);
-    const float p = tkn < w.tok_end ? expf(z - m_new) : 0.f;
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;  // a chunk with every key masked
+    const float alpha = expf(m_run - m_use);
+    const float p = expf(z - m_use);  // masked keys and keys past the range have z = -inf
     ps[tid] = p;
     float sm = p;
     for (int off = 32; off > 0; off >>= 1) sm += __shfl_xor(sm, off);
@@ -580,7 +681,7 @@ __global__ __launch_bounds__(256) void decode_attn_f32_kernel(AttnArgs a) {
     __syncthreads();
   }
   float* o_ptr = (float*)a.o_out + (w.out_row + h) * kDc;
-  const bool empty = w.tok_end <= w.tok_begin;
+  const bool empty = w.tok_end <= w.tok_begin || l_run == 0.f;
   o_ptr[tid] = empty ? 0.f : acc0 / l_run;
   o_ptr[tid + 256] = empty ? 0.f : acc1 / l_run;
   if (tid == 0 && a.lse_out) a.lse_out[w.out_row + h] = empty ? -INFINITY : m_run + logf(l_run);
@@ -680,9 +781,12 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const PartT* __restrict_
 }
 
 hipError_t launch_decode_attn(const AttnArgs& a, int rows, hipStream_t stream) {
+  forget_stale_error();
   const int nwg = rows * a.num_splits;
-  if (a.dtype_bf16)
-    hipLaunchKernelGGL(decode_attn_bf16_kernel, dim3(nwg), dim3(256), 0, stream, a);
+  if (a.dtype_bf16 && a.tree_parents)
+    hipLaunchKernelGGL(decode_attn_bf16_kernel<true>, dim3(nwg), dim3(256), 0, stream, a);
+  else if (a.dtype_bf16)
+    hipLaunchKernelGGL(decode_attn_bf16_kernel<false>, dim3(nwg), dim3(256), 0, stream, a);
   else
     hipLaunchKernelGGL(decode_attn_f32_kernel, dim3(nwg * kHeads), dim3(256), 0, stream, a);
   return hipGetLastError();
@@ -690,6 +794,7 @@ hipError_t launch_decode_attn(const AttnArgs& a, int rows, hipStream_t stream) {
 
 hipError_t launch_lse_merge(const void* o_part, bool part_bf16, const float* lse_part, float* o_lat, float* lse,
                             int rows, int num_splits, hipStream_t stream) {
+  forget_stale_error();
   const dim3 grid(rows * (kHeads / 4));
   if (part_bf16)
     hipLaunchKernelGGL(lse_merge_kernel<uint16_t>, grid, dim3(256), 0, stream, (const uint16_t*)o_part, lse_part,

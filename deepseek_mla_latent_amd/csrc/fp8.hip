@@ -345,6 +345,7 @@ __global__ __launch_bounds__(512) void out_proj_fp8_kernel(const float* __restri
 }
 
 hipError_t launch_quantize_weight_fp8(const void* w, void* packed, bool transpose, hipStream_t stream) {
+  forget_stale_error();
   uint8_t* codes = (uint8_t*)packed;
   float* scales = (float*)(codes + (size_t)kHeads * kDc * kDh);
   hipLaunchKernelGGL(quantize_weight_fp8_kernel, dim3(4, kHeads), dim3(256), 0, stream, (const uint16_t*)w, codes,
@@ -353,6 +354,7 @@ hipError_t launch_quantize_weight_fp8(const void* w, void* packed, bool transpos
 }
 
 hipError_t launch_absorb_q_fp8(const void* q_nope, const void* packed, void* q_lat, int tokens, hipStream_t stream) {
+  forget_stale_error();
   if (tokens == 0) return hipSuccess;
   const uint8_t* codes = (const uint8_t*)packed;
   const float* scales = (const float*)(codes + (size_t)kHeads * kDc * kDh);
@@ -362,6 +364,7 @@ hipError_t launch_absorb_q_fp8(const void* q_nope, const void* packed, void* q_l
 }
 
 hipError_t launch_out_proj_fp8(const float* o_lat, const void* packed, void* out, int tokens, hipStream_t stream) {
+  forget_stale_error();
   if (tokens == 0) return hipSuccess;
   const uint8_t* codes = (const uint8_t*)packed;
   const float* scales = (const float*)(codes + (size_t)kHeads * kDc * kDh);

@@ -25,6 +25,7 @@ struct AttnArgs {
   void* o_out;                 // final o_lat (B,S,H,512) fp32, or partials (B*S, splits, H, 512):
                                // bf16 for the bf16 kernel, fp32 for the fp32 kernel
   float* lse_out;              // final lse (B,S,H) (may be null), or partial lse (B*S, splits, H)
+  const int32_t* tree_parents;  // (B,S) draft-tree parents in [-1, j), or null (then `causal` applies)
   int B, S, max_pages, pages_per_split, num_splits, causal, final_out, dtype_bf16;
   float scale;       // softmax scale
   float scale_log2;  // softmax scale * log2(e)

@@ -148,9 +148,15 @@ size_t mla_decode_workspace_bytes(const mla_params* p, int32_t num_splits) {
   return s > 0 ? workspace_for(p, s) : 0;
 }
 
-mla_status mla_decode_attn(const void* q_lat, const void* q_pe, const void* kv_pool, const int32_t* block_table,
-                           const int32_t* seq_lens, float* o_lat, float* lse, void* workspace,
-                           size_t workspace_bytes, int32_t num_splits, const mla_params* p, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// mla_decode_attn and mla_decode_attn_tree: `tree_parents` null = the causal / full rule of p.
+mla_status decode_attn_impl(const void* q_lat, const void* q_pe, const void* kv_pool, const int32_t* block_table,
+                            const int32_t* seq_lens, const int32_t* tree_parents, float* o_lat, float* lse,
+                            void* workspace, size_t workspace_bytes, int32_t num_splits, const mla_params* p,
+                            void* stream) {
   mla_status st = check_params(p);
   if (st != MLA_OK) return st;
   if (num_splits < 0) return MLA_ERR_SHAPE;
@@ -160,7 +166,8 @@ mla_status mla_decode_attn(const void* q_lat, const void* q_pe, const void* kv_p
   if (!q_lat || !q_pe || !seq_lens || !o_lat) return MLA_ERR_NULL;
   if (max_pages > 0 && (!kv_pool || !block_table)) return MLA_ERR_NULL;
   if (!aligned16(q_lat) || !aligned16(q_pe) || !aligned16(kv_pool) || !aligned16(o_lat)) return MLA_ERR_ALIGN;
-  if (!std::isfinite(p->softmax_scale)) return MLA_ERR_SHAPE;
+  // the kernels take a tile's maximum before scaling: the scale must be positive
+  if (!std::isfinite(p->softmax_scale) || !(p->softmax_scale > 0.f)) return MLA_ERR_SHAPE;
   const int cus = num_splits > 0 ? 1 : cu_count();
   if (cus <= 0) return MLA_ERR_DEVICE;
   const SplitPlan plan = plan_splits(p, num_splits, cus);
@@ -179,6 +186,7 @@ mla_status mla_decode_attn(const void* q_lat, const void* q_pe, const void* kv_p
   a.pool = kv_pool;
   a.block_table = block_table;
   a.seq_lens = seq_lens;
+  a.tree_parents = tree_parents;
   a.B = p->batch;
   a.S = p->q_len;
   a.max_pages = p->max_pages_per_seq;
@@ -206,6 +214,29 @@ mla_status mla_decode_attn(const void* q_lat, const void* q_pe, const void* kv_p
   if (mla::launch_lse_merge(o_part, p->dtype == MLA_BF16, lse_part, o_lat, lse, rows, plan.splits, s) != hipSuccess)
     return MLA_ERR_LAUNCH;
   return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_decode_attn(const void* q_lat, const void* q_pe, const void* kv_pool, const int32_t* block_table,
+                           const int32_t* seq_lens, float* o_lat, float* lse, void* workspace,
+                           size_t workspace_bytes, int32_t num_splits, const mla_params* p, void* stream) {
+  return decode_attn_impl(q_lat, q_pe, kv_pool, block_table, seq_lens, nullptr, o_lat, lse, workspace,
+                          workspace_bytes, num_splits, p, stream);
+}
+
+mla_status mla_decode_attn_tree(const void* q_lat, const void* q_pe, const void* kv_pool,
+                                const int32_t* block_table, const int32_t* seq_lens, const int32_t* tree_parents,
+                                float* o_lat, float* lse, void* workspace, size_t workspace_bytes,
+                                int32_t num_splits, const mla_params* p, void* stream) {
+  mla_status st = check_params(p);
+  if (st != MLA_OK) return st;
+  if (p->q_len > 64) return MLA_ERR_SHAPE;  // one 64-bit visibility mask per query row
+  if (tokens_of(p) > 0 && !tree_parents) return MLA_ERR_NULL;
+  return decode_attn_impl(q_lat, q_pe, kv_pool, block_table, seq_lens, tree_parents, o_lat, lse, workspace,
+                          workspace_bytes, num_splits, p, stream);
 }
 
 mla_status mla_out_proj(const float* o_lat, const void* w_uv, void* out, const mla_params* p, void* stream) {
@@ -252,7 +283,7 @@ mla_status mla_prefill_attn(const void* q_nope, const void* q_pe, const void* kv
   if (!q_nope || !q_pe || !seq_lens || !out) return MLA_ERR_NULL;
   if (p->max_seq_len > 0 && !kv) return MLA_ERR_NULL;
   if (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(kv) || !aligned16(out)) return MLA_ERR_ALIGN;
-  if (!std::isfinite(p->softmax_scale)) return MLA_ERR_SHAPE;
+  if (!std::isfinite(p->softmax_scale) || !(p->softmax_scale > 0.f)) return MLA_ERR_SHAPE;  // as decode
   if (p->max_seq_len > 0 && kv_bytes < prefill_kv_bytes(p)) return MLA_ERR_WORKSPACE;
   const int nqb = (p->q_len + 255) / 256;  // 256 queries per workgroup
   if ((int64_t)p->batch * mla::kHeads * nqb > 0x7fffffffLL) return MLA_ERR_SHAPE;

@@ -266,6 +266,7 @@ __global__ __launch_bounds__(64) void kpe_copy_kernel(const uint16_t* __restrict
 hipError_t launch_kv_up_grid(const void* pool, const int32_t* block_table, const int32_t* seq_lens,
                              const void* w_uk, const void* w_uv, void* kv, void* kpe, int batch, int max_pages,
                              int pages_max, hipStream_t stream) {
+  forget_stale_error();
   if (batch == 0 || pages_max == 0) return hipSuccess;
   hipLaunchKernelGGL(kv_up_kernel, dim3(2 * kHeads), dim3(256), 0, stream, (const uint16_t*)pool, block_table,
                      seq_lens, (const uint16_t*)w_uk, (const uint16_t*)w_uv, (uint16_t*)kv, batch, max_pages,
@@ -565,6 +566,7 @@ __global__ __launch_bounds__(64 * kPfWaves, 1) void prefill_attn_kernel(PrefillA
 }
 
 hipError_t launch_prefill_attn(const PrefillArgs& a, hipStream_t stream) {
+  forget_stale_error();
   const int64_t grid = (int64_t)a.B * kHeads * a.nqb;
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL(prefill_attn_kernel, dim3((unsigned)grid), dim3(64 * kPfWaves), 0, stream, a);

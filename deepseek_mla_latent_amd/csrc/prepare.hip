@@ -190,6 +190,7 @@ int linear_splits(int M, int K, int N, int cus) {
 
 hipError_t launch_linear(const void* x, const void* w, void* y, float* partial, int M, int K, int N, int splits,
                          hipStream_t stream) {
+  forget_stale_error();
   const int mb = M >= 512 ? 4 : 1;
   const int mblocks = (M + 32 * mb - 1) / (32 * mb);
   const int64_t grid = (int64_t)mblocks * (N / 64) * splits;
@@ -275,6 +276,7 @@ __global__ __launch_bounds__(128) void rope_append_kernel(uint16_t* __restrict__
 
 hipError_t launch_rope_append(void* q_pe, const void* kv_a, int kv_stride, void* pool, const int32_t* block_table,
                               const int32_t* seq_lens, int B, int S, int max_pages, double base, hipStream_t stream) {
+  forget_stale_error();
   const int64_t grid = (int64_t)B * S;
   if (grid == 0) return hipSuccess;
   InvFreq f;

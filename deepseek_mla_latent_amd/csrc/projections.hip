@@ -301,6 +301,7 @@ __global__ __launch_bounds__(256) void out_proj_f32_kernel(const float* __restri
 
 hipError_t launch_absorb_q(const void* q_nope, const void* w_uk, void* q_lat, int tokens, bool bf16,
                            hipStream_t stream) {
+  forget_stale_error();
   const dim3 grid(kDc / 128, kHeads);
   if (bf16)
     hipLaunchKernelGGL(absorb_q_kernel<true>, grid, dim3(256), 0, stream, q_nope, w_uk, q_lat, tokens);
@@ -311,6 +312,7 @@ hipError_t launch_absorb_q(const void* q_nope, const void* w_uk, void* q_lat, in
 
 hipError_t launch_out_proj(const float* o_lat, const void* w_uv, void* out, int tokens, bool bf16,
                            hipStream_t stream) {
+  forget_stale_error();
   if (bf16)
     hipLaunchKernelGGL(out_proj_bf16_kernel, dim3(2 * kHeads), dim3(256), 0, stream, o_lat,
                        (const uint16_t*)w_uv, (uint16_t*)out, tokens);

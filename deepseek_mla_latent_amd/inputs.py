@@ -244,3 +244,24 @@ def generate_latent(w: DecodeWorkload, seed: int):
     q_lat = rng.standard_normal(shape, dtype=np.float32) * np.float32(math.sqrt(w.head_dim / w.kv_lora_rank))
     o_lat = rng.standard_normal(shape, dtype=np.float32)
     return _cast(q_lat, w.dtype), o_lat
+
+
+def draft_trees(batch: int, size: int, seed: int, *, max_children: int = 3) -> np.ndarray:
+    """Seeded draft trees for tree-masked verify: (batch, size) int32 parent indices.
+
+    Node 0 is the root (parent -1, a child of the last committed token); every later node j picks
+    its parent uniformly among the earlier nodes that still have fewer than ``max_children``
+    children, so parents always come before children (the order the nodes are cached in).  The
+    shape follows EAGLE-style speculation trees (a few candidates per level), which the Perplexity
+    post names as planned work (section "Будущая работа").
+    """
+    rng = np.random.default_rng(seed)
+    parents = np.full((batch, size), -1, dtype=np.int32)
+    for b in range(batch):
+        children = np.zeros(size, dtype=np.int64)
+        for j in range(1, size):
+            open_nodes = np.flatnonzero(children[:j] < max_children)
+            p = int(rng.choice(open_nodes))
+            parents[b, j] = p
+            children[p] += 1
+    return parents

@@ -73,7 +73,7 @@ typedef struct {
   int32_t page_size;         /* 64 tokens per cache page */
   int32_t max_pages_per_seq; /* row stride of block_table (>= ceil(max_seq_len / page_size)) */
   int32_t max_seq_len;       /* host-known upper bound on seq_lens[]: sizes the grid, no D2H copy */
-  float softmax_scale;       /* multiplies the whole logit (latent + RoPE parts), e.g. 1/sqrt(192) */
+  float softmax_scale;       /* > 0; multiplies the whole logit (latent + RoPE parts), e.g. 1/sqrt(192) */
   int32_t causal;            /* 1: query i of S sees seq_lens[b] - S + i + 1 keys; 0: all keys */
   mla_dtype dtype;           /* of q_nope, q_pe, q_lat, cache, W_UK, W_UV, out; accumulation is fp32 */
 } mla_params;
@@ -125,6 +125,29 @@ mla_status mla_decode_attn(const void* q_lat, const void* q_pe, const void* kv_p
                            const int32_t* block_table, const int32_t* seq_lens, float* o_lat,
                            float* lse, void* workspace, size_t workspace_bytes, int32_t num_splits,
                            const mla_params* p, void* stream);
+
+/*
+ * mla_decode_attn with a draft-tree mask in place of the causal rule (tree-masked verify of
+ * EAGLE-style speculation, which predicts several tokens arranged as a tree: Perplexity post,
+ * section "Будущая работа"). The S = q_len new tokens of sequence b are the nodes of a tree,
+ * cached at positions seq_lens[b] - S .. seq_lens[b] - 1 in an order where every parent comes
+ * before its children.
+ *   tree_parents (B,S) int32   node j's parent in [-1, j); -1 = a child of the last committed
+ *                              token. Query i sees the committed keys 0 .. seq_lens[b] - S - 1
+ *                              and the keys of node i's ancestors and of node i itself; a chain
+ *                              (parent j - 1) is the causal rule. A parent outside [-1, j) ends
+ *                              node j's ancestor walk (the node then has no further ancestors);
+ *                              node positions below 0 are not visible.
+ * Every other argument, the split count and the workspace (mla_decode_num_splits /
+ * mla_decode_workspace_bytes for the same p) are as for mla_decode_attn; p->causal is ignored.
+ * Errors: q_len > 64 gives MLA_ERR_SHAPE; tree_parents NULL (with B*S > 0) gives MLA_ERR_NULL.
+ * A split whose keys are all masked contributes nothing (lse -inf); an empty visible set gives
+ * o_lat = 0, lse = -inf.
+ */
+mla_status mla_decode_attn_tree(const void* q_lat, const void* q_pe, const void* kv_pool,
+                                const int32_t* block_table, const int32_t* seq_lens, const int32_t* tree_parents,
+                                float* o_lat, float* lse, void* workspace, size_t workspace_bytes,
+                                int32_t num_splits, const mla_params* p, void* stream);
 
 /*
  * out[b,s,h,v] = sum_c o_lat[b,s,h,c] * W_UV[h,c,v]

@@ -74,6 +74,8 @@ def test_attention_errors():
     assert _attn(P(max_pages_per_seq=2)) == -2  # 300 tokens need 5 pages per sequence
     assert _attn(P(), splits=-1) == -2
     assert _attn(P(softmax_scale=float("inf"))) == -2
+    assert _attn(P(softmax_scale=0.0)) == -2  # the kernels scale a tile's maximum: the scale must be > 0
+    assert _attn(P(softmax_scale=-0.1)) == -2
     # explicit split count: workspace size is host-computable, no device query
     need = lib.mla_decode_workspace_bytes(ctypes.byref(P()), 2)
     assert need == 2 * 1 * 2 * 128 * (512 * 2 + 4)  # bf16 partials + fp32 lse
@@ -82,6 +84,24 @@ def test_attention_errors():
     assert _attn(P(), ws=FAKE, ws_bytes=need - 4, splits=2) == -5
     assert _attn(P(), ws=MISALIGNED, ws_bytes=need, splits=2) == -4
     assert _attn(P(batch=0), splits=2) == 0
+
+
+def _tree(params, ptrs=None, parents=FAKE, ws=FAKE, ws_bytes=1 << 30, splits=2):
+    p = dict(q_lat=FAKE, q_pe=FAKE, pool=FAKE, bt=FAKE, lens=FAKE, o=FAKE, lse=FAKE)
+    p.update(ptrs or {})
+    return lib.mla_decode_attn_tree(p["q_lat"], p["q_pe"], p["pool"], p["bt"], p["lens"], parents, p["o"], p["lse"],
+                                    ws, ws_bytes, splits, ctypes.byref(params), None)
+
+
+def test_tree_attention_errors():
+    assert _tree(P(q_len=4), parents=None) == -1
+    assert _tree(P(q_len=65)) == -2  # one 64-bit visibility mask per query row
+    assert _tree(P(q_len=4), {"q_lat": None}) == -1
+    assert _tree(P(q_len=4), {"o": MISALIGNED}) == -4
+    assert _tree(P(q_len=4, softmax_scale=-1.0)) == -2
+    assert _tree(P(q_len=4, dtype=5)) == -3
+    assert _tree(P(q_len=4), ws=FAKE, ws_bytes=16) == -5
+    assert _tree(P(q_len=4, batch=0), parents=None) == 0  # empty batch: nothing to do
 
 
 def test_split_planning_is_page_aligned():
@@ -180,3 +200,34 @@ def test_fp8_errors():
         assert fn(FAKE, FAKE, MISALIGNED, ctypes.byref(P()), None) == -4
         assert fn(FAKE, FAKE, FAKE, ctypes.byref(P(head_dim=64)), None) == -6
         assert fn(FAKE, FAKE, FAKE, ctypes.byref(P(batch=0)), None) == 0
+
+
+def _run_py(code):
+    import subprocess
+    import sys
+    from tests.helpers import ROOT
+    return subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+
+
+def test_library_binds_to_the_runtime_torch_uses():
+    """Loaded through the binding, the library shares torch's HIP runtime (one runtime mapped)."""
+    r = _run_py("from deepseek_mla_latent_amd import binding\n"
+                "binding.load_library()\n"
+                "print(len(binding._hip_runtimes_mapped()))")
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip() == "1"
+
+
+def test_a_second_runtime_is_refused():
+    """The library opened raw before torch drags in a second HIP runtime; the binding refuses it."""
+    r = _run_py("import ctypes\n"
+                "from deepseek_mla_latent_amd import binding\n"
+                "ctypes.CDLL(binding.LIB_PATH)\n"
+                "import torch\n"
+                "assert len(binding._hip_runtimes_mapped()) == 2\n"
+                "try:\n"
+                "    binding.load_library()\n"
+                "except binding.MlaRuntimeConflict:\n"
+                "    print('refused')\n")
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip() == "refused"
