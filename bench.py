@@ -25,6 +25,10 @@ Prefill workloads (``--workload prefill_b1_s4096``): one step = mla_prefill_kv_u
 mla_prefill_attn over one batch of whole prompts (multi-head form), reported as prompt tokens/s
 against the MFMA roofline of the attention call.
 
+Tree-masked verify (``--workload tree_b32_s8_t4096``): the decode path with mla_decode_attn_tree in
+place of mla_decode_attn; 32 sequences of 4096 committed tokens each verify a seeded 8-node draft
+tree cached after them, reported as verified draft tokens/s (B x 8 per step).
+
 Prints one JSON line.
 """
 import argparse
@@ -89,7 +93,7 @@ def roofline_entry(kernel: str, call, dt: str, seconds: float, traffic=None) -> 
             "algorithmic_flops_per_launch": call.flops, "launch_us": seconds * 1e6}
 
 
-def cpu_baseline(x, target_seconds: float):
+def cpu_baseline(x, target_seconds: float, tree=None):
     """The fp64 oracle (non-absorbed route) on a bounded sample: whole sequences (all heads) in batch order,
     wrapping around, for about target_seconds."""
     import numpy as np
@@ -108,7 +112,7 @@ def cpu_baseline(x, target_seconds: float):
     n = 0
     while True:  # sequences in batch order, wrapping around, until about target_seconds of work
         ref.mla_decode_nonabsorbed(q_nope, q_pe, w_uk, w_uv, pool, x.block_table, x.seq_lens,
-                                   softmax_scale=w.softmax_scale, seqs=[n % w.batch])
+                                   softmax_scale=w.softmax_scale, seqs=[n % w.batch], tree=tree)
         n += 1
         el = time.perf_counter() - t0
         if el * (n + 1) / n > target_seconds:
@@ -533,9 +537,11 @@ def main():
     if args.workload in OPROJ_WORKLOADS:
         return run_oproj(args, dev)
 
-    w = gen.WORKLOADS[args.workload]
+    tree_wl = args.workload in gen.TREE_WORKLOADS
+    w = gen.TREE_WORKLOADS[args.workload] if tree_wl else gen.WORKLOADS[args.workload]
     x = gen.generate_named(args.workload)
     dt = "bf16" if x.is_bf16 else "f32"
+    parents = gen.draft_trees(w.batch, w.q_len, gen.TREE_SEEDS[args.workload]) if tree_wl else None
 
     def up(a):
         a = np.ascontiguousarray(a)
@@ -543,7 +549,7 @@ def main():
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(a).to(dev)
 
-    costs = accounting.path_costs(x.seq_lens, w.q_len, dt)
+    costs = accounting.path_costs(x.seq_lens, w.q_len, dt, tree=parents)
     per_replica = sum(c.bytes for c in costs)
     R = args.replicas or max(2, math.ceil(2 * MALL_BYTES / per_replica) + 1)
 
@@ -561,7 +567,8 @@ def main():
     reps = []
     for _ in range(R):
         d = dict(q_nope=up(x.q_nope), q_pe=up(x.q_pe), w_uk=up(x.w_uk), w_uv=up(x.w_uv), pool=up(x.pool),
-                 bt=torch.from_numpy(x.block_table).to(dev), lens=torch.from_numpy(x.seq_lens).to(dev))
+                 bt=torch.from_numpy(x.block_table).to(dev), lens=torch.from_numpy(x.seq_lens).to(dev),
+                 tree=torch.from_numpy(parents).to(dev) if tree_wl else None)
         d["bufs"] = binding.DecodeBuffers(params, args.num_splits, device=dev)
         reps.append(d)
 
@@ -575,10 +582,11 @@ def main():
             binding.mla_quantize_w_uv_fp8(d["w_uv"], pk_uv, params)
             d["w_uk"], d["w_uv"] = pk_uk, pk_uv
         torch.cuda.synchronize()
-        costs = accounting.path_costs(x.seq_lens, w.q_len, dt, fp8_projections=True)
+        costs = accounting.path_costs(x.seq_lens, w.q_len, dt, fp8_projections=True, tree=parents)
 
     def run(d, stream=None):
-        d["bufs"].run(d["q_nope"], d["q_pe"], d["w_uk"], d["w_uv"], d["pool"], d["bt"], d["lens"], stream, fp8=fp8)
+        d["bufs"].run(d["q_nope"], d["q_pe"], d["w_uk"], d["w_uv"], d["pool"], d["bt"], d["lens"], stream, fp8=fp8,
+                      tree_parents=d["tree"])
 
     # graphs: one per replica, captured after an eager warm-up on a side stream
     side = torch.cuda.Stream()
@@ -619,8 +627,12 @@ def main():
         e[0].record(stream)
         (binding.mla_absorb_q_fp8 if fp8 else binding.mla_absorb_q)(d["q_nope"], d["w_uk"], p.q_lat, params)
         e[1].record(stream)
-        binding.mla_decode_attn(p.q_lat, d["q_pe"], d["pool"], d["bt"], d["lens"], p.o_lat, p.lse, p.workspace,
-                                args.num_splits, params)
+        if tree_wl:
+            binding.mla_decode_attn_tree(p.q_lat, d["q_pe"], d["pool"], d["bt"], d["lens"], d["tree"], p.o_lat, p.lse,
+                                         p.workspace, args.num_splits, params)
+        else:
+            binding.mla_decode_attn(p.q_lat, d["q_pe"], d["pool"], d["bt"], d["lens"], p.o_lat, p.lse, p.workspace,
+                                    args.num_splits, params)
         e[2].record(stream)
         (binding.mla_out_proj_fp8 if fp8 else binding.mla_out_proj)(p.o_lat, d["w_uv"], p.out, params)
         e[3].record(stream)
@@ -649,15 +661,17 @@ def main():
                    "cache_len": int(x.seq_lens.max()), "heads": w.heads, "kv_lora_rank": w.kv_lora_rank,
                    "rope_dim": w.rope_dim, "head_dim": w.head_dim, "page_size": w.page_size,
                    "num_splits": splits, "replicas": R, "graph_replay": True,
-                   "projections": "fp8 block-quantised" if fp8 else dt},
-        "roofline": roofline_entry("mla_decode_attn (split attention + LSE merge)", attn, dt, attn_s, traffic),
+                   "projections": "fp8 block-quantised" if fp8 else dt,
+                   **({"draft_tree": "8 nodes, at most 3 children each (seeded)", "mask": "tree"} if tree_wl else {})},
+        "roofline": roofline_entry(("mla_decode_attn_tree (tree-masked split attention + LSE merge)" if tree_wl
+                                    else "mla_decode_attn (split attention + LSE merge)"), attn, dt, attn_s, traffic),
         "path_roofline": {"t_roof_us": t_roof * 1e6, "t_step_us": ms_per_step * 1e3,
                           "frac": t_roof / (ms_per_step * 1e-3),
                           "calls_us": dict(zip([c.name for c in costs], call_us)),
                           "calls_roof_us": {c.name: c.roof_seconds(dt) * 1e6 for c in costs}},
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(gen.generate_named(args.workload), args.cpu_seconds)
+        rec["cpu_baseline"] = cpu_baseline(gen.generate_named(args.workload), args.cpu_seconds, tree=parents)
     print(json.dumps(rec), flush=True)
 
 

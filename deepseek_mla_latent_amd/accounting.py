@@ -41,10 +41,30 @@ class CallCost:
         return "hbm" if self.bytes / HBM_PEAK_BYTES_S >= self.flops / MFMA_PEAK_FLOPS[dtype] else "mfma"
 
 
-def visible_pairs(seq_lens: Sequence[int], q_len: int, causal: bool = True) -> int:
+def _tree_visible_new_keys(parents, L: int) -> list:
+    """Per node of a draft tree: how many of the new keys it sees (itself and its ancestors, those at
+    positions >= 0), walking parent links."""
+    S = len(parents)
+    out = []
+    for i in range(S):
+        n, j = 0, i
+        while j >= 0:
+            n += 1 if L - S + j >= 0 else 0
+            p = int(parents[j])
+            j = p if p < j else -1
+        out.append(n)
+    return out
+
+
+def visible_pairs(seq_lens: Sequence[int], q_len: int, causal: bool = True, tree=None) -> int:
+    """(query, key) pairs the attention scores: causal / full rule, or a draft tree's mask
+    (``tree``: (B, S) parents)."""
     pairs = 0
-    for L in seq_lens:
+    for b, L in enumerate(seq_lens):
         L = int(L)
+        if tree is not None:
+            pairs += q_len * max(0, L - q_len) + sum(_tree_visible_new_keys(tree[b], L))
+            continue
         for i in range(q_len):
             n = L - q_len + i + 1 if causal else L
             pairs += max(0, min(L, n))
@@ -52,7 +72,8 @@ def visible_pairs(seq_lens: Sequence[int], q_len: int, causal: bool = True) -> i
 
 
 def path_costs(seq_lens: Sequence[int], q_len: int, dtype: str, *, heads: int = 128, d_c: int = 512,
-               d_r: int = 64, d_h: int = 128, page: int = 64, causal: bool = True, fp8_projections: bool = False):
+               d_r: int = 64, d_h: int = 128, page: int = 64, causal: bool = True, fp8_projections: bool = False,
+               tree=None):
     e = 2 if dtype == "bf16" else 4
     ew = 1 if fp8_projections else e  # weight element bytes (FP8 codes; scales added below)
     wsc = heads * (d_c // 128) * 4 if fp8_projections else 0
@@ -64,7 +85,9 @@ def path_costs(seq_lens: Sequence[int], q_len: int, dtype: str, *, heads: int = 
     tables = sum(-(-int(L) // page) for L in seq_lens) * 4 + B * 4
     attn = CallCost("mla_decode_attn",
                     cache + T * heads * (d_c + d_r) * e + tables + T * heads * (d_c + 1) * 4,
-                    2 * heads * (d_c + d_r + d_c) * visible_pairs(seq_lens, q_len, causal))
+                    2 * heads * (d_c + d_r + d_c) * visible_pairs(seq_lens, q_len, causal, tree))
+    if tree is not None:
+        attn = CallCost(attn.name, attn.bytes + T * 4, attn.flops)  # plus the parent table
     out = CallCost("mla_out_proj", heads * d_c * d_h * ew + wsc + T * heads * d_c * 4 + T * heads * d_h * e,
                    2 * T * heads * d_c * d_h)
     return [absorb, attn, out]

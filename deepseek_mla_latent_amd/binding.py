@@ -302,12 +302,18 @@ class DecodeBuffers:
         ws = mla_decode_workspace_bytes(params, num_splits)
         self.workspace = torch.empty(max(ws, 16) // 4 + 4, dtype=torch.float32, device=device) if ws else None
 
-    def run(self, q_nope, q_pe, w_uk, w_uv, kv_pool, block_table, seq_lens, stream=None, fp8: bool = False):
+    def run(self, q_nope, q_pe, w_uk, w_uv, kv_pool, block_table, seq_lens, stream=None, fp8: bool = False,
+            tree_parents=None):
         """The three calls; with ``fp8`` the weights are packed FP8 weights and the two projections
-        run block-quantised (mla_absorb_q_fp8 / mla_out_proj_fp8)."""
+        run block-quantised (mla_absorb_q_fp8 / mla_out_proj_fp8); with ``tree_parents`` (B, S)
+        int32 the attention is the tree-masked verify (mla_decode_attn_tree)."""
         p = self.params
         (mla_absorb_q_fp8 if fp8 else mla_absorb_q)(q_nope, w_uk, self.q_lat, p, stream)
-        mla_decode_attn(self.q_lat, q_pe, kv_pool, block_table, seq_lens, self.o_lat, self.lse, self.workspace,
-                        self.num_splits, p, stream)
+        if tree_parents is None:
+            mla_decode_attn(self.q_lat, q_pe, kv_pool, block_table, seq_lens, self.o_lat, self.lse, self.workspace,
+                            self.num_splits, p, stream)
+        else:
+            mla_decode_attn_tree(self.q_lat, q_pe, kv_pool, block_table, seq_lens, tree_parents, self.o_lat, self.lse,
+                                 self.workspace, self.num_splits, p, stream)
         (mla_out_proj_fp8 if fp8 else mla_out_proj)(self.o_lat, w_uv, self.out, p, stream)
         return self.out

@@ -96,6 +96,15 @@ PREFILL_WORKLOADS = {
 }
 WORKLOAD_SEEDS.update({name: 101 + i for i, name in enumerate(PREFILL_WORKLOADS)})
 
+# Tree-masked verify: each of 32 sequences (4096 committed tokens) verifies an 8-node draft tree
+# (``draft_trees``, at most 3 children per node) cached after them, so L = 4096 + 8.
+TREE_WORKLOADS = {
+    "tree_b32_s8_t4096": DecodeWorkload("tree_b32_s8_t4096", batch=32, q_len=8, cache_len=4096 + 8, dtype="bf16",
+                                        paged=True),
+}
+WORKLOAD_SEEDS.update({name: 201 + i for i, name in enumerate(TREE_WORKLOADS)})
+TREE_SEEDS = {name: 301 + i for i, name in enumerate(TREE_WORKLOADS)}  # of the draft trees
+
 
 def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """fp32 -> bf16 bit patterns (uint16), round-to-nearest-even; NaN stays NaN."""
@@ -220,8 +229,8 @@ def generate(w: DecodeWorkload, seed: int, *, poison_unused: bool = False,
 
 
 def generate_named(name: str, *, poison_unused: bool = False) -> DecodeInputs:
-    """The batch for one of the named workloads (decode or prefill), with its fixed seed."""
-    w = WORKLOADS[name] if name in WORKLOADS else PREFILL_WORKLOADS[name]
+    """The batch for one of the named workloads (decode, prefill or tree verify), with its fixed seed."""
+    w = {**WORKLOADS, **PREFILL_WORKLOADS, **TREE_WORKLOADS}[name]
     return generate(w, WORKLOAD_SEEDS[name], poison_unused=poison_unused)
 
 
