@@ -6,7 +6,7 @@
 // activations quantised on the fly, one scale per 128-element vector along the reduction
 // dimension.  Format E4M3 (bias 7, 3 mantissa bits, no infinities, largest finite 448); a block's
 // scale is amax / 448 in fp32; a value is coded as x * (448 / amax) (one fp32 division per block,
-// fp32 products) rounded to the nearest E4M3 value, ties to even.
+// fp32 products) rounded to the nearest E4M3 value, ties to even, by the hardware conversion.
 //
 //   quantize_weight_fp8_kernel  W (H, 512, 128) bf16 -> codes + scales (H, 4); W_UV's codes are
 //                               stored transposed, (H, 128 v, 512 c), so both products read
@@ -30,41 +30,18 @@ namespace {
 
 constexpr float kE4M3Max = 448.0f;
 
-// E4M3 code of v (|v| <= about 464): the nearest E4M3 value, ties to even, 448 at most.
-__device__ __forceinline__ uint32_t e4m3_code(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 31) << 7;
-  const float a = fabsf(v);
-  uint32_t E, M;
-  if (a >= 0.015625f) {  // normal: spacing 2^(e-3)
-    int e = (int)((__float_as_uint(a) >> 23) & 0xff) - 127;
-    uint32_t m = (uint32_t)rintf(ldexpf(a, 3 - e));  // 8 .. 16
-    if (m == 16) {
-      m = 8;
-      ++e;
-    }
-    E = (uint32_t)(e + 7);
-    M = m - 8;
-    if (E > 15 || (E == 15 && M == 7)) {  // above 448: saturate
-      E = 15;
-      M = 6;
-    }
-  } else {  // subnormal: spacing 2^-9
-    const uint32_t m = (uint32_t)rintf(a * 512.0f);  // 0 .. 8
-    E = m == 8 ? 1u : 0u;
-    M = m == 8 ? 0u : m;
-  }
-  return sign | (E << 3) | M;
-}
-
-// N values -> N codes (N/4 words, 4 codes per word, little-endian) of x * factor
+// N values -> N codes (N/4 words, 4 codes per word, little-endian) of x * factor.  The conversion
+// is the hardware's (v_cvt_pk_fp8_f32: OCP E4M3, round to nearest even, subnormals kept), two
+// values per instruction.  |x * factor| <= 448 (1 + 2^-23) by construction, which rounds to at
+// most 448, so no value reaches the overflow encoding.  An all-zero block (factor 0) has codes 0
+// (a -0.0 input would otherwise give the code of -0).
 template <int N>
 __device__ __forceinline__ void code_n(const float (&x)[N], float factor, uint32_t (&w)[N / 4]) {
 #pragma unroll
   for (int i = 0; i < N / 4; ++i) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) word |= e4m3_code(x[4 * i + j] * factor) << (8 * j);
-    w[i] = word;
+    int word = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * i] * factor, x[4 * i + 1] * factor, 0, false);
+    word = __builtin_amdgcn_cvt_pk_fp8_f32(x[4 * i + 2] * factor, x[4 * i + 3] * factor, word, true);
+    w[i] = factor > 0.f ? (uint32_t)word : 0u;
   }
 }
 __device__ __forceinline__ float code_factor(float amax) { return amax > 0.f ? kE4M3Max / amax : 0.f; }

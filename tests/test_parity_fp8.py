@@ -55,6 +55,37 @@ def test_weight_quantisation_is_bit_exact(which):
     np.testing.assert_array_equal(codes.reshape(want_codes.shape), want_codes)
 
 
+@pytest.mark.parametrize("which", ["w_uk", "w_uv"])
+def test_weight_codes_at_ties_subnormals_and_zero_blocks(which):
+    """Blocks whose maximum is 448 (factor exactly 1) holding exact E4M3 ties (normal and
+    subnormal, both signs), a block of -0.0 and a block of +0.0 (codes 0), next to random blocks:
+    the codes must match the oracle's round-to-nearest-even bit for bit."""
+    say("fp8 weight edge codes", which)
+    rng = np.random.default_rng(502)
+    w = rng.standard_normal((128, 512, 128)).astype(np.float32) / np.float32(np.sqrt(512))
+    ties = np.array([1.0625, 1.1875, 3.25, 3.75, 0.5 * 2.0 ** -9, 1.5 * 2.0 ** -9, 2.5 * 2.0 ** -9,
+                     7.5 * 2.0 ** -9, 2.0 ** -6 + 2.0 ** -10, 240.0, 432.0, 2.0 ** -11], dtype=np.float32)
+    for h, cb in ((0, 0), (5, 3), (127, 1)):
+        blk = np.zeros((128, 128), np.float32)
+        vals = np.concatenate([ties, -ties])
+        blk.flat[:vals.size] = vals
+        blk[-1, -1] = 448.0
+        w[h, 128 * cb:128 * cb + 128] = blk
+    w[1, 0:128] = -0.0
+    w[2, 128:256] = 0.0
+    bits = gen.round_to_bf16_bits(w)
+    assert np.array_equal(gen.bf16_bits_to_f32(bits)[0, :128], w[0, :128])  # every tie is a bf16 value
+    packed = _packed(bits, which == "w_uv")
+    codes, scales = _unpack(packed)
+    vals, sc = ref.quantize(gen.bf16_bits_to_f32(bits), (1, 128, 128))
+    want_codes = ref.e4m3_encode(vals)
+    if which == "w_uv":
+        want_codes = np.ascontiguousarray(np.swapaxes(want_codes, 1, 2))
+    np.testing.assert_array_equal(scales, sc[:, :, 0])
+    np.testing.assert_array_equal(codes.reshape(want_codes.shape), want_codes)
+    assert scales[0, 0] == np.float32(1.0) and scales[1, 0] == 0 and scales[2, 1] == 0
+
+
 @pytest.mark.parametrize("tokens", [1, 33, 128])
 def test_absorb_q_fp8(tokens):
     say("absorb_q fp8", tokens)
