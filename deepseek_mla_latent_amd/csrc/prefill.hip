@@ -299,6 +299,18 @@ hipError_t launch_kv_up_grid(const void* pool, const int32_t* block_table, const
 __device__ __forceinline__ int pf_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 __device__ __forceinline__ int pf_swz_pe(int r) { return (r >> 1) & 7; }
 
+// max of three / two without NaN canonicalisation (inputs are scores or -inf): written as fmaxf the
+// compiler adds a canonicalising max per MFMA result, which doubles the VALU work of the tile max
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float vmax2(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 constexpr int kPfWaves = 8;
 constexpr int kPfRing = 4;
 constexpr int kPfAhead = 2;  // tiles in flight beyond the one being computed
@@ -429,11 +441,17 @@ __global__ __launch_bounds__(64 * kPfWaves, 1) void prefill_attn_kernel(PrefillA
           }
       }
     } else if (st == 1) {
-      float mt = -INFINITY;
+      float mc[4];  // four independent max3 chains over 8 scores each
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; e += 2) mt = fmaxf(mt, fmaxf(s[kb][e], s[kb][e + 1]));
+      for (int c = 0; c < 4; ++c) {
+        const f32x16& x = s[c >> 1];
+        const int e0 = (c & 1) * 8;
+        mc[c] = vmax3(x[e0], x[e0 + 1], x[e0 + 2]);
+        mc[c] = vmax3(mc[c], x[e0 + 3], x[e0 + 4]);
+        mc[c] = vmax3(mc[c], x[e0 + 5], x[e0 + 6]);
+        mc[c] = vmax2(mc[c], x[e0 + 7]);
+      }
+      float mt = vmax2(vmax3(mc[0], mc[1], mc[2]), mc[3]);
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
       mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sl2;
       const bool raise = __any(mt > m_run + 8.0f);  // wave-uniform
@@ -444,14 +462,15 @@ __global__ __launch_bounds__(64 * kPfWaves, 1) void prefill_attn_kernel(PrefillA
       m_run = m_new;
     } else {
       const float msub = m_run == -INFINITY ? 0.f : m_run;  // no visible key yet: every p is 0
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int e = (st - 2) * 2 + q;  // 0..31
-        const int kb = e >> 4, ee = e & 15;
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][ee], sl2, -msub));
-        l_run += p;
-        pn[kb * 2 + (ee >> 3)][ee & 7] = (__bf16)p;
-      }
+      const int e = (st - 2) * 2;  // 0..30: the pair e, e + 1 (one dword of a P operand)
+      const int kb = e >> 4, ee = e & 15;
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][ee], sl2, -msub));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][ee + 1], sl2, -msub));
+      const bf16x2 pr = {(__bf16)p0, (__bf16)p1};
+      // the row sum takes the bf16 probabilities the weighted sum uses, two per dot2 instruction
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, l_run, false);
+      pn[kb * 2 + (ee >> 3)][ee & 7] = pr[0];
+      pn[kb * 2 + (ee >> 3)][(ee & 7) + 1] = pr[1];
     }
   };
   // [sum of the previous tile (operands pk) | softmax of the current tile (stages over the slots)]
