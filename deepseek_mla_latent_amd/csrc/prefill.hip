@@ -512,54 +512,98 @@ __global__ __launch_bounds__(64 * kPfWaves, 1) void prefill_attn_kernel(PrefillA
     for (int i = tid; i < kPfBufBytes / 16; i += 64 * kPfWaves) *(MLA_LDS u32x4*)(z + i * 16) = u32x4{0u, 0u, 0u, 0u};
   }
 
-  bool done = false;  // this wave's queries see no key of this tile, nor of any later one
-  for (int t = 0; t < ntiles; ++t) {
-    pf_wait_tiles(min(ntiles - 1 - t, kPfAhead - 1));
-    __syncthreads();  // tile t is in LDS; every wave is done with tile t - 2's buffer
-    if (t + kPfAhead < ntiles) issue_tile(t + kPfAhead);
-    if (done) continue;
-    const int key0 = t * kPfKeys;
-    const MLA_LDS char* tile = lds + (t % kPfRing) * kPfBufBytes;
-    const MLA_LDS char* prev = lds + ((t + kPfRing - 1) % kPfRing) * kPfBufBytes;
-    if (key0 >= wave_vis_hi) {  // wave-uniform: finish the sum over the previous tile
-      scale_o();
-      sum_with_softmax(prev, 0, false, false);
-      done = true;
-      continue;
-    }
-
-    // scores: the key operands stream through a ring two k-steps ahead of their MFMAs
+  // scores of one tile into s: the key operands stream through a ring two k-steps ahead of their
+  // MFMAs
+  auto compute_scores = [&](const MLA_LDS char* tile) {
     s[0] = f32x16{};
     s[1] = f32x16{};
-    {
-      bf16x8 kr[3][2];
+    bf16x8 kr[3][2];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) kr[ks][kb] = lds_b128(tile + kofs[ks] + k_imm(kb, ks));
+      for (int kb = 0; kb < 2; ++kb) kr[ks][kb] = lds_b128(tile + kofs[ks] + k_imm(kb, ks));
 #pragma unroll
-      for (int ks = 0; ks < 12; ++ks) {
-        if (ks + 2 < 12) {
+    for (int ks = 0; ks < 12; ++ks) {
+      if (ks + 2 < 12) {
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) kr[(ks + 2) % 3][kb] = lds_b128(tile + kofs[ks + 2] + k_imm(kb, ks + 2));
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32x32x16(kr[ks % 3][kb], qf[ks], s[kb]);
+        for (int kb = 0; kb < 2; ++kb) kr[(ks + 2) % 3][kb] = lds_b128(tile + kofs[ks + 2] + k_imm(kb, ks + 2));
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32x32x16(kr[ks % 3][kb], qf[ks], s[kb]);
     }
-
-    // [sum(t-1) | softmax(t)]
-    scale_o();
-    sum_with_softmax(prev, key0, key0 + kPfKeys > wave_vis_lo, true);
-    pending_rescale = rescale;
-    pending_alpha = alpha;
+  };
+  // the softmax of the scores in s on its own, for the sum that follows at once: P into pk, O
+  // brought to the new reference
+  auto softmax_now = [&](int key0, bool need_mask) {
+#pragma unroll
+    for (int st = 0; st < 18; ++st) sm_stage(st, key0, need_mask);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) pk[kk] = pn[kk];
-  }
-  if (!done && ntiles > 0) {
+    pending_rescale = rescale;
+    pending_alpha = alpha;
     scale_o();
-    sum_with_softmax(lds + ((ntiles - 1) % kPfRing) * kPfBufBytes, 0, false, false);
+    pending_rescale = false;
+  };
+
+  // The per-tile barrier starts every wave's iteration together.  Waves 0-3 score the new tile
+  // first (MFMA-heavy) and then sum the previous one with the new softmax riding along (VALU-heavy);
+  // waves 4-7, which share the SIMDs with waves 0-3, take the phases the other way round: the
+  // softmax and sum of the previous tile first, then the scores of the new one.  A SIMD then pairs
+  // matrix work of one wave with vector work of the other instead of running both waves through the
+  // same phase at once.  Both orders finish reading tile t - 1 before the barrier of tile t + 1,
+  // after which its buffer is refilled.
+  bool done = false;  // this wave's queries see no key of this tile, nor of any later one
+  if (wave >= kPfWaves / 2) {
+    for (int t = 0; t < ntiles; ++t) {
+      pf_wait_tiles(min(ntiles - 1 - t, kPfAhead - 1));
+      __syncthreads();  // tile t is in LDS; every wave is done with tile t - 2's buffer
+      if (t + kPfAhead < ntiles) issue_tile(t + kPfAhead);
+      if (done) continue;
+      const int key0 = t * kPfKeys;
+      if (t > 0) {
+        softmax_now(key0 - kPfKeys, key0 > wave_vis_lo);
+        sum_with_softmax(lds + ((t + kPfRing - 1) % kPfRing) * kPfBufBytes, 0, false, false);
+      }
+      if (key0 >= wave_vis_hi) {  // wave-uniform: no query of the wave sees this tile or later ones
+        done = true;
+        continue;
+      }
+      compute_scores(lds + (t % kPfRing) * kPfBufBytes);
+    }
+    if (!done && ntiles > 0) {
+      const int key0 = (ntiles - 1) * kPfKeys;
+      softmax_now(key0, key0 + kPfKeys > wave_vis_lo);
+      sum_with_softmax(lds + ((ntiles - 1) % kPfRing) * kPfBufBytes, 0, false, false);
+    }
+  } else {
+    for (int t = 0; t < ntiles; ++t) {
+      pf_wait_tiles(min(ntiles - 1 - t, kPfAhead - 1));
+      __syncthreads();  // tile t is in LDS; every wave is done with tile t - 2's buffer
+      if (t + kPfAhead < ntiles) issue_tile(t + kPfAhead);
+      if (done) continue;
+      const int key0 = t * kPfKeys;
+      const MLA_LDS char* tile = lds + (t % kPfRing) * kPfBufBytes;
+      const MLA_LDS char* prev = lds + ((t + kPfRing - 1) % kPfRing) * kPfBufBytes;
+      if (key0 >= wave_vis_hi) {  // wave-uniform: finish the sum over the previous tile
+        scale_o();
+        sum_with_softmax(prev, 0, false, false);
+        done = true;
+        continue;
+      }
+      compute_scores(tile);
+      // [sum(t-1) | softmax(t)]
+      scale_o();
+      sum_with_softmax(prev, key0, key0 + kPfKeys > wave_vis_lo, true);
+      pending_rescale = rescale;
+      pending_alpha = alpha;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) pk[kk] = pn[kk];
+    }
+    if (!done && ntiles > 0) {
+      scale_o();
+      sum_with_softmax(lds + ((ntiles - 1) % kPfRing) * kPfBufBytes, 0, false, false);
+    }
   }
 
   // normalise and store: element e of block cb is O^T[32 cb + 8 (e/4) + 4 hf + e%4][query]
