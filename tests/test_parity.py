@@ -236,27 +236,41 @@ def test_end_to_end_small_mtp_all_heads():
 
 
 # ------------------------------------------------------------------------------------ boundary
-def test_graph_capture_replays_match_eager():
-    """The three calls captured in one HIP graph; replays interleaved with eager work all match."""
-    say("graph capture")
+@pytest.mark.parametrize("variant", ["causal", "tree", "fp8"])
+def test_graph_capture_replays_match_eager(variant):
+    """The three calls captured in one HIP graph; replays interleaved with eager work all match the
+    eager run bit for bit (decode as is, with a draft-tree mask, and with the FP8 projections)."""
+    say("graph capture", variant)
     torch = _torch()
-    w = gen.small_workload(4, 1, ragged=(200, 700), dtype="bf16", paged=True)
+    S = 4 if variant == "tree" else 1
+    w = gen.small_workload(4, S, ragged=(200, 700), dtype="bf16", paged=True)
     x = gen.generate(w, 23, poison_unused=True)
     d = to_device(x)
-    p = params_for(x)
+    p = params_for(x, causal=variant != "tree")
+    kw = {}
+    w_uk, w_uv = d["w_uk"], d["w_uv"]
+    if variant == "tree":
+        kw["tree_parents"] = torch.from_numpy(gen.draft_trees(4, S, 24)).cuda()
+    if variant == "fp8":
+        w_uk = torch.empty(binding.mla_fp8_weight_bytes(), dtype=torch.uint8, device="cuda")
+        w_uv = torch.empty_like(w_uk)
+        binding.mla_quantize_w_uk_fp8(d["w_uk"], w_uk, p)
+        binding.mla_quantize_w_uv_fp8(d["w_uv"], w_uv, p)
+        kw["fp8"] = True
+    args = (d["q_nope"], d["q_pe"], w_uk, w_uv, d["pool"], d["block_table"], d["seq_lens"])
     eager = binding.DecodeBuffers(p)
-    eager.run(d["q_nope"], d["q_pe"], d["w_uk"], d["w_uv"], d["pool"], d["block_table"], d["seq_lens"])
+    eager.run(*args, **kw)
     torch.cuda.synchronize()
     ref_out, ref_lse = eager.out.clone(), eager.lse.clone()
     gb = binding.DecodeBuffers(p)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        gb.run(d["q_nope"], d["q_pe"], d["w_uk"], d["w_uv"], d["pool"], d["block_table"], d["seq_lens"])
+        gb.run(*args, **kw)
     torch.cuda.current_stream().wait_stream(s)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        gb.run(d["q_nope"], d["q_pe"], d["w_uk"], d["w_uv"], d["pool"], d["block_table"], d["seq_lens"])
+        gb.run(*args, **kw)
     for it in range(4):
         gb.out.fill_(float("nan"))
         gb.lse.fill_(float("nan"))

@@ -1,10 +1,13 @@
 """Property-based GPU parity: hypothesis draws small decode batches and every one must match the oracle.
 
-Drawn: batch 1..4, query tokens S in {1, 2}, per-sequence cache lengths L >= S (up to five pages, so
+Drawn for the causal / full rule: batch 1..4, query tokens S in {1, 2}, per-sequence cache lengths L >= S (up to five pages, so
 ragged last pages and multi-tile walks both occur), contiguous or randomly permuted pages, causal or
 not, the split count (1, 2, 3, 5 or the library's own choice) and the dtype.  Unused pool slots are
 NaN, so any read outside the sequences fails the NaN check.  Same bar as the fixed parity cases:
 max |gpu - ref| / max |ref| <= 2e-2 (bf16) or 1e-4 (fp32) on o_lat and lse.
+Drawn for tree-masked verify: batch 1..3, trees of 1, 3, 8, 17 or 64 nodes with random parents
+(several roots, and parents out of range, which end the ancestor walk), lengths 1..320 (so some
+sequences hold fewer tokens than their tree), split counts and dtypes as above.
 """
 import numpy as np
 import pytest
@@ -53,6 +56,64 @@ def test_attention_matches_oracle(case):
     q_lat_f32 = gen.bf16_bits_to_f32(q_lat) if x.is_bf16 else q_lat
     want = ref.latent_attention_reference(q_lat_f32, x.f32("q_pe"), x.f32("pool"), x.block_table, x.seq_lens,
                                           softmax_scale=w.softmax_scale, causal=case["causal"])
+    assert not np.isnan(o).any() and not np.isnan(lse).any()
+    assert rel_err(o, want["o_lat"]) <= tol_for(x)
+    assert np.array_equal(np.isneginf(lse), np.isneginf(want["lse"]))
+    fin = np.isfinite(want["lse"])
+    if fin.any():
+        assert rel_err(lse[fin], want["lse"][fin]) <= tol_for(x)
+
+
+@st.composite
+def tree_cases(draw):
+    """Draft trees as parent tables: each node's parent is -1 or an earlier node, with an occasional
+    out-of-range parent (>= j or < -1), which ends that node's ancestor walk."""
+    batch = draw(st.integers(1, 3))
+    q_len = draw(st.sampled_from([1, 3, 8, 17, 64]))
+    parents = []
+    for _ in range(batch):
+        row = []
+        for j in range(q_len):
+            kind = draw(st.integers(0, 9))
+            if kind == 0:
+                row.append(-1)
+            elif kind == 1:
+                row.append(draw(st.sampled_from([j, j + 3, -2, 1000])))  # out of range: a root in effect
+            else:
+                row.append(draw(st.integers(0, j - 1)) if j > 0 else -1)
+        parents.append(row)
+    lens = draw(st.lists(st.integers(1, 5 * 64), min_size=batch, max_size=batch))
+    return dict(batch=batch, q_len=q_len, parents=parents, lens=lens, paged=draw(st.booleans()),
+                splits=draw(st.sampled_from([0, 1, 2, 3, 5])), dtype=draw(st.sampled_from(["bf16", "f32"])),
+                seed=draw(st.integers(0, 2**31 - 1)))
+
+
+@settings(max_examples=30, deadline=None, derandomize=True, suppress_health_check=list(HealthCheck))
+@given(case=tree_cases())
+def test_tree_attention_matches_oracle(case):
+    """mla_decode_attn_tree on drawn trees (lengths may be shorter than the tree) against the oracle
+    run on the same tree with out-of-range parents replaced by -1."""
+    import torch
+    print("[case]", case, flush=True)
+    w = gen.small_workload(case["batch"], case["q_len"], cache_len=1, dtype=case["dtype"], paged=case["paged"])
+    x = gen.generate(w, case["seed"], poison_unused=True, seq_lens=case["lens"])
+    q_lat, _ = gen.generate_latent(w, case["seed"] + 1)
+    parents = np.array(case["parents"], dtype=np.int32).reshape(case["batch"], case["q_len"])
+    d = to_device(x)
+    p = params_for(x, causal=False)
+    o = torch.full((w.batch, w.q_len, 128, 512), float("nan"), device="cuda")
+    lse = torch.full((w.batch, w.q_len, 128), float("nan"), device="cuda")
+    ws_bytes = binding.mla_decode_workspace_bytes(p, case["splits"])
+    ws = torch.empty(max(ws_bytes, 16) // 4, dtype=torch.float32, device="cuda") if ws_bytes else None
+    binding.mla_decode_attn_tree(device_array(q_lat, x.is_bf16), d["q_pe"], d["pool"], d["block_table"],
+                                 d["seq_lens"], torch.from_numpy(parents).cuda(), o, lse, ws, case["splits"], p)
+    torch.cuda.synchronize()
+    o, lse = to_host(o), to_host(lse)
+
+    valid = np.where((parents >= -1) & (parents < np.arange(case["q_len"])[None, :]), parents, -1)
+    q_lat_f32 = gen.bf16_bits_to_f32(q_lat) if x.is_bf16 else q_lat
+    want = ref.latent_attention_reference(q_lat_f32, x.f32("q_pe"), x.f32("pool"), x.block_table, x.seq_lens,
+                                          softmax_scale=w.softmax_scale, tree=valid)
     assert not np.isnan(o).any() and not np.isnan(lse).any()
     assert rel_err(o, want["o_lat"]) <= tol_for(x)
     assert np.array_equal(np.isneginf(lse), np.isneginf(want["lse"]))
