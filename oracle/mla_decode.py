@@ -72,12 +72,13 @@ def tree_ancestors(parents) -> np.ndarray:
     return A
 
 
-def visible_key_index(L: int, S: int, i: int, causal: bool, ancestors: Optional[np.ndarray] = None) -> np.ndarray:
-    """Indices of the keys query token i of S sees.  Without a tree: the first
-    ``visible_keys`` ones.  With a tree (``ancestors`` from ``tree_ancestors``): the committed
-    keys and the new keys of node i's ancestors and itself."""
+def visible_key_index(L: int, S: int, i: int, causal: bool, ancestors: Optional[np.ndarray] = None):
+    """The keys query token i of S sees, as an index into the sequence's rows.  Without a tree:
+    the first ``visible_keys`` ones (a slice, so rows are views, not copies).  With a tree
+    (``ancestors`` from ``tree_ancestors``): an index array of the committed keys and the new keys
+    of node i's ancestors and itself."""
     if ancestors is None:
-        return np.arange(visible_keys(L, S, i, causal))
+        return slice(0, visible_keys(L, S, i, causal))
     base = L - S
     new = [base + j for j in range(S) if ancestors[i, j] and base + j >= 0]
     return np.concatenate([np.arange(max(base, 0)), np.asarray(new, dtype=np.int64)]).astype(np.int64)
@@ -132,7 +133,7 @@ def mla_decode_nonabsorbed(q_nope, q_pe, w_uk, w_uv, pool, block_table, seq_lens
             V = C @ np.asarray(w_uv[h], dtype=np.float64)  # (L, d_h)  v of every cached token
             for i in range(S):
                 idx = visible_key_index(L, S, i, causal, anc)
-                n = idx.size
+                n = idx.stop if isinstance(idx, slice) else idx.size
                 z = softmax_scale * (K[idx] @ q_nope[b, i, h] + R[idx] @ q_pe[b, i, h])
                 p, lse[b, i, h] = _softmax_stats(z)
                 out[b, i, h] = p @ V[idx] if n else 0.0
@@ -199,7 +200,7 @@ def latent_attention_reference(q_lat, q_pe, pool, block_table, seq_lens, *, soft
         anc = None if tree is None else tree_ancestors(tree[b])
         for i in range(S):
             idx = visible_key_index(L, S, i, causal, anc)
-            n = idx.size
+            n = idx.stop if isinstance(idx, slice) else idx.size
             Z = softmax_scale * (C[idx] @ q_lat[b, i].T + R[idx] @ q_pe[b, i].T)  # (n, H): one column per head
             for h in range(H):
                 p, lse[b, i, h] = _softmax_stats(Z[:, h])
