@@ -271,8 +271,10 @@ mla_status mla_rope_append(void* q_pe, const void* kv_a, int32_t kv_a_stride, vo
  * quantised statically, one scale per 128 x 128 block; activations on the fly, one scale per
  * 128-element vector along the reduction dimension. Format E4M3 (bias 7, largest finite 448;
  * the pages name no format). A block's scale is amax / 448 in fp32; a value is coded as
- * x / scale (fp32 division) rounded to the nearest E4M3 value, ties to even. An all-zero block
- * has codes 0. The products accumulate in fp32 per block, then scale. bf16 activations only.
+ * x * (448 / amax) (the factor one fp32 division per block, the product an fp32 multiplication)
+ * rounded to the nearest E4M3 value, ties to even (the hardware conversion, subnormals kept).
+ * An all-zero block has scale 0 and codes 0. The products accumulate in fp32 per block, then
+ * scale. bf16 activations only.
  *
  * Packed weight (mla_fp8_weight_bytes() bytes, 16-byte aligned, owned by the caller): E4M3 codes,
  * H x 512 x 128 bytes (W_UK: (H, 512 c, 128 d) as the weight; W_UV: transposed, (H, 128 v, 512 c)),
