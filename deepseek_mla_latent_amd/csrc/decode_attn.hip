@@ -256,9 +256,16 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
   // accordingly), so the loop reads them with ds_read + readfirstlane.  A global load in the
   // loop would make the compiler drain the vector-memory counter, i.e. wait for the tiles in
   // flight; a scalar load would share the LDS counter and make every operand wait a full drain.
+  // Their loads are issued here and stored to LDS after the query loads below, so the two
+  // round trips overlap; the barrier that hands the buffers to the tiles also publishes them.
   const int npages = (ntok + kPage - 1) / kPage;
-  for (int j = threadIdx.x; j < npages; j += 256) lds_pages[j] = bt[j];
-  __syncthreads();
+  constexpr int kPidPerThread = kMaxSplitPages / 256;
+  int pid[kPidPerThread];
+#pragma unroll
+  for (int k = 0; k < kPidPerThread; ++k) {
+    const int j = threadIdx.x + 256 * k;
+    pid[k] = j < npages ? bt[j] : 0;
+  }
   auto row_of = [&](int t, int page) -> const uint16_t* {  // first token row of tile t
     return pool + ((size_t)page * kPage + (t & 1) * kTile) * kRow;
   };
@@ -299,6 +306,9 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) asm volatile("" ::"v"(q[32 + ks]));
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int k = 0; k < kPidPerThread; ++k)
+      if (threadIdx.x + 256 * k < npages) lds_pages[threadIdx.x + 256 * k] = pid[k];
     const MLA_LDS char* qrowp = smem + wave * 32 * 1024 + l32 * 1024;
 #pragma unroll
     for (int ks = 0; ks < 32; ++ks) q[ks] = lds_read_b128(qrowp + (((2 * ks + hf) ^ (l32 & 15)) * 16));
@@ -324,7 +334,7 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
     if (lane == 0) lds_tree[0] = t_first;
     if (lane == 2 || lane == 3) lds_tree[lane] = 0;
   }
-  __syncthreads();  // every wave has its q: the buffers take the tiles now
+  __syncthreads();  // every wave has its q and the page ids are in LDS: the buffers take the tiles now
   auto prologue_tile = [&](int t) {
     const uint16_t* src = row_of(t, __builtin_amdgcn_readfirstlane(lds_pages[t >> 1]));
     const int cnt = tile_count(t);
