@@ -80,9 +80,11 @@ __global__ __launch_bounds__(128) void linear_kernel(const uint16_t* __restrict_
   MLA_LDS char* lds = (MLA_LDS char*)lds_raw;
 
   const int nblocks = N / 64, mblocks = (M + 32 * MB - 1) / (32 * MB);
-  const int nb = blockIdx.x % nblocks;
-  const int mblk = (blockIdx.x / nblocks) % mblocks;
-  const int split = blockIdx.x / (nblocks * mblocks);
+  // consecutive logical ids share an XCD (and its L2): neighbouring column blocks of one K range
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int nb = bid % nblocks;
+  const int mblk = (bid / nblocks) % mblocks;
+  const int split = bid / (nblocks * mblocks);
   const int n0 = nb * 64, m0 = mblk * 32 * MB;
   const int k0 = split * k_per_split, k1 = min(K, k0 + k_per_split);
   const int nchunks = (k1 - k0) / kChunk;
@@ -122,8 +124,7 @@ __global__ __launch_bounds__(128) void linear_kernel(const uint16_t* __restrict_
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x16{};
   for (int c = 0; c < kLinRing - 1 && c < nchunks; ++c) issue_chunk(c);
-  for (int c = 0; c < nchunks; ++c) {
-    lin_wait<MB>(min(nchunks - 1 - c, kLinRing - 2));
+  auto consume = [&](int c) {
     __syncthreads();  // chunk c is in LDS; every wave is done with chunk c - 1's buffer
     if (c + kLinRing - 1 < nchunks) issue_chunk(c + kLinRing - 1);
     const MLA_LDS char* wb = lds + (c % kLinRing) * kBuf;
@@ -139,6 +140,17 @@ __global__ __launch_bounds__(128) void linear_kernel(const uint16_t* __restrict_
         acc[mb] = mfma32x32x16(af, bf, acc[mb]);
       }
     }
+  };
+  // Steady state: kLinRing - 2 younger chunks stay in flight, a constant wait (a wait chosen per
+  // chunk by a switch put a chain of compares and branches into every iteration: 4% slower).
+  int c = 0;
+  for (; c + kLinRing - 2 < nchunks; ++c) {
+    lin_wait<MB>(kLinRing - 2);
+    consume(c);
+  }
+  for (; c < nchunks; ++c) {  // the last kLinRing - 2 chunks
+    lin_wait<MB>(nchunks - 1 - c);
+    consume(c);
   }
 
   // element e of block mb: column n0 + 32 wave + 8 (e/4) + 4 hf + e%4, row m0 + 32 mb + l32
@@ -183,8 +195,10 @@ int linear_splits(int M, int K, int N, int cus) {
   const int mb = M >= 512 ? 4 : 1;
   const int tiles = ((M + 32 * mb - 1) / (32 * mb)) * (N / 64);
   int s = 1;
-  // about one workgroup per compute unit; keep >= 4 chunks of 64 per split
-  while (tiles * s * 2 <= 2 * cus && (K / (s * 2)) % 64 == 0 && K / (s * 2) >= 256) s *= 2;
+  // the fewest K splits that give at least 7/8 of a workgroup per compute unit (more splits only
+  // add partial traffic and a second workgroup per unit, which measured slower); every split keeps
+  // >= 4 chunks of 64
+  while (8 * tiles * s < 7 * cus && (K / (s * 2)) % 64 == 0 && K / (s * 2) >= 256) s *= 2;
   return s;
 }
 
