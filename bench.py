@@ -6,10 +6,13 @@ One step = one pass of the whole decode path over one batch: mla_absorb_q -> mla
 sequences x 1 query token, 128 heads, d_c 512, d_R 64, d_h 128, 4096 cached tokens each (bf16,
 contiguous cache = identity page table).  Inputs are seeded synthetic data already resident in HBM.
 
-Timing: the three calls of each step are captured in a HIP graph (one graph per input replica);
-`--warmup` untimed replays, then `--steps` timed replays bracketed by torch.cuda.synchronize().
-Replicas rotate so consecutive steps touch disjoint buffers whose total exceeds twice the 256 MB
-Infinity Cache, so cache rows really come from HBM.  Separately, the same steps run eagerly with
+Timing: the three calls of each step go into HIP graphs.  Replicas rotate so consecutive steps
+touch disjoint buffers whose total exceeds twice the 256 MB Infinity Cache, so cache rows really
+come from HBM; the R replicas' steps are captured back to back in one graph (a serving loop
+likewise captures many layers per graph), and `--steps` steps are timed from its replays,
+bracketed by torch.cuda.synchronize(), after about 0.3 s of untimed replays (so the GPU clocks
+have settled) and at least `--warmup` untimed steps.  The same steps
+timed with one graph launch per step are reported beside it (`ms_per_step_one_graph_per_step`).  Separately, the same steps run eagerly with
 HIP events around each call (on the stream the kernels are launched on) to give per-call launch
 durations; the dominant call's algorithmic bytes over that duration is the roofline figure.
 
@@ -156,6 +159,56 @@ def prefill_cpu_baseline(x, target_seconds: float):
                       f"keys), fp64 numpy K/V up-projection + per-head attention, {el:.1f} s"}
 
 
+SETTLE_S = 0.3  # untimed replays before the warm-up steps, in seconds
+
+
+def time_graph_steps(run, reps, steps, warmup):
+    """Time exactly `steps` steps (one call of `run` per replica in turn) replayed from HIP graphs.
+
+    The R replicas' steps are captured back to back in one graph, as a serving loop captures many
+    layers or steps per graph; the timed region replays it steps // R times, then single-step
+    graphs for the remaining steps % R.  For comparison the same number of steps is also timed
+    with one graph launch per step.  Returns (ms per step, ms per step with one graph per step).
+    """
+    import torch
+
+    R = len(reps)
+    multi = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(multi):
+        for d in reps:
+            run(d)
+    singles = []
+    for d in reps:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run(d)
+        singles.append(g)
+    # Keep the GPU busy for SETTLE_S seconds first (untimed): after the host-side set-up its clocks
+    # take longer than a few warm-up steps to settle, and a cold first loop measured up to 12% slow.
+    t_end = time.perf_counter() + SETTLE_S
+    while time.perf_counter() < t_end:
+        for _ in range(4):
+            multi.replay()
+        torch.cuda.synchronize()
+    for _ in range(-(-warmup // R)):
+        multi.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps // R):
+        multi.replay()
+    for k in range(steps % R):
+        singles[k].replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    for k in range(warmup):
+        singles[k % R].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        singles[k % R].replay()
+    torch.cuda.synchronize()
+    return ms, (time.perf_counter() - t0) * 1e3 / steps
+
 def run_prefill(args, dev):
     import numpy as np
     import torch
@@ -203,20 +256,7 @@ def run_prefill(args, dev):
             run(d)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    graphs = []
-    for d in reps:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            run(d)
-        graphs.append(g)
-    for k in range(args.warmup):
-        graphs[k % R].replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        graphs[k % R].replay()
-    torch.cuda.synchronize()
-    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_per_step, ms_single = time_graph_steps(run, reps, args.steps, args.warmup)
 
     stream = torch.cuda.current_stream()
     n_ev = max(10, min(args.steps, 50))
@@ -239,6 +279,7 @@ def run_prefill(args, dev):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "ms_per_step_one_graph_per_step": ms_single,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -247,7 +288,7 @@ def run_prefill(args, dev):
         "config": {"workload": args.workload, "batch": w.batch, "prompt_len": w.q_len,
                    "cache_len": int(x.seq_lens.max()), "heads": w.heads, "kv_lora_rank": w.kv_lora_rank,
                    "rope_dim": w.rope_dim, "head_dim": w.head_dim, "page_size": w.page_size, "causal": True,
-                   "replicas": R, "graph_replay": True},
+                   "replicas": R, "graph_replay": True, "steps_per_graph": R},
         "roofline": roofline_entry("mla_prefill_attn", costs[1], dt, call_us[1] * 1e-6),
         "path_roofline": {"t_roof_us": t_roof * 1e6, "t_step_us": ms_per_step * 1e3,
                           "frac": t_roof / (ms_per_step * 1e-3),
@@ -313,20 +354,7 @@ def run_prepare(args, dev):
             run(d)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    graphs = []
-    for d in reps:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            run(d)
-        graphs.append(g)
-    for k in range(args.warmup):
-        graphs[k % R].replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        graphs[k % R].replay()
-    torch.cuda.synchronize()
-    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_per_step, ms_single = time_graph_steps(run, reps, args.steps, args.warmup)
 
     stream = torch.cuda.current_stream()
     n_ev = max(20, min(args.steps, 200))
@@ -350,6 +378,7 @@ def run_prepare(args, dev):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "ms_per_step_one_graph_per_step": ms_single,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -357,7 +386,7 @@ def run_prepare(args, dev):
         "data": "synthetic (seeded N(0,1) hidden states and cache, N(0,1/d_model) projection weights)",
         "config": {"workload": args.workload, "batch": B, "q_len": S, "cache_len": L, "d_model": D,
                    "projection_out": N, "linear_splits_workspace_bytes": ws_bytes, "replicas": R,
-                   "graph_replay": True},
+                   "graph_replay": True, "steps_per_graph": R},
         "roofline": roofline_entry("mla_linear (fused a-projection)", lin, "bf16", call_us[0] * 1e-6),
         "path_roofline": {"t_roof_us": t_roof * 1e6, "t_step_us": ms_per_step * 1e3,
                           "frac": t_roof / (ms_per_step * 1e-3),
@@ -438,20 +467,7 @@ def run_oproj(args, dev):
             run(d)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    graphs = []
-    for d in reps:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            run(d)
-        graphs.append(g)
-    for k in range(args.warmup):
-        graphs[k % R].replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        graphs[k % R].replay()
-    torch.cuda.synchronize()
-    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_per_step, ms_single = time_graph_steps(run, reps, args.steps, args.warmup)
     stream = torch.cuda.current_stream()
     n_ev = max(20, min(args.steps, 100))
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_ev)]
@@ -469,13 +485,14 @@ def run_oproj(args, dev):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "ms_per_step_one_graph_per_step": ms_single,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) per-head outputs, N(0,1/16384) weights)",
         "config": {"workload": args.workload, "tokens": M, "k": K, "n": N, "workspace_bytes": ws_bytes,
-                   "replicas": R, "graph_replay": True},
+                   "replicas": R, "graph_replay": True, "steps_per_graph": R},
         "roofline": roofline_entry("mla_linear (W_O)", lin, "bf16", call_us * 1e-6),
         "path_roofline": {"t_roof_us": lin.roof_seconds("bf16") * 1e6, "t_step_us": ms_per_step * 1e3,
                           "frac": lin.roof_seconds("bf16") / (ms_per_step * 1e-3)},
@@ -588,7 +605,7 @@ def main():
         d["bufs"].run(d["q_nope"], d["q_pe"], d["w_uk"], d["w_uv"], d["pool"], d["bt"], d["lens"], stream, fp8=fp8,
                       tree_parents=d["tree"])
 
-    # graphs: one per replica, captured after an eager warm-up on a side stream
+    # graphs (captured in time_graph_steps) follow an eager warm-up on a side stream
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -596,22 +613,7 @@ def main():
             run(d)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    graphs = []
-    for d in reps:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            run(d)
-        graphs.append(g)
-
-    for k in range(args.warmup):
-        graphs[k % R].replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        graphs[k % R].replay()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    ms_per_step, ms_single = time_graph_steps(run, reps, args.steps, args.warmup)
 
     # per-call launch durations: eager steps with HIP events on the launch stream
     stream = torch.cuda.current_stream()
@@ -652,6 +654,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "ms_per_step_one_graph_per_step": ms_single,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -660,7 +663,7 @@ def main():
         "config": {"workload": args.workload, "batch": w.batch, "q_len": w.q_len,
                    "cache_len": int(x.seq_lens.max()), "heads": w.heads, "kv_lora_rank": w.kv_lora_rank,
                    "rope_dim": w.rope_dim, "head_dim": w.head_dim, "page_size": w.page_size,
-                   "num_splits": splits, "replicas": R, "graph_replay": True,
+                   "num_splits": splits, "replicas": R, "graph_replay": True, "steps_per_graph": R,
                    "projections": "fp8 block-quantised" if fp8 else dt,
                    **({"draft_tree": "8 nodes, at most 3 children each (seeded)", "mask": "tree"} if tree_wl else {})},
         "roofline": roofline_entry(("mla_decode_attn_tree (tree-masked split attention + LSE merge)" if tree_wl
