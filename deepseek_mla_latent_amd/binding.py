@@ -24,7 +24,7 @@ STATUS = {
     -5: "MLA_ERR_WORKSPACE", -6: "MLA_ERR_UNSUPPORTED", -7: "MLA_ERR_LAUNCH", -8: "MLA_ERR_DEVICE",
 }
 EXPORTS = ("mla_absorb_q", "mla_decode_workspace_bytes", "mla_decode_num_splits", "mla_decode_attn",
-           "mla_decode_attn_tree",
+           "mla_decode_attn_tree", "mla_decode_attn_out_proj_workspace_bytes", "mla_decode_attn_out_proj",
            "mla_out_proj", "mla_prefill_kv_bytes", "mla_prefill_kv_up", "mla_prefill_attn",
            "mla_linear_workspace_bytes", "mla_linear", "mla_rope_append", "mla_fp8_weight_bytes",
            "mla_quantize_w_uk_fp8", "mla_quantize_w_uv_fp8", "mla_absorb_q_fp8", "mla_out_proj_fp8", "mla_status_str")
@@ -101,6 +101,10 @@ def load_library(path: Optional[str] = None):
     lib.mla_decode_attn.restype = i32
     lib.mla_decode_attn_tree.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i32, pp, vp]
     lib.mla_decode_attn_tree.restype = i32
+    lib.mla_decode_attn_out_proj_workspace_bytes.argtypes = [pp, i32]
+    lib.mla_decode_attn_out_proj_workspace_bytes.restype = sz
+    lib.mla_decode_attn_out_proj.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i32, pp, vp]
+    lib.mla_decode_attn_out_proj.restype = i32
     lib.mla_out_proj.argtypes = [vp, vp, vp, pp, vp]
     lib.mla_out_proj.restype = i32
     lib.mla_prefill_kv_bytes.argtypes = [pp]
@@ -210,6 +214,20 @@ def mla_decode_attn_tree(q_lat, q_pe, kv_pool, block_table, seq_lens, tree_paren
                                     _stream(stream)), "mla_decode_attn_tree")
 
 
+def mla_decode_attn_out_proj_workspace_bytes(params: mla_params, num_splits: int = 0) -> int:
+    return int(load_library().mla_decode_attn_out_proj_workspace_bytes(ctypes.byref(params), num_splits))
+
+
+def mla_decode_attn_out_proj(q_lat, q_pe, kv_pool, block_table, seq_lens, tree_parents, w_uv, out, o_lat, lse,
+                             workspace, num_splits: int, params: mla_params, stream=None,
+                             workspace_bytes: Optional[int] = None) -> None:
+    lib = load_library()
+    _check(lib.mla_decode_attn_out_proj(_ptr(q_lat), _ptr(q_pe), _ptr(kv_pool), _ptr(block_table), _ptr(seq_lens),
+                                        _ptr(tree_parents), _ptr(w_uv), _ptr(out), _ptr(o_lat), _ptr(lse),
+                                        _ptr(workspace), _nbytes(workspace, workspace_bytes), num_splits,
+                                        ctypes.byref(params), _stream(stream)), "mla_decode_attn_out_proj")
+
+
 def mla_out_proj(o_lat, w_uv, out, params: mla_params, stream=None) -> None:
     lib = load_library()
     _check(lib.mla_out_proj(_ptr(o_lat), _ptr(w_uv), _ptr(out), ctypes.byref(params), _stream(stream)),
@@ -300,15 +318,26 @@ class DecodeBuffers:
         self.lse = torch.empty((B, S, H), dtype=torch.float32, device=device)
         self.out = torch.empty((B, S, H, params.head_dim), dtype=dt, device=device)
         ws = mla_decode_workspace_bytes(params, num_splits)
+        if params.dtype == MLA_BF16:  # room for the fused route too
+            ws = max(ws, mla_decode_attn_out_proj_workspace_bytes(params, num_splits))
         self.workspace = torch.empty(max(ws, 16) // 4 + 4, dtype=torch.float32, device=device) if ws else None
 
     def run(self, q_nope, q_pe, w_uk, w_uv, kv_pool, block_table, seq_lens, stream=None, fp8: bool = False,
-            tree_parents=None):
+            tree_parents=None, fused: bool = False, latent_outputs: bool = True):
         """The three calls; with ``fp8`` the weights are packed FP8 weights and the two projections
         run block-quantised (mla_absorb_q_fp8 / mla_out_proj_fp8); with ``tree_parents`` (B, S)
-        int32 the attention is the tree-masked verify (mla_decode_attn_tree)."""
+        int32 the attention is the tree-masked verify (mla_decode_attn_tree).  With ``fused`` (bf16
+        weights) the attention and the out-projection are one call, mla_decode_attn_out_proj, which
+        writes o_lat and lse only with ``latent_outputs``."""
         p = self.params
         (mla_absorb_q_fp8 if fp8 else mla_absorb_q)(q_nope, w_uk, self.q_lat, p, stream)
+        if fused:
+            if fp8:
+                raise ValueError("the fused attention + out-projection takes bf16 W_UV")
+            mla_decode_attn_out_proj(self.q_lat, q_pe, kv_pool, block_table, seq_lens, tree_parents, w_uv, self.out,
+                                     self.o_lat if latent_outputs else None, self.lse if latent_outputs else None,
+                                     self.workspace, self.num_splits, p, stream)
+            return self.out
         if tree_parents is None:
             mla_decode_attn(self.q_lat, q_pe, kv_pool, block_table, seq_lens, self.o_lat, self.lse, self.workspace,
                             self.num_splits, p, stream)

@@ -82,6 +82,20 @@ size_t workspace_for(const mla_params* p, int splits) {
   return n * mla::kDc * part_elem_bytes(p) + n * sizeof(float);
 }
 
+// mla_decode_attn_out_proj: with at least one 16-row block of query rows the merge runs inside the
+// W_UV kernel, which reads bf16 partials (one split included).  With fewer rows most of that
+// kernel's lanes would idle while each walks every split, so the call takes the separate merge and
+// out-projection instead, with o_lat in the workspace after the partials when the caller wants none.
+bool merge_in_out_proj(const mla_params* p) { return tokens_of(p) >= 16; }
+
+size_t fused_workspace_for(const mla_params* p, int splits) {
+  if (merge_in_out_proj(p)) {
+    const size_t n = (size_t)tokens_of(p) * (splits < 1 ? 1 : splits) * mla::kHeads;
+    return n * mla::kDc * 2 + n * sizeof(float);
+  }
+  return workspace_for(p, splits) + (size_t)tokens_of(p) * mla::kHeads * mla::kDc * sizeof(float);
+}
+
 // Prefill buffer: [K_nope | V] (B, H, Lp, 256) then k_pe (B, Lp, 64), bf16, Lp = max_pages * page.
 size_t prefill_kv_bytes(const mla_params* p) {
   const size_t Lp = (size_t)p->max_pages_per_seq * mla::kPage;
@@ -112,7 +126,7 @@ const char* mla_status_str(mla_status s) {
     case MLA_OK: return "MLA_OK";
     case MLA_ERR_NULL: return "MLA_ERR_NULL: a required pointer is NULL";
     case MLA_ERR_SHAPE: return "MLA_ERR_SHAPE: a size is out of range";
-    case MLA_ERR_DTYPE: return "MLA_ERR_DTYPE: dtype must be MLA_F32 or MLA_BF16";
+    case MLA_ERR_DTYPE: return "MLA_ERR_DTYPE: dtype not supported by this call (MLA_F32 or MLA_BF16; prefill and the fused decode call: MLA_BF16 only)";
     case MLA_ERR_ALIGN: return "MLA_ERR_ALIGN: pointers must be 16-byte aligned";
     case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace too small";
     case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: only H=128, d_c=512, d_R=64, d_h=128, page 64";
@@ -153,19 +167,25 @@ size_t mla_decode_workspace_bytes(const mla_params* p, int32_t num_splits) {
 namespace {
 
 // mla_decode_attn and mla_decode_attn_tree: `tree_parents` null = the causal / full rule of p.
+// With w_uv and out (the fused route): the split partials are merged and projected by W_UV in one
+// kernel; o_lat and lse are then optional outputs.
 mla_status decode_attn_impl(const void* q_lat, const void* q_pe, const void* kv_pool, const int32_t* block_table,
                             const int32_t* seq_lens, const int32_t* tree_parents, float* o_lat, float* lse,
                             void* workspace, size_t workspace_bytes, int32_t num_splits, const mla_params* p,
-                            void* stream) {
+                            void* stream, const void* w_uv = nullptr, void* out = nullptr) {
+  const bool fused = w_uv != nullptr || out != nullptr;
   mla_status st = check_params(p);
   if (st != MLA_OK) return st;
   if (num_splits < 0) return MLA_ERR_SHAPE;
   const int max_pages = (p->max_seq_len + mla::kPage - 1) / mla::kPage;
   if (p->max_pages_per_seq < max_pages) return MLA_ERR_SHAPE;
+  if (fused && p->dtype != MLA_BF16) return MLA_ERR_DTYPE;
   if (tokens_of(p) == 0) return MLA_OK;
-  if (!q_lat || !q_pe || !seq_lens || !o_lat) return MLA_ERR_NULL;
+  if (!q_lat || !q_pe || !seq_lens || (!fused && !o_lat)) return MLA_ERR_NULL;
+  if (fused && (!w_uv || !out)) return MLA_ERR_NULL;
   if (max_pages > 0 && (!kv_pool || !block_table)) return MLA_ERR_NULL;
   if (!aligned16(q_lat) || !aligned16(q_pe) || !aligned16(kv_pool) || !aligned16(o_lat)) return MLA_ERR_ALIGN;
+  if (fused && (!aligned16(w_uv) || !aligned16(out))) return MLA_ERR_ALIGN;
   // the kernels take a tile's maximum before scaling: the scale must be positive
   if (!std::isfinite(p->softmax_scale) || !(p->softmax_scale > 0.f)) return MLA_ERR_SHAPE;
   const int cus = num_splits > 0 ? 1 : cu_count();
@@ -173,11 +193,21 @@ mla_status decode_attn_impl(const void* q_lat, const void* q_pe, const void* kv_
   const SplitPlan plan = plan_splits(p, num_splits, cus);
   const int64_t grid = tokens_of(p) * plan.splits * (p->dtype == MLA_BF16 ? 1 : mla::kHeads);
   if (grid > 0x7fffffffLL) return MLA_ERR_SHAPE;
-  const size_t need = workspace_for(p, plan.splits);
+  const size_t need = fused ? fused_workspace_for(p, plan.splits) : workspace_for(p, plan.splits);
+  const bool merge_in_proj = fused && merge_in_out_proj(p);
   if (need > 0) {
     if (!workspace) return MLA_ERR_NULL;
     if (workspace_bytes < need) return MLA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return MLA_ERR_ALIGN;
+  }
+  if (fused && !merge_in_proj) {  // the separate merge and out-projection, o_lat maybe in the workspace
+    float* o = o_lat ? o_lat : (float*)((char*)workspace + workspace_for(p, plan.splits));
+    st = decode_attn_impl(q_lat, q_pe, kv_pool, block_table, seq_lens, tree_parents, o, lse, workspace,
+                          workspace_bytes, num_splits, p, stream);
+    if (st != MLA_OK) return st;
+    if (mla::launch_out_proj(o, w_uv, out, (int)tokens_of(p), true, (hipStream_t)stream) != hipSuccess)
+      return MLA_ERR_LAUNCH;
+    return MLA_OK;
   }
 
   mla::AttnArgs a;
@@ -198,7 +228,7 @@ mla_status decode_attn_impl(const void* q_lat, const void* q_pe, const void* kv_
   a.scale_log2 = (float)((double)p->softmax_scale * 1.4426950408889634);
   const int rows = (int)tokens_of(p);
   hipStream_t s = (hipStream_t)stream;
-  if (plan.splits == 1) {
+  if (plan.splits == 1 && !merge_in_proj) {
     a.o_out = o_lat;
     a.lse_out = lse;
     a.final_out = 1;
@@ -211,6 +241,11 @@ mla_status decode_attn_impl(const void* q_lat, const void* q_pe, const void* kv_
   a.lse_out = lse_part;
   a.final_out = 0;
   if (mla::launch_decode_attn(a, rows, s) != hipSuccess) return MLA_ERR_LAUNCH;
+  if (merge_in_proj) {
+    if (mla::launch_merge_out_proj(o_part, lse_part, w_uv, out, o_lat, lse, rows, plan.splits, s) != hipSuccess)
+      return MLA_ERR_LAUNCH;
+    return MLA_OK;
+  }
   if (mla::launch_lse_merge(o_part, p->dtype == MLA_BF16, lse_part, o_lat, lse, rows, plan.splits, s) != hipSuccess)
     return MLA_ERR_LAUNCH;
   return MLA_OK;
@@ -237,6 +272,24 @@ mla_status mla_decode_attn_tree(const void* q_lat, const void* q_pe, const void*
   if (tokens_of(p) > 0 && !tree_parents) return MLA_ERR_NULL;
   return decode_attn_impl(q_lat, q_pe, kv_pool, block_table, seq_lens, tree_parents, o_lat, lse, workspace,
                           workspace_bytes, num_splits, p, stream);
+}
+
+size_t mla_decode_attn_out_proj_workspace_bytes(const mla_params* p, int32_t num_splits) {
+  const int32_t s = mla_decode_num_splits(p, num_splits);
+  return s > 0 ? fused_workspace_for(p, s) : 0;
+}
+
+mla_status mla_decode_attn_out_proj(const void* q_lat, const void* q_pe, const void* kv_pool,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    const int32_t* tree_parents, const void* w_uv, void* out, float* o_lat,
+                                    float* lse, void* workspace, size_t workspace_bytes, int32_t num_splits,
+                                    const mla_params* p, void* stream) {
+  mla_status st = check_params(p);
+  if (st != MLA_OK) return st;
+  if (tree_parents && p->q_len > 64) return MLA_ERR_SHAPE;  // one 64-bit visibility mask per query row
+  if (!w_uv || !out) return tokens_of(p) == 0 ? MLA_OK : MLA_ERR_NULL;
+  return decode_attn_impl(q_lat, q_pe, kv_pool, block_table, seq_lens, tree_parents, o_lat, lse, workspace,
+                          workspace_bytes, num_splits, p, stream, w_uv, out);
 }
 
 mla_status mla_out_proj(const float* o_lat, const void* w_uv, void* out, const mla_params* p, void* stream) {

@@ -10,6 +10,9 @@
  *                    reduced to a latent output o_lat = sum_j p_j c_j, plus its log-sum-exp
  *   mla_out_proj     out = W_UV^T o_lat      per head (values are never built)
  *
+ * mla_decode_attn_out_proj does the last two in one call (the split merge inside the W_UV
+ * kernel, so o_lat need not pass through memory; bf16 only).
+ *
  * The method: "DeepSeek-V2的推理成本如何计算？" (izhida.com), answer "专家" — W_K is applied
  * transposed to q and W_V after the latent attention-weighted average, so neither K nor V is
  * computed; RoPE is a separate key shared by all heads whose score is added to the latent
@@ -53,7 +56,7 @@ typedef enum {
   MLA_OK = 0,
   MLA_ERR_NULL = -1,        /* a required pointer is NULL */
   MLA_ERR_SHAPE = -2,       /* a size is out of range (batch < 0, q_len < 1, tables too small ...) */
-  MLA_ERR_DTYPE = -3,       /* dtype is not MLA_F32 or MLA_BF16 (prefill: not MLA_BF16) */
+  MLA_ERR_DTYPE = -3,       /* dtype is not MLA_F32 or MLA_BF16 (prefill, fused decode: not MLA_BF16) */
   MLA_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
   MLA_ERR_WORKSPACE = -5,   /* workspace / kv buffer smaller than its _bytes() query */
   MLA_ERR_UNSUPPORTED = -6, /* head dims / page size other than the supported set */
@@ -159,6 +162,43 @@ mla_status mla_decode_attn_tree(const void* q_lat, const void* q_pe, const void*
  */
 mla_status mla_out_proj(const float* o_lat, const void* w_uv, void* out, const mla_params* p,
                         void* stream);
+
+/*
+ * Workspace bytes of mla_decode_attn_out_proj for this p and split request (0 for an invalid p),
+ * with k = mla_decode_num_splits(p, num_splits): B * S * k * H * (d_c * 2 + 4) when B * S >= 16
+ * (bf16 split partials, one split included); for fewer query rows the call runs the separate
+ * merge and out-projection, and the workspace is mla_decode_workspace_bytes(p, num_splits) plus
+ * B * S * H * d_c * 4 bytes for o_lat.
+ */
+size_t mla_decode_attn_out_proj_workspace_bytes(const mla_params* p, int32_t num_splits);
+
+/*
+ * mla_decode_attn followed by mla_out_proj in two launches: the split attention, then the
+ * log-sum-exp merge of its partials fused with the W_UV product, so the merged latent output
+ * need not round-trip through memory. bf16 only (MLA_F32 gives MLA_ERR_DTYPE).
+ *   tree_parents (B,S) int32 or NULL  NULL: the causal / full rule of p (as mla_decode_attn);
+ *                                     otherwise the draft-tree rule of mla_decode_attn_tree
+ *                                     (q_len > 64 gives MLA_ERR_SHAPE)
+ *   w_uv  (H,d_c,d_h) bf16            value up-projection, head-major
+ *   out   (B,S,H,d_h) bf16 (out)      per-head attention output (before W_O)
+ *   o_lat (B,S,H,d_c) fp32 (out, may be NULL)  the merged latent output
+ *   lse   (B,S,H)     fp32 (out, may be NULL)
+ *   workspace / workspace_bytes       at least mla_decode_attn_out_proj_workspace_bytes(p,
+ *                                     num_splits); contents are scratch
+ * The other arguments are as for mla_decode_attn. With B * S >= 16 the partials are bf16 (as in
+ * mla_decode_attn with more than one split) also for a single split, and the merge runs in fp32
+ * inside the W_UV kernel; with fewer rows (where that kernel would leave most lanes idle) the call
+ * makes exactly the launches of mla_decode_attn followed by mla_out_proj, with o_lat in the
+ * workspace when o_lat is NULL. Errors as for mla_decode_attn / mla_decode_attn_tree, plus
+ * MLA_ERR_NULL for a NULL w_uv or out (with B*S > 0).
+ * Cites: absorption note §三.2 steps 1-2 (the latent weighted sum, then W_V after it); izhida
+ * answer "专家" (W_V applied after the latent average).
+ */
+mla_status mla_decode_attn_out_proj(const void* q_lat, const void* q_pe, const void* kv_pool,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    const int32_t* tree_parents, const void* w_uv, void* out, float* o_lat,
+                                    float* lse, void* workspace, size_t workspace_bytes, int32_t num_splits,
+                                    const mla_params* p, void* stream);
 
 /*
  * ---- Prefill in multi-head form ("order 1") --------------------------------------------------

@@ -104,6 +104,35 @@ def test_tree_attention_errors():
     assert _tree(P(q_len=4, batch=0), parents=None) == 0  # empty batch: nothing to do
 
 
+def _fused(params, ptrs=None, parents=None, ws=FAKE, ws_bytes=1 << 30, splits=2):
+    p = dict(q_lat=FAKE, q_pe=FAKE, pool=FAKE, bt=FAKE, lens=FAKE, w_uv=FAKE, out=FAKE, o=None, lse=None)
+    p.update(ptrs or {})
+    return lib.mla_decode_attn_out_proj(p["q_lat"], p["q_pe"], p["pool"], p["bt"], p["lens"], parents, p["w_uv"],
+                                        p["out"], p["o"], p["lse"], ws, ws_bytes, splits, ctypes.byref(params), None)
+
+
+def test_fused_attention_out_proj_errors():
+    row = 128 * (512 * 2 + 4)  # one split's bf16 partial rows and lse values of one query row
+    olat = 128 * 512 * 4  # one query row of o_lat
+    ws = lambda params, k: lib.mla_decode_attn_out_proj_workspace_bytes(ctypes.byref(params), k)  # noqa: E731
+    assert ws(P(batch=16), 2) == 16 * 2 * row  # merge inside the W_UV kernel
+    assert ws(P(batch=16), 1) == 16 * row  # one split: partials too
+    assert ws(P(), 2) == 2 * 2 * row + 2 * olat  # two rows: separate merge, o_lat in the workspace
+    assert ws(P(), 1) == 2 * olat
+    assert _fused(P(batch=16), ws_bytes=16 * 2 * row - 4) == -5
+    assert _fused(P(dtype=binding.MLA_F32)) == -3  # bf16 only
+    assert _fused(P(), {"w_uv": None}) == -1
+    assert _fused(P(), {"out": None}) == -1
+    assert _fused(P(), {"q_lat": None}) == -1
+    assert _fused(P(), {"out": MISALIGNED}) == -4
+    assert _fused(P(), {"o": MISALIGNED}) == -4  # the latent outputs are optional, aligned when given
+    assert _fused(P(q_len=65), parents=FAKE) == -2
+    assert _fused(P(softmax_scale=-1.0)) == -2
+    assert _fused(P(), ws_bytes=2 * 2 * row + 2 * olat - 4) == -5
+    assert _fused(P(), ws=None, ws_bytes=0, splits=1) == -1
+    assert _fused(P(batch=0), {"w_uv": None}) == 0  # empty batch: nothing to do
+
+
 def test_split_planning_is_page_aligned():
     # explicit requests are clamped to the page count and trimmed of empty trailing splits
     for L, req, want in [(300, 2, 2), (300, 5, 5), (300, 9, 5), (64, 4, 1), (4096, 8, 8), (4096, 7, 7),

@@ -1,0 +1,171 @@
+"""GPU parity of the fused attention + out-projection (mla_decode_attn_out_proj) against the fp64
+oracle: out = W_UV^T o_lat with (o_lat, lse) the latent attention over the visible keys.
+
+Bar as for the separate calls: max |gpu - ref| / max |ref| <= 2e-2 per output tensor (bf16); lse
+within the same bound of max |lse| where finite and -inf exactly where the oracle has it.  Unused
+cache slots hold NaN, so a read outside the sequences shows up as NaN.  The optional latent outputs
+must not change `out`, which is checked bit for bit.
+"""
+import numpy as np
+import pytest
+
+from deepseek_mla_latent_amd import binding
+from deepseek_mla_latent_amd import inputs as gen
+from oracle import mla_decode as ref
+from tests.helpers import device_array, params_for, rel_err, to_device, to_host, tol_for
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _run_fused(x, q_lat_bits, splits, causal=True, parents=None, latent=True):
+    import torch
+    d = to_device(x)
+    p = params_for(x, causal=causal)
+    w = x.workload
+    q_lat = device_array(q_lat_bits, True)
+    par = None if parents is None else torch.from_numpy(np.ascontiguousarray(parents, dtype=np.int32)).cuda()
+    out = torch.full((w.batch, w.q_len, 128, 128), float("nan"), device="cuda").to(torch.bfloat16)
+    o = torch.full((w.batch, w.q_len, 128, 512), float("nan"), device="cuda") if latent else None
+    lse = torch.full((w.batch, w.q_len, 128), float("nan"), device="cuda") if latent else None
+    ws_bytes = binding.mla_decode_attn_out_proj_workspace_bytes(p, splits)
+    ws = torch.full((ws_bytes // 4,), float("nan"), device="cuda")
+    binding.mla_decode_attn_out_proj(q_lat, d["q_pe"], d["pool"], d["block_table"], d["seq_lens"], par, d["w_uv"],
+                                     out, o, lse, ws, splits, p)
+    torch.cuda.synchronize()
+    return to_host(out), (to_host(o) if latent else None), (to_host(lse) if latent else None)
+
+
+def _check(x, q_lat_bits, splits, causal=True, parents=None):
+    out, o, lse = _run_fused(x, q_lat_bits, splits, causal, parents)
+    want = ref.latent_attention_reference(gen.bf16_bits_to_f32(q_lat_bits), x.f32("q_pe"), x.f32("pool"),
+                                          x.block_table, x.seq_lens, softmax_scale=x.workload.softmax_scale,
+                                          causal=causal, tree=parents)
+    want_out = ref.out_proj_reference(want["o_lat"], x.f32("w_uv"))
+    for name, got in (("out", out), ("o_lat", o), ("lse", lse)):
+        assert not np.isnan(got).any(), name
+    errs = {"out": rel_err(out, want_out), "o_lat": rel_err(o, want["o_lat"])}
+    say("  rel errs", errs)
+    for k, e in errs.items():
+        assert e <= tol_for(x), k
+    assert np.array_equal(np.isneginf(lse), np.isneginf(want["lse"]))
+    fin = np.isfinite(want["lse"])
+    if fin.any():
+        assert rel_err(lse[fin], want["lse"][fin]) <= tol_for(x)
+    bare, _, _ = _run_fused(x, q_lat_bits, splits, causal, parents, latent=False)
+    assert np.array_equal(bare, out)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 0])
+def test_fused_ragged_paged(splits):
+    say("fused ragged paged, splits", splits)
+    w = gen.small_workload(3, 1, ragged=(1, 300), dtype="bf16", paged=True)
+    x = gen.generate(w, 7, poison_unused=True)
+    q_lat, _ = gen.generate_latent(w, 8)
+    _check(x, q_lat, splits)
+
+
+def test_fused_edge_lengths():
+    """Empty (out 0, lse -inf), single-token, page-boundary and off-by-one lengths."""
+    lens = [0, 1, 63, 64, 65, 128, 129, 2]
+    w = gen.small_workload(len(lens), 1, cache_len=1, dtype="bf16", paged=True)
+    x = gen.generate(w, 11, poison_unused=True, seq_lens=lens)
+    q_lat, _ = gen.generate_latent(w, 12)
+    for splits in (1, 2, 0):
+        say("fused edge lengths", lens, "splits", splits)
+        _check(x, q_lat, splits)
+
+
+@pytest.mark.parametrize("B,S,causal", [(5, 1, True), (3, 7, True), (3, 2, False), (17, 1, True)])
+def test_fused_row_blocks(B, S, causal):
+    """Row counts that do not fill the 16-row blocks of the merge (5, 21, 6, 17 rows)."""
+    say("fused rows", B * S, "causal", causal)
+    w = gen.small_workload(B, S, ragged=(S, 200), dtype="bf16", paged=True)
+    x = gen.generate(w, 30 + B, poison_unused=True)
+    q_lat, _ = gen.generate_latent(w, 31 + B)
+    _check(x, q_lat, 0, causal)
+    _check(x, q_lat, 2, causal)
+
+
+def test_fused_many_splits():
+    """More splits than the two batches of four the merge keeps in flight (24 two-page and 47
+    one-page ranges)."""
+    lens = [3000, 2500]
+    w = gen.small_workload(len(lens), 1, cache_len=1, dtype="bf16", paged=True)
+    x = gen.generate(w, 51, poison_unused=True, seq_lens=lens)
+    q_lat, _ = gen.generate_latent(w, 52)
+    for splits in (24, 47):
+        say("fused splits", splits)
+        _check(x, q_lat, splits)
+
+
+@pytest.mark.parametrize("S,splits", [(8, 0), (8, 3), (64, 1)])
+def test_fused_tree(S, splits):
+    say("fused tree S", S, "splits", splits)
+    lens = [S + 100, 70, max(S - 1, 1)]
+    w = gen.small_workload(len(lens), S, cache_len=1, dtype="bf16", paged=True)
+    x = gen.generate(w, 60 + S, poison_unused=True, seq_lens=lens)
+    q_lat, _ = gen.generate_latent(w, 61 + S)
+    parents = gen.draft_trees(len(lens), S, 62 + S)
+    _check(x, q_lat, splits, causal=False, parents=parents)
+
+
+def test_fused_step_full_size_sampled():
+    """The whole fused step (absorb -> attention + merge + W_UV) at batch 32 x 4096 cached tokens
+    against the non-absorbed oracle on sampled sequences and heads."""
+    import torch
+    x = gen.generate_named("b32_t4096", poison_unused=True)
+    seqs, heads = [0, 13, 31], [0, 37, 64, 127]
+    say("fused full size", seqs, heads)
+    d = to_device(x)
+    p = params_for(x)
+    bufs = binding.DecodeBuffers(p, 0)
+    bufs.run(d["q_nope"], d["q_pe"], d["w_uk"], d["w_uv"], d["pool"], d["block_table"], d["seq_lens"], fused=True)
+    torch.cuda.synchronize()
+    w = x.workload
+    r = ref.mla_decode_nonabsorbed(x.f32("q_nope"), x.f32("q_pe"), x.f32("w_uk"), x.f32("w_uv"), x.f32("pool"),
+                                   x.block_table, x.seq_lens, softmax_scale=w.softmax_scale, seqs=seqs, heads=heads)
+    sel = np.ix_(seqs, range(w.q_len), heads)
+    errs = {k: rel_err(to_host(getattr(bufs, k))[sel], r[k][sel]) for k in ("o_lat", "out")}
+    say("  rel errs", errs)
+    for k, e in errs.items():
+        assert e <= tol_for(x), k
+    assert not torch.isnan(bufs.out).any().item()
+
+
+def test_fused_graph_replays_match_eager():
+    """The fused step captured in a HIP graph: every replay equals the eager result bit for bit,
+    with eager work and synchronisations between the replays."""
+    import torch
+    w = gen.small_workload(4, 1, ragged=(64, 700), dtype="bf16", paged=True)
+    x = gen.generate(w, 71, poison_unused=True)
+    d = to_device(x)
+    p = params_for(x)
+    bufs = binding.DecodeBuffers(p, 0)
+
+    def run():
+        bufs.run(d["q_nope"], d["q_pe"], d["w_uk"], d["w_uv"], d["pool"], d["block_table"], d["seq_lens"],
+                 fused=True, latent_outputs=False)
+
+    run()
+    torch.cuda.synchronize()
+    eager = bufs.out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for k in range(3):
+        bufs.out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        say("  replay", k)
+        assert torch.equal(bufs.out, eager)
+        run()
+        torch.cuda.synchronize()
