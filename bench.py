@@ -1,12 +1,14 @@
 #!/usr/bin/env python3
 """Absorbed-MLA decode throughput on one MI355X.
 
-One step = one pass of the whole decode path over one batch: mla_absorb_q -> mla_decode_attn
-(split-K attention + log-sum-exp merge) -> mla_out_proj, for one layer.  Default workload: batch 32
+One step = one pass of the whole decode path over one batch, for one layer: with bf16 weights
+mla_absorb_q -> mla_decode_attn_out_proj (split-K attention, then the log-sum-exp merge of the
+splits fused with W_UV); with fp32, FP8 projections or --unfused mla_absorb_q -> mla_decode_attn
+(split-K attention + merge) -> mla_out_proj.  Default workload: batch 32
 sequences x 1 query token, 128 heads, d_c 512, d_R 64, d_h 128, 4096 cached tokens each (bf16,
 contiguous cache = identity page table).  Inputs are seeded synthetic data already resident in HBM.
 
-Timing: the three calls of each step go into HIP graphs.  Replicas rotate so consecutive steps
+Timing: the calls of each step go into HIP graphs.  Replicas rotate so consecutive steps
 touch disjoint buffers whose total exceeds twice the 256 MB Infinity Cache, so cache rows really
 come from HBM; the R replicas' steps are captured back to back in one graph (a serving loop
 likewise captures many layers per graph), and `--steps` steps are timed from its replays,
@@ -47,7 +49,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_attn_b32_t4096_hbm_counters.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "deepseek_mla_latent_amd", "csrc", f) for f in ("decode_attn.hip", "common.h")]
+KERNEL_SOURCES = [os.path.join(ROOT, "deepseek_mla_latent_amd", "csrc", f)
+                  for f in ("decode_attn.hip", "projections.hip", "common.h")]
 METRIC = "MLA absorbed-decode tokens/s per layer + % of HBM/MFMA roofline, 1 GPU"
 PREFILL_METRIC = "MLA prefill (multi-head form) prompt tokens/s per layer + % of MFMA roofline, 1 GPU"
 PREPARE_METRIC = "MLA step before attention (fused a-projection + RoPE + AppendKV) tokens/s per layer + % of HBM roofline, 1 GPU"
@@ -71,7 +74,7 @@ def _source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(launch_bytes_key: str, workload: str):
+def measured_traffic(launch_bytes_key: str, workload: str, route=None):
     """HBM bytes per launch from committed rocprofv3 counters, if taken on this workload and on the
     current kernel source."""
     try:
@@ -79,6 +82,8 @@ def measured_traffic(launch_bytes_key: str, workload: str):
     except (OSError, ValueError):
         return None
     if rec.get("kernel_source_sha256_16") != _source_hash() or rec.get("workload") != workload:
+        return None
+    if route is not None and rec.get("route") != route:
         return None
     return rec.get(launch_bytes_key)
 
@@ -525,6 +530,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough to exceed 2x the 256 MB MALL")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="bf16: run mla_decode_attn and mla_out_proj as two calls instead of mla_decode_attn_out_proj")
     ap.add_argument("--fp8-projections", action="store_true",
                     help="decode: run the two per-head projections FP8 block-quantised (bf16 workloads)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -566,7 +573,9 @@ def main():
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(a).to(dev)
 
-    costs = accounting.path_costs(x.seq_lens, w.q_len, dt, tree=parents)
+    fp8 = bool(args.fp8_projections)
+    fused = x.is_bf16 and not fp8 and not args.unfused  # attention + merge/W_UV in one call
+    costs = accounting.path_costs(x.seq_lens, w.q_len, dt, tree=parents, fused=fused)
     per_replica = sum(c.bytes for c in costs)
     R = args.replicas or max(2, math.ceil(2 * MALL_BYTES / per_replica) + 1)
 
@@ -589,7 +598,6 @@ def main():
         d["bufs"] = binding.DecodeBuffers(params, args.num_splits, device=dev)
         reps.append(d)
 
-    fp8 = bool(args.fp8_projections)
     if fp8:
         assert x.is_bf16, "FP8 projections take bf16 activations"
         for d in reps:  # static weight quantisation, once, outside the timed steps
@@ -603,7 +611,7 @@ def main():
 
     def run(d, stream=None):
         d["bufs"].run(d["q_nope"], d["q_pe"], d["w_uk"], d["w_uv"], d["pool"], d["bt"], d["lens"], stream, fp8=fp8,
-                      tree_parents=d["tree"])
+                      tree_parents=d["tree"], fused=fused, latent_outputs=False)
 
     # graphs (captured in time_graph_steps) follow an eager warm-up on a side stream
     side = torch.cuda.Stream()
@@ -618,7 +626,8 @@ def main():
     # per-call launch durations: eager steps with HIP events on the launch stream
     stream = torch.cuda.current_stream()
     n_ev = max(20, min(args.steps, 200))
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_ev)]
+    ncalls = len(costs)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(ncalls + 1)] for _ in range(n_ev)]
     for k in range(min(R, 4)):
         run(reps[k % R])
     torch.cuda.synchronize()
@@ -629,6 +638,11 @@ def main():
         e[0].record(stream)
         (binding.mla_absorb_q_fp8 if fp8 else binding.mla_absorb_q)(d["q_nope"], d["w_uk"], p.q_lat, params)
         e[1].record(stream)
+        if fused:
+            binding.mla_decode_attn_out_proj(p.q_lat, d["q_pe"], d["pool"], d["bt"], d["lens"], d["tree"], d["w_uv"],
+                                             p.out, None, None, p.workspace, args.num_splits, params)
+            e[2].record(stream)
+            continue
         if tree_wl:
             binding.mla_decode_attn_tree(p.q_lat, d["q_pe"], d["pool"], d["bt"], d["lens"], d["tree"], p.o_lat, p.lse,
                                          p.workspace, args.num_splits, params)
@@ -639,12 +653,20 @@ def main():
         (binding.mla_out_proj_fp8 if fp8 else binding.mla_out_proj)(p.o_lat, d["w_uv"], p.out, params)
         e[3].record(stream)
     torch.cuda.synchronize()
-    call_us = [float(np.mean([evs[k][j].elapsed_time(evs[k][j + 1]) for k in range(n_ev)])) * 1e3 for j in range(3)]
+    call_us = [float(np.mean([evs[k][j].elapsed_time(evs[k][j + 1]) for k in range(n_ev)])) * 1e3
+               for j in range(ncalls)]
 
     tokens = w.batch * w.q_len
     attn = costs[1]
     attn_s = call_us[1] * 1e-6
-    traffic = measured_traffic("hbm_bytes_per_launch", args.workload)
+    route = "fused" if fused else ("fp8" if fp8 else "three calls")
+    traffic = measured_traffic("hbm_bytes_per_launch", args.workload, route)
+    if fused:
+        kernel = ("mla_decode_attn_out_proj with a draft-tree mask (split attention + merge/W_UV)" if tree_wl
+                  else "mla_decode_attn_out_proj (split attention + merge/W_UV)")
+    else:
+        kernel = ("mla_decode_attn_tree (tree-masked split attention + LSE merge)" if tree_wl
+                  else "mla_decode_attn (split attention + LSE merge)")
     t_roof = sum(c.roof_seconds(dt) for c in costs)
     rec = {
         "metric": METRIC,
@@ -665,9 +687,10 @@ def main():
                    "rope_dim": w.rope_dim, "head_dim": w.head_dim, "page_size": w.page_size,
                    "num_splits": splits, "replicas": R, "graph_replay": True, "steps_per_graph": R,
                    "projections": "fp8 block-quantised" if fp8 else dt,
+                   "route": ("absorb -> attention + merge/W_UV (2 calls)" if fused
+                             else "absorb -> attention + merge -> out-proj (3 calls)"),
                    **({"draft_tree": "8 nodes, at most 3 children each (seeded)", "mask": "tree"} if tree_wl else {})},
-        "roofline": roofline_entry(("mla_decode_attn_tree (tree-masked split attention + LSE merge)" if tree_wl
-                                    else "mla_decode_attn (split attention + LSE merge)"), attn, dt, attn_s, traffic),
+        "roofline": roofline_entry(kernel, attn, dt, attn_s, traffic),
         "path_roofline": {"t_roof_us": t_roof * 1e6, "t_step_us": ms_per_step * 1e3,
                           "frac": t_roof / (ms_per_step * 1e-3),
                           "calls_us": dict(zip([c.name for c in costs], call_us)),

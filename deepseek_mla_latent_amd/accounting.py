@@ -73,7 +73,10 @@ def visible_pairs(seq_lens: Sequence[int], q_len: int, causal: bool = True, tree
 
 def path_costs(seq_lens: Sequence[int], q_len: int, dtype: str, *, heads: int = 128, d_c: int = 512,
                d_r: int = 64, d_h: int = 128, page: int = 64, causal: bool = True, fp8_projections: bool = False,
-               tree=None):
+               tree=None, fused: bool = False):
+    """Algorithmic bytes and FLOPs of each call of one decode step.  With ``fused`` the attention
+    and the out-projection are one call (mla_decode_attn_out_proj, without the optional latent
+    outputs): its bytes are the attention's reads plus W_UV and the output."""
     e = 2 if dtype == "bf16" else 4
     ew = 1 if fp8_projections else e  # weight element bytes (FP8 codes; scales added below)
     wsc = heads * (d_c // 128) * 4 if fp8_projections else 0
@@ -90,6 +93,10 @@ def path_costs(seq_lens: Sequence[int], q_len: int, dtype: str, *, heads: int = 
         attn = CallCost(attn.name, attn.bytes + T * 4, attn.flops)  # plus the parent table
     out = CallCost("mla_out_proj", heads * d_c * d_h * ew + wsc + T * heads * d_c * 4 + T * heads * d_h * e,
                    2 * T * heads * d_c * d_h)
+    if fused:
+        reads = attn.bytes - T * heads * (d_c + 1) * 4  # no o_lat / lse written
+        return [absorb, CallCost("mla_decode_attn_out_proj", reads + heads * d_c * d_h * e + T * heads * d_h * e,
+                                 attn.flops + out.flops)]
     return [absorb, attn, out]
 
 

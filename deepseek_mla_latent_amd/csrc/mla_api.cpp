@@ -82,15 +82,16 @@ size_t workspace_for(const mla_params* p, int splits) {
   return n * mla::kDc * part_elem_bytes(p) + n * sizeof(float);
 }
 
-// mla_decode_attn_out_proj: with at least one 16-row block of query rows the merge runs inside the
-// W_UV kernel, which reads bf16 partials (one split included).  With fewer rows most of that
-// kernel's lanes would idle while each walks every split, so the call takes the separate merge and
-// out-projection instead, with o_lat in the workspace after the partials when the caller wants none.
-bool merge_in_out_proj(const mla_params* p) { return tokens_of(p) >= 16; }
+// mla_decode_attn_out_proj: with at least one 16-row block of query rows and more than one split,
+// the merge runs inside the W_UV kernel, which reads the bf16 partials.  With fewer rows most of
+// that kernel's lanes would idle while each walks every split, and with one split there is no
+// merge to save (the attention writes o_lat itself), so the call then takes the separate kernels,
+// with o_lat in the workspace after any partials when the caller wants none.
+bool merge_in_out_proj(const mla_params* p, int splits) { return tokens_of(p) >= 16 && splits > 1; }
 
 size_t fused_workspace_for(const mla_params* p, int splits) {
-  if (merge_in_out_proj(p)) {
-    const size_t n = (size_t)tokens_of(p) * (splits < 1 ? 1 : splits) * mla::kHeads;
+  if (merge_in_out_proj(p, splits)) {
+    const size_t n = (size_t)tokens_of(p) * splits * mla::kHeads;
     return n * mla::kDc * 2 + n * sizeof(float);
   }
   return workspace_for(p, splits) + (size_t)tokens_of(p) * mla::kHeads * mla::kDc * sizeof(float);
@@ -194,7 +195,7 @@ mla_status decode_attn_impl(const void* q_lat, const void* q_pe, const void* kv_
   const int64_t grid = tokens_of(p) * plan.splits * (p->dtype == MLA_BF16 ? 1 : mla::kHeads);
   if (grid > 0x7fffffffLL) return MLA_ERR_SHAPE;
   const size_t need = fused ? fused_workspace_for(p, plan.splits) : workspace_for(p, plan.splits);
-  const bool merge_in_proj = fused && merge_in_out_proj(p);
+  const bool merge_in_proj = fused && merge_in_out_proj(p, plan.splits);
   if (need > 0) {
     if (!workspace) return MLA_ERR_NULL;
     if (workspace_bytes < need) return MLA_ERR_WORKSPACE;

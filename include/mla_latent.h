@@ -165,10 +165,9 @@ mla_status mla_out_proj(const float* o_lat, const void* w_uv, void* out, const m
 
 /*
  * Workspace bytes of mla_decode_attn_out_proj for this p and split request (0 for an invalid p),
- * with k = mla_decode_num_splits(p, num_splits): B * S * k * H * (d_c * 2 + 4) when B * S >= 16
- * (bf16 split partials, one split included); for fewer query rows the call runs the separate
- * merge and out-projection, and the workspace is mla_decode_workspace_bytes(p, num_splits) plus
- * B * S * H * d_c * 4 bytes for o_lat.
+ * with k = mla_decode_num_splits(p, num_splits): B * S * k * H * (d_c * 2 + 4) (the bf16 split
+ * partials) when B * S >= 16 and k > 1; otherwise the call runs the separate kernels, and the
+ * workspace is mla_decode_workspace_bytes(p, num_splits) plus B * S * H * d_c * 4 bytes for o_lat.
  */
 size_t mla_decode_attn_out_proj_workspace_bytes(const mla_params* p, int32_t num_splits);
 
@@ -185,11 +184,11 @@ size_t mla_decode_attn_out_proj_workspace_bytes(const mla_params* p, int32_t num
  *   lse   (B,S,H)     fp32 (out, may be NULL)
  *   workspace / workspace_bytes       at least mla_decode_attn_out_proj_workspace_bytes(p,
  *                                     num_splits); contents are scratch
- * The other arguments are as for mla_decode_attn. With B * S >= 16 the partials are bf16 (as in
- * mla_decode_attn with more than one split) also for a single split, and the merge runs in fp32
- * inside the W_UV kernel; with fewer rows (where that kernel would leave most lanes idle) the call
- * makes exactly the launches of mla_decode_attn followed by mla_out_proj, with o_lat in the
- * workspace when o_lat is NULL. Errors as for mla_decode_attn / mla_decode_attn_tree, plus
+ * The other arguments are as for mla_decode_attn. With B * S >= 16 query rows and more than one
+ * split the merge of the bf16 partials runs in fp32 inside the W_UV kernel; otherwise (fewer rows
+ * would leave most of that kernel's lanes idle, and one split has no merge to save) the call makes
+ * exactly the launches of mla_decode_attn followed by mla_out_proj, with o_lat in the workspace
+ * when o_lat is NULL. Errors as for mla_decode_attn / mla_decode_attn_tree, plus
  * MLA_ERR_NULL for a NULL w_uv or out (with B*S > 0).
  * Cites: absorption note §三.2 steps 1-2 (the latent weighted sum, then W_V after it); izhida
  * answer "专家" (W_V applied after the latent average).

@@ -116,7 +116,7 @@ def test_fused_attention_out_proj_errors():
     olat = 128 * 512 * 4  # one query row of o_lat
     ws = lambda params, k: lib.mla_decode_attn_out_proj_workspace_bytes(ctypes.byref(params), k)  # noqa: E731
     assert ws(P(batch=16), 2) == 16 * 2 * row  # merge inside the W_UV kernel
-    assert ws(P(batch=16), 1) == 16 * row  # one split: partials too
+    assert ws(P(batch=16), 1) == 16 * olat  # one split: the separate kernels, o_lat in the workspace
     assert ws(P(), 2) == 2 * 2 * row + 2 * olat  # two rows: separate merge, o_lat in the workspace
     assert ws(P(), 1) == 2 * olat
     assert _fused(P(batch=16), ws_bytes=16 * 2 * row - 4) == -5

@@ -68,6 +68,17 @@ def test_fused_ragged_paged(splits):
     _check(x, q_lat, splits)
 
 
+def test_fused_routes():
+    """Which kernels run: the merge inside the W_UV kernel needs 16 query rows and two splits."""
+    mk = lambda B: binding.make_params(batch=B, q_len=1, max_seq_len=300, softmax_scale=0.1,  # noqa: E731
+                                       dtype=binding.MLA_BF16)
+    ws = binding.mla_decode_attn_out_proj_workspace_bytes
+    olat = 128 * 512 * 4
+    assert ws(mk(16), 2) == 16 * 2 * 128 * (512 * 2 + 4)
+    assert ws(mk(16), 1) == 16 * olat
+    assert ws(mk(15), 2) == binding.mla_decode_workspace_bytes(mk(15), 2) + 15 * olat
+
+
 def test_fused_edge_lengths():
     """Empty (out 0, lse -inf), single-token, page-boundary and off-by-one lengths."""
     lens = [0, 1, 63, 64, 65, 128, 129, 2]
@@ -92,8 +103,8 @@ def test_fused_row_blocks(B, S, causal):
 
 def test_fused_many_splits():
     """More splits than the two batches of four the merge keeps in flight (24 two-page and 47
-    one-page ranges)."""
-    lens = [3000, 2500]
+    one-page ranges), over one full 16-row block, so the merge runs inside the W_UV kernel."""
+    lens = [3000, 2500] + [1200 + 97 * i for i in range(14)]
     w = gen.small_workload(len(lens), 1, cache_len=1, dtype="bf16", paged=True)
     x = gen.generate(w, 51, poison_unused=True, seq_lens=lens)
     q_lat, _ = gen.generate_latent(w, 52)
