@@ -8,6 +8,9 @@ max |gpu - ref| / max |ref| <= 2e-2 (bf16) or 1e-4 (fp32) on o_lat and lse.
 Drawn for tree-masked verify: batch 1..3, trees of 1, 3, 8, 17 or 64 nodes with random parents
 (several roots, and parents out of range, which end the ancestor walk), lengths 1..320 (so some
 sequences hold fewer tokens than their tree), split counts and dtypes as above.
+Drawn for the fused attention + out-projection (bf16): batch 1..24 and S in {1, 2, 3}, so both of
+its routes run; split counts up to 9; the causal / full rule or a drawn draft tree; the optional
+latent outputs on or off.
 """
 import numpy as np
 import pytest
@@ -120,3 +123,55 @@ def test_tree_attention_matches_oracle(case):
     fin = np.isfinite(want["lse"])
     if fin.any():
         assert rel_err(lse[fin], want["lse"][fin]) <= tol_for(x)
+
+
+@st.composite
+def fused_cases(draw):
+    batch = draw(st.integers(1, 24))
+    q_len = draw(st.sampled_from([1, 2, 3]))
+    lens = draw(st.lists(st.integers(q_len, 5 * 64), min_size=batch, max_size=batch))
+    tree = draw(st.booleans())
+    parents = [[draw(st.integers(-1, j - 1)) for j in range(q_len)] for _ in range(batch)] if tree else None
+    return dict(batch=batch, q_len=q_len, lens=lens, paged=draw(st.booleans()), causal=draw(st.booleans()),
+                parents=parents, splits=draw(st.sampled_from([0, 1, 2, 3, 5, 9])), latent=draw(st.booleans()),
+                seed=draw(st.integers(0, 2**31 - 1)))
+
+
+@settings(max_examples=30, deadline=None, derandomize=True, suppress_health_check=list(HealthCheck))
+@given(case=fused_cases())
+def test_fused_attention_out_proj_matches_oracle(case):
+    """mla_decode_attn_out_proj (bf16) on drawn batches, on both of its routes (fewer or more than
+    16 query rows; one or several splits), with or without a draft tree and the latent outputs:
+    out against W_UV^T of the oracle's latent attention, o_lat and lse when asked for."""
+    import torch
+    print("[case]", case, flush=True)
+    w = gen.small_workload(case["batch"], case["q_len"], cache_len=1, dtype="bf16", paged=case["paged"])
+    x = gen.generate(w, case["seed"], poison_unused=True, seq_lens=case["lens"])
+    q_lat, _ = gen.generate_latent(w, case["seed"] + 1)
+    d = to_device(x)
+    p = params_for(x, causal=case["causal"])
+    parents = None if case["parents"] is None else np.array(case["parents"], dtype=np.int32)
+    out = torch.full((w.batch, w.q_len, 128, 128), float("nan"), device="cuda").to(torch.bfloat16)
+    o = torch.full((w.batch, w.q_len, 128, 512), float("nan"), device="cuda") if case["latent"] else None
+    lse = torch.full((w.batch, w.q_len, 128), float("nan"), device="cuda") if case["latent"] else None
+    ws_bytes = binding.mla_decode_attn_out_proj_workspace_bytes(p, case["splits"])
+    ws = torch.full((max(ws_bytes, 16) // 4,), float("nan"), device="cuda")
+    binding.mla_decode_attn_out_proj(device_array(q_lat, True), d["q_pe"], d["pool"], d["block_table"],
+                                     d["seq_lens"], None if parents is None else torch.from_numpy(parents).cuda(),
+                                     d["w_uv"], out, o, lse, ws, case["splits"], p)
+    torch.cuda.synchronize()
+
+    want = ref.latent_attention_reference(gen.bf16_bits_to_f32(q_lat), x.f32("q_pe"), x.f32("pool"), x.block_table,
+                                          x.seq_lens, softmax_scale=w.softmax_scale, causal=case["causal"],
+                                          tree=parents)
+    got = to_host(out)
+    assert not np.isnan(got).any()
+    assert rel_err(got, ref.out_proj_reference(want["o_lat"], x.f32("w_uv"))) <= tol_for(x)
+    if case["latent"]:
+        o, lse = to_host(o), to_host(lse)
+        assert not np.isnan(o).any() and not np.isnan(lse).any()
+        assert rel_err(o, want["o_lat"]) <= tol_for(x)
+        assert np.array_equal(np.isneginf(lse), np.isneginf(want["lse"]))
+        fin = np.isfinite(want["lse"])
+        if fin.any():
+            assert rel_err(lse[fin], want["lse"][fin]) <= tol_for(x)
