@@ -245,14 +245,16 @@ __global__ __launch_bounds__(256, 1) void out_proj_bf16_kernel(const float* __re
 // a round trip through HBM (it is written only when asked for).  Merging is "【笔记】MLA矩阵吸收分析"
 // §三.2 step 1 over key ranges, the projection its step 2.
 //
-// Workgroup = (head h, block of 16 rows); the blocks of one head have consecutive logical ids (one
-// XCD, so W_UV[h] comes from HBM once).  Wave w owns latent rows [128 w, +128):
-//   * its 32 KiB slice of W_UV[h] goes to LDS first (direct-to-LDS, 4 rows of 256 B per load);
-//   * lane l merges row l % 16 at latent 128 w + 32 ks + 8 (l / 16) + j (ks < 4, j < 8): exactly
+// Workgroup = (head h, block of 16 rows), 8 waves (two per SIMD); the blocks of one head have
+// consecutive logical ids (one XCD, so W_UV[h] comes from HBM once).  Wave w owns latent rows
+// [64 w, +64), so each wave's loads (2 batches of 4 splits' partials and lse, 16 W loads) stay
+// within the 63 the vector-memory counter tracks and go out in one round trip:
+//   * its 16 KiB slice of W_UV[h] goes to LDS (direct-to-LDS, 4 rows of 256 B per load);
+//   * lane l merges row l % 16 at latent 64 w + 32 ks + 8 (l / 16) + j (ks < 2, j < 8): exactly
 //     the B operand of a 16x16x32 MFMA, so the merged values never leave the lane.  They are split
 //     into hi + lo bf16 (two MFMAs, about 16 mantissa bits of the fp32 merge kept);
-//   * D(16 values x 16 rows) for the 8 value blocks over its 128 latent rows, A = W_UV^T by
-//     transposed LDS reads; the four waves' partial sums meet in LDS.
+//   * D(16 values x 16 rows) for the 8 value blocks over its 64 latent rows, A = W_UV^T by
+//     transposed LDS reads; the eight waves' partial sums meet in LDS.
 // LDS row c of a wave's slice holds 32-byte block b (16 values) at block b ^ fsw(c) with
 // fsw(c) = (c & 3) | ((c >> 3) & 1) << 2: a transposed read covers 16 rows x 32 B, which this puts
 // on every bank pair exactly twice.
@@ -263,7 +265,7 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-__global__ __launch_bounds__(256, 1) void merge_out_proj_kernel(const uint16_t* __restrict__ o_part,
+__global__ __launch_bounds__(512, 1) void merge_out_proj_kernel(const uint16_t* __restrict__ o_part,
                                                                 const float* __restrict__ lse_part,
                                                                 const uint16_t* __restrict__ w_uv,
                                                                 uint16_t* __restrict__ out, float* __restrict__ o_lat,
@@ -275,8 +277,8 @@ __global__ __launch_bounds__(256, 1) void merge_out_proj_kernel(const uint16_t* 
   const int h = id / nblk, r0 = (id % nblk) * kMopRows;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, g = lane >> 4, s16 = lane & 15;
-  const int c0 = 128 * wave;
-  MLA_LDS char* const ws = wl + wave * (128 * kDh * 2);  // this wave's 128 rows x 256 B
+  const int c0 = 64 * wave;
+  MLA_LDS char* const ws = wl + wave * (64 * kDh * 2);  // this wave's 64 rows x 256 B
 
   // merge: row n = r0 + s16 (a row past the end reads row r0, which exists, and stores nothing)
   const int n = r0 + s16 < rows ? r0 + s16 : r0;
@@ -285,7 +287,7 @@ __global__ __launch_bounds__(256, 1) void merge_out_proj_kernel(const uint16_t* 
   const uint16_t* op = o_part + base * kDc + c0 + 8 * g;  // + 32 ks
   // Batches of 4 splits (a split past the end repeats the last one with weight 0), two in flight.
   struct Batch {
-    u32x4 x[4][4];  // [split][ks]
+    u32x4 x[4][2];  // [split][ks]
     float l[4];
   };
   auto load = [&](int kb, Batch& bt) {
@@ -294,18 +296,18 @@ __global__ __launch_bounds__(256, 1) void merge_out_proj_kernel(const uint16_t* 
       const int k = kb + j < num_splits ? kb + j : num_splits - 1;
       bt.l[j] = kb + j < num_splits ? lp[(size_t)k * kHeads] : -INFINITY;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) bt.x[j][ks] = *(const u32x4*)(op + (size_t)k * kHeads * kDc + 32 * ks);
+      for (int ks = 0; ks < 2; ++ks) bt.x[j][ks] = *(const u32x4*)(op + (size_t)k * kHeads * kDc + 32 * ks);
     }
   };
   Batch b0, b1;
   load(0, b0);
   if (4 < num_splits) load(4, b1);
-  // W_UV[h] rows [c0, c0 + 128) after the first partials, so waiting for those does not wait for
+  // W_UV[h] rows [c0, c0 + 64) after the first partials, so waiting for those does not wait for
   // W: load i covers local rows 4 i .. 4 i + 3 (16 lanes each)
   {
     const char* src = (const char*)(w_uv + ((size_t)h * kDc + c0) * kDh);
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
+    for (int i = 0; i < 16; ++i) {
       const int c = 4 * i + g, u = s16;
       const int us = 2 * ((u >> 1) ^ mop_swz(c)) + (u & 1);
       __builtin_amdgcn_global_load_lds((const MLA_GLOBAL void*)(src + (size_t)c * kDh * 2 + us * 16),
@@ -316,9 +318,9 @@ __global__ __launch_bounds__(256, 1) void merge_out_proj_kernel(const uint16_t* 
   // Running log-sum-exp merge: weights are taken against the largest lse seen so far, and the
   // sums are rescaled when a batch raises it (an empty split has lse = -inf and weight 0).
   constexpr float kLog2e = 1.4426950408889634f;
-  f32x4 acc_o[8];  // latent 32 ks + 8 g + 4 e2 + e in acc_o[2 ks + e2][e]
+  f32x4 acc_o[4];  // latent 32 ks + 8 g + 4 e2 + e in acc_o[2 ks + e2][e]
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc_o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < 4; ++i) acc_o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY, sum = 0.f;
   auto consume = [&](const Batch& bt) {
     const float m_new = fmaxf(fmaxf(m, fmaxf(bt.l[0], bt.l[1])), fmaxf(bt.l[2], bt.l[3]));
@@ -326,13 +328,13 @@ __global__ __launch_bounds__(256, 1) void merge_out_proj_kernel(const uint16_t* 
     m = m_new;
     sum *= scale;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc_o[i] *= scale;
+    for (int i = 0; i < 4; ++i) acc_o[i] *= scale;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float w = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((bt.l[j] - m) * kLog2e);
       sum += w;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
+      for (int ks = 0; ks < 2; ++ks) {
         const u32x4 u = bt.x[j][ks];
         acc_o[2 * ks] += w * f32x4{__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xffff0000u),
                                    __uint_as_float(u[1] << 16), __uint_as_float(u[1] & 0xffff0000u)};
@@ -351,9 +353,9 @@ __global__ __launch_bounds__(256, 1) void merge_out_proj_kernel(const uint16_t* 
   }
   const float inv = sum > 0.f ? 1.0f / sum : 0.f;
   const bool live = r0 + s16 < rows;
-  bf16x8 bh[4], bl[4];
+  bf16x8 bh[2], bl[2];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
+  for (int ks = 0; ks < 2; ++ks) {
     const f32x4 a = acc_o[2 * ks] * inv, b = acc_o[2 * ks + 1] * inv;
     if (o_lat && live) {
       f32x4* dst = (f32x4*)(o_lat + ((size_t)n * kHeads + h) * kDc + c0 + 32 * ks + 8 * g);
@@ -383,7 +385,7 @@ __global__ __launch_bounds__(256, 1) void merge_out_proj_kernel(const uint16_t* 
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
+  for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
       const MLA_LDS char* p = a_row + ks * 32 * (kDh * 2) + ((mb ^ fsw) * 32);
@@ -395,9 +397,9 @@ __global__ __launch_bounds__(256, 1) void merge_out_proj_kernel(const uint16_t* 
       acc[mb] = mfma16x16x32(av, bl[ks], acc[mb]);
     }
 
-  // The four waves' partial sums meet in LDS (over the W slices, once every wave is done with
+  // The eight waves' partial sums meet in LDS (over the W slices, once every wave is done with
   // them): red[((w * 8 + mb) * 4 + i) * 64 + lane], element i of lane l being value 16 mb + 4 g + i
-  // of row s16.  Wave w then adds value blocks 2 w and 2 w + 1.
+  // of row s16.  Wave w then adds value block w.
   __syncthreads();
   MLA_LDS float* red = (MLA_LDS float*)wl;
 #pragma unroll
@@ -405,14 +407,16 @@ __global__ __launch_bounds__(256, 1) void merge_out_proj_kernel(const uint16_t* 
 #pragma unroll
     for (int i = 0; i < 4; ++i) red[((wave * 8 + mb) * 4 + i) * 64 + lane] = acc[mb][i];
   __syncthreads();
-#pragma unroll
-  for (int mm = 0; mm < 2; ++mm) {
-    const int mb = 2 * wave + mm;
+  {
+    const int mb = wave;
     float sv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      sv[i] = red[((0 * 8 + mb) * 4 + i) * 64 + lane] + red[((1 * 8 + mb) * 4 + i) * 64 + lane] +
-              red[((2 * 8 + mb) * 4 + i) * 64 + lane] + red[((3 * 8 + mb) * 4 + i) * 64 + lane];
+    for (int i = 0; i < 4; ++i) {
+      float t = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < 8; ++ww) t += red[((ww * 8 + mb) * 4 + i) * 64 + lane];
+      sv[i] = t;
+    }
     if (live) {
       const u32x2 pk = {pack_bf16x2(sv[0], sv[1]), pack_bf16x2(sv[2], sv[3])};
       *(u32x2*)(out + ((size_t)n * kHeads + h) * kDh + 16 * mb + 4 * g) = pk;
@@ -496,7 +500,7 @@ hipError_t launch_merge_out_proj(const void* o_part, const float* lse_part, cons
   forget_stale_error();
   const int64_t grid = (int64_t)kHeads * ((rows + kMopRows - 1) / kMopRows);
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(merge_out_proj_kernel, dim3((unsigned)grid), dim3(256), 0, stream, (const uint16_t*)o_part,
+  hipLaunchKernelGGL(merge_out_proj_kernel, dim3((unsigned)grid), dim3(512), 0, stream, (const uint16_t*)o_part,
                      lse_part, (const uint16_t*)w_uv, (uint16_t*)out, o_lat, lse, rows, num_splits);
   return hipGetLastError();
 }
