@@ -23,76 +23,109 @@ __device__ __forceinline__ void settle(const T& x) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// absorb: grid (4 latent blocks of 128, 128 heads), 4 waves; wave w owns 32 latent rows
+// absorb, fp32: grid (4 latent blocks of 128, 128 heads), 4 waves; wave w owns 32 latent rows
 // c in [128 bx + 32 w, +32).  D(c x tokens) = W_UK[h] rows (A, straight from global) x q_nope^T
-// (B).  Columns of D belong to single tokens, so a token slot past the end reads a valid row
-// (token 0) and its column is simply not stored.
-template <bool BF16>
-__global__ __launch_bounds__(256) void absorb_q_kernel(const void* __restrict__ q_nope,
-                                                       const void* __restrict__ w_uk, void* __restrict__ q_lat,
-                                                       int tokens) {
+// (B) on fp32 MFMAs.  Columns of D belong to single tokens, so a token slot past the end reads a
+// valid row (token 0) and its column is simply not stored.
+__global__ __launch_bounds__(256) void absorb_q_f32_kernel(const void* __restrict__ q_nope,
+                                                           const void* __restrict__ w_uk,
+                                                           void* __restrict__ q_lat, int tokens) {
   const int h = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hf = lane >> 5;
   const int c_base = 128 * blockIdx.x + 32 * wave;
   const size_t wrow = ((size_t)h * kDc + c_base + l32) * kDh;
-  if constexpr (BF16) {
-    // A: lane holds W[c_base + l32][16 ks + 8 hf .. +7]
-    bf16x8 aw[8];
-    const bf16x8* W = (const bf16x8*)((const uint16_t*)w_uk + wrow + 8 * hf);
+  // fp32: k step (m, j) pairs lane half hf with d = 8 m + 4 hf + j (a float4 per m).
+  f32x4 aw[16];
+  const f32x4* W = (const f32x4*)((const float*)w_uk + wrow + 4 * hf);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) aw[ks] = W[2 * ks];
-    for (int nb = 0; nb * 32 < tokens; ++nb) {
-      const int n = 32 * nb + l32;
-      const bool ok = n < tokens;
-      const bf16x8* Q = (const bf16x8*)((const uint16_t*)q_nope + ((size_t)(ok ? n : 0) * kHeads + h) * kDh + 8 * hf);
-      bf16x8 bq[8];
+  for (int m = 0; m < 16; ++m) aw[m] = W[2 * m];
+  for (int nb = 0; nb * 32 < tokens; ++nb) {
+    const int n = 32 * nb + l32;
+    const bool ok = n < tokens;
+    const f32x4* Q = (const f32x4*)((const float*)q_nope + ((size_t)(ok ? n : 0) * kHeads + h) * kDh + 4 * hf);
+    f32x4 bq[16];
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) bq[ks] = Q[2 * ks];
+    for (int m = 0; m < 16; ++m) bq[m] = Q[2 * m];
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) settle(bq[ks]);
-      f32x16 acc;
+    for (int m = 0; m < 16; ++m) settle(bq[m]);
+    f32x16 acc;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) acc = mfma32x32x16(aw[ks], bq[ks], acc);
-      if (ok) {  // element e: latent c_base + (e/4)*8 + 4 hf + e%4 of token n
-        uint16_t* dst = (uint16_t*)q_lat + ((size_t)n * kHeads + h) * kDc + c_base + 4 * hf;
+    for (int m = 0; m < 16; ++m)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          uint2 v = {pack_bf16x2(acc[4 * g], acc[4 * g + 1]), pack_bf16x2(acc[4 * g + 2], acc[4 * g + 3])};
-          *(uint2*)(dst + 8 * g) = v;
-        }
-      }
+      for (int j = 0; j < 4; ++j) acc = mfma32x32x2f32(aw[m][j], bq[m][j], acc);
+    if (ok) {
+      float* dst = (float*)q_lat + ((size_t)n * kHeads + h) * kDc + c_base + 4 * hf;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *(f32x4*)(dst + 8 * g) = f32x4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
     }
-  } else {
-    // fp32: k step (m, j) pairs lane half hf with d = 8 m + 4 hf + j (a float4 per m).
-    f32x4 aw[16];
-    const f32x4* W = (const f32x4*)((const float*)w_uk + wrow + 4 * hf);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// absorb, bf16: grid (4 latent blocks of 128, 128 heads), 4 waves; wave w owns latent rows
+// c in [128 bx + 32 w, +32).  Its W_UK rows and each 32-token block's q_nope rows reach LDS by
+// 1 KiB direct-to-LDS loads (4 rows of 256 B; 16-byte unit u of row r stored at u ^ (r & 15)), so
+// every global read covers whole cache lines and q_nope is read once per workgroup, not per wave.
+// D(c x tokens) = W_UK[h] rows (A) x q_nope^T (B); the block's 32 x 128 outputs leave through LDS
+// as whole 256-byte rows.  A token slot past the end reads token 0 and is not stored.
+__global__ __launch_bounds__(256) void absorb_q_bf16_kernel(const uint16_t* __restrict__ q_nope,
+                                                            const uint16_t* __restrict__ w_uk,
+                                                            uint16_t* __restrict__ q_lat, int tokens) {
+  __shared__ __attribute__((aligned(1024))) char w_lds[128 * 256];  // the workgroup's 128 W rows
+  __shared__ __attribute__((aligned(1024))) char q_lds[32 * 256];   // one token block of q_nope
+  __shared__ __attribute__((aligned(1024))) char o_lds[32 * 256];   // its 32 x 128 outputs
+  const int h = blockIdx.y, cb = 128 * blockIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, l32 = lane & 31, hf = lane >> 5, r16 = lane >> 4, u16 = lane & 15;
+  {  // this wave's 32 W rows: load i covers rows 4 i .. 4 i + 3
+    const char* src = (const char*)(w_uk + ((size_t)h * kDc + cb + 32 * wave) * kDh);
 #pragma unroll
-    for (int m = 0; m < 16; ++m) aw[m] = W[2 * m];
-    for (int nb = 0; nb * 32 < tokens; ++nb) {
-      const int n = 32 * nb + l32;
-      const bool ok = n < tokens;
-      const f32x4* Q = (const f32x4*)((const float*)q_nope + ((size_t)(ok ? n : 0) * kHeads + h) * kDh + 4 * hf);
-      f32x4 bq[16];
-#pragma unroll
-      for (int m = 0; m < 16; ++m) bq[m] = Q[2 * m];
-#pragma unroll
-      for (int m = 0; m < 16; ++m) settle(bq[m]);
-      f32x16 acc;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[e] = 0.f;
-#pragma unroll
-      for (int m = 0; m < 16; ++m)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc = mfma32x32x2f32(aw[m][j], bq[m][j], acc);
-      if (ok) {
-        float* dst = (float*)q_lat + ((size_t)n * kHeads + h) * kDc + c_base + 4 * hf;
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          *(f32x4*)(dst + 8 * g) = f32x4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
-      }
+    for (int i = 0; i < 8; ++i) {
+      const int r = 4 * i + r16;
+      __builtin_amdgcn_global_load_lds((const MLA_GLOBAL void*)(src + r * 256 + ((u16 ^ (r & 15)) * 16)),
+                                       (MLA_LDS void*)(w_lds + (32 * wave + 4 * i) * 256), 16, 0, 0);
     }
+  }
+  for (int nb = 0; nb * 32 < tokens; ++nb) {
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {  // token rows 4 j .. 4 j + 3 of the block, two loads per wave
+      const int t = 4 * (2 * wave + jj) + r16;
+      const int n = 32 * nb + t < tokens ? 32 * nb + t : 0;
+      const char* src = (const char*)(q_nope + ((size_t)n * kHeads + h) * kDh);
+      __builtin_amdgcn_global_load_lds((const MLA_GLOBAL void*)(src + ((u16 ^ (t & 15)) * 16)),
+                                       (MLA_LDS void*)(q_lds + 4 * (2 * wave + jj) * 256), 16, 0, 0);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's W rows and q rows have landed
+    __syncthreads();                                  // every wave's q rows
+    f32x16 acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const int u = (2 * ks + hf) ^ (l32 & 15);
+      const bf16x8 aw = *(const MLA_LDS bf16x8*)(w_lds + (32 * wave + l32) * 256 + u * 16);
+      const bf16x8 bq = *(const MLA_LDS bf16x8*)(q_lds + l32 * 256 + u * 16);
+      acc = mfma32x32x16(aw, bq, acc);
+    }
+    // element e: latent 32 w + (e/4)*8 + 4 hf + e%4 (of the block's 128) of token l32: 8 bytes at
+    // 16-byte unit 4 w + e/4, half hf, of the token's 256-byte staging row
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const u32x2 v = {pack_bf16x2(acc[4 * g], acc[4 * g + 1]), pack_bf16x2(acc[4 * g + 2], acc[4 * g + 3])};
+      *(MLA_LDS u32x2*)(o_lds + l32 * 256 + (((4 * wave + g) ^ (l32 & 15)) * 16) + hf * 8) = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {  // token rows 4 j .. 4 j + 3, 16 lanes (256 B) per row
+      const int t = 4 * (2 * wave + jj) + r16;
+      const int n = 32 * nb + t;
+      const u32x4 v = *(const MLA_LDS u32x4*)(o_lds + t * 256 + ((u16 ^ (t & 15)) * 16));
+      if (n < tokens) *(u32x4*)(q_lat + ((size_t)n * kHeads + h) * kDc + cb + 8 * u16) = v;
+    }
+    __syncthreads();  // the block's q and output rows are read before the next block reuses them
   }
 }
 
@@ -489,9 +522,10 @@ hipError_t launch_absorb_q(const void* q_nope, const void* w_uk, void* q_lat, in
   forget_stale_error();
   const dim3 grid(kDc / 128, kHeads);
   if (bf16)
-    hipLaunchKernelGGL(absorb_q_kernel<true>, grid, dim3(256), 0, stream, q_nope, w_uk, q_lat, tokens);
+    hipLaunchKernelGGL(absorb_q_bf16_kernel, grid, dim3(256), 0, stream, (const uint16_t*)q_nope,
+                       (const uint16_t*)w_uk, (uint16_t*)q_lat, tokens);
   else
-    hipLaunchKernelGGL(absorb_q_kernel<false>, grid, dim3(256), 0, stream, q_nope, w_uk, q_lat, tokens);
+    hipLaunchKernelGGL(absorb_q_f32_kernel, grid, dim3(256), 0, stream, q_nope, w_uk, q_lat, tokens);
   return hipGetLastError();
 }
 
