@@ -157,11 +157,18 @@ __global__ __launch_bounds__(256, 1) void kv_up_kernel(const uint16_t* __restric
     return {count, nv, 0, pool};
   };
   // one page: 64 latent rows of 1 KiB, all issued by wave 0; LDS position q of row t gets unit
-  // q ^ (t & 15)
-  auto issue_page = [&](const Page& pg, int buf) {
+  // q ^ (t & 15).  Rows [t0, t1) at a time: the vector-memory counter tracks at most 63 loads, and
+  // a 64th would hold wave 0 at its issue until the first returned, so the next page goes out in
+  // three parts spread over the current page's MFMAs.
+  auto issue_rows = [&](const Page& pg, int buf, int t0, int t1) {
 #pragma unroll
-    for (int t = 0; t < kPage; ++t)
+    for (int t = t0; t < t1; ++t)
       dma16(pg.rows, (uint32_t)(t * kRow * 2 + ((lane ^ (t & 15)) << 4)), lds_u32(lds + buf * kPageBytes + t * 1024));
+  };
+  auto issue_page = [&](const Page& pg, int buf) {
+    issue_rows(pg, buf, 0, 32);
+    issue_rows(pg, buf, 32, 63);
+    issue_rows(pg, buf, 63, 64);
   };
   const int b_off[2] = {(l32 * 1024), ((32 + l32) * 1024)};  // this lane's token rows (tb = 0, 1)
 
@@ -202,11 +209,9 @@ __global__ __launch_bounds__(256, 1) void kv_up_kernel(const uint16_t* __restric
     if (wave == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this page (wave 0 stores nothing)
     __syncthreads();  // page in LDS; the other buffer is free; the previous results are staged
     const Page next = find(cur.jj + 1);
-    if (wave == 0) {
-      if (next.jj < count) issue_page(next, (idx + 1) & 1);
-    } else if (prev.jj < count) {
-      write_out(prev);
-    }
+    const bool issue = wave == 0 && next.jj < count;  // wave-uniform
+    if (issue) issue_rows(next, (idx + 1) & 1, 0, 32);
+    if (wave != 0 && prev.jj < count) write_out(prev);
     const MLA_LDS char* pg = lds + (idx & 1) * kPageBytes;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
@@ -224,6 +229,8 @@ __global__ __launch_bounds__(256, 1) void kv_up_kernel(const uint16_t* __restric
     read_b(1, ring[1]);
 #pragma unroll
     for (int ks = 0; ks < 32; ++ks) {
+      if (ks == 10 && issue) issue_rows(next, (idx + 1) & 1, 32, 63);
+      if (ks == 20 && issue) issue_rows(next, (idx + 1) & 1, 63, 64);
       if (ks + 2 < 32) read_b(ks + 2, ring[(ks + 2) % 3]);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
