@@ -124,21 +124,31 @@ def test_fused_tree(S, splits):
     _check(x, q_lat, splits, causal=False, parents=parents)
 
 
-def test_fused_step_full_size_sampled():
-    """The whole fused step (absorb -> attention + merge + W_UV) at batch 32 x 4096 cached tokens
-    against the non-absorbed oracle on sampled sequences and heads."""
+@pytest.mark.parametrize("name,seqs,heads", [
+    ("b32_t4096", [0, 13, 31], [0, 37, 64, 127]),
+    ("ragged_b128", [0, 77, 127], [5, 96]),
+    ("mtp_b64_s2_t16384", [0, 63], [1, 127]),
+    ("tree_b32_s8_t4096", [0, 17, 31], [3, 64, 126]),
+])
+def test_fused_step_full_size_sampled(name, seqs, heads):
+    """The whole fused step (absorb -> attention + merge + W_UV) at the benchmark sizes against the
+    non-absorbed oracle on sampled sequences and heads (the draft-tree workload through its
+    parents; at one split it takes the separate kernels)."""
     import torch
-    x = gen.generate_named("b32_t4096", poison_unused=True)
-    seqs, heads = [0, 13, 31], [0, 37, 64, 127]
-    say("fused full size", seqs, heads)
+    tree = name in gen.TREE_WORKLOADS
+    x = gen.generate_named(name, poison_unused=True)
+    parents = gen.draft_trees(x.workload.batch, x.workload.q_len, gen.TREE_SEEDS[name]) if tree else None
+    say("fused full size", name, seqs, heads)
     d = to_device(x)
-    p = params_for(x)
+    p = params_for(x, causal=not tree)
     bufs = binding.DecodeBuffers(p, 0)
-    bufs.run(d["q_nope"], d["q_pe"], d["w_uk"], d["w_uv"], d["pool"], d["block_table"], d["seq_lens"], fused=True)
+    bufs.run(d["q_nope"], d["q_pe"], d["w_uk"], d["w_uv"], d["pool"], d["block_table"], d["seq_lens"], fused=True,
+             tree_parents=None if parents is None else torch.from_numpy(parents).cuda())
     torch.cuda.synchronize()
     w = x.workload
     r = ref.mla_decode_nonabsorbed(x.f32("q_nope"), x.f32("q_pe"), x.f32("w_uk"), x.f32("w_uv"), x.f32("pool"),
-                                   x.block_table, x.seq_lens, softmax_scale=w.softmax_scale, seqs=seqs, heads=heads)
+                                   x.block_table, x.seq_lens, softmax_scale=w.softmax_scale, seqs=seqs, heads=heads,
+                                   tree=parents)
     sel = np.ix_(seqs, range(w.q_len), heads)
     errs = {k: rel_err(to_host(getattr(bufs, k))[sel], r[k][sel]) for k in ("o_lat", "out")}
     say("  rel errs", errs)
