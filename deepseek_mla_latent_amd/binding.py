@@ -27,7 +27,8 @@ EXPORTS = ("mla_absorb_q", "mla_decode_workspace_bytes", "mla_decode_num_splits"
            "mla_decode_attn_tree", "mla_decode_attn_out_proj_workspace_bytes", "mla_decode_attn_out_proj",
            "mla_out_proj", "mla_prefill_kv_bytes", "mla_prefill_kv_up", "mla_prefill_attn",
            "mla_linear_workspace_bytes", "mla_linear", "mla_rope_append", "mla_fp8_weight_bytes",
-           "mla_quantize_w_uk_fp8", "mla_quantize_w_uv_fp8", "mla_absorb_q_fp8", "mla_out_proj_fp8", "mla_status_str")
+           "mla_quantize_w_uk_fp8", "mla_quantize_w_uv_fp8", "mla_absorb_q_fp8", "mla_out_proj_fp8", "mla_status_str",
+           "mla_debug_attn_schedule")
 
 
 class MlaLibraryMissing(RuntimeError):
@@ -129,6 +130,8 @@ def load_library(path: Optional[str] = None):
         getattr(lib, name).restype = i32
     lib.mla_status_str.argtypes = [i32]
     lib.mla_status_str.restype = ctypes.c_char_p
+    lib.mla_debug_attn_schedule.argtypes = [i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.mla_debug_attn_schedule.restype = i32
     if path is None:
         _lib = lib
     return lib
@@ -168,6 +171,14 @@ def _stream(stream) -> Optional[int]:
 def _check(code: int, where: str):
     if code != 0:
         raise MlaError(code, where)
+
+
+def mla_debug_attn_schedule(ntiles: int):
+    """(dma_buffer, barrier_after) lists of the attention kernel's LDS ring over ntiles tiles."""
+    buf = (ctypes.c_int32 * ntiles)()
+    bar = (ctypes.c_int32 * ntiles)()
+    _check(load_library().mla_debug_attn_schedule(ntiles, buf, bar), "mla_debug_attn_schedule")
+    return list(buf), [bool(v) for v in bar]
 
 
 def mla_status_str(code: int) -> str:

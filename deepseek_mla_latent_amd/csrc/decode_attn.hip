@@ -31,6 +31,7 @@
 // sees the committed keys and the keys of its ancestors and itself.  The row's visibility of the
 // S new keys is one 64-bit mask (S <= 64), built once per workgroup by walking parent links and
 // applied only to tiles that reach position L-S.
+#include "attn_schedule.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -41,7 +42,6 @@ constexpr int kUnitsA = kDc / 8;                      // 16-byte units of c_KV p
 constexpr int kUnitsB = kDr / 8;                      // 16-byte units of k_pe per token (8)
 constexpr int kRegionA = kTile * kUnitsA * 16;        // 32768 B: c_KV part of a tile
 constexpr int kBufBytes = kRegionA + kTile * kUnitsB * 16;  // 36864 B per tile buffer
-constexpr int kNumBufs = 4;                           // LDS ring: tile t lives in buffer t % 4
 constexpr int kDmaPerTile = 9;                        // direct-to-LDS loads per wave per tile
 constexpr float kRescaleSlack = 8.0f;                 // log2 units
 
@@ -518,11 +518,11 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
     const int tn = t + kNumBufs - 1;
     // Past the last tile the nine loads still issue (a branch per load in the MFMA stream costs
     // more than the load), but every lane then reads the same 16 bytes at the start of the pool,
-    // into the buffer of tile t-1, which nothing reads again.
+    // into a buffer that the ring schedule (attn_schedule.h) proves no other wave is reading.
     const bool more = tn < ntiles;
     const uint16_t* nsrc = more ? row_of(tn, page_ahead) : pool;
     const int ncnt = more ? tile_count(tn) : 0;
-    const uint32_t ndst = lds_addr(smem) + (tn % kNumBufs) * kBufBytes;
+    const uint32_t ndst = lds_addr(smem) + attn_dma_buffer(t, ntiles) * kBufBytes;
     // The per-lane DMA offsets are loop-invariant; recomputing them (one XOR each) is cheaper than
     // the registers LICM would pin across the loop, so hide the lane id from it.
     uint32_t lane16 = lane * 16;
@@ -561,7 +561,7 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
     // kTree: mask the next tile's scores here, where the operand ring is dead (its registers are
     // what the masking needs) and 32 MFMAs separate the last write of sn from these reads
     if constexpr (kTree) tree_mask_tile(sn, t + 1);
-    if (t + 2 < ntiles) {  // every read of tile t done, tile t+2 landed: publish, then prefetch
+    if (attn_barrier_after(t, ntiles)) {  // every read of tile t done, tile t+2 landed: publish, then prefetch
       dma_wait_tiles(1);
       __builtin_amdgcn_s_barrier();
       advance_qk(t + 1);

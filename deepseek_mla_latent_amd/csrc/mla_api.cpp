@@ -6,6 +6,7 @@
 #include <cmath>
 
 #include "../../include/mla_latent.h"
+#include "attn_schedule.h"
 #include "kernels.h"
 
 namespace {
@@ -455,6 +456,16 @@ mla_status mla_out_proj_fp8(const float* o_lat, const void* w_uv_fp8, void* out,
   if (!aligned16(o_lat) || !aligned16(w_uv_fp8) || !aligned16(out)) return MLA_ERR_ALIGN;
   if (mla::launch_out_proj_fp8(o_lat, w_uv_fp8, out, (int)tokens_of(p), (hipStream_t)stream) != hipSuccess)
     return MLA_ERR_LAUNCH;
+  return MLA_OK;
+}
+
+mla_status mla_debug_attn_schedule(int32_t ntiles, int32_t* dma_buffer, int32_t* barrier_after) {
+  if (ntiles < 1) return MLA_ERR_SHAPE;
+  if (!dma_buffer || !barrier_after) return MLA_ERR_NULL;
+  for (int t = 0; t < ntiles; ++t) {
+    dma_buffer[t] = mla::attn_dma_buffer(t, ntiles);
+    barrier_after[t] = mla::attn_barrier_after(t, ntiles) ? 1 : 0;
+  }
   return MLA_OK;
 }
 

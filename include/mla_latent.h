@@ -347,6 +347,16 @@ mla_status mla_out_proj_fp8(const float* o_lat, const void* w_uv_fp8, void* out,
 /* Static string for a status code (never NULL). */
 const char* mla_status_str(mla_status s);
 
+/*
+ * Introspection for tests (host only, touches no device): the LDS ring schedule the bf16
+ * attention kernel follows over a key range of ntiles 32-token tiles. For each iteration
+ * t < ntiles, dma_buffer[t] receives the ring buffer (0..3) that the direct-to-LDS loads issued in
+ * iteration t write, and barrier_after[t] receives 1 if a workgroup barrier closes iteration t,
+ * else 0. Both arrays are caller-owned host arrays of at least ntiles entries.
+ * Returns MLA_ERR_SHAPE if ntiles < 1, MLA_ERR_NULL if an array is NULL, else MLA_OK.
+ */
+mla_status mla_debug_attn_schedule(int32_t ntiles, int32_t* dma_buffer, int32_t* barrier_after);
+
 #ifdef __cplusplus
 }
 #endif

@@ -208,6 +208,39 @@ def latent_attention_reference(q_lat, q_pe, pool, block_table, seq_lens, *, soft
     return {"o_lat": o_lat, "lse": lse}
 
 
+def softmax_mass(q_lat, q_pe, pool, block_table, seq_lens, lse, rows, *, softmax_scale: float,
+                 page_size: int = 64, causal: bool = True, tree=None):
+    """For each (b, i, h) in ``rows``: the sum over the keys that query sees of exp(z_j - lse[b,i,h]),
+    with z_j = scale·(q_lat·c_j + q_pe·k_pe_j) computed here in fp64.
+
+    The attention output is an attention-weighted average (izhida answer "专家"), so its weights
+    e^{z_j - lse} sum to one exactly when ``lse`` is the log of their normaliser.  Handed an lse
+    from elsewhere, this returns how far its weights are from summing to one.  Rows whose key set
+    is empty give NaN (no weights; lse is -inf there).  ``tree`` as in ``mla_decode_nonabsorbed``.
+    """
+    q_lat = np.asarray(q_lat, dtype=np.float64)
+    q_pe = np.asarray(q_pe, dtype=np.float64)
+    lse = np.asarray(lse, dtype=np.float64)
+    B, S, H, Dc = q_lat.shape
+    mass = np.full(len(rows), np.nan)
+    by_seq = {}
+    for k, (b, i, h) in enumerate(rows):
+        by_seq.setdefault(int(b), []).append((k, int(i), int(h)))
+    for b, items in by_seq.items():
+        L = int(seq_lens[b])
+        data = gather_rows(pool, block_table[b], L, page_size)
+        C, R = data[:, :Dc], data[:, Dc:]
+        anc = None if tree is None else tree_ancestors(tree[b])
+        for k, i, h in items:
+            idx = visible_key_index(L, S, i, causal, anc)
+            n = idx.stop if isinstance(idx, slice) else idx.size
+            if n == 0:
+                continue
+            z = softmax_scale * (C[idx] @ q_lat[b, i, h] + R[idx] @ q_pe[b, i, h])
+            mass[k] = np.sum(np.exp(z - lse[b, i, h]))
+    return mass
+
+
 def o_proj_reference(out, w_o):
     """y[b,s,e] = sum over heads h and value dims v of out[b,s,h,v] W_O[h,v,e], fp64.
 

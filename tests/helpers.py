@@ -31,6 +31,47 @@ def tol_for(x) -> float:
     return BF16_TOL if x.is_bf16 else F32_TOL
 
 
+def check_lse(gpu, refv, tol) -> float:
+    """lse: -inf exactly where the oracle has it; elsewhere |gpu - ref| <= tol in absolute terms.
+    lse enters every softmax weight as e^{z - lse}, so an absolute error d rescales all weights of
+    the row by e^{-d}: the bar is on d itself, not on d relative to the size of lse."""
+    gpu = np.asarray(gpu, np.float64)
+    refv = np.asarray(refv, np.float64)
+    assert gpu.shape == refv.shape, (gpu.shape, refv.shape)
+    assert not np.isnan(gpu).any(), "lse holds NaN"
+    assert np.array_equal(np.isneginf(gpu), np.isneginf(refv)), "-inf pattern differs"
+    fin = np.isfinite(refv)
+    err = float(np.max(np.abs(gpu[fin] - refv[fin]))) if fin.any() else 0.0
+    assert err <= tol, f"lse abs err {err:.3e} > {tol}"
+    return err
+
+
+def sample_rows(lse_ref, n: int = 48, seed: int = 0, seqs=None):
+    """Up to n (b, i, h) rows with a finite oracle lse (a seeded sample, the first and last always in)."""
+    lse_ref = np.asarray(lse_ref)
+    idx = np.argwhere(np.isfinite(lse_ref))
+    if seqs is not None:
+        idx = idx[np.isin(idx[:, 0], list(seqs))]
+    if len(idx) <= n:
+        return [tuple(int(v) for v in r) for r in idx]
+    pick = np.random.default_rng(seed).choice(len(idx), n - 2, replace=False)
+    pick = np.unique(np.concatenate([[0, len(idx) - 1], pick]))
+    return [tuple(int(v) for v in idx[k]) for k in pick]
+
+
+def check_softmax_mass(q_lat, q_pe, pool, block_table, seq_lens, lse_gpu, rows, *, softmax_scale, tol,
+                       causal=True, tree=None) -> float:
+    """The oracle recomputes each sampled row's scores and sums e^{z_j - lse_gpu}: the GPU's lse must
+    normalise the softmax to one within tol."""
+    from oracle import mla_decode as ref
+    mass = ref.softmax_mass(q_lat, q_pe, pool, block_table, seq_lens, lse_gpu, rows, softmax_scale=softmax_scale,
+                            causal=causal, tree=tree)
+    assert not np.isnan(mass).any(), "a sampled row has no keys"
+    err = float(np.max(np.abs(mass - 1.0))) if len(rows) else 0.0
+    assert err <= tol, f"softmax mass off by {err:.3e} > {tol}"
+    return err
+
+
 def to_device(x, device="cuda"):
     """Upload a DecodeInputs batch (bf16 as bit-exact torch.bfloat16)."""
     import torch

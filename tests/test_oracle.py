@@ -90,6 +90,44 @@ def test_softmax_rows_sum_to_one():
         assert len(p) == ref.visible_keys(int(t["seq_lens"][b]), 2, i, True)
 
 
+@pytest.mark.parametrize("tree", [False, True])
+def test_softmax_mass_of_the_oracle_lse_is_one(tree):
+    """softmax_mass recomputes the absorbed logits itself; fed the lse of the non-absorbed route it
+    must give exactly one per row, fed lse + d it must give e^{-d}, and counting keys the row does
+    not see (a wrong mask) must show as mass above one."""
+    t = _tiny(seed=5, S=3, lens=(9, 13))
+    scale = 0.4
+    parents = np.array([[-1, 0, 0], [-1, -1, 1]], dtype=np.int32) if tree else None
+    r = _nonabsorbed(t, scale, tree=parents)
+    q_lat = ref.absorb_q_reference(t["q_nope"], t["w_uk"])
+    rows = [(b, i, h) for b in range(2) for i in range(3) for h in range(4)]
+    kw = dict(softmax_scale=scale, page_size=t["page"], tree=parents)
+    m = ref.softmax_mass(q_lat, t["q_pe"], t["pool"], t["block_table"], t["seq_lens"], r["lse"], rows, **kw)
+    assert np.max(np.abs(m - 1.0)) < 1e-12
+    m2 = ref.softmax_mass(q_lat, t["q_pe"], t["pool"], t["block_table"], t["seq_lens"], r["lse"] + 0.25, rows, **kw)
+    np.testing.assert_allclose(m2, np.exp(-0.25), rtol=1e-12)
+    if not tree:
+        wide = ref.softmax_mass(q_lat, t["q_pe"], t["pool"], t["block_table"], t["seq_lens"], r["lse"], rows,
+                                softmax_scale=scale, page_size=t["page"], causal=False)
+        first = [k for k, (b, i, h) in enumerate(rows) if i == 0]
+        assert np.all(wide[first] > 1.0 + 1e-6)
+
+
+def test_softmax_mass_single_key_by_hand():
+    t = _tiny(seed=6, B=1, S=1, lens=(1,))
+    row = t["pool"][t["block_table"][0, 0], 0]
+    q_lat = ref.absorb_q_reference(t["q_nope"], t["w_uk"])
+    z = 0.9 * (q_lat[0, 0, 2] @ row[:16] + t["q_pe"][0, 0, 2] @ row[16:])
+    lse = np.zeros((1, 1, 4))
+    lse[0, 0, 2] = 1.5
+    m = ref.softmax_mass(q_lat, t["q_pe"], t["pool"], t["block_table"], t["seq_lens"], lse, [(0, 0, 2)],
+                         softmax_scale=0.9, page_size=t["page"])
+    assert abs(m[0] - math.exp(z - 1.5)) < 1e-12
+    empty = ref.softmax_mass(q_lat, t["q_pe"], t["pool"], t["block_table"], np.array([0]), lse, [(0, 0, 2)],
+                             softmax_scale=0.9, page_size=t["page"])
+    assert np.isnan(empty[0])
+
+
 def test_single_key_returns_that_key():
     """L = 1: p = [1], o_lat = c_0, out = W_UV^T c_0, lse = the one logit."""
     t = _tiny(seed=4, B=1, S=1, lens=(1,))

@@ -1,8 +1,10 @@
 """GPU parity: every call of the C-ABI library against the fp64 CPU oracle on the same seeded inputs.
 
 Bar (the stated tolerance of the method on bf16 inputs with fp32 accumulation, and on fp32 inputs):
-max |gpu - ref| / max |ref| <= 2e-2 (bf16) and <= 1e-4 (fp32), per output tensor.  Every batch has
-its unused cache slots poisoned with NaN, so a read outside the sequences shows up as NaN.
+max |gpu - ref| / max |ref| <= 2e-2 (bf16) and <= 1e-4 (fp32), per output tensor; lse within the
+same numbers in absolute terms (-inf exactly where the oracle has it), and on sampled rows the
+oracle's own logits normalised by the GPU's lse sum to one within them.  Every batch has its unused
+cache slots poisoned with NaN, so a read outside the sequences shows up as NaN.
 """
 import math
 
@@ -12,7 +14,8 @@ import pytest
 from deepseek_mla_latent_amd import binding
 from deepseek_mla_latent_amd import inputs as gen
 from oracle import mla_decode as ref
-from tests.helpers import device_array, params_for, rel_err, to_device, to_host, tol_for
+from tests.helpers import (check_lse, check_softmax_mass, device_array, params_for, rel_err, sample_rows, to_device,
+                           to_host, tol_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -24,16 +27,6 @@ def say(*a):
 def _torch():
     import torch
     return torch
-
-
-def _lse_close(gpu, refv, tol):
-    """lse: -inf where the reference is -inf, else within tol of max |ref| (finite part)."""
-    gpu = np.asarray(gpu, np.float64)
-    refv = np.asarray(refv, np.float64)
-    assert np.array_equal(np.isneginf(gpu), np.isneginf(refv))
-    fin = np.isfinite(refv)
-    if fin.any():
-        assert rel_err(gpu[fin], refv[fin]) <= tol
 
 
 # ------------------------------------------------------------------------------------ projections
@@ -99,9 +92,12 @@ def _attn_case(x, seed, splits, causal=True):
                                           softmax_scale=x.workload.softmax_scale, causal=causal)
     assert not np.isnan(o).any() and not np.isnan(lse).any()
     err = rel_err(o, want["o_lat"])
-    say("  o_lat rel err", err)
+    lerr = check_lse(lse, want["lse"], tol_for(x))
+    merr = check_softmax_mass(q_lat_f32, x.f32("q_pe"), x.f32("pool"), x.block_table, x.seq_lens, lse,
+                              sample_rows(want["lse"], seed=seed), softmax_scale=x.workload.softmax_scale,
+                              tol=tol_for(x), causal=causal)
+    say("  o_lat rel err", err, "lse abs err", lerr, "mass err", merr)
     assert err <= tol_for(x)
-    _lse_close(lse, want["lse"], tol_for(x))
     return o, lse
 
 
@@ -206,7 +202,12 @@ def _end_to_end(x, seqs, heads, splits=0):
     say("  rel errs", errs)
     for k, e in errs.items():
         assert e <= tol, k
-    _lse_close(to_host(bufs.lse)[sel], r["lse"][sel], tol)
+    lse = to_host(bufs.lse)
+    check_lse(lse[sel], r["lse"][sel], tol)
+    rows = [(b, i, h) for b in seqs for i in range(w.q_len) for h in heads if np.isfinite(r["lse"][b, i, h])]
+    merr = check_softmax_mass(ref.absorb_q_reference(x.f32("q_nope"), x.f32("w_uk")), x.f32("q_pe"), x.f32("pool"),
+                              x.block_table, x.seq_lens, lse, rows, softmax_scale=w.softmax_scale, tol=tol)
+    say("  softmax mass err", merr)
     assert not torch.isnan(bufs.out).any().item()
 
 
