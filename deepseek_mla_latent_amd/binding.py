@@ -130,7 +130,7 @@ def load_library(path: Optional[str] = None):
         getattr(lib, name).restype = i32
     lib.mla_status_str.argtypes = [i32]
     lib.mla_status_str.restype = ctypes.c_char_p
-    lib.mla_debug_attn_schedule.argtypes = [i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.mla_debug_attn_schedule.argtypes = [i32, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.mla_debug_attn_schedule.restype = i32
     if path is None:
         _lib = lib
@@ -174,11 +174,10 @@ def _check(code: int, where: str):
 
 
 def mla_debug_attn_schedule(ntiles: int):
-    """(dma_buffer, barrier_after) lists of the attention kernel's LDS ring over ntiles tiles."""
-    buf = (ctypes.c_int32 * ntiles)()
-    bar = (ctypes.c_int32 * ntiles)()
-    _check(load_library().mla_debug_attn_schedule(ntiles, buf, bar), "mla_debug_attn_schedule")
-    return list(buf), [bool(v) for v in bar]
+    """(a_buffer, b_buffer, p_buffer) lists of the attention kernel's LDS rings over ntiles tiles."""
+    arrs = [(ctypes.c_int32 * ntiles)() for _ in range(3)]
+    _check(load_library().mla_debug_attn_schedule(ntiles, *arrs), "mla_debug_attn_schedule")
+    return tuple(list(a) for a in arrs)
 
 
 def mla_status_str(code: int) -> str:

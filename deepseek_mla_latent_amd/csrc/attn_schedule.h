@@ -1,32 +1,43 @@
 // LDS ring schedule of the bf16 decode-attention kernel, shared by the kernel and the host (where
 // mla_debug_attn_schedule exposes it so a CPU test can walk it).
 //
-// A workgroup walks its key range in ntiles tiles of 32 tokens.  Tile t lives in ring buffer
-// t % kNumBufs.  The prologue loads tiles 0-2; iteration t (0 <= t < ntiles) then scores tile t+1,
-// takes the weighted sum of tile t, and issues the direct-to-LDS loads of tile t+3 into buffer
-// (t+3) % 4, the one tile t-1 used.  A workgroup barrier closes iteration t only while tiles remain
-// to publish (t + 2 < ntiles); it is what orders the loads of iteration t+1 after every wave's
-// reads of tile t.
+// A workgroup walks its key range in ntiles tiles of 32 tokens.  A tile is stored in two parts: its
+// 32 latent rows (c_KV, 32 KiB) in ring A and its 32 RoPE-key rows (k_pe, 4 KiB) in ring B.  Each of
+// the four waves computes the scores of its own 32 heads, and holds the weighted sum of every head
+// over its own quarter of the latent columns, so the probabilities of a tile pass between the waves
+// through a third ring, P.
 //
-// Past the last tile the loads of an iteration still issue (a branch per load inside the MFMA
-// stream measured slower than the load) and carry bytes nobody reads; they must still never land
-// in a buffer another wave may be reading.  Iterations ntiles-3 and ntiles-2 write buffer
-// (t+3) % 4 = tile t-1's, which the barrier closing iteration t-1 (t + 1 < ntiles) already freed.
-// The last iteration has no such barrier behind it (tile t-1 = ntiles-2 may still be summed by a
-// slower wave), so its loads go to buffer (t+2) % 4 instead: tile t-2's, freed by the barrier that
-// closed iteration t-2, or a buffer no tile ever used when t < 2.
+// Iteration u (0 <= u < ntiles), between the barriers Z(u-1) and Z(u):
+//   * scores of tile u (reads ring A and ring B of tile u); the loads of tile u + 2 are issued;
+//   * weighted sum of tile u - 1 (reads ring A of tile u - 1 and ring P of tile u - 1), with the
+//     softmax of tile u running in the gaps of its MFMA chain;
+//   * the probabilities of tile u (and the rescale words that go with them) are written to ring P;
+//     every wave then waits for its loads of tile u + 1 and meets the others at Z(u).
+// The prologue loads tiles 0 and 1 and publishes tile 0 with a barrier; after Z(ntiles - 1) the
+// weighted sum of the last tile runs.
+//
+// Why the rings are as deep as they are:
+//   * ring A, 4 buffers: tile j is read in iterations j and j + 1, so its buffer is free only after
+//     Z(j + 1); tile u + 2 therefore goes where tile u - 2 was, freed by Z(u - 1) at the start of
+//     iteration u;
+//   * ring B, 3 buffers: the k_pe rows of tile j are read only in iteration j, so tile u + 2 may go
+//     where tile u - 1 was, freed by Z(u - 1);
+//   * ring P, 2 buffers: the probabilities of tile u are written in iteration u and read in
+//     iteration u + 1; the next write into the same buffer is in iteration u + 2, after Z(u + 1).
+// Loads past the last tile still issue (a branch per load inside the MFMA stream measured slower
+// than the load); they carry no data anyone reads and go to the buffers the ring assigns to their
+// tile index, which by the argument above nobody is reading.
 #pragma once
 
 namespace mla {
 
-constexpr int kNumBufs = 4;  // LDS tile buffers in the ring
+constexpr int kNumBufsA = 4;  // latent parts of tiles
+constexpr int kNumBufsB = 3;  // RoPE-key parts of tiles
+constexpr int kNumBufsP = 2;  // probabilities of a tile
+constexpr int kLoadAhead = 2;  // iteration u issues the loads of tile u + kLoadAhead
 
-// Whether a workgroup barrier closes iteration t.
-__host__ __device__ constexpr bool attn_barrier_after(int t, int ntiles) { return t + 2 < ntiles; }
-
-// Ring buffer that the loads issued in iteration t write.
-__host__ __device__ constexpr int attn_dma_buffer(int t, int ntiles) {
-  return (t + 1 < ntiles ? t + 3 : t + 2) % kNumBufs;
-}
+__host__ __device__ constexpr int attn_a_buffer(int tile) { return tile % kNumBufsA; }
+__host__ __device__ constexpr int attn_b_buffer(int tile) { return tile % kNumBufsB; }
+__host__ __device__ constexpr int attn_p_buffer(int tile) { return tile % kNumBufsP; }
 
 }  // namespace mla

@@ -10,22 +10,27 @@
 // of order 2 in "【笔记】MLA矩阵吸收分析" §二.2 and §三.2.
 //
 // bf16 kernel (one workgroup = 4 waves = 128 heads of one (b, i), one contiguous page range):
-//   * the key range is walked in tiles of 32 tokens (half a page).  Tiles stream HBM -> LDS by
-//     direct-to-LDS loads (16 B per lane, no register staging) into a ring of 4 LDS buffers,
-//     three tiles ahead of the one being computed, so about 100 KiB per CU are in flight;
-//   * each LDS tile is XOR-swizzled in 16-byte units so both read patterns below are free of
+//   * the key range is walked in tiles of 32 tokens (half a page), streamed HBM -> LDS by
+//     direct-to-LDS loads (16 B per lane, no register staging): the latent rows into a ring of 4
+//     buffers, the RoPE-key rows into a ring of 3, two tiles ahead (attn_schedule.h);
+//   * each LDS tile is XOR-swizzled in 16-byte units so that both read patterns below are free of
 //     bank conflicts;
-//   * scores are computed transposed, S^T = tile * Q^T, on 32x32x16 bf16 MFMAs: the tile is the
-//     A operand (ds_read_b128), the wave's 32 heads' [q_lat | q_pe] stay in registers as the B
-//     operand.  The accumulator layout then gives every lane one head and 16 tokens, which is
-//     already the B-operand layout of the next product (no cross-lane shuffle for P);
-//   * O^T (latent x heads) += tile^T * P^T reuses the same LDS tile as the value; its transposed
-//     A operand comes from ds_read_b64_tr_b16 (4 tokens x 1 latent column per lane per read);
+//   * scores: wave w takes heads 32w..32w+31.  S^T = tile * Q^T on 32x32x16 bf16 MFMAs, the tile as
+//     the A operand (ds_read_b128), the wave's [q_lat | q_pe] in registers as the B operand.  Each
+//     lane ends up with one head and 16 tokens, which is already the B-operand layout of the
+//     weighted sum (no cross-lane shuffle for P);
 //   * online softmax in base 2 with the scale folded in; the running max is only raised (and O
-//     rescaled) when a tile's max exceeds it by more than 2^8, which keeps exp2 arguments <= 8
-//     and skips almost every rescale of the 256 accumulator registers.
+//     rescaled) when a tile's max exceeds it by more than 2^8;
+//   * weighted sum: wave w holds O^T for latent columns 128w..128w+127 of all 128 heads.  The
+//     probabilities of a tile pass between the waves through LDS (32 tokens x 128 heads, 8 KiB), so
+//     each transposed A operand (ds_read_b64_tr_b16 from the same LDS tile: c_KV is key and value)
+//     feeds four MFMAs, one per head block.  Per tile a wave reads 52 KiB from LDS in 60
+//     instructions instead of the 68 KiB in 100 that a wave holding all 512 columns of its own 32
+//     heads needs;
+//   * iteration u: scores of tile u, then the weighted sum of tile u-1 with the softmax of tile u
+//     in the gaps of its MFMA chain; one workgroup barrier per tile.
 // Long contexts are split into page ranges (split-K over tokens); each range writes a normalised
-// partial (o_k, lse_k) and lse_merge_kernel combines them.
+// partial (o_k, lse_k) and lse_merge_kernel (or the merge in the out-projection) combines them.
 // Tree-masked verify (EAGLE-style draft trees: the Perplexity post, section "Будущая работа"): the
 // S new tokens are tree nodes cached at positions L-S .. L-1, parents before children; query i
 // sees the committed keys and the keys of its ancestors and itself.  The row's visibility of the
@@ -37,33 +42,43 @@
 
 namespace mla {
 
-constexpr int kTile = 32;                             // tokens per LDS tile (half a page)
-constexpr int kUnitsA = kDc / 8;                      // 16-byte units of c_KV per token (64)
-constexpr int kUnitsB = kDr / 8;                      // 16-byte units of k_pe per token (8)
-constexpr int kRegionA = kTile * kUnitsA * 16;        // 32768 B: c_KV part of a tile
-constexpr int kBufBytes = kRegionA + kTile * kUnitsB * 16;  // 36864 B per tile buffer
-constexpr int kDmaPerTile = 9;                        // direct-to-LDS loads per wave per tile
-constexpr float kRescaleSlack = 8.0f;                 // log2 units
+constexpr int kTile = 32;                        // tokens per LDS tile (half a page)
+constexpr int kUnitsA = kDc / 8;                 // 16-byte units of c_KV per token (64)
+constexpr int kUnitsB = kDr / 8;                 // 16-byte units of k_pe per token (8)
+constexpr int kBufA = kTile * kUnitsA * 16;      // 32768 B: latent rows of a tile
+constexpr int kBufB = kTile * kUnitsB * 16;      // 4096 B: RoPE-key rows of a tile
+constexpr int kBufP = 4 * 2 * 64 * 16;           // 8192 B: bf16 P of a tile, [head block][token half][lane]
+// LDS layout of the bf16 kernel (bytes)
+constexpr int kOffB = kNumBufsA * kBufA;                 // ring B
+constexpr int kOffP = kOffB + kNumBufsB * kBufB;         // ring P
+constexpr int kOffAlpha = kOffP + kNumBufsP * kBufP;     // per ring-P buffer: rescale factor per head
+constexpr int kOffFlags = kOffAlpha + kNumBufsP * kHeads * 4;  // per ring-P buffer: rescale flag per head block
+constexpr int kOffInvL = kOffFlags + kNumBufsP * 16;     // final 1 / sum of weights per head
+constexpr int kOffPages = kOffInvL + kHeads * 4;         // page ids of the range
+constexpr int kOffTree = kOffPages + kMaxSplitPages * 4;  // draft-tree masked-key windows (12 words)
+constexpr int kLdsBytes = kOffTree + 12 * 4;
+static_assert(kLdsBytes <= 160 * 1024, "LDS of one workgroup");
+static_assert(kNumBufsA * kBufA >= kHeads * 1024, "the query rows are staged through ring A");
+constexpr int kStageRow = kDc * 2 + 16;  // bf16 output row staged in LDS (1040 B: 2-way bank conflicts)
+static_assert(kHeads * kStageRow <= kOffP, "output staging fits in rings A and B");
+constexpr int kDmaPerTile = 9;           // direct-to-LDS loads per wave per tile
+constexpr float kRescaleSlack = 8.0f;    // log2 units
 
 __device__ __forceinline__ uint32_t lds_addr(const MLA_LDS char* p) { return (uint32_t)(uintptr_t)p; }
 
 // Swizzle: 16-byte unit u of token t is stored at unit (u ^ swz(t)) of the token's LDS row.
-// Region A (64 units per row): bit-rotated low 4 bits of t, so 16 consecutive tokens at one unit
+// Ring A (64 units per row): bit-rotated low 4 bits of t, so 16 consecutive tokens at one unit
 // (the score A-operand read) and 8 tokens x 4 units (the transposed read) both spread over banks.
 __device__ __forceinline__ int swz_a(int t) { return ((t & 3) << 2) | ((t >> 2) & 3); }
 __device__ __forceinline__ int swz_b(int t) { return (t >> 1) & 7; }
 __device__ __forceinline__ int off_a(int t, int u) { return (t * kUnitsA + (u ^ swz_a(t))) * 16; }
-__device__ __forceinline__ int off_b(int t, int u) { return kRegionA + (t * kUnitsB + (u ^ swz_b(t))) * 16; }
 
-// Direct-to-LDS load of 16 bytes per lane: lane l's bytes land at LDS address lds + 16 l.
-// Issued from asm: the compiler models this instruction as pending in the LDS counter as well,
-// which would turn every LDS operand wait of the tile computed meanwhile into a full drain.  It
-// has no register outputs; completion is awaited explicitly (dma_wait_tiles) before the barrier
-// that publishes a tile.  M0 is not otherwise used by this kernel.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory");
-}
-// The same from a wave-uniform base plus a 32-bit per-lane byte offset (no 64-bit vector math).
+// Direct-to-LDS load of 16 bytes per lane from a wave-uniform base plus a 32-bit per-lane byte
+// offset: lane l's bytes land at LDS address lds + 16 l.  Issued from asm: the compiler models
+// this instruction as pending in the LDS counter as well, which would turn every LDS operand wait
+// of the tile computed meanwhile into a full drain.  It has no register outputs; completion is
+// awaited explicitly (dma_wait_tiles) before the barrier that publishes a tile.  M0 is not
+// otherwise used by this kernel.
 __device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
                : "memory");
@@ -72,9 +87,7 @@ __device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, uint32
 // Vector-memory loads complete in order, so this retires every older tile; loads the compiler
 // issues itself only ever make the wait stricter.
 __device__ __forceinline__ void dma_wait_tiles(int younger) {
-  if (younger >= 2)
-    asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-  else if (younger == 1)
+  if (younger >= 1)
     asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
   else
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -105,13 +118,13 @@ __device__ __forceinline__ float acc_read_scaled(float x, float scale) {
   return tmp;
 }
 
-// MFMAs of the main loop are issued from asm volatile statements with a memory clobber: the
-// compiler keeps them in program order and cannot move the LDS operand loads (ordinary builtins,
-// whose waits it still inserts exactly) across them, so the software pipeline below is executed
-// as written.  Being opaque, these statements also hide hazards from the compiler; the few that
-// matter are handled explicitly:
+// MFMAs are issued from asm volatile statements with a memory clobber: the compiler keeps them in
+// program order and cannot move the LDS operand loads (ordinary builtins, whose waits it still
+// inserts exactly) across them, so the software pipeline below is executed as written.  Being
+// opaque, these statements also hide hazards from the compiler; the few that matter are handled
+// explicitly:
 //   * VALU write -> MFMA source read needs 2 wait states: the first score MFMA takes SrcC = 0
-//     (no VALU zeroing) and P goes through pin_after_valu() before use;
+//     (no VALU zeroing), and the VALU rescale of O is followed by s_nop 4;
 //   * MFMA result -> VALU read needs 18 wait states (16-pass XDL op): the last score MFMA of a
 //     chain carries them (mfma_acc_v_last), O goes through acc_wait_mfma();
 //   * dependent accumulation chains (same SrcC/Dst) need none.
@@ -129,7 +142,6 @@ __device__ __forceinline__ void mfma_acc_a(f32x16& d, const bf16x8& a, const bf1
 __device__ __forceinline__ void mfma_acc_v_last(f32x16& d, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 15\n\ts_nop 3" : "+v"(d) : "v"(a), "v"(b) : "memory");
 }
-__device__ __forceinline__ void pin_after_valu(bf16x8& x, bf16x8& y) { asm volatile("s_nop 1" : "+v"(x), "+v"(y)); }
 
 __device__ __forceinline__ bf16x8 lds_read_b128(const MLA_LDS char* p) { return *(const MLA_LDS bf16x8*)p; }
 
@@ -147,7 +159,6 @@ __device__ __forceinline__ bf16x8 lds_read_tr_pair(const MLA_LDS char* lo, const
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// Token range and output slots of one workgroup; shared by both dtypes.
 // Visibility of the S new keys to query (b, i) under a draft tree (S <= 64), wave-uniform: bit j
 // set iff node j is node i or one of its ancestors.  Lane j loads node j's parent once; the walk
 // then follows parent links through readlane while they point strictly backwards, so it ends
@@ -166,6 +177,7 @@ __device__ __forceinline__ uint64_t tree_walk(int par, int S, int i) {
   return m;
 }
 
+// Token range and output slots of one workgroup; shared by both dtypes.
 struct WorkItem {
   int b, i, split;
   int tok_begin, tok_end;  // [tok_begin, tok_end) of sequence b, page aligned at tok_begin
@@ -197,55 +209,41 @@ __device__ __forceinline__ WorkItem make_work(const AttnArgs& a, int id) {
 
 template <bool kTree>
 __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(1024))) char lds_raw[kNumBufs * kBufBytes];
-  // Page ids of the range, then 12 words for kTree: word 0 = the first tile of the range that
+  __shared__ __attribute__((aligned(1024))) char lds_raw[kLdsBytes];
+  MLA_LDS char* const smem = (MLA_LDS char*)lds_raw;
+  // Page ids of the range, then for kTree 12 words: word 0 = the first tile of the range that
   // reaches a draft-tree key; words 2-3 = zeros (no key of an earlier tile is masked); words 4-11
   // = the masked-key windows of that tile and the next three, two per tile (lanes 0-31, lanes
-  // 32-63).  Read back per tile: held in registers across the loop they would not fit, and kept in
-  // the page-id array so that both are addressed from one base.
-  __shared__ __attribute__((aligned(16))) int lds_pages[kMaxSplitPages + 12];
-  int* const lds_tree = lds_pages + kMaxSplitPages;
-  MLA_LDS char* const smem = (MLA_LDS char*)lds_raw;
+  // 32-63).  Read back per tile: held in registers across the loop they would not fit.
+  MLA_LDS int* const lds_pages = (MLA_LDS int*)(smem + kOffPages);
+  MLA_LDS int* const lds_tree = (MLA_LDS int*)(smem + kOffTree);
 
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   const WorkItem w = make_work(a, id);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int l32 = lane & 31, hf = lane >> 5;
-  const int h = wave * 32 + l32;
   // kTree: node `lane`'s parent, loaded here and walked once the query prologue has waited for its
   // loads
   const int tpar = kTree ? tree_parent_of_lane(a.tree_parents, w.b, a.S, lane) : -1;
 
-  // Output slots of this lane (head h, latent columns 8 g + 4 hf + 32 cb ..).  Computed where
-  // they are used: held across the loop they would cost two 64-bit registers.
-  // Final outputs are fp32; split partials are bf16 (the merge widens them again).
-  auto out_ptrs = [&](int ln, size_t& o_idx, float*& lse_ptr) {
-    const int hh = wave * 32 + (ln & 31);
-    o_idx = (w.out_row + hh) * kDc + 4 * (ln >> 5);
-    lse_ptr = a.lse_out ? a.lse_out + w.out_row + hh : nullptr;
-  };
-  // Element e of the 4 at (cb, g): latent column 32 cb + 8 g + 4 hf + e.
-  auto store4 = [&](size_t o_idx, int cb, int g, const f32x4& v) {
-    if (a.final_out) {
-      *(f32x4*)((float*)a.o_out + o_idx + 32 * cb + 8 * g) = v;
-    } else {
-      const uint2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-      *(uint2*)((uint16_t*)a.o_out + o_idx + 32 * cb + 8 * g) = pk;
-    }
-  };
-
+  // Final outputs are fp32 (written by this kernel's lanes directly); split partials are bf16
+  // rows (the merge widens them again), staged through LDS so each store writes a whole row.
   const int ntok = w.tok_end - w.tok_begin;
-  if (ntok <= 0) {  // empty key range: o = 0, lse = -inf
-    size_t o_idx;
-    float* lse_ptr;
-    out_ptrs(lane, o_idx, lse_ptr);
+  if (ntok <= 0) {  // empty key range: o = 0, lse = -inf (wave w writes the rows of its 32 heads)
+    const size_t row = w.out_row + wave * 32 + l32;
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int cb = 0; cb < 16; ++cb)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) store4(o_idx, cb, g, z);
-    if (hf == 0 && lse_ptr) *lse_ptr = -INFINITY;
+    for (int c = 0; c < kDc / 8; c += 2) {  // this lane: 16-byte pieces hf, hf + 2, .. of the row
+      const int col = (c + hf) * 8;
+      if (a.final_out) {
+        *(f32x4*)((float*)a.o_out + row * kDc + col) = z;
+        *(f32x4*)((float*)a.o_out + row * kDc + col + 4) = z;
+      } else {
+        *(u32x4*)((uint16_t*)a.o_out + row * kDc + col) = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    if (hf == 0 && a.lse_out) a.lse_out[row] = -INFINITY;
     return;
   }
   const int ntiles = (ntok + kTile - 1) / kTile;
@@ -257,7 +255,7 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
   // loop would make the compiler drain the vector-memory counter, i.e. wait for the tiles in
   // flight; a scalar load would share the LDS counter and make every operand wait a full drain.
   // Their loads are issued here and stored to LDS after the query loads below, so the two
-  // round trips overlap; the barrier that hands the buffers to the tiles also publishes them.
+  // round trips overlap; the barrier that hands ring A to the tiles also publishes them.
   const int npages = (ntok + kPage - 1) / kPage;
   constexpr int kPidPerThread = kMaxSplitPages / 256;
   int pid[kPidPerThread];
@@ -271,28 +269,44 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
   };
   auto tile_count = [&](int t) { return ntok - t * kTile < kTile ? ntok - t * kTile : kTile; };
 
-  // One step of copying a tile (cnt valid tokens, rows from `src`) into LDS buffer `dst`:
-  // steps 0-7 fill this wave's 8 tokens' 1 KiB c_KV rows (region A), step 8 the 128 B k_pe rows
-  // of 8 tokens (region B).  Tokens past cnt re-read token 0 (always valid), so LDS never holds
-  // bytes from outside the sequence; their scores are masked.
-  // lane16 = 16 * lane: the per-lane part of every address is one XOR with a wave-uniform value.
-  auto dma_step = [&](const uint16_t* src, int cnt, uint32_t dst, int k, uint32_t lane16) {
+  // One step of copying a tile (cnt valid tokens, rows from `src`) into ring-A buffer dst_a and
+  // ring-B buffer dst_b: steps 0-7 fill this wave's 8 tokens' 1 KiB c_KV rows, step 8 the 128 B
+  // k_pe rows of 8 tokens.  Tokens past cnt re-read token 0 (always valid), so LDS never holds
+  // bytes from outside the sequence; their scores are masked.  lane16 = 16 * lane: the per-lane
+  // part of every address is one XOR with a wave-uniform value (0 for loads past the last tile,
+  // which then all read the first 16 bytes of the pool).
+  auto dma_step = [&](const uint16_t* src, int cnt, uint32_t dst_a, uint32_t dst_b, int k, uint32_t lane16) {
     const char* base = (const char*)src;
     if (k < 8) {
       const int t = wave * 8 + k;  // wave-uniform
       const int ts = t < cnt ? t : 0;
-      dma16_s(base + ts * (kRow * 2), lane16 ^ (swz_a(t) * 16), dst + t * 1024);
+      dma16_s(base + ts * (kRow * 2), lane16 ^ (swz_a(t) * 16), dst_a + t * 1024);
     } else {
       const int t = wave * 8 + (int)(lane16 >> 7);
       const int ts = t < cnt ? t : 0;
       const uint32_t u = ((lane16 >> 4) & 7) ^ swz_b(t);
-      dma16_s(base, ts * (kRow * 2) + kDc * 2 + u * 16, dst + kRegionA + wave * 1024);
+      dma16_s(base, ts * (kRow * 2) + kDc * 2 + u * 16, dst_b + wave * 1024);
     }
   };
-  // Prologue.  The query rows come in first, through LDS: each wave copies its 32 heads' q_lat
-  // rows (1 KiB each, one load per row, 16-byte unit u of row r stored at u ^ (r & 15)) into the
-  // tile buffers, which are still free, and reads its B operands from there; q_pe (4 loads) comes
-  // straight from memory.  Then tiles 0-2 start streaming into the buffers.
+  struct Group {  // the nine loads of one tile (or of none, past the last tile)
+    const uint16_t* src;
+    int cnt;
+    uint32_t dst_a, dst_b, lane16;
+  };
+  auto make_group = [&](int u, int page, uint32_t lane16_live) -> Group {
+    const bool live = u < ntiles;
+    Group g;
+    g.src = live ? row_of(u, page) : pool;
+    g.cnt = live ? tile_count(u) : 0;
+    g.dst_a = lds_addr(smem) + attn_a_buffer(u) * kBufA;
+    g.dst_b = lds_addr(smem) + kOffB + attn_b_buffer(u) * kBufB;
+    g.lane16 = live ? lane16_live : 0u;
+    return g;
+  };
+
+  // Prologue.  The query rows come in first, through ring A: each wave copies its 32 heads' q_lat
+  // rows (1 KiB each, one load per row, 16-byte unit u of row r stored at u ^ (r & 15)) and reads
+  // its B operands from there; q_pe (4 loads) comes straight from memory.
   bf16x8 q[36];  // this lane's head as the score B operand: [q_lat | q_pe][16 ks + 8 hf .. +7]
   {
     const size_t qrow0 = ((size_t)w.b * a.S + w.i) * kHeads + wave * 32;
@@ -334,27 +348,25 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
     if (lane == 0) lds_tree[0] = t_first;
     if (lane == 2 || lane == 3) lds_tree[lane] = 0;
   }
-  __syncthreads();  // every wave has its q and the page ids are in LDS: the buffers take the tiles now
-  auto prologue_tile = [&](int t) {
-    const uint16_t* src = row_of(t, __builtin_amdgcn_readfirstlane(lds_pages[t >> 1]));
-    const int cnt = tile_count(t);
-    const uint32_t dst = lds_addr(smem) + t * kBufBytes;
+  __syncthreads();  // every wave has its q and the page ids are in LDS: ring A takes the tiles now
 #pragma unroll
-    for (int k = 0; k < kDmaPerTile; ++k) dma_step(src, cnt, dst, k, lane * 16);
-  };
-  for (int t = 0; t < kNumBufs - 1 && t < ntiles; ++t) prologue_tile(t);
-  dma_wait_tiles(ntiles - 1 < 2 ? ntiles - 1 : 2);  // tile 0 has landed (this wave's part)
+  for (int u = 0; u < kLoadAhead; ++u) {
+    const Group g = make_group(u, u < ntiles ? __builtin_amdgcn_readfirstlane(lds_pages[u >> 1]) : 0, lane * 16);
+#pragma unroll
+    for (int k = 0; k < kDmaPerTile; ++k) dma_step(g.src, g.cnt, g.dst_a, g.dst_b, k, g.lane16);
+  }
 
-  // Per-lane LDS byte offsets of the swizzled reads, relative to smem; the score offsets follow
-  // the tile being scored, the sum offsets the (previous) tile being summed, one buffer per tile.
-  // score step r (r < 32): qk_a[r % 8] + 256 (r / 8); (r >= 32): qk_b[r - 32].
-  // sum step m: latent block cb = m / 2, token step kk = m % 2 -> pv_lo/hi[cb % 4] + 256 (cb / 4)
-  // + 16384 kk.  All immediates stay below 64 KiB.
-  int qk_a[8], qk_b[4], pv_lo[4], pv_hi[4];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) qk_a[k] = off_a(l32, 2 * k + hf);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) qk_b[k] = off_b(l32, 2 * k + hf);
+  // Per-lane LDS byte offsets of the swizzled reads.
+  // Score operand g of the tile in ring-A buffer at A0 / ring-B buffer at B0 (g < 32: latent
+  // units 2 (g & 7) + hf + 16 (g >> 3); g >= 32: k_pe units 2 (g - 32) + hf):
+  //   (A0 + xa) ^ 32 (g & 7), plus 256 (g >> 3);  (B0 + xb) ^ 32 (g - 32).
+  // The XOR only touches bits 5-7, which in A0 + xa / B0 + xb come from the swizzled unit alone.
+  const uint32_t xa = l32 * 1024 + 16 * (hf ^ swz_a(l32));
+  const uint32_t xb = l32 * 128 + 16 * (hf ^ swz_b(l32));
+  // Weighted-sum A operand (tile^T) for latent block 4 wave + c, token half kk: the transposed
+  // read pair at pv_lo[c] / pv_hi[c] + 16384 kk of the summed tile's ring-A buffer; lanes get the
+  // tokens in the same order as the score accumulator hands them to the softmax.
+  int pv_lo[4], pv_hi[4];
   {
     const int r4 = (lane >> 2) & 3;
     const int colq = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
@@ -362,41 +374,17 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int c = 32 * k + colq;
-      pv_lo[k] = off_a(tb, c >> 3) + (c & 7) * 2;
-      pv_hi[k] = off_a(tb + 8, c >> 3) + (c & 7) * 2;
+      pv_lo[k] = off_a(tb, c >> 3) + (c & 7) * 2 + 256 * wave;
+      pv_hi[k] = off_a(tb + 8, c >> 3) + (c & 7) * 2 + 256 * wave;
     }
   }
-  auto read_qk = [&](int g) -> bf16x8 {  // A operand of score MFMA g (0..35)
-    if (g < 32) return lds_read_b128(smem + qk_a[g & 7] + 256 * (g >> 3));
-    return lds_read_b128(smem + qk_b[g - 32]);
-  };
-  auto read_pv = [&](int m) -> bf16x8 {  // A operand of sum MFMA m (0..31)
-    const int cb = m >> 1, kk = m & 1;
-    const int imm = 256 * (cb >> 2) + 16384 * kk;
-    return lds_read_tr_pair(smem + pv_lo[cb & 3] + imm, smem + pv_hi[cb & 3] + imm);
-  };
-  auto step_of = [](int t) { return (t % kNumBufs) == kNumBufs - 1 ? -(kNumBufs - 1) * kBufBytes : kBufBytes; };
-  auto advance_qk = [&](int t) {  // from tile t's buffer to tile t+1's
-    const int s = step_of(t);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) qk_a[k] += s;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) qk_b[k] += s;
-  };
-  auto advance_pv = [&](int t) {
-    const int s = step_of(t);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      pv_lo[k] += s;
-      pv_hi[k] += s;
-    }
-  };
+  const uint32_t p_lane = kOffP + lane * 16;  // ring P: [buffer][head block][token half][lane] x 16 B
 
-  f32x16 o[16];
+  f32x16 o[16];  // o[4 c + hb]: O^T for latent block 4 wave + c, heads 32 hb .. 32 hb + 31
 #pragma unroll
-  for (int cb = 0; cb < 16; ++cb)
+  for (int k = 0; k < 16; ++k)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) o[cb][e] = 0.f;
+    for (int e = 0; e < 16; ++e) o[k][e] = 0.f;
   // The reference starts at the lowest finite float, so a tile whose keys are all masked (a draft
   // tree can hide whole tiles, even the first of a range) gives exp2(-inf) = 0, never inf - inf.
   float m_run = -3.402823466e38f, l_run = 0.f;
@@ -406,16 +394,14 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
   const float scale_log2 = a.scale_log2;
   asm volatile("" ::"s"(scale_log2), "s"(ntiles), "s"(ntok));
 
-
   // ---- online softmax of one tile's raw scores sc (element e = token (e/4)*8 + 4 hf + e%4 of
   // the tile), in base 2 with the scale folded into the exponent's FMA, cut into stages so that
-  // its instructions can ride between the MFMAs of the next tile's scores.  Masked keys get a raw
-  // score of -inf.  Output: P in bf16 (pk), already in the B layout of the weighted sum.
+  // its instructions can ride between the MFMAs of the weighted sum.  Masked keys get a raw score
+  // of -inf.  Output: P in bf16 (pk), already in the B layout of the weighted sum, and for the
+  // other waves the rescale factor of each of this wave's heads.
   bf16x8 pk[2];
   float mx[5], mt = 0.f, alpha = 1.f;
   bool rescale = false;  // wave-uniform
-  // Stage s runs in score slot s: 0-2 the tile max and the new reference, then one probability in
-  // every second slot (3, 5, .., 33), so no slot holds more VALU work than one MFMA's duration.
   auto softmax_stage = [&](int s, int cnt, f32x16& sc) {
     if (s == 0) {
       if (cnt < kTile) {  // wave-uniform: only the last tile of a range can be partial
@@ -431,8 +417,8 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
       mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
     } else if (s == 2) {
-      // Branch-free on purpose: a branch here lets the compiler duplicate the rest of the score
-      // chain per outcome.  O itself is rescaled right before the sum, outside the chain.
+      // Branch-free on purpose: a branch here lets the compiler duplicate the rest of the chain
+      // per outcome.  O itself is rescaled (by every wave) before the next weighted sum.
       const bool raise = __any(mt > m_run + kRescaleSlack);  // wave-uniform
       const float m_new = raise ? fmaxf(m_run, mt) : m_run;
       rescale = raise && started;  // O and l hold something: rescale them to the new reference
@@ -449,16 +435,14 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
       asm volatile("" : "+v"(pk[e >> 3]), "+v"(l_run));
     }
   };
-  constexpr int kSoftmaxStages = 35;
+  constexpr int kSoftmaxStages = 34;
 
   // kTree: raw scores of tile t.  A key of a node that is neither the query's node nor one of its
   // ancestors gets -inf; committed keys stay.  Tiles before the first one that reaches the tree
-  // keep everything; a range meets at most three such tiles (64 nodes), a fourth entry covers the
-  // stale tile scored past the end.
+  // keep everything; a range meets at most four such tiles (64 nodes).
   // Element e: a signed extract of its masked-key bit (0 or all ones) selects the score or -inf
-  // (an instruction literal), two temporaries at a time.  The kernel has no register to spare
-  // across the loop, so nothing here may be hoisted out of it: the LDS address and the lane half
-  // are hidden from loop-invariant code motion.
+  // (an instruction literal), two temporaries at a time.  The LDS address and the lane half are
+  // hidden from loop-invariant code motion, which would otherwise pin registers across the loop.
   auto tree_mask_tile = [&](f32x16& sc, int t) {
     int z = 0;  // an opaque zero in the addresses: a constant LDS address would be hoisted
     asm volatile("" : "+s"(z));
@@ -479,152 +463,208 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
     }
   };
 
-  // ---- scores of tile 0 (nothing to overlap yet)
-  __builtin_amdgcn_s_barrier();  // every wave's part of tile 0 has landed
-  bf16x8 ring[4];
-  f32x16 sa, sb;  // raw scores: the two buffers swap roles every tile (no copy between them)
-#pragma unroll
-  for (int g = 0; g < 4; ++g) ring[g] = read_qk(g);
-#pragma unroll
-  for (int ks = 0; ks < 36; ++ks) {
-    if (ks == 0)
-      mfma_first_v(sa, ring[0], q[0]);
-    else if (ks < 35)
-      mfma_acc_v(sa, ring[ks & 3], q[ks]);
-    else
-      mfma_acc_v_last(sa, ring[ks & 3], q[ks]);
-    if (ks + 4 < 36) ring[ks & 3] = read_qk(ks + 4);
-  }
-  if constexpr (kTree) tree_mask_tile(sa, 0);
-  if (ntiles > 1) {  // tile 1 has landed everywhere; start its operand reads
-    dma_wait_tiles(ntiles > 2 ? 1 : 0);
-    __builtin_amdgcn_s_barrier();
-    advance_qk(0);
-#pragma unroll
-    for (int g = 0; g < 4; ++g) ring[g] = read_qk(g);
-  }
-  // page id of tile 3 (the first one the loop streams in)
-  int page_ahead = ntiles > 3 ? __builtin_amdgcn_readfirstlane(lds_pages[3 >> 1]) : 0;
+  f32x16 s;           // raw scores of the tile being scored
+  bf16x8 ring[4];     // score A operands in flight
+  bf16x8 pp[8];       // weighted-sum B operands: P of the summed tile, [token half * 4 + head block]
+  bf16x8 apv[3];      // weighted-sum A operands in flight (group j of four MFMAs uses apv[j % 3])
+  uint32_t flags = 0;
 
-  // ---- steady state, iteration t: scores of tile t+1 with the softmax of tile t riding in the
-  // gaps of that MFMA chain, then the weighted sum of tile t.  Tile t+3 streams in meanwhile, into
-  // the buffer tile t-1 used.  One barrier per tile follows the sum: every read of tile t has
-  // completed (the sum MFMAs consumed them) and tile t+2 has landed; then the first operand reads
-  // of tile t+2's scores are issued.
-  // The last iteration scores a stale buffer (its result is never used) to keep a single copy of
-  // the softmax and the sum in the code.
-  auto iteration = [&](int t, f32x16& sc, f32x16& sn) {
-    const int cnt = tile_count(t);
-    const int tn = t + kNumBufs - 1;
-    // Past the last tile the nine loads still issue (a branch per load in the MFMA stream costs
-    // more than the load), but every lane then reads the same 16 bytes at the start of the pool,
-    // into a buffer that the ring schedule (attn_schedule.h) proves no other wave is reading.
-    const bool more = tn < ntiles;
-    const uint16_t* nsrc = more ? row_of(tn, page_ahead) : pool;
-    const int ncnt = more ? tile_count(tn) : 0;
-    const uint32_t ndst = lds_addr(smem) + attn_dma_buffer(t, ntiles) * kBufBytes;
-    // The per-lane DMA offsets are loop-invariant; recomputing them (one XOR each) is cheaper than
+  auto read_pv = [&](int c, int kk) -> bf16x8 {
+    return lds_read_tr_pair(smem + pv_lo[c] + 16384 * kk, smem + pv_hi[c] + 16384 * kk);
+  };
+  // P of tile j (all four head blocks) and its rescale flags, from ring P
+  auto read_p = [&](int j, int i) -> bf16x8 {  // i = token half * 4 + head block
+    const uint32_t base = p_lane + attn_p_buffer(j) * kBufP;
+    return lds_read_b128(smem + base + (i & 3) * 2048 + (i >> 2) * 1024);
+  };
+  auto read_flags = [&](int j) -> uint32_t {
+    const u32x4 f = *(const MLA_LDS u32x4*)(smem + kOffFlags + attn_p_buffer(j) * 16);
+    return __builtin_amdgcn_readfirstlane(f[0] | (f[1] << 1) | (f[2] << 2) | (f[3] << 3));
+  };
+  // O columns of the head blocks whose owner raised its reference with tile j: scaled by the
+  // owner's factor before tile j's weighted sum adds to them (rare).
+  auto rescale_o = [&](int j, uint32_t fl) {
+    if (fl != 0) {
+      acc_wait_mfma();
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb)
+        if (fl & (1u << hb)) {
+          const float al = *(const MLA_LDS float*)(smem + kOffAlpha + attn_p_buffer(j) * (kHeads * 4) +
+                                                   (32 * hb + l32) * 4);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) acc_scale(o[4 * c + hb], al);
+        }
+      asm volatile("s_nop 4" ::: "memory");
+    }
+  };
+
+  // ---- scores of tile t (ring A/B buffers of t), the loads of tile t + 2 (steps 0-4 of 9) and,
+  // from step 24 on, the operands of the weighted sum of tile t - 1 (when there is one).
+  auto score_chain = [&](int t, bool pv_next) {
+    const uint32_t la = (uint32_t)(attn_a_buffer(t) * kBufA) + xa;
+    const uint32_t lb = (uint32_t)(kOffB + attn_b_buffer(t) * kBufB) + xb;
+    auto rd = [&](int g) -> bf16x8 {
+      if (g < 32) return lds_read_b128(smem + ((la ^ (32u * (g & 7))) + 256 * (g >> 3)));
+      return lds_read_b128(smem + (lb ^ (32u * (g - 32))));
+    };
+    const int un = t + kLoadAhead;
+    // The per-lane load offsets are loop-invariant; recomputing them (one XOR each) is cheaper than
     // the registers LICM would pin across the loop, so hide the lane id from it.
     uint32_t lane16 = lane * 16;
     asm volatile("" : "+v"(lane16));
-    lane16 = more ? lane16 : 0u;
-
-    int pid_v = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) ring[k] = rd(k);
+    // page of tile un, read from LDS here and taken to a scalar register two MFMAs later
+    const int pid_v = lds_pages[un < ntiles ? un >> 1 : 0];
+    Group g;
 #pragma unroll
     for (int ks = 0; ks < 36; ++ks) {
       if (ks == 0)
-        mfma_first_v(sn, ring[0], q[0]);
+        mfma_first_v(s, ring[0], q[0]);
+      else if (ks < 35)
+        mfma_acc_v(s, ring[ks & 3], q[ks]);
       else
-        mfma_acc_v(sn, ring[ks & 3], q[ks]);
-      ring[ks & 3] = ks + 4 < 36 ? read_qk(ks + 4) : read_pv(ks + 4 - 36);
-      if (ks % 7 == 2) dma_step(nsrc, ncnt, ndst, ks / 7, lane16);  // loads 0-4 (slots 2, 9, .., 30)
-      if (ks < kSoftmaxStages) softmax_stage(ks, cnt, sc);
-      if (ks == 12) pid_v = lds_pages[((t + kNumBufs) >> 1) < npages ? (t + kNumBufs) >> 1 : 0];
+        mfma_acc_v_last(s, ring[ks & 3], q[ks]);
+      if (ks + 4 < 36) ring[ks & 3] = rd(ks + 4);
+      if (ks == 2) g = make_group(un, __builtin_amdgcn_readfirstlane(pid_v), lane16);
+      if (ks % 7 == 2) dma_step(g.src, g.cnt, g.dst_a, g.dst_b, ks / 7, g.lane16);  // loads 0-4
+      if (pv_next) {
+        if (ks == 20) flags = read_flags(t - 1);
+        if (ks >= 24 && ks < 32) pp[ks - 24] = read_p(t - 1, ks - 24);
+        if (ks == 32) apv[0] = read_pv(0, 0);
+        if (ks == 34) apv[1] = read_pv(1, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (rescale) {
-      acc_wait_mfma();
-#pragma unroll
-      for (int cb = 0; cb < 16; ++cb) acc_scale(o[cb], alpha);
-      asm volatile("s_nop 4" ::: "memory");
-    }
-    pin_after_valu(pk[0], pk[1]);
+    return g;
+  };
 
+  // ---- weighted sum of one tile: O^T[latent block 4 wave + c][head block hb] += tile^T P^T, in
+  // the order (token half kk, latent block c, head block hb); each A operand serves four MFMAs.
+  // With a softmax (of the tile scored just before), its stages ride in the MFMA gaps, and the
+  // last four loads of group g go out in between.
+  auto pv_chain = [&](bool with_softmax, int cnt, const Group* g) {
 #pragma unroll
     for (int m = 0; m < 32; ++m) {
-      mfma_acc_a(o[m >> 1], ring[m & 3], pk[m & 1]);
-      if (m + 4 < 32) ring[m & 3] = read_pv(m + 4);
-      if (m % 7 == 3 && m < 28) dma_step(nsrc, ncnt, ndst, 5 + m / 7, lane16);  // loads 5-8 (slots 3, .., 24)
-      if (m == 8) page_ahead = __builtin_amdgcn_readfirstlane(pid_v);
+      const int j = m >> 2, hb = m & 3, kk = j >> 2, c = j & 3;
+      mfma_acc_a(o[4 * c + hb], apv[j % 3], pp[kk * 4 + hb]);
+      if (hb == 0 && j + 2 < 8) apv[(j + 2) % 3] = read_pv((j + 2) & 3, (j + 2) >> 2);
+      if (with_softmax && m < kSoftmaxStages) softmax_stage(m, cnt, s);
+      if (g && m % 7 == 3 && m < 28) dma_step(g->src, g->cnt, g->dst_a, g->dst_b, 5 + m / 7, g->lane16);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // kTree: mask the next tile's scores here, where the operand ring is dead (its registers are
-    // what the masking needs) and 32 MFMAs separate the last write of sn from these reads
-    if constexpr (kTree) tree_mask_tile(sn, t + 1);
-    if (attn_barrier_after(t, ntiles)) {  // every read of tile t done, tile t+2 landed: publish, then prefetch
-      dma_wait_tiles(1);
-      __builtin_amdgcn_s_barrier();
-      advance_qk(t + 1);
+    if (with_softmax) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) ring[g] = read_qk(g);
-    } else if constexpr (kTree) {
-      // Past the last tile the ring keeps its spent values for the stale scores; refilled from the
-      // current buffer instead (any LDS bytes do), its old values die before the masking above.
-#pragma unroll
-      for (int g = 0; g < 4; ++g) ring[g] = read_qk(g);
+      for (int st = 32; st < kSoftmaxStages; ++st) softmax_stage(st, cnt, s);
     }
-    advance_pv(t);
   };
-  // Unrolled twice so that the two score buffers alternate: a loop-carried copy of an MFMA result
-  // (which the compiler cannot see being written) could be placed before the write completes.
-  for (int t = 0; t < ntiles; t += 2) {
-    iteration(t, sa, sb);
-    if (t + 1 < ntiles) iteration(t + 1, sb, sa);
+
+  // ---- probabilities of tile t to ring P for every wave, with this wave's rescale word and
+  // factors; then the barrier that publishes them and tile t + 1.
+  auto publish = [&](int t) {
+    const uint32_t pb = attn_p_buffer(t);
+    *(MLA_LDS bf16x8*)(smem + p_lane + pb * kBufP + wave * 2048) = pk[0];
+    *(MLA_LDS bf16x8*)(smem + p_lane + pb * kBufP + wave * 2048 + 1024) = pk[1];
+    *(MLA_LDS float*)(smem + kOffAlpha + pb * (kHeads * 4) + (32 * wave + l32) * 4) = alpha;
+    if (lane == 0) *(MLA_LDS uint32_t*)(smem + kOffFlags + pb * 16 + wave * 4) = rescale ? 1u : 0u;
+    dma_wait_tiles(1);  // this wave's loads of tile t + 1 have landed
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  auto advance_pv = [&](int t) {  // from tile t's ring-A buffer to tile t + 1's
+    const int st = attn_a_buffer(t + 1) * kBufA - attn_a_buffer(t) * kBufA;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      pv_lo[k] += st;
+      pv_hi[k] += st;
+    }
+  };
+
+  dma_wait_tiles(1);  // tile 0 has landed (this wave's part)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  // iteration 0: scores of tile 0, then its softmax alone (no weighted sum yet)
+  {
+    const Group g = score_chain(0, false);
+    if constexpr (kTree) tree_mask_tile(s, 0);
+    const int cnt = tile_count(0);
+#pragma unroll
+    for (int st = 0; st < kSoftmaxStages; ++st) softmax_stage(st, cnt, s);
+#pragma unroll
+    for (int k = 5; k < kDmaPerTile; ++k) dma_step(g.src, g.cnt, g.dst_a, g.dst_b, k, g.lane16);
+    publish(0);
+  }
+  for (int t = 1; t < ntiles; ++t) {
+    const Group g = score_chain(t, true);
+    if constexpr (kTree) tree_mask_tile(s, t);
+    rescale_o(t - 1, flags);
+    pv_chain(true, tile_count(t), &g);
+    advance_pv(t - 1);
+    publish(t);
+  }
+  // weighted sum of the last tile
+  {
+    const int t = ntiles;
+    flags = read_flags(t - 1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pp[i] = read_p(t - 1, i);
+    apv[0] = read_pv(0, 0);
+    apv[1] = read_pv(1, 0);
+    rescale_o(t - 1, flags);
+    pv_chain(false, 0, nullptr);
   }
 
+  // ---- epilogue: 1 / sum of weights of every head from its owner, then the output rows
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;  // every key masked: o = 0, lse = -inf
-  size_t o_idx;
-  float* lse_ptr;
-  {
-    int lane_e = lane;
-    asm volatile("" : "+v"(lane_e));
-    out_ptrs(lane_e, o_idx, lse_ptr);
-  }
-  // The last loads (stale prefetches) land in LDS before the staging below reuses it, and every
-  // wave has finished reading the tile buffers.
+  *(MLA_LDS float*)(smem + kOffInvL + (32 * wave + l32) * 4) = inv;
+  if (hf == 0 && a.lse_out) a.lse_out[w.out_row + 32 * wave + l32] = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
+  // The last loads (past the last tile) land before the staging below reuses the rings, and every
+  // wave has finished reading them.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   acc_wait_mfma();
+  float invh[4];
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb) invh[hb] = *(const MLA_LDS float*)(smem + kOffInvL + (32 * hb + l32) * 4);
+  // Element e of o[4 c + hb] of this lane: head 32 hb + l32, latent 32 (4 wave + c) + 8 (e/4) + 4 hf + e%4.
   if (a.final_out) {
 #pragma unroll
-    for (int cb = 0; cb < 16; ++cb)
+    for (int c = 0; c < 4; ++c)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4 v = {acc_read_scaled(o[cb][4 * g], inv), acc_read_scaled(o[cb][4 * g + 1], inv),
-                   acc_read_scaled(o[cb][4 * g + 2], inv), acc_read_scaled(o[cb][4 * g + 3], inv)};
-        store4(o_idx, cb, g, v);
+      for (int hb = 0; hb < 4; ++hb) {
+        float* row = (float*)a.o_out + (w.out_row + 32 * hb + l32) * kDc + 32 * (4 * wave + c) + 4 * hf;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x16& acc = o[4 * c + hb];
+          const f32x4 v = {acc_read_scaled(acc[4 * g4], invh[hb]), acc_read_scaled(acc[4 * g4 + 1], invh[hb]),
+                           acc_read_scaled(acc[4 * g4 + 2], invh[hb]), acc_read_scaled(acc[4 * g4 + 3], invh[hb])};
+          *(f32x4*)(row + 8 * g4) = v;
+        }
       }
   } else {
-    // bf16 partial rows go out through LDS: each lane holds 4-value pieces of one head's row, so
-    // direct stores would write 32 rows x 16 B per instruction; staged, one store writes one
-    // whole 1 KiB row.  Rows are 1040 B apart in LDS (2-way bank conflicts on the writes).
-    constexpr int kStageRow = kDc * 2 + 16;
-    MLA_LDS char* stage = smem + wave * (32 * kStageRow);
+    // bf16 partial rows go out through LDS: each lane holds 4-value pieces of four heads' rows, so
+    // direct stores would write 32 rows x 8 B per instruction; staged, one store writes one
+    // whole 1 KiB row.
 #pragma unroll
-    for (int cb = 0; cb < 16; ++cb)
+    for (int c = 0; c < 4; ++c)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const u32x2 v = {pack_bf16x2(acc_read_scaled(o[cb][4 * g], inv), acc_read_scaled(o[cb][4 * g + 1], inv)),
-                         pack_bf16x2(acc_read_scaled(o[cb][4 * g + 2], inv), acc_read_scaled(o[cb][4 * g + 3], inv))};
-        *(MLA_LDS u32x2*)(stage + l32 * kStageRow + (32 * cb + 8 * g + 4 * hf) * 2) = v;
-      }
+      for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x16& acc = o[4 * c + hb];
+          const u32x2 v = {pack_bf16x2(acc_read_scaled(acc[4 * g4], invh[hb]), acc_read_scaled(acc[4 * g4 + 1], invh[hb])),
+                           pack_bf16x2(acc_read_scaled(acc[4 * g4 + 2], invh[hb]), acc_read_scaled(acc[4 * g4 + 3], invh[hb]))};
+          *(MLA_LDS u32x2*)(smem + (32 * hb + l32) * kStageRow + (32 * (4 * wave + c) + 8 * g4 + 4 * hf) * 2) = v;
+        }
+    __syncthreads();
     uint16_t* rows = (uint16_t*)a.o_out + (w.out_row + wave * 32) * kDc + 8 * lane;
 #pragma unroll 8
     for (int r = 0; r < 32; ++r)
-      *(u32x4*)(rows + (size_t)r * kDc) = *(const MLA_LDS u32x4*)(stage + r * kStageRow + 16 * lane);
+      *(u32x4*)(rows + (size_t)r * kDc) = *(const MLA_LDS u32x4*)(smem + (wave * 32 + r) * kStageRow + 16 * lane);
   }
-  if (hf == 0 && lse_ptr) *lse_ptr = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
 }
 
 // fp32 path: one workgroup per (b, i, split, head); 256 threads.  Logits one token per thread,

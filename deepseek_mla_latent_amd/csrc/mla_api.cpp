@@ -459,12 +459,13 @@ mla_status mla_out_proj_fp8(const float* o_lat, const void* w_uv_fp8, void* out,
   return MLA_OK;
 }
 
-mla_status mla_debug_attn_schedule(int32_t ntiles, int32_t* dma_buffer, int32_t* barrier_after) {
+mla_status mla_debug_attn_schedule(int32_t ntiles, int32_t* a_buffer, int32_t* b_buffer, int32_t* p_buffer) {
   if (ntiles < 1) return MLA_ERR_SHAPE;
-  if (!dma_buffer || !barrier_after) return MLA_ERR_NULL;
-  for (int t = 0; t < ntiles; ++t) {
-    dma_buffer[t] = mla::attn_dma_buffer(t, ntiles);
-    barrier_after[t] = mla::attn_barrier_after(t, ntiles) ? 1 : 0;
+  if (!a_buffer || !b_buffer || !p_buffer) return MLA_ERR_NULL;
+  for (int u = 0; u < ntiles; ++u) {
+    a_buffer[u] = mla::attn_a_buffer(u + mla::kLoadAhead);
+    b_buffer[u] = mla::attn_b_buffer(u + mla::kLoadAhead);
+    p_buffer[u] = mla::attn_p_buffer(u);
   }
   return MLA_OK;
 }

@@ -350,12 +350,14 @@ const char* mla_status_str(mla_status s);
 /*
  * Introspection for tests (host only, touches no device): the LDS ring schedule the bf16
  * attention kernel follows over a key range of ntiles 32-token tiles. For each iteration
- * t < ntiles, dma_buffer[t] receives the ring buffer (0..3) that the direct-to-LDS loads issued in
- * iteration t write, and barrier_after[t] receives 1 if a workgroup barrier closes iteration t,
- * else 0. Both arrays are caller-owned host arrays of at least ntiles entries.
- * Returns MLA_ERR_SHAPE if ntiles < 1, MLA_ERR_NULL if an array is NULL, else MLA_OK.
+ * u < ntiles: a_buffer[u] and b_buffer[u] receive the ring-A buffer (0..3, latent rows) and the
+ * ring-B buffer (0..2, RoPE-key rows) that the loads issued in iteration u write (those of tile
+ * u + 2, which carry data only while u + 2 < ntiles), and p_buffer[u] the ring-P buffer (0..1)
+ * that the probabilities of tile u are written to. The arrays are caller-owned host arrays of at
+ * least ntiles entries. Returns MLA_ERR_SHAPE if ntiles < 1, MLA_ERR_NULL if an array is NULL,
+ * else MLA_OK.
  */
-mla_status mla_debug_attn_schedule(int32_t ntiles, int32_t* dma_buffer, int32_t* barrier_after);
+mla_status mla_debug_attn_schedule(int32_t ntiles, int32_t* a_buffer, int32_t* b_buffer, int32_t* p_buffer);
 
 #ifdef __cplusplus
 }
