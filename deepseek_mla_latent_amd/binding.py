@@ -22,13 +22,14 @@ MLA_BF16 = 1
 STATUS = {
     0: "MLA_OK", -1: "MLA_ERR_NULL", -2: "MLA_ERR_SHAPE", -3: "MLA_ERR_DTYPE", -4: "MLA_ERR_ALIGN",
     -5: "MLA_ERR_WORKSPACE", -6: "MLA_ERR_UNSUPPORTED", -7: "MLA_ERR_LAUNCH", -8: "MLA_ERR_DEVICE",
+    -9: "MLA_ERR_SCRATCH",
 }
 EXPORTS = ("mla_absorb_q", "mla_decode_workspace_bytes", "mla_decode_num_splits", "mla_decode_attn",
            "mla_decode_attn_tree", "mla_decode_attn_out_proj_workspace_bytes", "mla_decode_attn_out_proj",
            "mla_out_proj", "mla_prefill_kv_bytes", "mla_prefill_kv_up", "mla_prefill_attn",
            "mla_linear_workspace_bytes", "mla_linear", "mla_rope_append", "mla_fp8_weight_bytes",
            "mla_quantize_w_uk_fp8", "mla_quantize_w_uv_fp8", "mla_absorb_q_fp8", "mla_out_proj_fp8", "mla_status_str",
-           "mla_debug_attn_schedule")
+           "mla_debug_attn_schedule", "mla_decode_attn_out_proj_static")
 
 
 class MlaLibraryMissing(RuntimeError):
@@ -106,6 +107,8 @@ def load_library(path: Optional[str] = None):
     lib.mla_decode_attn_out_proj_workspace_bytes.restype = sz
     lib.mla_decode_attn_out_proj.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i32, pp, vp]
     lib.mla_decode_attn_out_proj.restype = i32
+    lib.mla_decode_attn_out_proj_static.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, pp, vp]
+    lib.mla_decode_attn_out_proj_static.restype = i32
     lib.mla_out_proj.argtypes = [vp, vp, vp, pp, vp]
     lib.mla_out_proj.restype = i32
     lib.mla_prefill_kv_bytes.argtypes = [pp]
@@ -236,6 +239,15 @@ def mla_decode_attn_out_proj(q_lat, q_pe, kv_pool, block_table, seq_lens, tree_p
                                         _ptr(tree_parents), _ptr(w_uv), _ptr(out), _ptr(o_lat), _ptr(lse),
                                         _ptr(workspace), _nbytes(workspace, workspace_bytes), num_splits,
                                         ctypes.byref(params), _stream(stream)), "mla_decode_attn_out_proj")
+
+
+def mla_decode_attn_out_proj_static(q_lat, q_pe, kv_pool, block_table, seq_lens, tree_parents, w_uv, out, o_lat,
+                                    lse, num_splits: int, params: mla_params, stream=None) -> None:
+    lib = load_library()
+    _check(lib.mla_decode_attn_out_proj_static(_ptr(q_lat), _ptr(q_pe), _ptr(kv_pool), _ptr(block_table),
+                                               _ptr(seq_lens), _ptr(tree_parents), _ptr(w_uv), _ptr(out),
+                                               _ptr(o_lat), _ptr(lse), num_splits, ctypes.byref(params),
+                                               _stream(stream)), "mla_decode_attn_out_proj_static")
 
 
 def mla_out_proj(o_lat, w_uv, out, params: mla_params, stream=None) -> None:

@@ -134,6 +134,7 @@ const char* mla_status_str(mla_status s) {
     case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: only H=128, d_c=512, d_R=64, d_h=128, page 64";
     case MLA_ERR_LAUNCH: return "MLA_ERR_LAUNCH: kernel launch failed";
     case MLA_ERR_DEVICE: return "MLA_ERR_DEVICE: no usable HIP device";
+    case MLA_ERR_SCRATCH: return "MLA_ERR_SCRATCH: the call needs more than MLA_STATIC_SCRATCH_BYTES of static scratch";
   }
   return "unknown mla_status";
 }

@@ -61,7 +61,8 @@ typedef enum {
   MLA_ERR_WORKSPACE = -5,   /* workspace / kv buffer smaller than its _bytes() query */
   MLA_ERR_UNSUPPORTED = -6, /* head dims / page size other than the supported set */
   MLA_ERR_LAUNCH = -7,      /* the HIP runtime rejected a launch */
-  MLA_ERR_DEVICE = -8       /* no usable HIP device */
+  MLA_ERR_DEVICE = -8,      /* no usable HIP device */
+  MLA_ERR_SCRATCH = -9      /* the request needs more than MLA_STATIC_SCRATCH_BYTES of static scratch */
 } mla_status;
 
 typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
@@ -198,6 +199,31 @@ mla_status mla_decode_attn_out_proj(const void* q_lat, const void* q_pe, const v
                                     const int32_t* tree_parents, const void* w_uv, void* out, float* o_lat,
                                     float* lse, void* workspace, size_t workspace_bytes, int32_t num_splits,
                                     const mla_params* p, void* stream);
+
+/*
+ * Static scratch of mla_decode_attn_out_proj_static: 64 MiB of device memory per GPU, held from the
+ * library's load until the process ends (the split partials of 32 sequences x 8 key ranges, or of
+ * 256 query rows x 2 ranges, take 33.7 MB).
+ */
+#define MLA_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * mla_decode_attn_out_proj without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP-graph capture, serving loops and harnesses that forbid allocation): the
+ * scratch the call needs (mla_decode_attn_out_proj_workspace_bytes(p, num_splits) bytes) is taken
+ * from a static device array of MLA_STATIC_SCRATCH_BYTES that each GPU holds for the life of the
+ * process. The call allocates and frees nothing. Every other argument, every output and every error
+ * is as for mla_decode_attn_out_proj, plus MLA_ERR_SCRATCH (returned before any launch) when the
+ * scratch needed exceeds MLA_STATIC_SCRATCH_BYTES, and MLA_ERR_DEVICE when the array's device
+ * address cannot be looked up. The array keeps what the last call left in it; all calls on one
+ * GPU share it, so calls that overlap on one GPU (on different streams, or from different
+ * threads without ordering) race and give undefined results.
+ */
+mla_status mla_decode_attn_out_proj_static(const void* q_lat, const void* q_pe, const void* kv_pool,
+                                           const int32_t* block_table, const int32_t* seq_lens,
+                                           const int32_t* tree_parents, const void* w_uv, void* out,
+                                           float* o_lat, float* lse, int32_t num_splits, const mla_params* p,
+                                           void* stream);
 
 /*
  * ---- Prefill in multi-head form ("order 1") --------------------------------------------------

@@ -260,3 +260,17 @@ def test_a_second_runtime_is_refused():
                 "    print('refused')\n")
     assert r.returncode == 0, r.stderr
     assert r.stdout.strip() == "refused"
+
+
+def test_static_scratch_limit_is_checked_on_the_host():
+    """mla_decode_attn_out_proj_static refuses a request larger than its static scratch before it
+    touches any device (explicit split count: no device query either)."""
+    p = P(batch=4096, q_len=2, max_seq_len=131072)
+    need = binding.mla_decode_attn_out_proj_workspace_bytes(p, 8)
+    assert need > (64 << 20)
+    r = lib.mla_decode_attn_out_proj_static(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, None, 8,
+                                            ctypes.byref(p), None)
+    assert r == -9
+    assert lib.mla_status_str(-9).decode().startswith("MLA_ERR_SCRATCH")
+    assert lib.mla_decode_attn_out_proj_static(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, None, 8,
+                                               None, None) == -1
