@@ -278,16 +278,18 @@ __global__ __launch_bounds__(256, 1) void out_proj_bf16_kernel(const float* __re
 // a round trip through HBM (it is written only when asked for).  Merging is "【笔记】MLA矩阵吸收分析"
 // §三.2 step 1 over key ranges, the projection its step 2.
 //
-// Workgroup = (head h, block of 16 rows), 8 waves (two per SIMD); the blocks of one head have
-// consecutive logical ids (one XCD, so W_UV[h] comes from HBM once).  Wave w owns latent rows
-// [64 w, +64), so each wave's loads (2 batches of 4 splits' partials and lse, 16 W loads) stay
-// within the 63 the vector-memory counter tracks and go out in one round trip:
+// Workgroup = (head h, a run of 16-row blocks), 8 waves (two per SIMD); a head has two workgroups
+// with consecutive logical ids (one XCD, so W_UV[h] comes from HBM once), and each stages its
+// W_UV[h] slices once for all of its row blocks.  Wave w owns latent rows [64 w, +64), so each
+// wave's first loads (2 batches of 4 splits' partials and lse, 16 W loads) stay within the 63 the
+// vector-memory counter tracks and go out in one round trip:
 //   * its 16 KiB slice of W_UV[h] goes to LDS (direct-to-LDS, 4 rows of 256 B per load);
-//   * lane l merges row l % 16 at latent 64 w + 32 ks + 8 (l / 16) + j (ks < 2, j < 8): exactly
-//     the B operand of a 16x16x32 MFMA, so the merged values never leave the lane.  They are split
-//     into hi + lo bf16 (two MFMAs, about 16 mantissa bits of the fp32 merge kept);
+//   * lane l merges row l % 16 of the block at latent 64 w + 32 ks + 8 (l / 16) + j (ks < 2,
+//     j < 8): exactly the B operand of a 16x16x32 MFMA, so the merged values never leave the lane.
+//     They are split into hi + lo bf16 (two MFMAs, about 16 mantissa bits of the fp32 merge kept);
 //   * D(16 values x 16 rows) for the 8 value blocks over its 64 latent rows, A = W_UV^T by
-//     transposed LDS reads; the eight waves' partial sums meet in LDS.
+//     transposed LDS reads; the next block's first partials load meanwhile;
+//   * the eight waves' partial sums meet in four 8 KiB slots in LDS, beside the W slices.
 // LDS row c of a wave's slice holds 32-byte block b (16 values) at block b ^ fsw(c) with
 // fsw(c) = (c & 3) | ((c >> 3) & 1) << 2: a transposed read covers 16 rows x 32 B, which this puts
 // on every bank pair exactly twice.
@@ -302,28 +304,33 @@ __global__ __launch_bounds__(512, 1) void merge_out_proj_kernel(const uint16_t* 
                                                                 const float* __restrict__ lse_part,
                                                                 const uint16_t* __restrict__ w_uv,
                                                                 uint16_t* __restrict__ out, float* __restrict__ o_lat,
-                                                                float* __restrict__ lse, int rows, int num_splits) {
-  __shared__ __attribute__((aligned(1024))) char wl_raw[kDc * kDh * 2];  // 128 KiB, then the sums
+                                                                float* __restrict__ lse, int rows, int num_splits,
+                                                                int blocks_per_wg) {
+  __shared__ __attribute__((aligned(1024))) char wl_raw[kDc * kDh * 2];  // 128 KiB: the W_UV[h] slices
+  __shared__ __attribute__((aligned(1024))) char red_raw[4 * 8 * 4 * 64 * 4];  // 32 KiB: four sum slots
   MLA_LDS char* const wl = (MLA_LDS char*)wl_raw;
+  MLA_LDS float* const red = (MLA_LDS float*)red_raw;  // slot s: [value block][element][lane]
   const int nblk = (rows + kMopRows - 1) / kMopRows;
+  const int wph = (nblk + blocks_per_wg - 1) / blocks_per_wg;  // workgroups per head
   const int id = xcd_remap(blockIdx.x, gridDim.x);
-  const int h = id / nblk, r0 = (id % nblk) * kMopRows;
+  const int h = id / wph, blk0 = (id % wph) * blocks_per_wg;
+  const int blk_end = blk0 + blocks_per_wg < nblk ? blk0 + blocks_per_wg : nblk;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, g = lane >> 4, s16 = lane & 15;
   const int c0 = 64 * wave;
   MLA_LDS char* const ws = wl + wave * (64 * kDh * 2);  // this wave's 64 rows x 256 B
 
-  // merge: row n = r0 + s16 (a row past the end reads row r0, which exists, and stores nothing)
-  const int n = r0 + s16 < rows ? r0 + s16 : r0;
-  const size_t base = (size_t)n * num_splits * kHeads + h;  // split k at base + k * kHeads
-  const float* lp = lse_part + base;
-  const uint16_t* op = o_part + base * kDc + c0 + 8 * g;  // + 32 ks
+  // merge: row n = 16 blk + s16 (a row past the end reads row 16 blk, which exists, and stores nothing)
+  auto row_of = [&](int blk) { return 16 * blk + s16 < rows ? 16 * blk + s16 : 16 * blk; };
   // Batches of 4 splits (a split past the end repeats the last one with weight 0), two in flight.
   struct Batch {
     u32x4 x[4][2];  // [split][ks]
     float l[4];
   };
-  auto load = [&](int kb, Batch& bt) {
+  auto load = [&](int blk, int kb, Batch& bt) {
+    const size_t base = (size_t)row_of(blk) * num_splits * kHeads + h;  // split k at base + k * kHeads
+    const float* lp = lse_part + base;
+    const uint16_t* op = o_part + base * kDc + c0 + 8 * g;  // + 32 ks
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int k = kb + j < num_splits ? kb + j : num_splits - 1;
@@ -333,10 +340,11 @@ __global__ __launch_bounds__(512, 1) void merge_out_proj_kernel(const uint16_t* 
     }
   };
   Batch b0, b1;
-  load(0, b0);
-  if (4 < num_splits) load(4, b1);
+  load(blk0, 0, b0);
+  if (4 < num_splits) load(blk0, 4, b1);
   // W_UV[h] rows [c0, c0 + 64) after the first partials, so waiting for those does not wait for
-  // W: load i covers local rows 4 i .. 4 i + 3 (16 lanes each)
+  // W: load i covers local rows 4 i .. 4 i + 3 (16 lanes each).  Staged once for every row block of
+  // the workgroup.
   {
     const char* src = (const char*)(w_uv + ((size_t)h * kDc + c0) * kDh);
 #pragma unroll
@@ -347,113 +355,129 @@ __global__ __launch_bounds__(512, 1) void merge_out_proj_kernel(const uint16_t* 
                                        (MLA_LDS void*)(ws + i * 1024), 16, 0, 0);
     }
   }
-
-  // Running log-sum-exp merge: weights are taken against the largest lse seen so far, and the
-  // sums are rescaled when a batch raises it (an empty split has lse = -inf and weight 0).
-  constexpr float kLog2e = 1.4426950408889634f;
-  f32x4 acc_o[4];  // latent 32 ks + 8 g + 4 e2 + e in acc_o[2 ks + e2][e]
-#pragma unroll
-  for (int i = 0; i < 4; ++i) acc_o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, sum = 0.f;
-  auto consume = [&](const Batch& bt) {
-    const float m_new = fmaxf(fmaxf(m, fmaxf(bt.l[0], bt.l[1])), fmaxf(bt.l[2], bt.l[3]));
-    const float scale = m_new > m ? (m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - m_new) * kLog2e)) : 1.f;
-    m = m_new;
-    sum *= scale;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc_o[i] *= scale;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float w = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((bt.l[j] - m) * kLog2e);
-      sum += w;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const u32x4 u = bt.x[j][ks];
-        acc_o[2 * ks] += w * f32x4{__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xffff0000u),
-                                   __uint_as_float(u[1] << 16), __uint_as_float(u[1] & 0xffff0000u)};
-        acc_o[2 * ks + 1] += w * f32x4{__uint_as_float(u[2] << 16), __uint_as_float(u[2] & 0xffff0000u),
-                                       __uint_as_float(u[3] << 16), __uint_as_float(u[3] & 0xffff0000u)};
-      }
-    }
-  };
-  for (int kb = 0; kb < num_splits; kb += 8) {
-    consume(b0);
-    if (kb + 8 < num_splits) load(kb + 8, b0);
-    if (kb + 4 < num_splits) {
-      consume(b1);
-      if (kb + 12 < num_splits) load(kb + 12, b1);
-    }
-  }
-  const float inv = sum > 0.f ? 1.0f / sum : 0.f;
-  const bool live = r0 + s16 < rows;
-  bf16x8 bh[2], bl[2];
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const f32x4 a = acc_o[2 * ks] * inv, b = acc_o[2 * ks + 1] * inv;
-    if (o_lat && live) {
-      f32x4* dst = (f32x4*)(o_lat + ((size_t)n * kHeads + h) * kDc + c0 + 32 * ks + 8 * g);
-      dst[0] = a;
-      dst[1] = b;
-    }
-    const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    u32x4 hw, lw;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      hw[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
-      const float d0 = v[2 * j] - __uint_as_float(hw[j] << 16);
-      const float d1 = v[2 * j + 1] - __uint_as_float(hw[j] & 0xffff0000u);
-      lw[j] = pack_bf16x2(d0, d1);
-    }
-    bh[ks] = __builtin_bit_cast(bf16x8, hw);
-    bl[ks] = __builtin_bit_cast(bf16x8, lw);
-  }
-  if (lse && live && wave == 0 && g == 0) lse[(size_t)n * kHeads + h] = m == -INFINITY ? -INFINITY : m + logf(sum);
-
   // A operand of value block mb, k step ks: two transposed reads; source lane s of group g gives
   // local row 32 ks + 8 g + 4 t + s/4 and values 16 mb + 4 (s%4) .. +3 (t = 0, 1).
   const int fsw = (s16 >> 2) | ((g & 1) << 2);  // mop_swz of every row this lane addresses
   const MLA_LDS char* a_row = ws + (8 * g + (s16 >> 2)) * (kDh * 2) + (s16 & 3) * 8;
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's W rows have landed
-  f32x4 acc[8];
-#pragma unroll
-  for (int mb = 0; mb < 8; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
-      const MLA_LDS char* p = a_row + ks * 32 * (kDh * 2) + ((mb ^ fsw) * 32);
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)p);
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(p + 4 * (kDh * 2)));
-      const i16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      const bf16x8 av = __builtin_bit_cast(bf16x8, a8);
-      acc[mb] = mfma16x16x32(av, bh[ks], acc[mb]);
-      acc[mb] = mfma16x16x32(av, bl[ks], acc[mb]);
-    }
+  constexpr float kLog2e = 1.4426950408889634f;
 
-  // The eight waves' partial sums meet in LDS (over the W slices, once every wave is done with
-  // them): red[((w * 8 + mb) * 4 + i) * 64 + lane], element i of lane l being value 16 mb + 4 g + i
-  // of row s16.  Wave w then adds value block w.
-  __syncthreads();
-  MLA_LDS float* red = (MLA_LDS float*)wl;
+  for (int blk = blk0; blk < blk_end; ++blk) {
+    const int n = row_of(blk);
+    const bool live = 16 * blk + s16 < rows;
+    // Running log-sum-exp merge: weights are taken against the largest lse seen so far, and the
+    // sums are rescaled when a batch raises it (an empty split has lse = -inf and weight 0).
+    f32x4 acc_o[4];  // latent 32 ks + 8 g + 4 e2 + e in acc_o[2 ks + e2][e]
 #pragma unroll
-  for (int mb = 0; mb < 8; ++mb)
+    for (int i = 0; i < 4; ++i) acc_o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, sum = 0.f;
+    auto consume = [&](const Batch& bt) {
+      const float m_new = fmaxf(fmaxf(m, fmaxf(bt.l[0], bt.l[1])), fmaxf(bt.l[2], bt.l[3]));
+      const float scale = m_new > m ? (m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - m_new) * kLog2e)) : 1.f;
+      m = m_new;
+      sum *= scale;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) red[((wave * 8 + mb) * 4 + i) * 64 + lane] = acc[mb][i];
-  __syncthreads();
-  {
-    const int mb = wave;
-    float sv[4];
+      for (int i = 0; i < 4; ++i) acc_o[i] *= scale;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float t = 0.f;
+      for (int j = 0; j < 4; ++j) {
+        const float w = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((bt.l[j] - m) * kLog2e);
+        sum += w;
 #pragma unroll
-      for (int ww = 0; ww < 8; ++ww) t += red[((ww * 8 + mb) * 4 + i) * 64 + lane];
-      sv[i] = t;
+        for (int ks = 0; ks < 2; ++ks) {
+          const u32x4 u = bt.x[j][ks];
+          acc_o[2 * ks] += w * f32x4{__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xffff0000u),
+                                     __uint_as_float(u[1] << 16), __uint_as_float(u[1] & 0xffff0000u)};
+          acc_o[2 * ks + 1] += w * f32x4{__uint_as_float(u[2] << 16), __uint_as_float(u[2] & 0xffff0000u),
+                                         __uint_as_float(u[3] << 16), __uint_as_float(u[3] & 0xffff0000u)};
+        }
+      }
+    };
+    for (int kb = 0; kb < num_splits; kb += 8) {
+      consume(b0);
+      if (kb + 8 < num_splits) load(blk, kb + 8, b0);
+      if (kb + 4 < num_splits) {
+        consume(b1);
+        if (kb + 12 < num_splits) load(blk, kb + 12, b1);
+      }
     }
-    if (live) {
-      const u32x2 pk = {pack_bf16x2(sv[0], sv[1]), pack_bf16x2(sv[2], sv[3])};
-      *(u32x2*)(out + ((size_t)n * kHeads + h) * kDh + 16 * mb + 4 * g) = pk;
+    const float inv = sum > 0.f ? 1.0f / sum : 0.f;
+    bf16x8 bh[2], bl[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const f32x4 a = acc_o[2 * ks] * inv, b = acc_o[2 * ks + 1] * inv;
+      if (o_lat && live) {
+        f32x4* dst = (f32x4*)(o_lat + ((size_t)n * kHeads + h) * kDc + c0 + 32 * ks + 8 * g);
+        dst[0] = a;
+        dst[1] = b;
+      }
+      const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+      u32x4 hw, lw;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        hw[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
+        const float d0 = v[2 * j] - __uint_as_float(hw[j] << 16);
+        const float d1 = v[2 * j + 1] - __uint_as_float(hw[j] & 0xffff0000u);
+        lw[j] = pack_bf16x2(d0, d1);
+      }
+      bh[ks] = __builtin_bit_cast(bf16x8, hw);
+      bl[ks] = __builtin_bit_cast(bf16x8, lw);
     }
+    if (lse && live && wave == 0 && g == 0) lse[(size_t)n * kHeads + h] = m == -INFINITY ? -INFINITY : m + logf(sum);
+
+    if (blk == blk0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's W rows have landed
+    // the next row block's first partials stream in during this block's products and sums
+    if (blk + 1 < blk_end) {
+      load(blk + 1, 0, b0);
+      if (4 < num_splits) load(blk + 1, 4, b1);
+    }
+    f32x4 acc[8];
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) {
+        const MLA_LDS char* p = a_row + ks * 32 * (kDh * 2) + ((mb ^ fsw) * 32);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)p);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(p + 4 * (kDh * 2)));
+        const i16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const bf16x8 av = __builtin_bit_cast(bf16x8, a8);
+        acc[mb] = mfma16x16x32(av, bh[ks], acc[mb]);
+        acc[mb] = mfma16x16x32(av, bl[ks], acc[mb]);
+      }
+
+    // The eight waves' partial sums (over their latent rows) meet in the four sum slots: waves 4-7
+    // put theirs in slots 0-3, waves 0-3 add them and put the pair sums back, then wave w adds value
+    // block w over the four slots.  Element i of lane l is value 16 mb + 4 g + i of row s16.
+    auto slot = [&](int sl, int mb, int i) -> MLA_LDS float& { return red[((sl * 8 + mb) * 4 + i) * 64 + lane]; };
+    if (wave >= 4) {
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) slot(wave - 4, mb, i) = acc[mb][i];
+    }
+    __syncthreads();
+    if (wave < 4) {
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[mb][i] += slot(wave, mb, i);
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) slot(wave, mb, i) = acc[mb][i];
+    }
+    __syncthreads();
+    {
+      const int mb = wave;
+      float sv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sv[i] = (slot(0, mb, i) + slot(1, mb, i)) + (slot(2, mb, i) + slot(3, mb, i));
+      if (live) {
+        const u32x2 pk = {pack_bf16x2(sv[0], sv[1]), pack_bf16x2(sv[2], sv[3])};
+        *(u32x2*)(out + ((size_t)n * kHeads + h) * kDh + 16 * mb + 4 * g) = pk;
+      }
+    }
+    __syncthreads();  // the slots are free for the next row block
   }
 }
 
@@ -532,10 +556,15 @@ hipError_t launch_absorb_q(const void* q_nope, const void* w_uk, void* q_lat, in
 hipError_t launch_merge_out_proj(const void* o_part, const float* lse_part, const void* w_uv, void* out,
                                  float* o_lat, float* lse, int rows, int num_splits, hipStream_t stream) {
   forget_stale_error();
-  const int64_t grid = (int64_t)kHeads * ((rows + kMopRows - 1) / kMopRows);
-  if (grid == 0) return hipSuccess;
+  // two workgroups per head (one per CU at 128 heads), each over a run of 16-row blocks, so a
+  // workgroup stages its W_UV[h] slices once for all of its rows
+  const int nblk = (rows + kMopRows - 1) / kMopRows;
+  const int wph = nblk < 2 ? nblk : 2;
+  if (wph == 0) return hipSuccess;
+  const int bpw = (nblk + wph - 1) / wph;
+  const int64_t grid = (int64_t)kHeads * ((nblk + bpw - 1) / bpw);
   hipLaunchKernelGGL(merge_out_proj_kernel, dim3((unsigned)grid), dim3(512), 0, stream, (const uint16_t*)o_part,
-                     lse_part, (const uint16_t*)w_uv, (uint16_t*)out, o_lat, lse, rows, num_splits);
+                     lse_part, (const uint16_t*)w_uv, (uint16_t*)out, o_lat, lse, rows, num_splits, bpw);
   return hipGetLastError();
 }
 
