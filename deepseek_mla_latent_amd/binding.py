@@ -15,6 +15,7 @@ from typing import Optional
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmla_latent.so")
+DEBUG_LIB_PATH = os.path.join(PKG, "libmla_latent_debug.so")  # bounds-checked build of the same sources
 
 MLA_F32 = 0
 MLA_BF16 = 1
@@ -29,7 +30,10 @@ EXPORTS = ("mla_absorb_q", "mla_decode_workspace_bytes", "mla_decode_num_splits"
            "mla_out_proj", "mla_prefill_kv_bytes", "mla_prefill_kv_up", "mla_prefill_attn",
            "mla_linear_workspace_bytes", "mla_linear", "mla_rope_append", "mla_fp8_weight_bytes",
            "mla_quantize_w_uk_fp8", "mla_quantize_w_uv_fp8", "mla_absorb_q_fp8", "mla_out_proj_fp8", "mla_status_str",
-           "mla_debug_attn_schedule", "mla_decode_attn_out_proj_static")
+           "mla_debug_attn_schedule", "mla_decode_attn_out_proj_static", "mla_debug_bounds_enabled",
+           "mla_debug_bounds_read")
+BOUNDS_BAD_SEQ_LEN = 1  # error-word bits of the bounds-checked build
+BOUNDS_BAD_PAGE = 2
 
 
 class MlaLibraryMissing(RuntimeError):
@@ -48,6 +52,7 @@ class mla_params(ctypes.Structure):
         ("kv_lora_rank", ctypes.c_int32), ("rope_dim", ctypes.c_int32), ("head_dim", ctypes.c_int32),
         ("page_size", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float), ("causal", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
     ]
 
 
@@ -65,6 +70,72 @@ def _hip_runtimes_mapped():
             return sorted({line.split()[-1] for line in f if "libamdhip64" in line})
     except OSError:
         return []
+
+
+def declare(lib, *, partial: bool = False):
+    """Set the ctypes signatures of every exported function on ``lib`` (a ctypes.CDLL).  With
+    ``partial``, functions the library does not export are skipped (a host-only build of the
+    C-ABI layer links a subset of the sources)."""
+
+    class _Lib:
+        def __getattr__(self, name):
+            if partial and not hasattr(lib, name):
+                return _Sink()
+            return getattr(lib, name)
+
+    class _Sink:
+        pass
+
+    L = _Lib()
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    pp = ctypes.POINTER(mla_params)
+    L.mla_absorb_q.argtypes = [vp, vp, vp, pp, vp]
+    L.mla_absorb_q.restype = i32
+    L.mla_decode_workspace_bytes.argtypes = [pp, i32]
+    L.mla_decode_workspace_bytes.restype = sz
+    L.mla_decode_num_splits.argtypes = [pp, i32]
+    L.mla_decode_num_splits.restype = i32
+    L.mla_decode_attn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i32, pp, vp]
+    L.mla_decode_attn.restype = i32
+    L.mla_decode_attn_tree.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i32, pp, vp]
+    L.mla_decode_attn_tree.restype = i32
+    L.mla_decode_attn_out_proj_workspace_bytes.argtypes = [pp, i32]
+    L.mla_decode_attn_out_proj_workspace_bytes.restype = sz
+    L.mla_decode_attn_out_proj.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i32, pp, vp]
+    L.mla_decode_attn_out_proj.restype = i32
+    L.mla_decode_attn_out_proj_static.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, pp, vp]
+    L.mla_decode_attn_out_proj_static.restype = i32
+    L.mla_out_proj.argtypes = [vp, vp, vp, pp, vp]
+    L.mla_out_proj.restype = i32
+    L.mla_prefill_kv_bytes.argtypes = [pp]
+    L.mla_prefill_kv_bytes.restype = sz
+    L.mla_prefill_kv_up.argtypes = [vp, vp, vp, vp, vp, vp, sz, pp, vp]
+    L.mla_prefill_kv_up.restype = i32
+    L.mla_prefill_attn.argtypes = [vp, vp, vp, sz, vp, vp, vp, pp, vp]
+    L.mla_prefill_attn.restype = i32
+    L.mla_linear_workspace_bytes.argtypes = [i32, i32, i32]
+    L.mla_linear_workspace_bytes.restype = sz
+    L.mla_linear.argtypes = [vp, vp, vp, i32, i32, i32, vp, sz, vp]
+    L.mla_linear.restype = i32
+    L.mla_rope_append.argtypes = [vp, vp, i32, vp, vp, vp, ctypes.c_float, pp, vp]
+    L.mla_rope_append.restype = i32
+    L.mla_fp8_weight_bytes.argtypes = []
+    L.mla_fp8_weight_bytes.restype = sz
+    for name in ("mla_quantize_w_uk_fp8", "mla_quantize_w_uv_fp8"):
+        getattr(L, name).argtypes = [vp, vp, sz, pp, vp]
+        getattr(L, name).restype = i32
+    for name in ("mla_absorb_q_fp8", "mla_out_proj_fp8"):
+        getattr(L, name).argtypes = [vp, vp, vp, pp, vp]
+        getattr(L, name).restype = i32
+    L.mla_status_str.argtypes = [i32]
+    L.mla_status_str.restype = ctypes.c_char_p
+    L.mla_debug_attn_schedule.argtypes = [i32, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    L.mla_debug_attn_schedule.restype = i32
+    L.mla_debug_bounds_enabled.argtypes = []
+    L.mla_debug_bounds_enabled.restype = i32
+    L.mla_debug_bounds_read.argtypes = [ctypes.POINTER(ctypes.c_uint32), i32]
+    L.mla_debug_bounds_read.restype = i32
+    return lib
 
 
 def load_library(path: Optional[str] = None):
@@ -91,50 +162,7 @@ def load_library(path: Optional[str] = None):
     if len(runtimes) > 1:
         raise MlaRuntimeConflict(f"{p} was loaded next to another HIP runtime: {runtimes}; load it in a process "
                                  "whose HIP runtime is already the one torch uses (import torch first)")
-    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
-    pp = ctypes.POINTER(mla_params)
-    lib.mla_absorb_q.argtypes = [vp, vp, vp, pp, vp]
-    lib.mla_absorb_q.restype = i32
-    lib.mla_decode_workspace_bytes.argtypes = [pp, i32]
-    lib.mla_decode_workspace_bytes.restype = sz
-    lib.mla_decode_num_splits.argtypes = [pp, i32]
-    lib.mla_decode_num_splits.restype = i32
-    lib.mla_decode_attn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i32, pp, vp]
-    lib.mla_decode_attn.restype = i32
-    lib.mla_decode_attn_tree.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i32, pp, vp]
-    lib.mla_decode_attn_tree.restype = i32
-    lib.mla_decode_attn_out_proj_workspace_bytes.argtypes = [pp, i32]
-    lib.mla_decode_attn_out_proj_workspace_bytes.restype = sz
-    lib.mla_decode_attn_out_proj.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i32, pp, vp]
-    lib.mla_decode_attn_out_proj.restype = i32
-    lib.mla_decode_attn_out_proj_static.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, pp, vp]
-    lib.mla_decode_attn_out_proj_static.restype = i32
-    lib.mla_out_proj.argtypes = [vp, vp, vp, pp, vp]
-    lib.mla_out_proj.restype = i32
-    lib.mla_prefill_kv_bytes.argtypes = [pp]
-    lib.mla_prefill_kv_bytes.restype = sz
-    lib.mla_prefill_kv_up.argtypes = [vp, vp, vp, vp, vp, vp, sz, pp, vp]
-    lib.mla_prefill_kv_up.restype = i32
-    lib.mla_prefill_attn.argtypes = [vp, vp, vp, sz, vp, vp, vp, pp, vp]
-    lib.mla_prefill_attn.restype = i32
-    lib.mla_linear_workspace_bytes.argtypes = [i32, i32, i32]
-    lib.mla_linear_workspace_bytes.restype = sz
-    lib.mla_linear.argtypes = [vp, vp, vp, i32, i32, i32, vp, sz, vp]
-    lib.mla_linear.restype = i32
-    lib.mla_rope_append.argtypes = [vp, vp, i32, vp, vp, vp, ctypes.c_float, pp, vp]
-    lib.mla_rope_append.restype = i32
-    lib.mla_fp8_weight_bytes.argtypes = []
-    lib.mla_fp8_weight_bytes.restype = sz
-    for name in ("mla_quantize_w_uk_fp8", "mla_quantize_w_uv_fp8"):
-        getattr(lib, name).argtypes = [vp, vp, sz, pp, vp]
-        getattr(lib, name).restype = i32
-    for name in ("mla_absorb_q_fp8", "mla_out_proj_fp8"):
-        getattr(lib, name).argtypes = [vp, vp, vp, pp, vp]
-        getattr(lib, name).restype = i32
-    lib.mla_status_str.argtypes = [i32]
-    lib.mla_status_str.restype = ctypes.c_char_p
-    lib.mla_debug_attn_schedule.argtypes = [i32, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32)]
-    lib.mla_debug_attn_schedule.restype = i32
+    declare(lib)
     if path is None:
         _lib = lib
     return lib
@@ -143,13 +171,13 @@ def load_library(path: Optional[str] = None):
 def make_params(*, batch: int, q_len: int, max_seq_len: int, max_pages_per_seq: Optional[int] = None,
                 softmax_scale: Optional[float] = None, causal: bool = True, dtype: int = MLA_BF16,
                 num_heads: int = 128, kv_lora_rank: int = 512, rope_dim: int = 64, head_dim: int = 128,
-                page_size: int = 64) -> mla_params:
+                page_size: int = 64, num_pages: int = 0) -> mla_params:
     if max_pages_per_seq is None:
         max_pages_per_seq = max(1, -(-max_seq_len // page_size))
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(head_dim + rope_dim)
     return mla_params(batch, q_len, num_heads, kv_lora_rank, rope_dim, head_dim, page_size, max_pages_per_seq,
-                      max_seq_len, softmax_scale, 1 if causal else 0, dtype)
+                      max_seq_len, softmax_scale, 1 if causal else 0, dtype, num_pages)
 
 
 def _ptr(x) -> Optional[int]:
@@ -181,6 +209,14 @@ def mla_debug_attn_schedule(ntiles: int):
     arrs = [(ctypes.c_int32 * ntiles)() for _ in range(3)]
     _check(load_library().mla_debug_attn_schedule(ntiles, *arrs), "mla_debug_attn_schedule")
     return tuple(list(a) for a in arrs)
+
+
+def mla_debug_bounds_read(lib=None, clear: bool = True):
+    """(violation bits, report count) of the bounds-checked library's error word (waits for the
+    device); clears it unless ``clear`` is False."""
+    words = (ctypes.c_uint32 * 2)()
+    _check((lib or load_library()).mla_debug_bounds_read(words, 1 if clear else 0), "mla_debug_bounds_read")
+    return int(words[0]), int(words[1])
 
 
 def mla_status_str(code: int) -> str:

@@ -52,4 +52,34 @@ __device__ __forceinline__ int xcd_remap(int w, int n) {
   return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
 }
 
+// Table checks of the bounds-checked build (see Bounds in kernels.h); without MLA_DEBUG_BOUNDS
+// they compile to nothing.  The flag and the count go out as vector atomics.
+#ifdef MLA_DEBUG_BOUNDS
+__device__ __forceinline__ void bounds_report(const Bounds& bd, uint32_t what) {
+  atomicOr(bd.err, what);
+  atomicAdd(bd.err + 1, 1u);
+}
+// seq_lens entry L, clamped into [0, max_seq_len]
+__device__ __forceinline__ int checked_len(const Bounds& bd, int L) {
+  if (L < 0 || L > bd.max_seq_len) {
+    bounds_report(bd, kBoundsBadSeqLen);
+    L = L < 0 ? 0 : bd.max_seq_len;
+  }
+  return L;
+}
+// whether page id pid may be used (num_pages 0: any non-negative id)
+__device__ __forceinline__ bool page_ok(const Bounds& bd, int pid) {
+  const uint32_t lim = bd.num_pages > 0 ? (uint32_t)bd.num_pages : 0x80000000u;
+  if ((uint32_t)pid < lim) return true;
+  bounds_report(bd, kBoundsBadPage);
+  return false;
+}
+// a page id to read from: pid, or page 0 when it is out of range
+__device__ __forceinline__ int checked_page(const Bounds& bd, int pid) { return page_ok(bd, pid) ? pid : 0; }
+#else
+__device__ __forceinline__ int checked_len(const Bounds&, int L) { return L; }
+__device__ __forceinline__ bool page_ok(const Bounds&, int) { return true; }
+__device__ __forceinline__ int checked_page(const Bounds&, int pid) { return pid; }
+#endif
+
 }  // namespace mla

@@ -191,7 +191,7 @@ __device__ __forceinline__ WorkItem make_work(const AttnArgs& a, int id) {
   const int rest = id / a.S;
   w.split = rest % a.num_splits;
   w.b = rest / a.num_splits;
-  const int L = a.seq_lens[w.b];
+  const int L = checked_len(a.bounds, a.seq_lens[w.b]);
   int n = a.causal && !a.tree_parents ? L - a.S + w.i + 1 : L;
   n = n < 0 ? 0 : (n > L ? L : n);
   const int p_begin = w.split * a.pages_per_split;
@@ -262,7 +262,7 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
   for (int k = 0; k < kPidPerThread; ++k) {
     const int j = threadIdx.x + 256 * k;
-    pid[k] = j < npages ? bt[j] : 0;
+    pid[k] = j < npages ? checked_page(a.bounds, bt[j]) : 0;
   }
   auto row_of = [&](int t, int page) -> const uint16_t* {  // first token row of tile t
     return pool + ((size_t)page * kPage + (t & 1) * kTile) * kRow;
@@ -697,7 +697,7 @@ __global__ __launch_bounds__(256) void decode_attn_f32_kernel(AttnArgs a) {
     const int tkn = start + tid;
     float z = -INFINITY;
     if (tkn < w.tok_end && visible(tkn)) {
-      const float* row = pool + ((size_t)bt[tkn / kPage] * kPage + tkn % kPage) * kRow;
+      const float* row = pool + ((size_t)checked_page(a.bounds, bt[tkn / kPage]) * kPage + tkn % kPage) * kRow;
       float d = 0.f;
       for (int c = 0; c < kRow; ++c) d = fmaf(qs[c], row[c], d);
       z = d * a.scale;
@@ -723,7 +723,7 @@ __global__ __launch_bounds__(256) void decode_attn_f32_kernel(AttnArgs a) {
     const int cnt = w.tok_end - start < 256 ? w.tok_end - start : 256;
     for (int j = 0; j < cnt; ++j) {
       const int tj = start + j;
-      const float* row = pool + ((size_t)bt[tj / kPage] * kPage + tj % kPage) * kRow;
+      const float* row = pool + ((size_t)checked_page(a.bounds, bt[tj / kPage]) * kPage + tj % kPage) * kRow;
       acc0 = fmaf(ps[j], row[tid], acc0);
       acc1 = fmaf(ps[j], row[tid + 256], acc1);
     }

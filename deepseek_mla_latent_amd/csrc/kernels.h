@@ -16,6 +16,21 @@ constexpr int kDh = 128;      // no-RoPE head dim = value head dim
 constexpr int kPage = 64;     // tokens per cache page
 constexpr int kMaxSplitPages = 512;  // pages one attention workgroup may walk (32768 tokens)
 
+// Preconditions on the page table that only the device can check.  In the bounds-checked build
+// (MLA_DEBUG_BOUNDS) every kernel that walks the table tests each seq_lens entry it uses against
+// [0, max_seq_len] and each page id against [0, num_pages) (num_pages 0: only negative ids are
+// caught); a violation sets its bit in err[0], counts in err[1], and the kernel goes on with a safe
+// value instead (the length clamped; a read from page 0; no write).  err is the device address of
+// the library's error word (bounds_error_word); the other build carries the fields and tests nothing.
+struct Bounds {
+  uint32_t* err;
+  int max_seq_len, num_pages;
+};
+constexpr uint32_t kBoundsBadSeqLen = 1u;  // a seq_lens entry outside [0, max_seq_len]
+constexpr uint32_t kBoundsBadPage = 2u;    // a block_table entry outside [0, num_pages)
+// Device address of the error word on the current device (bounds-checked build), else null.
+uint32_t* bounds_error_word();
+
 struct AttnArgs {
   const void* q_lat;           // (B,S,H,512) bf16 or fp32
   const void* q_pe;            // (B,S,H,64)
@@ -29,6 +44,7 @@ struct AttnArgs {
   int B, S, max_pages, pages_per_split, num_splits, causal, final_out, dtype_bf16;
   float scale;       // softmax scale
   float scale_log2;  // softmax scale * log2(e)
+  Bounds bounds;
 };
 
 // decode attention over rows = B*S (b, i) pairs x num_splits page ranges
@@ -54,7 +70,7 @@ hipError_t launch_out_proj(const float* o_lat, const void* w_uv, void* out, int 
 // block-table row stride.
 hipError_t launch_kv_up_grid(const void* pool, const int32_t* block_table, const int32_t* seq_lens,
                              const void* w_uk, const void* w_uv, void* kv, void* kpe, int batch, int max_pages,
-                             int pages_max, hipStream_t stream);
+                             int pages_max, const Bounds& bounds, hipStream_t stream);
 
 struct PrefillArgs {
   const void* q_nope;  // (B,S,H,128) bf16
@@ -66,12 +82,12 @@ struct PrefillArgs {
   float* lse;          // (B,S,H) or null
   int B, S, Lp, nqb, causal;
   float scale_log2;    // softmax scale * log2(e)
+  Bounds bounds;
 };
 hipError_t launch_prefill_attn(const PrefillArgs& a, hipStream_t stream);
 
 // y (M x N) = x (M x K) W (K x N), bf16 row-major, fp32 accumulation; K % 64 == 0, N % 64 == 0.
 // splits > 1 splits K (K / splits % 64 == 0) and needs partial = splits * M * N floats.
-int linear_splits(int M, int K, int N, int cus);
 hipError_t launch_linear(const void* x, const void* w, void* y, float* partial, int M, int K, int N, int splits,
                          hipStream_t stream);
 // FP8 block-quantised per-head products.  Packed weight = E4M3 codes (H x 512 x 128 bytes; W_UV's
@@ -83,6 +99,7 @@ hipError_t launch_out_proj_fp8(const float* o_lat, const void* packed, void* out
 // kv_stride elements, [c_KV 512 | k_pe 64] at the row start), and AppendKV of [c_KV | k_pe] into
 // the paged pool at positions seq_lens[b] - S + i.
 hipError_t launch_rope_append(void* q_pe, const void* kv_a, int kv_stride, void* pool, const int32_t* block_table,
-                              const int32_t* seq_lens, int B, int S, int max_pages, double base, hipStream_t stream);
+                              const int32_t* seq_lens, int B, int S, int max_pages, double base, const Bounds& bounds,
+                              hipStream_t stream);
 
 }  // namespace mla

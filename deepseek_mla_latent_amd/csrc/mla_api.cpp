@@ -35,12 +35,39 @@ mla_status check_params(const mla_params* p) {
   if (p->num_heads != mla::kHeads || p->kv_lora_rank != mla::kDc || p->rope_dim != mla::kDr ||
       p->head_dim != mla::kDh || p->page_size != mla::kPage)
     return MLA_ERR_UNSUPPORTED;
-  if (p->batch < 0 || p->q_len < 1 || p->max_seq_len < 0 || p->max_pages_per_seq < 0) return MLA_ERR_SHAPE;
+  if (p->batch < 0 || p->q_len < 1 || p->max_seq_len < 0 || p->max_pages_per_seq < 0 || p->num_pages < 0)
+    return MLA_ERR_SHAPE;
   if ((int64_t)p->batch * p->q_len > (int64_t)(1 << 24)) return MLA_ERR_SHAPE;
   return MLA_OK;
 }
 
 int64_t tokens_of(const mla_params* p) { return (int64_t)p->batch * p->q_len; }
+
+// Pages that max_seq_len tokens occupy (64-bit sum: max_seq_len may be INT32_MAX).
+int pages_of(const mla_params* p) { return (int)(((int64_t)p->max_seq_len + mla::kPage - 1) / mla::kPage); }
+
+// The table limits the kernels test in the bounds-checked build (mla::Bounds); that build needs
+// the device's error word, the other one passes the limits along unused.
+mla_status table_bounds(const mla_params* p, mla::Bounds* b) {
+  b->err = mla::bounds_error_word();
+  b->max_seq_len = p->max_seq_len;
+  b->num_pages = p->num_pages;
+#ifdef MLA_DEBUG_BOUNDS
+  if (!b->err) return MLA_ERR_DEVICE;
+#endif
+  return MLA_OK;
+}
+
+// K splits of mla_linear: the fewest that give at least 7/8 of a workgroup per compute unit (more
+// splits only add partial traffic and a second workgroup per unit, which measured slower); every
+// split keeps >= 4 chunks of 64.
+int linear_splits(int M, int K, int N, int cus) {
+  const int mb = M >= 512 ? 4 : 1;
+  const int tiles = ((M + 32 * mb - 1) / (32 * mb)) * (N / 64);
+  int s = 1;
+  while (8 * tiles * s < 7 * cus && (K / (s * 2)) % 64 == 0 && K / (s * 2) >= 256) s *= 2;
+  return s;
+}
 
 // Split planning: one workgroup per (b, i, split); aim for about one workgroup per compute unit
 // (each holds a CU: 128 heads of accumulators and two 72 KiB LDS tiles) with page-aligned,
@@ -50,7 +77,7 @@ struct SplitPlan {
 };
 
 SplitPlan plan_splits(const mla_params* p, int requested, int cus) {
-  const int max_pages = (p->max_seq_len + mla::kPage - 1) / mla::kPage;
+  const int max_pages = pages_of(p);
   const int64_t rows = tokens_of(p);
   int s = requested;
   if (s <= 0) {
@@ -108,8 +135,10 @@ mla_status check_prefill(const mla_params* p) {
   mla_status st = check_params(p);
   if (st != MLA_OK) return st;
   if (p->dtype != MLA_BF16) return MLA_ERR_DTYPE;
-  const int max_pages = (p->max_seq_len + mla::kPage - 1) / mla::kPage;
+  const int max_pages = pages_of(p);
   if (p->max_pages_per_seq < max_pages) return MLA_ERR_SHAPE;
+  // the kv buffer holds B x (max_pages_per_seq x 64) rows per head: keep its size far from overflow
+  if ((int64_t)p->batch * p->max_pages_per_seq > 0x7fffffffLL / mla::kPage) return MLA_ERR_SHAPE;
   return MLA_OK;
 }
 
@@ -162,7 +191,8 @@ int32_t mla_decode_num_splits(const mla_params* p, int32_t num_splits) {
 
 size_t mla_decode_workspace_bytes(const mla_params* p, int32_t num_splits) {
   const int32_t s = mla_decode_num_splits(p, num_splits);
-  return s > 0 ? workspace_for(p, s) : 0;
+  // more (row, split) workgroups than a grid holds: the call rejects it (MLA_ERR_SHAPE)
+  return s > 0 && tokens_of(p) * s <= 0x7fffffffLL ? workspace_for(p, s) : 0;
 }
 
 }  // extern "C"
@@ -180,7 +210,7 @@ mla_status decode_attn_impl(const void* q_lat, const void* q_pe, const void* kv_
   mla_status st = check_params(p);
   if (st != MLA_OK) return st;
   if (num_splits < 0) return MLA_ERR_SHAPE;
-  const int max_pages = (p->max_seq_len + mla::kPage - 1) / mla::kPage;
+  const int max_pages = pages_of(p);
   if (p->max_pages_per_seq < max_pages) return MLA_ERR_SHAPE;
   if (fused && p->dtype != MLA_BF16) return MLA_ERR_DTYPE;
   if (tokens_of(p) == 0) return MLA_OK;
@@ -193,6 +223,9 @@ mla_status decode_attn_impl(const void* q_lat, const void* q_pe, const void* kv_
   if (!std::isfinite(p->softmax_scale) || !(p->softmax_scale > 0.f)) return MLA_ERR_SHAPE;
   const int cus = num_splits > 0 ? 1 : cu_count();
   if (cus <= 0) return MLA_ERR_DEVICE;
+  mla::Bounds bounds;
+  st = table_bounds(p, &bounds);
+  if (st != MLA_OK) return st;
   const SplitPlan plan = plan_splits(p, num_splits, cus);
   const int64_t grid = tokens_of(p) * plan.splits * (p->dtype == MLA_BF16 ? 1 : mla::kHeads);
   if (grid > 0x7fffffffLL) return MLA_ERR_SHAPE;
@@ -229,6 +262,7 @@ mla_status decode_attn_impl(const void* q_lat, const void* q_pe, const void* kv_
   a.dtype_bf16 = p->dtype == MLA_BF16;
   a.scale = p->softmax_scale;
   a.scale_log2 = (float)((double)p->softmax_scale * 1.4426950408889634);
+  a.bounds = bounds;
   const int rows = (int)tokens_of(p);
   hipStream_t s = (hipStream_t)stream;
   if (plan.splits == 1 && !merge_in_proj) {
@@ -279,7 +313,7 @@ mla_status mla_decode_attn_tree(const void* q_lat, const void* q_pe, const void*
 
 size_t mla_decode_attn_out_proj_workspace_bytes(const mla_params* p, int32_t num_splits) {
   const int32_t s = mla_decode_num_splits(p, num_splits);
-  return s > 0 ? fused_workspace_for(p, s) : 0;
+  return s > 0 && tokens_of(p) * s <= 0x7fffffffLL ? fused_workspace_for(p, s) : 0;
 }
 
 mla_status mla_decode_attn_out_proj(const void* q_lat, const void* q_pe, const void* kv_pool,
@@ -317,16 +351,19 @@ mla_status mla_prefill_kv_up(const void* kv_pool, const int32_t* block_table, co
                              void* stream) {
   mla_status st = check_prefill(p);
   if (st != MLA_OK) return st;
-  const int pages = (p->max_seq_len + mla::kPage - 1) / mla::kPage;
+  const int pages = pages_of(p);
   if (p->batch == 0 || pages == 0) return MLA_OK;
   if (!kv_pool || !block_table || !seq_lens || !w_uk || !w_uv || !kv) return MLA_ERR_NULL;
   if (!aligned16(kv_pool) || !aligned16(w_uk) || !aligned16(w_uv) || !aligned16(kv)) return MLA_ERR_ALIGN;
   if (kv_bytes < prefill_kv_bytes(p)) return MLA_ERR_WORKSPACE;
   if ((int64_t)p->batch * pages > 0x7fffffffLL) return MLA_ERR_SHAPE;
+  mla::Bounds bounds;
+  st = table_bounds(p, &bounds);
+  if (st != MLA_OK) return st;
   char* kpe = (char*)kv + (size_t)p->batch * mla::kHeads * p->max_pages_per_seq * mla::kPage * 2 * mla::kDh * 2;
   // the walk covers the pages max_seq_len needs; rows are laid out with the table's page stride
   if (mla::launch_kv_up_grid(kv_pool, block_table, seq_lens, w_uk, w_uv, kv, kpe, p->batch, p->max_pages_per_seq,
-                             pages, (hipStream_t)stream) != hipSuccess)
+                             pages, bounds, (hipStream_t)stream) != hipSuccess)
     return MLA_ERR_LAUNCH;
   return MLA_OK;
 }
@@ -344,6 +381,8 @@ mla_status mla_prefill_attn(const void* q_nope, const void* q_pe, const void* kv
   const int nqb = (p->q_len + 255) / 256;  // 256 queries per workgroup
   if ((int64_t)p->batch * mla::kHeads * nqb > 0x7fffffffLL) return MLA_ERR_SHAPE;
   mla::PrefillArgs a;
+  st = table_bounds(p, &a.bounds);
+  if (st != MLA_OK) return st;
   a.q_nope = q_nope;
   a.q_pe = q_pe;
   a.kv = kv;
@@ -366,7 +405,7 @@ size_t mla_linear_workspace_bytes(int32_t m, int32_t k, int32_t n) {
   if (check_linear(m, k, n) != MLA_OK || m == 0) return 0;
   const int cus = cu_count();
   if (cus <= 0) return 0;
-  const int s = mla::linear_splits(m, k, n, cus);
+  const int s = linear_splits(m, k, n, cus);
   return s > 1 ? (size_t)s * m * n * sizeof(float) : 0;
 }
 
@@ -379,7 +418,7 @@ mla_status mla_linear(const void* x, const void* w, void* y, int32_t m, int32_t 
   if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return MLA_ERR_ALIGN;
   const int cus = cu_count();
   if (cus <= 0) return MLA_ERR_DEVICE;
-  const int splits = mla::linear_splits(m, k, n, cus);
+  const int splits = linear_splits(m, k, n, cus);
   if (splits > 1) {
     if (!workspace) return MLA_ERR_NULL;
     if (workspace_bytes < (size_t)splits * m * n * sizeof(float)) return MLA_ERR_WORKSPACE;
@@ -396,15 +435,18 @@ mla_status mla_rope_append(void* q_pe, const void* kv_a, int32_t kv_a_stride, vo
   mla_status st = check_params(p);
   if (st != MLA_OK) return st;
   if (p->dtype != MLA_BF16) return MLA_ERR_DTYPE;
-  const int max_pages = (p->max_seq_len + mla::kPage - 1) / mla::kPage;
+  const int max_pages = pages_of(p);
   if (p->max_pages_per_seq < max_pages) return MLA_ERR_SHAPE;
   if (kv_a_stride < mla::kRow || kv_a_stride % 8 != 0) return MLA_ERR_SHAPE;
   if (!(rope_base > 0.f) || !std::isfinite(rope_base)) return MLA_ERR_SHAPE;
   if (tokens_of(p) == 0) return MLA_OK;
   if (!q_pe || !kv_a || !kv_pool || !block_table || !seq_lens) return MLA_ERR_NULL;
   if (!aligned16(q_pe) || !aligned16(kv_a) || !aligned16(kv_pool)) return MLA_ERR_ALIGN;
+  mla::Bounds bounds;
+  st = table_bounds(p, &bounds);
+  if (st != MLA_OK) return st;
   if (mla::launch_rope_append(q_pe, kv_a, kv_a_stride, kv_pool, block_table, seq_lens, p->batch, p->q_len,
-                              p->max_pages_per_seq, (double)rope_base, (hipStream_t)stream) != hipSuccess)
+                              p->max_pages_per_seq, (double)rope_base, bounds, (hipStream_t)stream) != hipSuccess)
     return MLA_ERR_LAUNCH;
   return MLA_OK;
 }

@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256, 1) void kv_up_kernel(const uint16_t* __restric
                                                        const int32_t* __restrict__ seq_lens,
                                                        const uint16_t* __restrict__ w_uk,
                                                        const uint16_t* __restrict__ w_uv, uint16_t* __restrict__ kv,
-                                                       int batch, int max_pages, int pages_max) {
+                                                       int batch, int max_pages, int pages_max, Bounds bounds) {
   constexpr int kPageBytes = kPage * kDc * 2;     // 64 KiB: the latent rows of one page
   constexpr int kOutBytes = kPage * kKvRow * 2;   // 32 KiB: the page's [K_nope | V] rows
   __shared__ __attribute__((aligned(16))) char lds_raw[2 * kPageBytes + kOutBytes];
@@ -148,9 +148,9 @@ __global__ __launch_bounds__(256, 1) void kv_up_kernel(const uint16_t* __restric
       j = j >= count ? j - count : j;
       const int v = __builtin_amdgcn_readfirstlane(part + 2 * j);
       const int b = v / pages_max, p = v - b * pages_max;
-      const int L = seq_lens[b];  // uniform address: a scalar load, no vector-memory wait
+      const int L = checked_len(bounds, seq_lens[b]);  // uniform address: a scalar load, no vector-memory wait
       if (p * kPage < L) {
-        const int pid = __builtin_amdgcn_readfirstlane(block_table[(size_t)b * max_pages + p]);
+        const int pid = __builtin_amdgcn_readfirstlane(checked_page(bounds, block_table[(size_t)b * max_pages + p]));
         return {jj, v, min(kPage, L - p * kPage), pool + (size_t)pid * kPage * kRow};
       }
     }
@@ -254,11 +254,11 @@ __global__ __launch_bounds__(256, 1) void kv_up_kernel(const uint16_t* __restric
 __global__ __launch_bounds__(64) void kpe_copy_kernel(const uint16_t* __restrict__ pool,
                                                       const int32_t* __restrict__ block_table,
                                                       const int32_t* __restrict__ seq_lens, uint16_t* __restrict__ kpe,
-                                                      int max_pages, int pages_max) {
+                                                      int max_pages, int pages_max, Bounds bounds) {
   const int b = blockIdx.x / pages_max, p = blockIdx.x % pages_max;
-  const int valid = min(kPage, seq_lens[b] - p * kPage);
+  const int valid = min(kPage, checked_len(bounds, seq_lens[b]) - p * kPage);
   if (valid <= 0) return;
-  const uint16_t* rows = pool + (size_t)block_table[(size_t)b * max_pages + p] * kPage * kRow;
+  const uint16_t* rows = pool + (size_t)checked_page(bounds, block_table[(size_t)b * max_pages + p]) * kPage * kRow;
   uint16_t* dst = kpe + ((size_t)b * max_pages + p) * kPage * kDr;
   const int lane = threadIdx.x;
 #pragma unroll
@@ -272,16 +272,16 @@ __global__ __launch_bounds__(64) void kpe_copy_kernel(const uint16_t* __restrict
 
 hipError_t launch_kv_up_grid(const void* pool, const int32_t* block_table, const int32_t* seq_lens,
                              const void* w_uk, const void* w_uv, void* kv, void* kpe, int batch, int max_pages,
-                             int pages_max, hipStream_t stream) {
+                             int pages_max, const Bounds& bounds, hipStream_t stream) {
   forget_stale_error();
   if (batch == 0 || pages_max == 0) return hipSuccess;
   hipLaunchKernelGGL(kv_up_kernel, dim3(2 * kHeads), dim3(256), 0, stream, (const uint16_t*)pool, block_table,
                      seq_lens, (const uint16_t*)w_uk, (const uint16_t*)w_uv, (uint16_t*)kv, batch, max_pages,
-                     pages_max);
+                     pages_max, bounds);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kpe_copy_kernel, dim3((unsigned)(batch * pages_max)), dim3(64), 0, stream, (const uint16_t*)pool,
-                     block_table, seq_lens, (uint16_t*)kpe, max_pages, pages_max);
+                     block_table, seq_lens, (uint16_t*)kpe, max_pages, pages_max, bounds);
   return hipGetLastError();
 }
 
@@ -340,7 +340,7 @@ __global__ __launch_bounds__(64 * kPfWaves, 1) void prefill_attn_kernel(PrefillA
   const int qb = a.nqb - 1 - id % a.nqb;  // longest key ranges first
   if (bh >= nbh) return;
   const int b = bh / kHeads, h = bh % kHeads;
-  const int L = a.seq_lens[b], S = a.S;
+  const int L = checked_len(a.bounds, a.seq_lens[b]), S = a.S;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);

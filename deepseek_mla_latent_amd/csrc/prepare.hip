@@ -191,17 +191,6 @@ __global__ __launch_bounds__(256) void linear_reduce_kernel(const float* __restr
   *(u32x2*)(y + (size_t)i * 4) = o;
 }
 
-int linear_splits(int M, int K, int N, int cus) {
-  const int mb = M >= 512 ? 4 : 1;
-  const int tiles = ((M + 32 * mb - 1) / (32 * mb)) * (N / 64);
-  int s = 1;
-  // the fewest K splits that give at least 7/8 of a workgroup per compute unit (more splits only
-  // add partial traffic and a second workgroup per unit, which measured slower); every split keeps
-  // >= 4 chunks of 64
-  while (8 * tiles * s < 7 * cus && (K / (s * 2)) % 64 == 0 && K / (s * 2) >= 256) s *= 2;
-  return s;
-}
-
 hipError_t launch_linear(const void* x, const void* w, void* y, float* partial, int M, int K, int N, int splits,
                          hipStream_t stream) {
   forget_stale_error();
@@ -240,7 +229,7 @@ __global__ __launch_bounds__(128) void rope_append_kernel(uint16_t* __restrict__
                                                           int kv_stride, uint16_t* __restrict__ pool,
                                                           const int32_t* __restrict__ block_table,
                                                           const int32_t* __restrict__ seq_lens, int S,
-                                                          int max_pages, InvFreq inv_freq_arg) {
+                                                          int max_pages, InvFreq inv_freq_arg, Bounds bounds) {
   __shared__ float cs[32], sn[32];
   __shared__ __attribute__((aligned(16))) uint16_t krot[kDr];
   const int token = blockIdx.x, b = token / S, i = token % S;
@@ -249,7 +238,7 @@ __global__ __launch_bounds__(128) void rope_append_kernel(uint16_t* __restrict__
   uint16_t* q = q_pe + ((size_t)token * kHeads + tid) * kDr;
   // every load is issued before any result is needed: the position and page, this head's q_pe
   // (thread = head), a 16-byte piece of c_KV (threads 0..63) and a k_pe pair (threads 0..31)
-  const int pos = seq_lens[b] - S + i;
+  const int pos = checked_len(bounds, seq_lens[b]) - S + i;
   const int page = pos >= 0 ? block_table[(size_t)b * max_pages + pos / kPage] : 0;
   u32x4 qv[8];
 #pragma unroll
@@ -281,7 +270,7 @@ __global__ __launch_bounds__(128) void rope_append_kernel(uint16_t* __restrict__
     }
     *(u32x4*)(q + u * 8) = v;
   }
-  if (pos < 0) return;
+  if (pos < 0 || !page_ok(bounds, page)) return;  // no slot (or, checked, an unusable page): no write
   uint16_t* dst = pool + ((size_t)page * kPage + pos % kPage) * kRow;
   if (tid < kDc / 8) *(u32x4*)(dst + tid * 8) = cv;  // c_KV: a copy
   else if (tid < kDc / 8 + kDr / 8)
@@ -289,14 +278,15 @@ __global__ __launch_bounds__(128) void rope_append_kernel(uint16_t* __restrict__
 }
 
 hipError_t launch_rope_append(void* q_pe, const void* kv_a, int kv_stride, void* pool, const int32_t* block_table,
-                              const int32_t* seq_lens, int B, int S, int max_pages, double base, hipStream_t stream) {
+                              const int32_t* seq_lens, int B, int S, int max_pages, double base, const Bounds& bounds,
+                              hipStream_t stream) {
   forget_stale_error();
   const int64_t grid = (int64_t)B * S;
   if (grid == 0) return hipSuccess;
   InvFreq f;
   for (int j = 0; j < 32; ++j) f.v[j] = pow(base, -2.0 * j / kDr);
   hipLaunchKernelGGL(rope_append_kernel, dim3((unsigned)grid), dim3(128), 0, stream, (uint16_t*)q_pe,
-                     (const uint16_t*)kv_a, kv_stride, (uint16_t*)pool, block_table, seq_lens, S, max_pages, f);
+                     (const uint16_t*)kv_a, kv_stride, (uint16_t*)pool, block_table, seq_lens, S, max_pages, f, bounds);
   return hipGetLastError();
 }
 

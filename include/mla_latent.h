@@ -36,10 +36,14 @@
  *   - Supported dims: num_heads 128, kv_lora_rank 512, rope_dim 64, head_dim 128,
  *     page_size 64. Other values give MLA_ERR_UNSUPPORTED.
  *   - Pointers must be 16-byte aligned (MLA_ERR_ALIGN).
- *   - Device-side preconditions (not checked; violating them is undefined behaviour):
- *     0 <= seq_lens[b] <= max_seq_len; block_table[b][p] in [0, num_pages) for every page p
- *     that holds one of the first seq_lens[b] tokens. With causal and q_len S, query i sees
- *     the first seq_lens[b] - S + i + 1 tokens (fewer than one: an empty set).
+ *   - Device-side preconditions: 0 <= seq_lens[b] <= max_seq_len; block_table[b][p] in
+ *     [0, num_pages) for every page p that holds one of the first seq_lens[b] tokens (P = the
+ *     pool's page count). libmla_latent.so does not check them (violating them is undefined
+ *     behaviour). The bounds-checked build of the same library, libmla_latent_debug.so
+ *     (compiled with MLA_DEBUG_BOUNDS), checks every entry a kernel uses, on the device, and
+ *     reports violations in an error word (mla_debug_bounds_read); see there. With causal and
+ *     q_len S, query i sees the first seq_lens[b] - S + i + 1 tokens (fewer than one: an empty
+ *     set).
  *   - An empty key set yields o_lat = 0 and lse = -inf.
  */
 #ifndef MLA_LATENT_H_
@@ -80,6 +84,9 @@ typedef struct {
   float softmax_scale;       /* > 0; multiplies the whole logit (latent + RoPE parts), e.g. 1/sqrt(192) */
   int32_t causal;            /* 1: query i of S sees seq_lens[b] - S + i + 1 keys; 0: all keys */
   mla_dtype dtype;           /* of q_nope, q_pe, q_lat, cache, W_UK, W_UV, out; accumulation is fp32 */
+  int32_t num_pages;         /* >= 0: pages in kv_pool, 0 = not given. Only the bounds-checked build
+                                reads it (page ids >= num_pages are violations; with 0, only
+                                negative ids are) */
 } mla_params;
 
 /*
@@ -384,6 +391,29 @@ const char* mla_status_str(mla_status s);
  * else MLA_OK.
  */
 mla_status mla_debug_attn_schedule(int32_t ntiles, int32_t* a_buffer, int32_t* b_buffer, int32_t* p_buffer);
+
+/*
+ * Bounds-checked build. mla_debug_bounds_enabled() is 1 in libmla_latent_debug.so and 0 in
+ * libmla_latent.so.
+ *
+ * In the bounds-checked build, every kernel that walks the page table (mla_decode_attn,
+ * mla_decode_attn_tree, mla_decode_attn_out_proj and its static-scratch form, mla_prefill_kv_up,
+ * mla_prefill_attn, mla_rope_append) tests each entry it uses: a seq_lens entry outside
+ * [0, max_seq_len] sets bit 1 of the error word and is clamped into that range; a block_table entry
+ * outside [0, num_pages) (num_pages 0: a negative entry) sets bit 2, a read then takes page 0 and
+ * the cache append skips its write. The outputs of an affected sequence are then meaningless, but
+ * no access leaves the buffers the preconditions describe. Reports are device atomics on a
+ * per-device word pair; the calls themselves stay asynchronous.
+ *
+ * mla_debug_bounds_read(words, clear) waits for the device (hipDeviceSynchronize), copies
+ *   words[0] = union of the violation bits since the last clear (1: seq_lens, 2: block_table),
+ *   words[1] = number of reports (one per GPU lane that saw a violation; 0 iff words[0] == 0),
+ * and with clear != 0 resets both to zero. words: HOST pointer to 2 uint32 (MLA_ERR_NULL if
+ * NULL). MLA_ERR_DEVICE if the device cannot be reached; MLA_ERR_UNSUPPORTED in libmla_latent.so.
+ * Cites: the page table of the Perplexity post, section "Слой MLA".
+ */
+int32_t mla_debug_bounds_enabled(void);
+mla_status mla_debug_bounds_read(uint32_t* words, int32_t clear);
 
 #ifdef __cplusplus
 }

@@ -274,3 +274,59 @@ def test_static_scratch_limit_is_checked_on_the_host():
     assert lib.mla_status_str(-9).decode().startswith("MLA_ERR_SCRATCH")
     assert lib.mla_decode_attn_out_proj_static(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, None, 8,
                                                None, None) == -1
+
+
+def test_release_library_has_no_bounds_checks():
+    assert lib.mla_debug_bounds_enabled() == 0
+    words = (ctypes.c_uint32 * 2)()
+    assert lib.mla_debug_bounds_read(words, 1) == -6
+
+
+def test_num_pages_must_not_be_negative():
+    assert _attn(P(num_pages=-1)) == -2
+    assert _tree(P(q_len=4, num_pages=-1)) == -2
+    assert _fused(P(num_pages=-1)) == -2
+    assert lib.mla_prefill_kv_bytes(ctypes.byref(P(num_pages=-1))) == 0
+    assert lib.mla_rope_append(FAKE, FAKE, 576, FAKE, FAKE, FAKE, 10000.0, ctypes.byref(P(num_pages=-1)), None) == -2
+    assert _attn(P(num_pages=7), ws=FAKE, ws_bytes=1 << 30) != -2  # any count >= 0 passes the host checks
+
+
+def test_size_queries_do_not_wrap():
+    """Shapes whose buffers would not fit a 64-bit size (or whose grid would not fit a launch) give
+    size 0 and are rejected by the call, instead of a wrapped-around small size."""
+    huge = P(batch=1 << 24, max_seq_len=2 ** 31 - 1, max_pages_per_seq=2 ** 31 - 1)
+    assert lib.mla_decode_workspace_bytes(ctypes.byref(huge), 2 ** 31 - 1) == 0
+    assert lib.mla_decode_attn_out_proj_workspace_bytes(ctypes.byref(huge), 2 ** 31 - 1) == 0
+    assert _attn(huge, ws=FAKE, ws_bytes=2 ** 63, splits=2 ** 31 - 1) == -2
+    wide = P(batch=1 << 20, max_seq_len=64, max_pages_per_seq=1 << 20)
+    assert lib.mla_prefill_kv_bytes(ctypes.byref(wide)) == 0
+    assert lib.mla_prefill_kv_up(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2 ** 63, ctypes.byref(wide), None) == -2
+
+
+@pytest.fixture(scope="module")
+def debug_lib():
+    import os
+    if not os.path.exists(binding.DEBUG_LIB_PATH):
+        pytest.skip("bounds-checked library not built")
+    return binding.load_library(binding.DEBUG_LIB_PATH)
+
+
+def test_bounds_checked_library_exports_the_same_functions(debug_lib):
+    for n in declared_functions():
+        assert hasattr(debug_lib, n), n
+    assert debug_lib.mla_debug_bounds_enabled() == 1
+    assert debug_lib.mla_debug_bounds_read(None, 1) == -1
+
+
+def test_bounds_checked_library_rejects_the_same_arguments(debug_lib):
+    def attn(params, ptrs=None, ws=None, ws_bytes=0, splits=2):
+        p = dict(q_lat=FAKE, q_pe=FAKE, pool=FAKE, bt=FAKE, lens=FAKE, o=FAKE, lse=FAKE)
+        p.update(ptrs or {})
+        return debug_lib.mla_decode_attn(p["q_lat"], p["q_pe"], p["pool"], p["bt"], p["lens"], p["o"], p["lse"], ws,
+                                         ws_bytes, splits, ctypes.byref(params), None)
+    for kw, ptrs, want in ((dict(), {"q_lat": None}, -1), (dict(), {"q_pe": MISALIGNED}, -4), (dict(dtype=2), None, -3),
+                           (dict(rope_dim=32), None, -6), (dict(max_pages_per_seq=2), None, -2),
+                           (dict(num_pages=-3), None, -2), (dict(softmax_scale=0.0), None, -2)):
+        assert attn(P(**kw), ptrs) == want, (kw, ptrs)
+    assert debug_lib.mla_decode_workspace_bytes(ctypes.byref(P()), 2) == lib.mla_decode_workspace_bytes(
+        ctypes.byref(P()), 2)
