@@ -3,7 +3,8 @@
 
 One step = one pass of the whole decode path over one batch, for one layer: with bf16 weights
 mla_absorb_q -> mla_decode_attn_out_proj (split-K attention, then the log-sum-exp merge of the
-splits fused with W_UV); with fp32, FP8 projections or --unfused mla_absorb_q -> mla_decode_attn
+splits fused with W_UV), with --fp8-projections the FP8 forms of both calls (mla_absorb_q_fp8 ->
+mla_decode_attn_out_proj_fp8); with fp32 or --unfused mla_absorb_q -> mla_decode_attn
 (split-K attention + merge) -> mla_out_proj.  Default workload: batch 32
 sequences x 1 query token, 128 heads, d_c 512, d_R 64, d_h 128, 4096 cached tokens each (bf16,
 contiguous cache = identity page table).  Inputs are seeded synthetic data already resident in HBM.
@@ -574,7 +575,7 @@ def main():
         return torch.from_numpy(a).to(dev)
 
     fp8 = bool(args.fp8_projections)
-    fused = x.is_bf16 and not fp8 and not args.unfused  # attention + merge/W_UV in one call
+    fused = x.is_bf16 and not args.unfused  # attention + merge/W_UV in one call
     costs = accounting.path_costs(x.seq_lens, w.q_len, dt, tree=parents, fused=fused)
     per_replica = sum(c.bytes for c in costs)
     R = args.replicas or max(2, math.ceil(2 * MALL_BYTES / per_replica) + 1)
@@ -607,7 +608,7 @@ def main():
             binding.mla_quantize_w_uv_fp8(d["w_uv"], pk_uv, params)
             d["w_uk"], d["w_uv"] = pk_uk, pk_uv
         torch.cuda.synchronize()
-        costs = accounting.path_costs(x.seq_lens, w.q_len, dt, fp8_projections=True, tree=parents)
+        costs = accounting.path_costs(x.seq_lens, w.q_len, dt, fp8_projections=True, tree=parents, fused=fused)
 
     def run(d, stream=None):
         d["bufs"].run(d["q_nope"], d["q_pe"], d["w_uk"], d["w_uv"], d["pool"], d["bt"], d["lens"], stream, fp8=fp8,
@@ -639,8 +640,9 @@ def main():
         (binding.mla_absorb_q_fp8 if fp8 else binding.mla_absorb_q)(d["q_nope"], d["w_uk"], p.q_lat, params)
         e[1].record(stream)
         if fused:
-            binding.mla_decode_attn_out_proj(p.q_lat, d["q_pe"], d["pool"], d["bt"], d["lens"], d["tree"], d["w_uv"],
-                                             p.out, None, None, p.workspace, args.num_splits, params)
+            (binding.mla_decode_attn_out_proj_fp8 if fp8 else binding.mla_decode_attn_out_proj)(
+                p.q_lat, d["q_pe"], d["pool"], d["bt"], d["lens"], d["tree"], d["w_uv"], p.out, None, None,
+                p.workspace, args.num_splits, params)
             e[2].record(stream)
             continue
         if tree_wl:
@@ -659,11 +661,12 @@ def main():
     tokens = w.batch * w.q_len
     attn = costs[1]
     attn_s = call_us[1] * 1e-6
-    route = "fused" if fused else ("fp8" if fp8 else "three calls")
+    route = ("fused fp8" if fp8 else "fused") if fused else ("fp8" if fp8 else "three calls")
     traffic = measured_traffic("hbm_bytes_per_launch", args.workload, route)
     if fused:
-        kernel = ("mla_decode_attn_out_proj with a draft-tree mask (split attention + merge/W_UV)" if tree_wl
-                  else "mla_decode_attn_out_proj (split attention + merge/W_UV)")
+        call = costs[1].name
+        kernel = (f"{call} with a draft-tree mask (split attention + merge/W_UV)" if tree_wl
+                  else f"{call} (split attention + merge/W_UV)")
     else:
         kernel = ("mla_decode_attn_tree (tree-masked split attention + LSE merge)" if tree_wl
                   else "mla_decode_attn (split attention + LSE merge)")

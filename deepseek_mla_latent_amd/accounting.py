@@ -75,8 +75,8 @@ def path_costs(seq_lens: Sequence[int], q_len: int, dtype: str, *, heads: int = 
                d_r: int = 64, d_h: int = 128, page: int = 64, causal: bool = True, fp8_projections: bool = False,
                tree=None, fused: bool = False):
     """Algorithmic bytes and FLOPs of each call of one decode step.  With ``fused`` the attention
-    and the out-projection are one call (mla_decode_attn_out_proj, without the optional latent
-    outputs): its bytes are the attention's reads plus W_UV and the output."""
+    and the out-projection are one call (mla_decode_attn_out_proj, or its FP8 form, without the
+    optional latent outputs): its bytes are the attention's reads plus W_UV and the output."""
     e = 2 if dtype == "bf16" else 4
     ew = 1 if fp8_projections else e  # weight element bytes (FP8 codes; scales added below)
     wsc = heads * (d_c // 128) * 4 if fp8_projections else 0
@@ -95,7 +95,8 @@ def path_costs(seq_lens: Sequence[int], q_len: int, dtype: str, *, heads: int = 
                    2 * T * heads * d_c * d_h)
     if fused:
         reads = attn.bytes - T * heads * (d_c + 1) * 4  # no o_lat / lse written
-        return [absorb, CallCost("mla_decode_attn_out_proj", reads + heads * d_c * d_h * e + T * heads * d_h * e,
+        name = "mla_decode_attn_out_proj_fp8" if fp8_projections else "mla_decode_attn_out_proj"
+        return [absorb, CallCost(name, reads + heads * d_c * d_h * ew + wsc + T * heads * d_h * e,
                                  attn.flops + out.flops)]
     return [absorb, attn, out]
 

@@ -31,7 +31,7 @@ EXPORTS = ("mla_absorb_q", "mla_decode_workspace_bytes", "mla_decode_num_splits"
            "mla_linear_workspace_bytes", "mla_linear", "mla_rope_append", "mla_fp8_weight_bytes",
            "mla_quantize_w_uk_fp8", "mla_quantize_w_uv_fp8", "mla_absorb_q_fp8", "mla_out_proj_fp8", "mla_status_str",
            "mla_debug_attn_schedule", "mla_decode_attn_out_proj_static", "mla_debug_bounds_enabled",
-           "mla_debug_bounds_read")
+           "mla_debug_bounds_read", "mla_decode_attn_out_proj_fp8")
 BOUNDS_BAD_SEQ_LEN = 1  # error-word bits of the bounds-checked build
 BOUNDS_BAD_PAGE = 2
 
@@ -103,6 +103,8 @@ def declare(lib, *, partial: bool = False):
     L.mla_decode_attn_out_proj_workspace_bytes.restype = sz
     L.mla_decode_attn_out_proj.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i32, pp, vp]
     L.mla_decode_attn_out_proj.restype = i32
+    L.mla_decode_attn_out_proj_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i32, pp, vp]
+    L.mla_decode_attn_out_proj_fp8.restype = i32
     L.mla_decode_attn_out_proj_static.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, pp, vp]
     L.mla_decode_attn_out_proj_static.restype = i32
     L.mla_out_proj.argtypes = [vp, vp, vp, pp, vp]
@@ -277,6 +279,17 @@ def mla_decode_attn_out_proj(q_lat, q_pe, kv_pool, block_table, seq_lens, tree_p
                                         ctypes.byref(params), _stream(stream)), "mla_decode_attn_out_proj")
 
 
+def mla_decode_attn_out_proj_fp8(q_lat, q_pe, kv_pool, block_table, seq_lens, tree_parents, w_uv_fp8, out, o_lat,
+                                 lse, workspace, num_splits: int, params: mla_params, stream=None,
+                                 workspace_bytes: Optional[int] = None) -> None:
+    lib = load_library()
+    _check(lib.mla_decode_attn_out_proj_fp8(_ptr(q_lat), _ptr(q_pe), _ptr(kv_pool), _ptr(block_table),
+                                            _ptr(seq_lens), _ptr(tree_parents), _ptr(w_uv_fp8), _ptr(out), _ptr(o_lat),
+                                            _ptr(lse), _ptr(workspace), _nbytes(workspace, workspace_bytes),
+                                            num_splits, ctypes.byref(params), _stream(stream)),
+           "mla_decode_attn_out_proj_fp8")
+
+
 def mla_decode_attn_out_proj_static(q_lat, q_pe, kv_pool, block_table, seq_lens, tree_parents, w_uv, out, o_lat,
                                     lse, num_splits: int, params: mla_params, stream=None) -> None:
     lib = load_library()
@@ -390,11 +403,10 @@ class DecodeBuffers:
         p = self.params
         (mla_absorb_q_fp8 if fp8 else mla_absorb_q)(q_nope, w_uk, self.q_lat, p, stream)
         if fused:
-            if fp8:
-                raise ValueError("the fused attention + out-projection takes bf16 W_UV")
-            mla_decode_attn_out_proj(self.q_lat, q_pe, kv_pool, block_table, seq_lens, tree_parents, w_uv, self.out,
-                                     self.o_lat if latent_outputs else None, self.lse if latent_outputs else None,
-                                     self.workspace, self.num_splits, p, stream)
+            (mla_decode_attn_out_proj_fp8 if fp8 else mla_decode_attn_out_proj)(
+                self.q_lat, q_pe, kv_pool, block_table, seq_lens, tree_parents, w_uv, self.out,
+                self.o_lat if latent_outputs else None, self.lse if latent_outputs else None, self.workspace,
+                self.num_splits, p, stream)
             return self.out
         if tree_parents is None:
             mla_decode_attn(self.q_lat, q_pe, kv_pool, block_table, seq_lens, self.o_lat, self.lse, self.workspace,

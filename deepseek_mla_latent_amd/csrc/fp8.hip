@@ -214,48 +214,53 @@ __device__ __forceinline__ void store_tile(const uint8_t* tile, int units, uint8
   }
 }
 
-// absorb: one workgroup per head, 8 waves; wave w owns latent rows c = 64 w + 32 mb + l32
-// (mb = 0, 1).  A = W_UK codes of those rows (the lane's k half: 64 bytes per row, loaded once).
-// Output per token: 512 bf16 (1 KiB) staged in LDS, then stored as whole rows.
-__global__ __launch_bounds__(512) void absorb_q_fp8_kernel(const uint16_t* __restrict__ q_nope,
+// absorb: grid (4 latent blocks of 128 rows, 128 heads), 4 waves: a workgroup's rows are exactly
+// one 128 x 128 weight block (one weight scale), and 512 workgroups keep every compute unit
+// streaming (8 KiB of codes per head and block half: 16 KiB per workgroup).  Wave w owns latent
+// rows cb + 32 w + l32.  Its 32 code rows (128 B each) reach LDS by four 1 KiB direct-to-LDS
+// loads, whole cache lines, with 16-byte unit u of row r stored at u ^ (r & 7); the A operand of
+// step ks is 8 bytes of that row.  Per block of 32 tokens the workgroup codes q_nope[., h, :] once
+// into LDS (one scale per token: K = 128 is one block), each wave runs 8 FP8 MFMAs, and the bf16
+// results leave through an LDS tile as whole 256-byte rows.
+__global__ __launch_bounds__(256) void absorb_q_fp8_kernel(const uint16_t* __restrict__ q_nope,
                                                            const uint8_t* __restrict__ codes,
                                                            const float* __restrict__ scales,
                                                            uint16_t* __restrict__ q_lat, int tokens) {
+  __shared__ __attribute__((aligned(1024))) uint8_t w_lds[128 * 128];
   __shared__ __attribute__((aligned(16))) ActCodes<1> st;
-  __shared__ __attribute__((aligned(16))) uint8_t tile[32 * kDc * 2];
-  const int h = blockIdx.x, tid = threadIdx.x;
+  __shared__ __attribute__((aligned(16))) uint8_t tile[32 * 256];
+  const int h = blockIdx.y, cb = blockIdx.x, tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
-  uint32_t aw[2][16];
+  {  // load i: rows 8 i .. 8 i + 7 of the wave's 32 (lane l: row 8 i + l / 8, LDS unit l % 8)
+    const uint8_t* src = codes + ((size_t)h * kDc + 128 * cb + 32 * wave) * kDh;
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    const uint8_t* src = codes + ((size_t)h * kDc + wave * 64 + mb * 32 + l32) * kDh + 64 * hf;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const u32x4 v = *(const u32x4*)(src + 16 * u);
-      aw[mb][4 * u] = v[0], aw[mb][4 * u + 1] = v[1], aw[mb][4 * u + 2] = v[2], aw[mb][4 * u + 3] = v[3];
+    for (int i = 0; i < 4; ++i) {
+      const int r = 8 * i + (lane >> 3);
+      const int u = (lane & 7) ^ (r & 7);
+      __builtin_amdgcn_global_load_lds((const MLA_GLOBAL void*)(src + r * 128 + u * 16),
+                                       (MLA_LDS void*)(w_lds + (32 * wave + 8 * i) * 128), 16, 0, 0);
     }
   }
-  const float sw = scales[h * 4 + (wave >> 1)];  // latent block of this wave's rows
+  const float sw = scales[h * 4 + cb];
+  const int r = 32 * wave + l32;  // this lane's code row (A operand row)
   for (int n0 = 0; n0 < tokens; n0 += 32) {
     __syncthreads();  // the previous block's codes and staged rows are consumed
-    code_tokens<1, 8, 512, true>(q_nope + (size_t)h * kDh, (size_t)kHeads * kDh, n0, tokens, tid, st);
+    code_tokens<1, 8, 256, true>(q_nope + (size_t)h * kDh, (size_t)kHeads * kDh, n0, tokens, tid, st);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's code rows have landed
     __syncthreads();
-    uint64_t bq[8];
+    f32x16 acc = {};
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) bq[ks] = act_b(st.codes, l32, hf, 0, 1, ks);
-    const float s = st.scale[l32] * sw;  // this lane's token
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      f32x16 acc = {};
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        acc = mfma_fp8(aw[mb][2 * ks], aw[mb][2 * ks + 1], (uint32_t)bq[ks], (uint32_t)(bq[ks] >> 32), acc);
-      stage_fragment(tile, kDc * 2 / 16, l32, hf, 2 * (wave * 64 + mb * 32), acc, s);
+    for (int ks = 0; ks < 8; ++ks) {  // k = 64 hf + 8 ks .. +7: unit 4 hf + ks / 2, half ks % 2
+      const int u = (4 * hf + (ks >> 1)) ^ (r & 7);
+      const u32x2 a = *(const u32x2*)&w_lds[r * 128 + u * 16 + (ks & 1) * 8];
+      const uint64_t b = act_b(st.codes, l32, hf, 0, 1, ks);
+      acc = mfma_fp8(a[0], a[1], (uint32_t)b, (uint32_t)(b >> 32), acc);
     }
+    stage_fragment(tile, 256 / 16, l32, hf, 2 * 32 * wave, acc, st.scale[l32] * sw);
     __syncthreads();
-    store_tile<512>(tile, kDc * 2 / 16, (uint8_t*)(q_lat + (size_t)h * kDc), (size_t)kHeads * kDc * 2, n0, tokens,
-                    tid);
+    store_tile<256>(tile, 256 / 16, (uint8_t*)(q_lat + (size_t)h * kDc + 128 * cb), (size_t)kHeads * kDc * 2, n0,
+                    tokens, tid);
   }
 }
 
@@ -335,7 +340,7 @@ hipError_t launch_absorb_q_fp8(const void* q_nope, const void* packed, void* q_l
   if (tokens == 0) return hipSuccess;
   const uint8_t* codes = (const uint8_t*)packed;
   const float* scales = (const float*)(codes + (size_t)kHeads * kDc * kDh);
-  hipLaunchKernelGGL(absorb_q_fp8_kernel, dim3(kHeads), dim3(512), 0, stream, (const uint16_t*)q_nope, codes,
+  hipLaunchKernelGGL(absorb_q_fp8_kernel, dim3(4, kHeads), dim3(256), 0, stream, (const uint16_t*)q_nope, codes,
                      scales, (uint16_t*)q_lat, tokens);
   return hipGetLastError();
 }

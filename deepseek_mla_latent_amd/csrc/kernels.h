@@ -57,8 +57,9 @@ hipError_t launch_lse_merge(const void* o_part, bool part_bf16, const float* lse
 hipError_t launch_absorb_q(const void* q_nope, const void* w_uk, void* q_lat, int tokens, bool bf16,
                            hipStream_t stream);
 // out[n,h,:] = W_UV[h]^T o_lat[n,h,:] for n < tokens
-// Split merge + out-proj in one kernel (bf16 partials and W_UV; o_lat and lse optional).
-hipError_t launch_merge_out_proj(const void* o_part, const float* lse_part, const void* w_uv, void* out,
+// Split merge + out-proj in one kernel (bf16 partials; W_UV bf16, or with w_fp8 the packed FP8 codes
+// and scales of launch_quantize_weight_fp8; o_lat and lse optional).
+hipError_t launch_merge_out_proj(const void* o_part, const float* lse_part, const void* w_uv, bool w_fp8, void* out,
                                  float* o_lat, float* lse, int rows, int num_splits, hipStream_t stream);
 hipError_t launch_out_proj(const float* o_lat, const void* w_uv, void* out, int tokens, bool bf16,
                            hipStream_t stream);

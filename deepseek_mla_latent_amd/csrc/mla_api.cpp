@@ -205,7 +205,7 @@ namespace {
 mla_status decode_attn_impl(const void* q_lat, const void* q_pe, const void* kv_pool, const int32_t* block_table,
                             const int32_t* seq_lens, const int32_t* tree_parents, float* o_lat, float* lse,
                             void* workspace, size_t workspace_bytes, int32_t num_splits, const mla_params* p,
-                            void* stream, const void* w_uv = nullptr, void* out = nullptr) {
+                            void* stream, const void* w_uv = nullptr, void* out = nullptr, bool w_fp8 = false) {
   const bool fused = w_uv != nullptr || out != nullptr;
   mla_status st = check_params(p);
   if (st != MLA_OK) return st;
@@ -241,9 +241,9 @@ mla_status decode_attn_impl(const void* q_lat, const void* q_pe, const void* kv_
     st = decode_attn_impl(q_lat, q_pe, kv_pool, block_table, seq_lens, tree_parents, o, lse, workspace,
                           workspace_bytes, num_splits, p, stream);
     if (st != MLA_OK) return st;
-    if (mla::launch_out_proj(o, w_uv, out, (int)tokens_of(p), true, (hipStream_t)stream) != hipSuccess)
-      return MLA_ERR_LAUNCH;
-    return MLA_OK;
+    const hipError_t e = w_fp8 ? mla::launch_out_proj_fp8(o, w_uv, out, (int)tokens_of(p), (hipStream_t)stream)
+                               : mla::launch_out_proj(o, w_uv, out, (int)tokens_of(p), true, (hipStream_t)stream);
+    return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
   }
 
   mla::AttnArgs a;
@@ -279,7 +279,7 @@ mla_status decode_attn_impl(const void* q_lat, const void* q_pe, const void* kv_
   a.final_out = 0;
   if (mla::launch_decode_attn(a, rows, s) != hipSuccess) return MLA_ERR_LAUNCH;
   if (merge_in_proj) {
-    if (mla::launch_merge_out_proj(o_part, lse_part, w_uv, out, o_lat, lse, rows, plan.splits, s) != hipSuccess)
+    if (mla::launch_merge_out_proj(o_part, lse_part, w_uv, w_fp8, out, o_lat, lse, rows, plan.splits, s) != hipSuccess)
       return MLA_ERR_LAUNCH;
     return MLA_OK;
   }
@@ -327,6 +327,19 @@ mla_status mla_decode_attn_out_proj(const void* q_lat, const void* q_pe, const v
   if (!w_uv || !out) return tokens_of(p) == 0 ? MLA_OK : MLA_ERR_NULL;
   return decode_attn_impl(q_lat, q_pe, kv_pool, block_table, seq_lens, tree_parents, o_lat, lse, workspace,
                           workspace_bytes, num_splits, p, stream, w_uv, out);
+}
+
+mla_status mla_decode_attn_out_proj_fp8(const void* q_lat, const void* q_pe, const void* kv_pool,
+                                        const int32_t* block_table, const int32_t* seq_lens,
+                                        const int32_t* tree_parents, const void* w_uv_fp8, void* out, float* o_lat,
+                                        float* lse, void* workspace, size_t workspace_bytes, int32_t num_splits,
+                                        const mla_params* p, void* stream) {
+  mla_status st = check_params(p);
+  if (st != MLA_OK) return st;
+  if (tree_parents && p->q_len > 64) return MLA_ERR_SHAPE;
+  if (!w_uv_fp8 || !out) return tokens_of(p) == 0 ? MLA_OK : MLA_ERR_NULL;
+  return decode_attn_impl(q_lat, q_pe, kv_pool, block_table, seq_lens, tree_parents, o_lat, lse, workspace,
+                          workspace_bytes, num_splits, p, stream, w_uv_fp8, out, true);
 }
 
 mla_status mla_out_proj(const float* o_lat, const void* w_uv, void* out, const mla_params* p, void* stream) {

@@ -293,21 +293,41 @@ __global__ __launch_bounds__(256, 1) void out_proj_bf16_kernel(const float* __re
 // LDS row c of a wave's slice holds 32-byte block b (16 values) at block b ^ fsw(c) with
 // fsw(c) = (c & 3) | ((c >> 3) & 1) << 2: a transposed read covers 16 rows x 32 B, which this puts
 // on every bank pair exactly twice.
+//
+// FP8 (kFp8): W_UV as the E4M3 codes mla_quantize_w_uv_fp8 writes, stored transposed (H, 128 v,
+// 512 c) with one scale per 128 x 128 block, and the merged rows coded on the fly with one scale
+// per 128-long latent vector, the block quantisation of the Perplexity post (sections "Слой MLA"
+// and "Квантование") that out_proj_fp8_kernel applies to o_lat:
+//   * wave w's slice is bytes [64 w, +64) of each of the 128 value rows (8 KiB, 16 rows x 64 B per
+//     load), 16-byte unit u of value row v stored at u ^ ((v >> 2) & 3);
+//   * vector kb of a row spans the latent rows of waves 2 kb and 2 kb + 1: each wave's row maxima
+//     reach its partner through LDS (one barrier), then every lane codes its 16 merged values, which
+//     are again the B operand of a 16x16x32 (FP8) MFMA;
+//   * A = W_UV^T codes, 8 bytes read straight from a value row (no transposed read); one MFMA per
+//     (ks, value block), the wave's sums scaled by the row's activation scale times the weight
+//     scale of block kb before the waves' sums meet.
 constexpr int kMopRows = 16;
 __device__ __forceinline__ int mop_swz(int c) { return (c & 3) | (((c >> 3) & 1) << 2); }
+__device__ __forceinline__ int mop_swz8(int v) { return (v >> 2) & 3; }
+
+constexpr float kE4M3MaxMop = 448.0f;  // largest finite E4M3 value: a vector's maximum codes to it
 
 __device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+template <bool kFp8>
 __global__ __launch_bounds__(512, 1) void merge_out_proj_kernel(const uint16_t* __restrict__ o_part,
                                                                 const float* __restrict__ lse_part,
-                                                                const uint16_t* __restrict__ w_uv,
+                                                                const void* __restrict__ w_uv,
+                                                                const float* __restrict__ w_scales,
                                                                 uint16_t* __restrict__ out, float* __restrict__ o_lat,
                                                                 float* __restrict__ lse, int rows, int num_splits,
                                                                 int blocks_per_wg) {
-  __shared__ __attribute__((aligned(1024))) char wl_raw[kDc * kDh * 2];  // 128 KiB: the W_UV[h] slices
+  constexpr int kSliceBytes = kFp8 ? 64 * kDh : 64 * kDh * 2;  // one wave's 64 latent rows of W_UV[h]
+  __shared__ __attribute__((aligned(1024))) char wl_raw[8 * kSliceBytes];  // 64 / 128 KiB: the W_UV[h] slices
   __shared__ __attribute__((aligned(1024))) char red_raw[4 * 8 * 4 * 64 * 4];  // 32 KiB: four sum slots
+  __shared__ float amax_x[kFp8 ? 8 * 16 : 1];  // FP8: each wave's row maxima over its 64 latent values
   MLA_LDS char* const wl = (MLA_LDS char*)wl_raw;
   MLA_LDS float* const red = (MLA_LDS float*)red_raw;  // slot s: [value block][element][lane]
   const int nblk = (rows + kMopRows - 1) / kMopRows;
@@ -318,7 +338,7 @@ __global__ __launch_bounds__(512, 1) void merge_out_proj_kernel(const uint16_t* 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, g = lane >> 4, s16 = lane & 15;
   const int c0 = 64 * wave;
-  MLA_LDS char* const ws = wl + wave * (64 * kDh * 2);  // this wave's 64 rows x 256 B
+  MLA_LDS char* const ws = wl + wave * kSliceBytes;  // this wave's slice
 
   // merge: row n = 16 blk + s16 (a row past the end reads row 16 blk, which exists, and stores nothing)
   auto row_of = [&](int blk) { return 16 * blk + s16 < rows ? 16 * blk + s16 : 16 * blk; };
@@ -345,8 +365,17 @@ __global__ __launch_bounds__(512, 1) void merge_out_proj_kernel(const uint16_t* 
   // W_UV[h] rows [c0, c0 + 64) after the first partials, so waiting for those does not wait for
   // W: load i covers local rows 4 i .. 4 i + 3 (16 lanes each).  Staged once for every row block of
   // the workgroup.
-  {
-    const char* src = (const char*)(w_uv + ((size_t)h * kDc + c0) * kDh);
+  if constexpr (kFp8) {  // load i: value rows 16 i .. 16 i + 15 (lane l: row 16 i + l / 4, LDS unit l % 4)
+    const uint8_t* src = (const uint8_t*)w_uv + (size_t)h * kDh * kDc + c0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int v = 16 * i + (lane >> 2);
+      const int u = (lane & 3) ^ mop_swz8(v);
+      __builtin_amdgcn_global_load_lds((const MLA_GLOBAL void*)(src + (size_t)v * kDc + u * 16),
+                                       (MLA_LDS void*)(ws + i * 1024), 16, 0, 0);
+    }
+  } else {
+    const char* src = (const char*)((const uint16_t*)w_uv + ((size_t)h * kDc + c0) * kDh);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int c = 4 * i + g, u = s16;
@@ -355,6 +384,7 @@ __global__ __launch_bounds__(512, 1) void merge_out_proj_kernel(const uint16_t* 
                                        (MLA_LDS void*)(ws + i * 1024), 16, 0, 0);
     }
   }
+  const float sw = kFp8 ? w_scales[h * 4 + (wave >> 1)] : 1.f;  // FP8: weight scale of block kb = w / 2
   // A operand of value block mb, k step ks: two transposed reads; source lane s of group g gives
   // local row 32 ks + 8 g + 4 t + s/4 and values 16 mb + 4 (s%4) .. +3 (t = 0, 1).
   const int fsw = (s16 >> 2) | ((g & 1) << 2);  // mop_swz of every row this lane addresses
@@ -400,7 +430,7 @@ __global__ __launch_bounds__(512, 1) void merge_out_proj_kernel(const uint16_t* 
       }
     }
     const float inv = sum > 0.f ? 1.0f / sum : 0.f;
-    bf16x8 bh[2], bl[2];
+    float ov[2][8];  // the merged row: latent 64 w + 32 ks + 8 g + j
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const f32x4 a = acc_o[2 * ks] * inv, b = acc_o[2 * ks + 1] * inv;
@@ -409,17 +439,47 @@ __global__ __launch_bounds__(512, 1) void merge_out_proj_kernel(const uint16_t* 
         dst[0] = a;
         dst[1] = b;
       }
-      const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-      u32x4 hw, lw;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        hw[j] = pack_bf16x2(v[2 * j], v[2 * j + 1]);
-        const float d0 = v[2 * j] - __uint_as_float(hw[j] << 16);
-        const float d1 = v[2 * j + 1] - __uint_as_float(hw[j] & 0xffff0000u);
-        lw[j] = pack_bf16x2(d0, d1);
+      for (int j = 0; j < 4; ++j) ov[ks][j] = a[j], ov[ks][4 + j] = b[j];
+    }
+    bf16x8 bh[2], bl[2];  // bf16: hi + lo parts
+    uint32_t bc[2][2];    // FP8: codes (8 per ks)
+    float s_row = 1.f;    // FP8: activation scale of this lane's row times the weight scale
+    if constexpr (kFp8) {
+      float m8 = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) m8 = fmaxf(m8, fabsf(ov[ks][j]));
+      m8 = fmaxf(m8, __shfl_xor(m8, 16));
+      m8 = fmaxf(m8, __shfl_xor(m8, 32));
+      if (g == 0) amax_x[wave * 16 + s16] = m8;
+      __syncthreads();
+      const float amax = fmaxf(m8, amax_x[(wave ^ 1) * 16 + s16]);
+      const float f = amax > 0.f ? kE4M3MaxMop / amax : 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          int word = __builtin_amdgcn_cvt_pk_fp8_f32(ov[ks][4 * i] * f, ov[ks][4 * i + 1] * f, 0, false);
+          word = __builtin_amdgcn_cvt_pk_fp8_f32(ov[ks][4 * i + 2] * f, ov[ks][4 * i + 3] * f, word, true);
+          bc[ks][i] = f > 0.f ? (uint32_t)word : 0u;
+        }
+      s_row = (amax / kE4M3MaxMop) * sw;
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        u32x4 hw, lw;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          hw[j] = pack_bf16x2(ov[ks][2 * j], ov[ks][2 * j + 1]);
+          const float d0 = ov[ks][2 * j] - __uint_as_float(hw[j] << 16);
+          const float d1 = ov[ks][2 * j + 1] - __uint_as_float(hw[j] & 0xffff0000u);
+          lw[j] = pack_bf16x2(d0, d1);
+        }
+        bh[ks] = __builtin_bit_cast(bf16x8, hw);
+        bl[ks] = __builtin_bit_cast(bf16x8, lw);
       }
-      bh[ks] = __builtin_bit_cast(bf16x8, hw);
-      bl[ks] = __builtin_bit_cast(bf16x8, lw);
     }
     if (lse && live && wave == 0 && g == 0) lse[(size_t)n * kHeads + h] = m == -INFINITY ? -INFINITY : m + logf(sum);
 
@@ -432,18 +492,33 @@ __global__ __launch_bounds__(512, 1) void merge_out_proj_kernel(const uint16_t* 
     f32x4 acc[8];
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (kFp8) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+      for (int ks = 0; ks < 2; ++ks) {
+        const long b = (long)(((uint64_t)bc[ks][1] << 32) | bc[ks][0]);
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb) {
-        const MLA_LDS char* p = a_row + ks * 32 * (kDh * 2) + ((mb ^ fsw) * 32);
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)p);
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(p + 4 * (kDh * 2)));
-        const i16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        const bf16x8 av = __builtin_bit_cast(bf16x8, a8);
-        acc[mb] = mfma16x16x32(av, bh[ks], acc[mb]);
-        acc[mb] = mfma16x16x32(av, bl[ks], acc[mb]);
+        for (int mb = 0; mb < 8; ++mb) {  // A: value row 16 mb + s16, latent bytes 32 ks + 8 g .. +7
+          const int v = 16 * mb + s16, u = 2 * ks + (g >> 1);
+          const long a = *(const MLA_LDS long*)(ws + v * 64 + ((u ^ mop_swz8(v)) * 16) + (g & 1) * 8);
+          acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, acc[mb], 0, 0, 0);
+        }
       }
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) acc[mb] *= s_row;
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb) {
+          const MLA_LDS char* p = a_row + ks * 32 * (kDh * 2) + ((mb ^ fsw) * 32);
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)p);
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)(p + 4 * (kDh * 2)));
+          const i16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          const bf16x8 av = __builtin_bit_cast(bf16x8, a8);
+          acc[mb] = mfma16x16x32(av, bh[ks], acc[mb]);
+          acc[mb] = mfma16x16x32(av, bl[ks], acc[mb]);
+        }
+    }
 
     // The eight waves' partial sums (over their latent rows) meet in the four sum slots: waves 4-7
     // put theirs in slots 0-3, waves 0-3 add them and put the pair sums back, then wave w adds value
@@ -553,7 +628,7 @@ hipError_t launch_absorb_q(const void* q_nope, const void* w_uk, void* q_lat, in
   return hipGetLastError();
 }
 
-hipError_t launch_merge_out_proj(const void* o_part, const float* lse_part, const void* w_uv, void* out,
+hipError_t launch_merge_out_proj(const void* o_part, const float* lse_part, const void* w_uv, bool w_fp8, void* out,
                                  float* o_lat, float* lse, int rows, int num_splits, hipStream_t stream) {
   forget_stale_error();
   // two workgroups per head (one per CU at 128 heads), each over a run of 16-row blocks, so a
@@ -563,8 +638,16 @@ hipError_t launch_merge_out_proj(const void* o_part, const float* lse_part, cons
   if (wph == 0) return hipSuccess;
   const int bpw = (nblk + wph - 1) / wph;
   const int64_t grid = (int64_t)kHeads * ((nblk + bpw - 1) / bpw);
-  hipLaunchKernelGGL(merge_out_proj_kernel, dim3((unsigned)grid), dim3(512), 0, stream, (const uint16_t*)o_part,
-                     lse_part, (const uint16_t*)w_uv, (uint16_t*)out, o_lat, lse, rows, num_splits, bpw);
+  if (w_fp8) {
+    const float* scales = (const float*)((const uint8_t*)w_uv + (size_t)kHeads * kDc * kDh);
+    hipLaunchKernelGGL(merge_out_proj_kernel<true>, dim3((unsigned)grid), dim3(512), 0, stream,
+                       (const uint16_t*)o_part, lse_part, w_uv, scales, (uint16_t*)out, o_lat, lse, rows, num_splits,
+                       bpw);
+  } else {
+    hipLaunchKernelGGL(merge_out_proj_kernel<false>, dim3((unsigned)grid), dim3(512), 0, stream,
+                       (const uint16_t*)o_part, lse_part, w_uv, (const float*)nullptr, (uint16_t*)out, o_lat, lse,
+                       rows, num_splits, bpw);
+  }
   return hipGetLastError();
 }
 

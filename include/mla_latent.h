@@ -208,6 +208,21 @@ mla_status mla_decode_attn_out_proj(const void* q_lat, const void* q_pe, const v
                                     const mla_params* p, void* stream);
 
 /*
+ * mla_decode_attn_out_proj with the W_UV product FP8 block-quantised (the Perplexity post, sections
+ * "Слой MLA" and "Квантование"): w_uv_fp8 is the packed buffer mla_quantize_w_uv_fp8 writes, and
+ * each merged latent row is coded on the fly with one scale per 128-long vector, the scheme of
+ * mla_out_proj_fp8. Every other argument, the workspace (mla_decode_attn_out_proj_workspace_bytes)
+ * and every error are those of mla_decode_attn_out_proj. With at least 16 query rows and more than
+ * one split, the merge, the coding and the FP8 product run in one kernel; otherwise the call runs
+ * the attention (with its merge) and then mla_out_proj_fp8's kernel on o_lat.
+ */
+mla_status mla_decode_attn_out_proj_fp8(const void* q_lat, const void* q_pe, const void* kv_pool,
+                                        const int32_t* block_table, const int32_t* seq_lens,
+                                        const int32_t* tree_parents, const void* w_uv_fp8, void* out, float* o_lat,
+                                        float* lse, void* workspace, size_t workspace_bytes, int32_t num_splits,
+                                        const mla_params* p, void* stream);
+
+/*
  * Static scratch of mla_decode_attn_out_proj_static: 64 MiB of device memory per GPU, held from the
  * library's load until the process ends (the split partials of 32 sequences x 8 key ranges, or of
  * 256 query rows x 2 ranges, take 33.7 MB).

@@ -106,24 +106,26 @@ def case_decode(batch, q_len, max_seq_len, splits, dtype, num_pages=0, tree=Fals
     print(f"decode B={batch} S={q_len} L={max_seq_len} splits={splits}->{n_split} dtype={dtype} tree={tree} ok")
 
 
-def case_fused(batch, q_len, max_seq_len, splits, latent_outputs):
+def case_fused(batch, q_len, max_seq_len, splits, latent_outputs, fp8=False):
     lib.san_set_cus(256)
     p = params(batch=batch, q_len=q_len, max_seq_len=max_seq_len)
     rows = batch * q_len
     q_lat, q_pe, pool = buf(rows * H * DC * 2), buf(rows * H * DR * 2), buf(PAGE * ROW * 2)
     bt, ln = table(batch, p.max_pages_per_seq, 1), lens(batch, max_seq_len)
-    w_uv, out = buf(H * DC * DH * 2), buf(rows * H * DH * 2)
+    w_uv = buf(lib.mla_fp8_weight_bytes() if fp8 else H * DC * DH * 2)
+    out = buf(rows * H * DH * 2)
     o = buf(rows * H * DC * 4) if latent_outputs else None
     lse = buf(rows * H * 4) if latent_outputs else None
     nbytes = lib.mla_decode_attn_out_proj_workspace_bytes(ctypes.byref(p), splits)
     ws = buf(nbytes)
     before = counts()
-    code = lib.mla_decode_attn_out_proj(q_lat, q_pe, pool, addr(bt), addr(ln), None, w_uv, out, o, lse, ws, nbytes,
-                                        splits, ctypes.byref(p), None)
-    expect(code, f"fused B={batch} S={q_len} splits={splits}")
+    call = lib.mla_decode_attn_out_proj_fp8 if fp8 else lib.mla_decode_attn_out_proj
+    code = call(q_lat, q_pe, pool, addr(bt), addr(ln), None, w_uv, out, o, lse, ws, nbytes, splits, ctypes.byref(p),
+                None)
+    expect(code, f"fused B={batch} S={q_len} splits={splits} fp8={fp8}")
     assert launched("attn", before) == 1
-    assert launched("merge_out_proj", before) + launched("out_proj", before) == 1
-    print(f"fused B={batch} S={q_len} L={max_seq_len} splits={splits} latent={latent_outputs} ok "
+    assert launched("merge_out_proj", before) + launched("out_proj_fp8" if fp8 else "out_proj", before) == 1
+    print(f"fused B={batch} S={q_len} L={max_seq_len} splits={splits} latent={latent_outputs} fp8={fp8} ok "
           f"(merge in W_UV: {launched('merge_out_proj', before)})")
 
 
@@ -214,6 +216,8 @@ if __name__ == "__main__":
     case_fused(2, 1, 700, 2, False)
     case_fused(2, 1, 700, 1, False)
     case_fused(32, 1, 4096, 0, True)
+    for args in ((16, 1, 700, 2, False), (2, 1, 700, 2, True), (32, 1, 4096, 0, True), (4, 1, 300, 1, False)):
+        case_fused(*args, fp8=True)
     case_prefill(2, 96, 160, 0)
     case_prefill(1, 300, 300, 2)
     for m, k, n, cus in ((32, 1024, 512, 256), (600, 7168, 2112, 256), (1, 64, 64, 1), (0, 64, 64, 256)):

@@ -96,13 +96,15 @@ hipError_t launch_absorb_q(const void* q_nope, const void* w_uk, void* q_lat, in
   return hipSuccess;
 }
 
-hipError_t launch_merge_out_proj(const void* o_part, const float* lse_part, const void* w_uv, void* out,
+constexpr size_t kFp8Bytes = (size_t)kHeads * kDc * kDh + (size_t)kHeads * 4 * 4;
+
+hipError_t launch_merge_out_proj(const void* o_part, const float* lse_part, const void* w_uv, bool w_fp8, void* out,
                                  float* o_lat, float* lse, int rows, int num_splits, hipStream_t) {
   ++g_launches[kMergeOutProj];
   const size_t n = (size_t)rows * num_splits * kHeads;
   touch(o_part, n * kDc * 2);
   touch(lse_part, n * 4);
-  touch(w_uv, (size_t)kHeads * kDc * kDh * 2);
+  touch(w_uv, w_fp8 ? kFp8Bytes : (size_t)kHeads * kDc * kDh * 2);
   touch(out, (size_t)rows * kHeads * kDh * 2);
   touch(o_lat, (size_t)rows * kHeads * kDc * 4);
   touch(lse, (size_t)rows * kHeads * 4);
@@ -155,8 +157,6 @@ hipError_t launch_linear(const void* x, const void* w, void* y, float* partial, 
   if (splits > 1) touch(partial, (size_t)splits * M * N * 4);
   return hipSuccess;
 }
-
-constexpr size_t kFp8Bytes = (size_t)kHeads * kDc * kDh + (size_t)kHeads * 4 * 4;
 
 hipError_t launch_quantize_weight_fp8(const void* w, void* packed, bool, hipStream_t) {
   ++g_launches[kQuant];

@@ -154,3 +154,50 @@ def test_fp8_decode_path_end_to_end():
     err = rel_err(to_host(bufs.out), want)
     say("  out rel err", err)
     assert err <= 2e-2
+
+
+@pytest.mark.parametrize("batch,q_len,splits,lens", [
+    (16, 1, 2, None),             # merge, coding and FP8 product in one kernel
+    (32, 1, 0, None),             # the library's split count
+    (8, 2, 3, None),              # two query tokens (16 rows), causal
+    (17, 1, 2, [0] + [300] * 16),  # a row with no keys: o_lat = 0, codes 0, out = 0; a ragged last block
+    (3, 1, 2, None),              # fewer than 16 rows: attention + merge, then the FP8 out-projection
+    (16, 1, 1, None),             # one split: attention writes o_lat, then the FP8 out-projection
+])
+def test_fused_attention_out_proj_fp8(batch, q_len, splits, lens):
+    """mla_decode_attn_out_proj_fp8 against the oracle's latent attention followed by its FP8
+    out-projection.  The call codes its own merged rows (bf16 partials merged in fp32), so where a
+    value lies within that rounding of an E4M3 rounding boundary its code can be one step from the
+    oracle's code of the exact o_lat; the output is therefore held to the bf16 bar (2e-2), not to
+    FP8_TOL, and to 5% of the unquantised product.  o_lat and lse (optional outputs) are held to
+    the bf16 bar as in the bf16 call."""
+    import torch
+    from tests.helpers import check_lse
+    say("fused attention + out-proj fp8", batch, q_len, splits, "lens" if lens else "ragged")
+    w = gen.small_workload(batch, q_len, ragged=None if lens else (100, 700), cache_len=1 if lens else None,
+                           dtype="bf16", paged=True)
+    x = gen.generate(w, 950 + batch + splits, poison_unused=True, seq_lens=lens)
+    d = to_device(x)
+    p = params_for(x)
+    q_bits, _ = gen.generate_latent(w, 951 + batch)
+    q_lat = torch.from_numpy(np.ascontiguousarray(q_bits).view(np.int16)).view(torch.bfloat16).cuda()
+    uv = _packed(x.w_uv, True)
+    out = torch.full((batch, q_len, 128, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    o = torch.full((batch, q_len, 128, 512), float("nan"), device="cuda")
+    lse = torch.full((batch, q_len, 128), float("nan"), device="cuda")
+    nb = binding.mla_decode_attn_out_proj_workspace_bytes(p, splits)
+    ws = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
+    binding.mla_decode_attn_out_proj_fp8(q_lat, d["q_pe"], d["pool"], d["block_table"], d["seq_lens"], None, uv, out,
+                                         o, lse, ws, splits, p, workspace_bytes=nb)
+    torch.cuda.synchronize()
+    att = dec.latent_attention_reference(gen.bf16_bits_to_f32(q_bits), x.f32("q_pe"), x.f32("pool"), x.block_table,
+                                         x.seq_lens, softmax_scale=w.softmax_scale)
+    want, _, _ = ref.out_proj_fp8_reference(att["o_lat"].astype(np.float32), x.f32("w_uv"))
+    got = to_host(out)
+    err, err_exact = rel_err(got, want), rel_err(got, dec.out_proj_reference(att["o_lat"], x.f32("w_uv")))
+    o_err, l_err = rel_err(to_host(o), att["o_lat"]), check_lse(to_host(lse), att["lse"], 2e-2)
+    say(f"  out rel err vs fp8 oracle {err:.2e}, vs unquantised {err_exact:.2e}; o_lat {o_err:.2e}; lse {l_err:.2e}")
+    assert not np.isnan(got).any()
+    assert err <= 2e-2 and err_exact <= 0.05 and o_err <= 2e-2
+    if lens:
+        assert np.all(got[0] == 0)
