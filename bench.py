@@ -38,6 +38,7 @@ tree cached after them, reported as verified draft tokens/s (B x 8 per step).
 Prints one JSON line.
 """
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -528,6 +529,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="b32_t4096")
     ap.add_argument("--num-splits", type=int, default=0, help="0 = library's choice")
+    ap.add_argument("--cache-len", type=int, default=0,
+                    help="fixed-length one-token decode workloads: run at this cache length instead (0 = the workload's)")
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough to exceed 2x the 256 MB MALL")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -564,7 +567,15 @@ def main():
 
     tree_wl = args.workload in gen.TREE_WORKLOADS
     w = gen.TREE_WORKLOADS[args.workload] if tree_wl else gen.WORKLOADS[args.workload]
-    x = gen.generate_named(args.workload)
+    if args.cache_len:
+        # the same workload at another fixed cache length (a sweep of the per-workgroup key range)
+        if w.ragged is not None or tree_wl or w.q_len != 1:
+            print("--cache-len applies to the fixed-length one-token decode workloads", file=sys.stderr)
+            sys.exit(2)
+        w = dataclasses.replace(w, cache_len=args.cache_len)
+        x = gen.generate(w, gen.WORKLOAD_SEEDS[args.workload])
+    else:
+        x = gen.generate_named(args.workload)
     dt = "bf16" if x.is_bf16 else "f32"
     parents = gen.draft_trees(w.batch, w.q_len, gen.TREE_SEEDS[args.workload]) if tree_wl else None
 
@@ -700,7 +711,7 @@ def main():
                           "calls_roof_us": {c.name: c.roof_seconds(dt) * 1e6 for c in costs}},
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(gen.generate_named(args.workload), args.cpu_seconds, tree=parents)
+        rec["cpu_baseline"] = cpu_baseline(x, args.cpu_seconds, tree=parents)
     print(json.dumps(rec), flush=True)
 
 

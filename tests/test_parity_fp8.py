@@ -166,11 +166,13 @@ def test_fp8_decode_path_end_to_end():
 ])
 def test_fused_attention_out_proj_fp8(batch, q_len, splits, lens):
     """mla_decode_attn_out_proj_fp8 against the oracle's latent attention followed by its FP8
-    out-projection.  The call codes its own merged rows (bf16 partials merged in fp32), so where a
-    value lies within that rounding of an E4M3 rounding boundary its code can be one step from the
-    oracle's code of the exact o_lat; the output is therefore held to the bf16 bar (2e-2), not to
-    FP8_TOL, and to 5% of the unquantised product.  o_lat and lse (optional outputs) are held to
-    the bf16 bar as in the bf16 call."""
+    out-projection.  The call codes its own merged rows (bf16 partials merged in fp32), which
+    differ from the exact o_lat by about one bf16 rounding, and E4M3 coding amplifies that: a value
+    within that distance of a rounding point takes the neighbouring code.  The oracle measures this
+    itself: s = the distance between its FP8 product of the bf16-rounded o_lat and its FP8 product
+    of the exact one (1.1e-2 to 2.1e-2 on these cases).  Bars: out within 2e-2 + s of the FP8
+    oracle, and within q + 2e-2 of the unquantised product, q being the oracle's own FP8 error
+    (2.7e-2 to 4.5e-2 here); o_lat and lse (optional outputs) at the bf16 bar as in the bf16 call."""
     import torch
     from tests.helpers import check_lse
     say("fused attention + out-proj fp8", batch, q_len, splits, "lens" if lens else "ragged")
@@ -192,12 +194,17 @@ def test_fused_attention_out_proj_fp8(batch, q_len, splits, lens):
     torch.cuda.synchronize()
     att = dec.latent_attention_reference(gen.bf16_bits_to_f32(q_bits), x.f32("q_pe"), x.f32("pool"), x.block_table,
                                          x.seq_lens, softmax_scale=w.softmax_scale)
-    want, _, _ = ref.out_proj_fp8_reference(att["o_lat"].astype(np.float32), x.f32("w_uv"))
+    o_ref = att["o_lat"].astype(np.float32)
+    want, _, _ = ref.out_proj_fp8_reference(o_ref, x.f32("w_uv"))
+    exact = dec.out_proj_reference(att["o_lat"], x.f32("w_uv"))
+    moved, _, _ = ref.out_proj_fp8_reference(gen.bf16_bits_to_f32(gen.round_to_bf16_bits(o_ref)), x.f32("w_uv"))
+    sens, q_err = rel_err(moved, want), rel_err(want, exact)
     got = to_host(out)
-    err, err_exact = rel_err(got, want), rel_err(got, dec.out_proj_reference(att["o_lat"], x.f32("w_uv")))
+    err, err_exact = rel_err(got, want), rel_err(got, exact)
     o_err, l_err = rel_err(to_host(o), att["o_lat"]), check_lse(to_host(lse), att["lse"], 2e-2)
-    say(f"  out rel err vs fp8 oracle {err:.2e}, vs unquantised {err_exact:.2e}; o_lat {o_err:.2e}; lse {l_err:.2e}")
+    say(f"  out rel err vs fp8 oracle {err:.2e} (bar 2e-2 + {sens:.2e}), vs unquantised {err_exact:.2e} "
+        f"(bar {q_err:.2e} + 2e-2); o_lat {o_err:.2e}; lse {l_err:.2e}")
     assert not np.isnan(got).any()
-    assert err <= 2e-2 and err_exact <= 0.05 and o_err <= 2e-2
+    assert err <= 2e-2 + sens and err_exact <= q_err + 2e-2 and o_err <= 2e-2
     if lens:
         assert np.all(got[0] == 0)
