@@ -237,14 +237,17 @@ def test_end_to_end_small_mtp_all_heads():
 
 
 # ------------------------------------------------------------------------------------ boundary
-@pytest.mark.parametrize("variant", ["causal", "tree", "fp8"])
+@pytest.mark.parametrize("variant", ["causal", "tree", "fp8", "fused", "fused fp8"])
 def test_graph_capture_replays_match_eager(variant):
-    """The three calls captured in one HIP graph; replays interleaved with eager work all match the
-    eager run bit for bit (decode as is, with a draft-tree mask, and with the FP8 projections)."""
+    """The step's calls captured in one HIP graph; replays interleaved with eager work all match the
+    eager run bit for bit (decode as is, with a draft-tree mask, with the FP8 projections, and the
+    fused attention + merge/W_UV call in bf16 and FP8 at 16 rows, where the merge runs inside the
+    W_UV kernel)."""
     say("graph capture", variant)
     torch = _torch()
     S = 4 if variant == "tree" else 1
-    w = gen.small_workload(4, S, ragged=(200, 700), dtype="bf16", paged=True)
+    B = 16 if variant.startswith("fused") else 4
+    w = gen.small_workload(B, S, ragged=(200, 700), dtype="bf16", paged=True)
     x = gen.generate(w, 23, poison_unused=True)
     d = to_device(x)
     p = params_for(x, causal=variant != "tree")
@@ -252,7 +255,9 @@ def test_graph_capture_replays_match_eager(variant):
     w_uk, w_uv = d["w_uk"], d["w_uv"]
     if variant == "tree":
         kw["tree_parents"] = torch.from_numpy(gen.draft_trees(4, S, 24)).cuda()
-    if variant == "fp8":
+    if variant.startswith("fused"):
+        kw["fused"] = True
+    if variant.endswith("fp8"):
         w_uk = torch.empty(binding.mla_fp8_weight_bytes(), dtype=torch.uint8, device="cuda")
         w_uv = torch.empty_like(w_uk)
         binding.mla_quantize_w_uk_fp8(d["w_uk"], w_uk, p)

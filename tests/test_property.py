@@ -9,9 +9,9 @@ terms on lse, and on sampled rows the oracle's logits normalised by the GPU's ls
 Drawn for tree-masked verify: batch 1..3, trees of 1, 3, 8, 17 or 64 nodes with random parents
 (several roots, and parents out of range, which end the ancestor walk), lengths 1..320 (so some
 sequences hold fewer tokens than their tree), split counts and dtypes as above.
-Drawn for the fused attention + out-projection (bf16): batch 1..24 and S in {1, 2, 3}, so both of
-its routes run; split counts up to 9; the causal / full rule or a drawn draft tree; the optional
-latent outputs on or off.
+Drawn for the fused attention + out-projection (bf16, and its FP8 form): batch 1..24 and S in
+{1, 2, 3}, so both of its routes run; split counts up to 9; the causal / full rule or a drawn
+draft tree; the optional latent outputs on or off.
 """
 import numpy as np
 import pytest
@@ -177,3 +177,53 @@ def test_fused_attention_out_proj_matches_oracle(case):
         check_softmax_mass(gen.bf16_bits_to_f32(q_lat), x.f32("q_pe"), x.f32("pool"), x.block_table, x.seq_lens, lse,
                            sample_rows(want["lse"], n=16, seed=case["seed"]), softmax_scale=w.softmax_scale,
                            tol=tol_for(x), causal=case["causal"], tree=parents)
+
+
+@settings(max_examples=20, deadline=None, derandomize=True, suppress_health_check=list(HealthCheck))
+@given(case=fused_cases())
+def test_fused_attention_out_proj_fp8_matches_oracle(case):
+    """mla_decode_attn_out_proj_fp8 on the same drawn batches: out against the oracle's FP8
+    out-projection of its latent attention, within 2e-2 plus the oracle's own distance between its
+    FP8 products of the bf16-rounded and of the exact o_lat (the call codes merged rows that carry
+    one bf16 rounding), and within the oracle's own FP8 error plus 2e-2 of the unquantised product;
+    o_lat and lse at the bf16 bar when asked for."""
+    import torch
+    from oracle import fp8 as ref8
+    print("[case]", case, flush=True)
+    w = gen.small_workload(case["batch"], case["q_len"], cache_len=1, dtype="bf16", paged=case["paged"])
+    x = gen.generate(w, case["seed"], poison_unused=True, seq_lens=case["lens"])
+    q_lat, _ = gen.generate_latent(w, case["seed"] + 1)
+    d = to_device(x)
+    p = params_for(x, causal=case["causal"])
+    parents = None if case["parents"] is None else np.array(case["parents"], dtype=np.int32)
+    uv = torch.zeros(binding.mla_fp8_weight_bytes(), dtype=torch.uint8, device="cuda")
+    binding.mla_quantize_w_uv_fp8(d["w_uv"], uv, p)
+    out = torch.full((w.batch, w.q_len, 128, 128), float("nan"), device="cuda").to(torch.bfloat16)
+    o = torch.full((w.batch, w.q_len, 128, 512), float("nan"), device="cuda") if case["latent"] else None
+    lse = torch.full((w.batch, w.q_len, 128), float("nan"), device="cuda") if case["latent"] else None
+    ws_bytes = binding.mla_decode_attn_out_proj_workspace_bytes(p, case["splits"])
+    ws = torch.full((max(ws_bytes, 16) // 4,), float("nan"), device="cuda")
+    binding.mla_decode_attn_out_proj_fp8(device_array(q_lat, True), d["q_pe"], d["pool"], d["block_table"],
+                                         d["seq_lens"], None if parents is None else torch.from_numpy(parents).cuda(),
+                                         uv, out, o, lse, ws, case["splits"], p)
+    torch.cuda.synchronize()
+
+    want = ref.latent_attention_reference(gen.bf16_bits_to_f32(q_lat), x.f32("q_pe"), x.f32("pool"), x.block_table,
+                                          x.seq_lens, softmax_scale=w.softmax_scale, causal=case["causal"],
+                                          tree=parents)
+    o_ref = want["o_lat"].astype(np.float32)
+    fp8_ref, _, _ = ref8.out_proj_fp8_reference(o_ref, x.f32("w_uv"))
+    moved, _, _ = ref8.out_proj_fp8_reference(gen.bf16_bits_to_f32(gen.round_to_bf16_bits(o_ref)), x.f32("w_uv"))
+    exact = ref.out_proj_reference(want["o_lat"], x.f32("w_uv"))
+    got = to_host(out)
+    assert not np.isnan(got).any()
+    sens, q_err = rel_err(moved, fp8_ref), rel_err(fp8_ref, exact)
+    err, err_exact = rel_err(got, fp8_ref), rel_err(got, exact)
+    print(f"[case]   out vs fp8 oracle {err:.2e} (bar 2e-2 + {sens:.2e}), vs unquantised {err_exact:.2e} "
+          f"(bar {q_err:.2e} + 2e-2)", flush=True)
+    assert err <= 2e-2 + sens and err_exact <= q_err + 2e-2
+    if case["latent"]:
+        o, lse = to_host(o), to_host(lse)
+        assert not np.isnan(o).any() and not np.isnan(lse).any()
+        assert rel_err(o, want["o_lat"]) <= tol_for(x)
+        check_lse(lse, want["lse"], tol_for(x))
