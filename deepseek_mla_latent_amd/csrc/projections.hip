@@ -329,7 +329,7 @@ __global__ __launch_bounds__(512, 1) void merge_out_proj_kernel(const uint16_t* 
   __shared__ __attribute__((aligned(1024))) char red_raw[4 * 8 * 4 * 64 * 4];  // 32 KiB: four sum slots
   __shared__ float amax_x[kFp8 ? 8 * 16 : 1];  // FP8: each wave's row maxima over its 64 latent values
   MLA_LDS char* const wl = (MLA_LDS char*)wl_raw;
-  MLA_LDS float* const red = (MLA_LDS float*)red_raw;  // slot s: [value block][element][lane]
+  MLA_LDS f32x4* const red = (MLA_LDS f32x4*)red_raw;  // slot s: [value block][lane], 4 elements each
   const int nblk = (rows + kMopRows - 1) / kMopRows;
   const int wph = (nblk + blocks_per_wg - 1) / blocks_per_wg;  // workgroups per head
   const int id = xcd_remap(blockIdx.x, gridDim.x);
@@ -523,30 +523,20 @@ __global__ __launch_bounds__(512, 1) void merge_out_proj_kernel(const uint16_t* 
     // The eight waves' partial sums (over their latent rows) meet in the four sum slots: waves 4-7
     // put theirs in slots 0-3, waves 0-3 add them and put the pair sums back, then wave w adds value
     // block w over the four slots.  Element i of lane l is value 16 mb + 4 g + i of row s16.
-    auto slot = [&](int sl, int mb, int i) -> MLA_LDS float& { return red[((sl * 8 + mb) * 4 + i) * 64 + lane]; };
+    auto slot = [&](int sl, int mb) -> MLA_LDS f32x4& { return red[(sl * 8 + mb) * 64 + lane]; };
     if (wave >= 4) {
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) slot(wave - 4, mb, i) = acc[mb][i];
+      for (int mb = 0; mb < 8; ++mb) slot(wave - 4, mb) = acc[mb];
     }
     __syncthreads();
     if (wave < 4) {
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[mb][i] += slot(wave, mb, i);
-#pragma unroll
-      for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) slot(wave, mb, i) = acc[mb][i];
+      for (int mb = 0; mb < 8; ++mb) slot(wave, mb) = acc[mb] + slot(wave, mb);
     }
     __syncthreads();
     {
       const int mb = wave;
-      float sv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sv[i] = (slot(0, mb, i) + slot(1, mb, i)) + (slot(2, mb, i) + slot(3, mb, i));
+      const f32x4 sv = (slot(0, mb) + slot(1, mb)) + (slot(2, mb) + slot(3, mb));
       if (live) {
         const u32x2 pk = {pack_bf16x2(sv[0], sv[1]), pack_bf16x2(sv[2], sv[3])};
         *(u32x2*)(out + ((size_t)n * kHeads + h) * kDh + 16 * mb + 4 * g) = pk;
