@@ -667,74 +667,175 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
   }
 }
 
-// fp32 path: one workgroup per (b, i, split, head); 256 threads.  Logits one token per thread,
-// block-wide max/sum, then each thread accumulates two latent columns over the chunk's tokens.
-// Natural-exp online softmax with the exact rescale at every 256-token chunk.
-__global__ __launch_bounds__(256) void decode_attn_f32_kernel(AttnArgs a) {
-  __shared__ float qs[kRow];
-  __shared__ float ps[256];
-  __shared__ float red[8];
+// fp32 path on the fp32 matrix cores (v_mfma_f32_32x32x2_f32): workgroup = (b, i, split, block of
+// 32 heads), 4 waves.  fp32 leaves no room for the bf16 kernel's layout (the query of 128 heads is
+// 288 KiB), so a workgroup takes 32 heads and the 128 heads of a key range are four workgroups,
+// each reading the range from L2 once.  Per 32-token tile (half a page, so one page id):
+//   * the tile's rows are staged in LDS with a padded row of kF32Ld floats; the next tile's rows
+//     are loaded into registers during this tile's work;
+//   * scores D(token x head) = tile x [q_lat | q_pe]^T: wave w takes k in [144 w, 144 w + 144), lane
+//     half hf the k values 144 w + 72 hf + s at step s, so its tile operand is one 16-byte read per
+//     4 steps and its query operand sits in 72 registers for the whole range; the four waves'
+//     partial sums meet in LDS and every wave adds them in the same order;
+//   * the online softmax (base 2, scale folded in) runs redundantly in every wave, each lane on the
+//     16 tokens of its head the score layout gives it; the probabilities go to the wave's own LDS
+//     area, read back as the weighted sum's operand;
+//   * weighted sum O^T(latent x head) += tile^T x P: wave w holds latent columns 128 w .. +127 of
+//     the 32 heads (four 32 x 32 blocks), lane half hf taking tokens (s & 7) + 16 (s >> 3) + 8 hf.
+// Row padding: 580 floats put the two lane halves of every read on disjoint banks.
+constexpr int kF32Tile = 32;             // tokens per tile
+constexpr int kF32Ld = kRow + 4;         // floats per staged tile row
+constexpr int kF32PLd = kF32Heads + 4;   // floats per probability row
+constexpr int kF32Loads = kF32Tile * kRow / 4 / 256;  // 16-byte loads per thread per tile (18)
+static_assert(kF32Tile * kRow % (4 * 256) == 0, "whole 16-byte loads per thread");
+
+__global__ __launch_bounds__(256, 1) void decode_attn_f32_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) float tile[kF32Tile * kF32Ld];
+  __shared__ __attribute__((aligned(16))) float spart[4 * 16 * 64];          // [wave][element][lane]
+  __shared__ __attribute__((aligned(16))) float pw[4 * kF32Tile * kF32PLd];  // [wave][token][head]
+  constexpr int kBlocks = kHeads / kF32Heads;
   const int id = xcd_remap(blockIdx.x, gridDim.x);
-  const int h = id % kHeads;
-  const WorkItem w = make_work(a, id / kHeads);
-  const int tid = threadIdx.x;
+  const int hb = id % kBlocks;
+  const WorkItem w = make_work(a, id / kBlocks);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, l32 = lane & 31, hf = lane >> 5;
+  const int head = kF32Heads * hb + l32;  // this lane's head (the MFMA column)
   const float* pool = (const float*)a.pool;
 
-  const size_t qrow = ((size_t)w.b * a.S + w.i) * kHeads + h;
-  for (int c = tid; c < kDc; c += 256) qs[c] = ((const float*)a.q_lat)[qrow * kDc + c];
-  if (tid < kDr) qs[kDc + tid] = ((const float*)a.q_pe)[qrow * kDr + tid];
-  __syncthreads();
-
-  const int32_t* bt = a.block_table + (size_t)w.b * a.max_pages;
-  const uint64_t tmask =
-      a.tree_parents ? tree_walk(tree_parent_of_lane(a.tree_parents, w.b, a.S, tid & 63), a.S, w.i) : 0ull;
-  auto visible = [&](int tkn) {
-    const int j = tkn - w.tail;
-    return !a.tree_parents || j < 0 || (j < 64 && ((tmask >> j) & 1ull));
-  };
-  float m_run = -INFINITY, l_run = 0.f, acc0 = 0.f, acc1 = 0.f;
-  for (int start = w.tok_begin; start < w.tok_end; start += 256) {
-    const int tkn = start + tid;
-    float z = -INFINITY;
-    if (tkn < w.tok_end && visible(tkn)) {
-      const float* row = pool + ((size_t)checked_page(a.bounds, bt[tkn / kPage]) * kPage + tkn % kPage) * kRow;
-      float d = 0.f;
-      for (int c = 0; c < kRow; ++c) d = fmaf(qs[c], row[c], d);
-      z = d * a.scale;
-    }
-    float m = z;
-    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-    if ((tid & 63) == 0) red[tid >> 6] = m;
-    __syncthreads();
-    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    const float m_new = fmaxf(m_run, m);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;  // a chunk with every key masked
-    const float alpha = expf(m_run - m_use);
-    const float p = expf(z - m_use);  // masked keys and keys past the range have z = -inf
-    ps[tid] = p;
-    float sm = p;
-    for (int off = 32; off > 0; off >>= 1) sm += __shfl_xor(sm, off);
-    __syncthreads();
-    if ((tid & 63) == 0) red[4 + (tid >> 6)] = sm;
-    __syncthreads();
-    l_run = l_run * alpha + (red[4] + red[5] + red[6] + red[7]);
-    acc0 *= alpha;
-    acc1 *= alpha;
-    const int cnt = w.tok_end - start < 256 ? w.tok_end - start : 256;
-    for (int j = 0; j < cnt; ++j) {
-      const int tj = start + j;
-      const float* row = pool + ((size_t)checked_page(a.bounds, bt[tj / kPage]) * kPage + tj % kPage) * kRow;
-      acc0 = fmaf(ps[j], row[tid], acc0);
-      acc1 = fmaf(ps[j], row[tid + 256], acc1);
-    }
-    m_run = m_new;
-    __syncthreads();
+  const int ntok = w.tok_end - w.tok_begin;
+  if (ntok <= 0) {  // empty key range: o = 0, lse = -inf; thread t writes 64 columns of head t / 8
+    const int hh = kF32Heads * hb + (threadIdx.x >> 3);
+    float* row = (float*)a.o_out + (w.out_row + hh) * kDc + 64 * (threadIdx.x & 7);
+#pragma unroll
+    for (int c = 0; c < 64; c += 4) *(f32x4*)(row + c) = f32x4{0.f, 0.f, 0.f, 0.f};
+    if ((threadIdx.x & 7) == 0 && a.lse_out) a.lse_out[w.out_row + hh] = -INFINITY;
+    return;
   }
-  float* o_ptr = (float*)a.o_out + (w.out_row + h) * kDc;
-  const bool empty = w.tok_end <= w.tok_begin || l_run == 0.f;
-  o_ptr[tid] = empty ? 0.f : acc0 / l_run;
-  o_ptr[tid + 256] = empty ? 0.f : acc1 / l_run;
-  if (tid == 0 && a.lse_out) a.lse_out[w.out_row + h] = empty ? -INFINITY : m_run + logf(l_run);
+  const int ntiles = (ntok + kF32Tile - 1) / kF32Tile;
+  const int32_t* bt = a.block_table + (size_t)w.b * a.max_pages;
+  // draft tree: visibility of the S new keys to this query row (wave-uniform)
+  const uint64_t tmask =
+      a.tree_parents ? tree_walk(tree_parent_of_lane(a.tree_parents, w.b, a.S, lane), a.S, w.i) : 0ull;
+
+  // The next tile's rows in registers: load r of thread t is float4 (t + 256 r) of the tile, row
+  // (t + 256 r) / 144.  Rows past the range re-read the tile's first token (finite values, masked).
+  f32x4 stage[kF32Loads];
+  auto fetch = [&](int t) {
+    const int t0 = w.tok_begin + kF32Tile * t;
+    const int cnt = w.tok_end - t0 < kF32Tile ? w.tok_end - t0 : kF32Tile;
+    const int page = checked_page(a.bounds, bt[t0 / kPage]);
+    const float* src = pool + ((size_t)page * kPage + t0 % kPage) * kRow;
+#pragma unroll
+    for (int r = 0; r < kF32Loads; ++r) {
+      const int u = threadIdx.x + 256 * r, row = u / (kRow / 4), c4 = u % (kRow / 4);
+      stage[r] = *(const f32x4*)(src + (size_t)(row < cnt ? row : 0) * kRow + 4 * c4);
+    }
+  };
+  auto put = [&]() {
+#pragma unroll
+    for (int r = 0; r < kF32Loads; ++r) {
+      const int u = threadIdx.x + 256 * r, row = u / (kRow / 4), c4 = u % (kRow / 4);
+      *(MLA_LDS f32x4*)(tile + row * kF32Ld + 4 * c4) = stage[r];
+    }
+  };
+  fetch(0);
+
+  // this lane's query operand: [q_lat | q_pe] of its head at k = 144 wave + 72 hf + s, s < 72
+  float q[72];
+  {
+    const size_t qrow = ((size_t)w.b * a.S + w.i) * kHeads + head;
+    const int k0 = 144 * wave + 72 * hf;
+#pragma unroll
+    for (int s4 = 0; s4 < 18; ++s4) {
+      const int k = k0 + 4 * s4;  // four values on one side of the q_lat / q_pe boundary (512 = 4 x 128)
+      const f32x4 v = k < kDc ? *(const f32x4*)((const float*)a.q_lat + qrow * kDc + k)
+                              : *(const f32x4*)((const float*)a.q_pe + qrow * kDr + (k - kDc));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) q[4 * s4 + j] = v[j];
+    }
+  }
+
+  float m_run = -INFINITY, l_run = 0.f;  // of this lane's head, in log2 units
+  f32x16 o[4];                           // block b: latent 128 wave + 32 b + 8 (e/4) + 4 hf + e%4
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[b][e] = 0.f;
+  MLA_LDS float* const my_p = (MLA_LDS float*)(pw + wave * kF32Tile * kF32PLd);
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int t0 = w.tok_begin + kF32Tile * t;
+    const int cnt = w.tok_end - t0 < kF32Tile ? w.tok_end - t0 : kF32Tile;
+    put();
+    __syncthreads();  // the tile is in LDS
+    if (t + 1 < ntiles) fetch(t + 1);
+
+    // scores over this wave's k range
+    f32x16 sc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sc[e] = 0.f;
+    const MLA_LDS float* arow = (const MLA_LDS float*)(tile + l32 * kF32Ld + 144 * wave + 72 * hf);
+#pragma unroll
+    for (int s4 = 0; s4 < 18; ++s4) {
+      const f32x4 av = *(const MLA_LDS f32x4*)(arow + 4 * s4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sc = mfma32x32x2f32(av[j], q[4 * s4 + j], sc);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) spart[(wave * 16 + e) * 64 + lane] = sc[e];
+    __syncthreads();  // every wave's partial scores
+    float z[16];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float v = (spart[e * 64 + lane] + spart[(16 + e) * 64 + lane]) +
+                      (spart[(32 + e) * 64 + lane] + spart[(48 + e) * 64 + lane]);
+      const int i = 8 * (e >> 2) + 4 * hf + (e & 3);  // token of element e within the tile
+      const int jn = t0 + i - w.tail;                  // draft-tree node index of that key
+      const bool vis = i < cnt && (!a.tree_parents || jn < 0 || (jn < 64 && ((tmask >> jn) & 1ull)));
+      z[e] = vis ? v * a.scale_log2 : -INFINITY;
+      mt = fmaxf(mt, z[e]);
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(m_run, mt);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;  // every key so far masked
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    float ls = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float pe = __builtin_amdgcn_exp2f(z[e] - m_use);  // masked keys: exp2(-inf) = 0
+      ls += pe;
+      my_p[(8 * (e >> 2) + 4 * hf + (e & 3)) * kF32PLd + l32] = pe;
+    }
+    ls += __shfl_xor(ls, 32);
+    l_run = l_run * alpha + ls;
+    m_run = m_new;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) o[b] *= alpha;
+
+    // weighted sum: this wave's latent columns, the tile as value
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const int k = (s & 7) + 16 * (s >> 3) + 8 * hf;
+      const float pb = my_p[k * kF32PLd + l32];
+      const MLA_LDS float* crow = (const MLA_LDS float*)(tile + k * kF32Ld + 128 * wave + l32);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) o[b] = mfma32x32x2f32(crow[32 * b], pb, o[b]);
+    }
+    __syncthreads();  // the tile, the partial scores and the probabilities are free again
+  }
+
+  const bool empty = l_run == 0.f;
+  const float inv = empty ? 0.f : 1.0f / l_run;
+  float* orow = (float*)a.o_out + (w.out_row + head) * kDc + 128 * wave + 4 * hf;
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *(f32x4*)(orow + 32 * b + 8 * g) =
+          f32x4{o[b][4 * g] * inv, o[b][4 * g + 1] * inv, o[b][4 * g + 2] * inv, o[b][4 * g + 3] * inv};
+  if (wave == 0 && hf == 0 && a.lse_out)
+    a.lse_out[w.out_row + head] = empty ? -INFINITY : (m_run + __log2f(l_run)) * 0.69314718055994531f;
 }
 
 // Merge the per-split partials of every (b, i, h): lse = log sum_k e^{lse_k},
@@ -838,7 +939,7 @@ hipError_t launch_decode_attn(const AttnArgs& a, int rows, hipStream_t stream) {
   else if (a.dtype_bf16)
     hipLaunchKernelGGL(decode_attn_bf16_kernel<false>, dim3(nwg), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL(decode_attn_f32_kernel, dim3(nwg * kHeads), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(decode_attn_f32_kernel, dim3(nwg * (kHeads / kF32Heads)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

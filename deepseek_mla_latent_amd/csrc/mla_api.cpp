@@ -227,7 +227,7 @@ mla_status decode_attn_impl(const void* q_lat, const void* q_pe, const void* kv_
   st = table_bounds(p, &bounds);
   if (st != MLA_OK) return st;
   const SplitPlan plan = plan_splits(p, num_splits, cus);
-  const int64_t grid = tokens_of(p) * plan.splits * (p->dtype == MLA_BF16 ? 1 : mla::kHeads);
+  const int64_t grid = tokens_of(p) * plan.splits * (p->dtype == MLA_BF16 ? 1 : mla::kHeads / mla::kF32Heads);
   if (grid > 0x7fffffffLL) return MLA_ERR_SHAPE;
   const size_t need = fused ? fused_workspace_for(p, plan.splits) : workspace_for(p, plan.splits);
   const bool merge_in_proj = fused && merge_in_out_proj(p, plan.splits);
