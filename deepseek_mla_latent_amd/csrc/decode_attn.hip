@@ -685,7 +685,9 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
 //     area, read back as the weighted sum's operand;
 //   * weighted sum O^T(latent x head) += tile^T x P: wave w holds latent columns 128 w .. +127 of
 //     the 32 heads (four 32 x 32 blocks), lane half hf taking tokens (s & 7) + 16 (s >> 3) + 8 hf.
-// Row padding: 580 floats put the two lane halves of every read on disjoint banks.
+// Row padding: a 580-float row is 4 banks past a multiple of 64, so a 16-byte score-operand read
+// (16 lanes on 16 rows per pass) covers all 64 banks once, and in the weighted-sum and probability
+// reads the two lane halves, 8 rows apart, fall on disjoint halves of the banks.
 constexpr int kF32Tile = 32;             // tokens per tile
 constexpr int kF32Ld = kRow + 4;         // floats per staged tile row
 constexpr int kF32PLd = kF32Heads + 4;   // floats per probability row
