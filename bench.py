@@ -558,6 +558,12 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_probe_mib:  # one plain device copy of known size, first (counter calibration)
+        src = torch.empty(args.copy_probe_mib * 2 ** 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if args.workload in gen.PREFILL_WORKLOADS:
         return run_prefill(args, dev)
     if args.workload in PREPARE_WORKLOADS:
@@ -590,13 +596,6 @@ def main():
     costs = accounting.path_costs(x.seq_lens, w.q_len, dt, tree=parents, fused=fused)
     per_replica = sum(c.bytes for c in costs)
     R = args.replicas or max(2, math.ceil(2 * MALL_BYTES / per_replica) + 1)
-
-    if args.copy_probe_mib:
-        src = torch.empty(args.copy_probe_mib * 2 ** 20, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
 
     params = binding.make_params(batch=w.batch, q_len=w.q_len, max_seq_len=x.max_seq_len,
                                  max_pages_per_seq=x.block_table.shape[1], softmax_scale=w.softmax_scale,
