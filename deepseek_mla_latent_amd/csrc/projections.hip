@@ -574,6 +574,46 @@ __global__ __launch_bounds__(256) void out_proj_f32_kernel(const float* __restri
   __syncthreads();
 
   const int ntb = (tokens + 31) / 32;
+  if (ntb == 1) {
+    // One token block: two (value block) items for four waves, so each item is split over two
+    // waves by latent half (rows [256 kh, +256)); the halves' sums meet in LDS, added in order.
+    __shared__ f32x4 half_sums[2 * 4 * 64];  // [value block][element group][lane] of latent half 1
+    const int vb = wave & 1, kh = wave >> 1;
+    const int n = l32;
+    const bool ok = n < tokens;
+    const float* O = o_lat + ((size_t)(ok ? n : 0) * kHeads + h) * kDc;
+    f32x16 acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+    for (int m0 = 32 * kh; m0 < 32 * kh + 32; m0 += 16) {
+      f32x4 xb[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) xb[k] = *(const f32x4*)(O + 8 * (m0 + k) + 4 * hf);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) settle(xb[k]);
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int c = 8 * (m0 + k) + 4 * hf + j;
+          acc = mfma32x32x2f32(wl[c * 64 + 32 * vb + l32], xb[k][j], acc);
+        }
+    }
+    if (kh == 1) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        half_sums[(vb * 4 + g) * 64 + lane] = f32x4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+    }
+    __syncthreads();
+    if (kh == 0 && ok) {  // element e: value 32 vb + (e/4)*8 + 4 hf + e%4 of token n
+      float* dst = out + ((size_t)n * kHeads + h) * kDh + 64 * vh + 32 * vb + 4 * hf;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *(f32x4*)(dst + 8 * g) =
+            f32x4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]} + half_sums[(vb * 4 + g) * 64 + lane];
+    }
+    return;
+  }
   for (int combo = wave; combo < 2 * ntb; combo += 4) {
     const int vb = combo & 1, nb = combo >> 1;
     const int n = 32 * nb + l32;
