@@ -670,50 +670,56 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
   }
 }
 
-// fp32 path on the fp32 matrix cores (v_mfma_f32_32x32x2_f32): workgroup = (b, i, split, block of
-// 32 heads), 4 waves.  fp32 leaves no room for the bf16 kernel's layout (the query of 128 heads is
-// 288 KiB), so a workgroup takes 32 heads and the 128 heads of a key range are four workgroups,
-// each reading the range from L2 once.  Per 32-token tile (half a page, so one page id):
+// fp32 path on the fp32 matrix cores (v_mfma_f32_16x16x4_f32): workgroup = (b, i, split, block of
+// 16 heads), 4 waves.  fp32 leaves no room for the bf16 kernel's layout (the query of 128 heads is
+// 288 KiB), so the 128 heads of a key range are eight workgroups, each reading the range from L2,
+// which also spreads a range's matrix work over eight compute units.  Per 32-token tile (half a
+// page, so one page id):
 //   * the tile's rows are staged in LDS with a padded row of kF32Ld floats; the next tile's rows
 //     are loaded into registers during this tile's work;
-//   * scores D(token x head) = tile x [q_lat | q_pe]^T: wave w takes k in [144 w, 144 w + 144), lane
-//     half hf the k values 144 w + 72 hf + s at step s, so its tile operand is one 16-byte read per
-//     4 steps and its query operand sits in 72 registers for the whole range; the four waves'
-//     partial sums meet in LDS and every wave adds them in the same order;
-//   * the online softmax (base 2, scale folded in) runs redundantly in every wave, each lane on the
-//     16 tokens of its head the score layout gives it; the probabilities go to the wave's own LDS
-//     area, read back as the weighted sum's operand;
+//   * scores D(token x head), two 16-token blocks: wave w takes k in [144 w, 144 w + 144), lane
+//     group g = l / 16 the k values 144 w + 36 g + s at step s, so its tile operand is one 16-byte
+//     read per 4 steps and its query operand sits in 36 registers; the four waves' partial sums
+//     meet in LDS and every wave adds them in the same order;
+//   * the online softmax (base 2, scale folded in) runs redundantly in every wave, each lane on
+//     the 8 tokens of its head the score layout gives it; the probabilities go to the wave's own
+//     LDS area, read back as the weighted sum's operand;
 //   * weighted sum O^T(latent x head) += tile^T x P: wave w holds latent columns 128 w .. +127 of
-//     the 32 heads (four 32 x 32 blocks), lane half hf taking tokens (s & 7) + 16 (s >> 3) + 8 hf.
+//     the 16 heads (eight 16 x 16 blocks), lane group g taking tokens (s & 3) + 4 g + 16 (s >> 2).
 // Row padding: a 580-float row is 4 banks past a multiple of 64, so a 16-byte score-operand read
-// (16 lanes on 16 rows per pass) covers all 64 banks once, and in the weighted-sum and probability
-// reads the two lane halves, 8 rows apart, fall on disjoint halves of the banks.
+// (16 lanes on 16 rows per pass) covers all 64 banks once, and in the weighted-sum reads the four
+// lane groups, 4 rows apart, fall on four disjoint 16-bank windows.
 constexpr int kF32Tile = 32;             // tokens per tile
 constexpr int kF32Ld = kRow + 4;         // floats per staged tile row
 constexpr int kF32PLd = kF32Heads + 4;   // floats per probability row
 constexpr int kF32Loads = kF32Tile * kRow / 4 / 256;  // 16-byte loads per thread per tile (18)
 static_assert(kF32Tile * kRow % (4 * 256) == 0, "whole 16-byte loads per thread");
+static_assert(kF32Heads == 16, "one 16 x 16 MFMA column block of heads");
+
+__device__ __forceinline__ f32x4 mfma16x16x4f32(float a, float b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
 
 __global__ __launch_bounds__(256, 1) void decode_attn_f32_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float tile[kF32Tile * kF32Ld];
-  __shared__ __attribute__((aligned(16))) float spart[4 * 16 * 64];          // [wave][element][lane]
+  __shared__ __attribute__((aligned(16))) float spart[4 * 8 * 64];          // [wave][element][lane]
   __shared__ __attribute__((aligned(16))) float pw[4 * kF32Tile * kF32PLd];  // [wave][token][head]
   constexpr int kBlocks = kHeads / kF32Heads;
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   const int hb = id % kBlocks;
   const WorkItem w = make_work(a, id / kBlocks);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63, l32 = lane & 31, hf = lane >> 5;
-  const int head = kF32Heads * hb + l32;  // this lane's head (the MFMA column)
+  const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
+  const int head = kF32Heads * hb + l16;  // this lane's head (the MFMA column)
   const float* pool = (const float*)a.pool;
 
   const int ntok = w.tok_end - w.tok_begin;
-  if (ntok <= 0) {  // empty key range: o = 0, lse = -inf; thread t writes 64 columns of head t / 8
-    const int hh = kF32Heads * hb + (threadIdx.x >> 3);
-    float* row = (float*)a.o_out + (w.out_row + hh) * kDc + 64 * (threadIdx.x & 7);
+  if (ntok <= 0) {  // empty key range: o = 0, lse = -inf; thread t writes 32 columns of head t / 16
+    const int hh = kF32Heads * hb + (threadIdx.x >> 4);
+    float* row = (float*)a.o_out + (w.out_row + hh) * kDc + 32 * (threadIdx.x & 15);
 #pragma unroll
-    for (int c = 0; c < 64; c += 4) *(f32x4*)(row + c) = f32x4{0.f, 0.f, 0.f, 0.f};
-    if ((threadIdx.x & 7) == 0 && a.lse_out) a.lse_out[w.out_row + hh] = -INFINITY;
+    for (int c = 0; c < 32; c += 4) *(f32x4*)(row + c) = f32x4{0.f, 0.f, 0.f, 0.f};
+    if ((threadIdx.x & 15) == 0 && a.lse_out) a.lse_out[w.out_row + hh] = -INFINITY;
     return;
   }
   const int ntiles = (ntok + kF32Tile - 1) / kF32Tile;
@@ -745,13 +751,13 @@ __global__ __launch_bounds__(256, 1) void decode_attn_f32_kernel(AttnArgs a) {
   };
   fetch(0);
 
-  // this lane's query operand: [q_lat | q_pe] of its head at k = 144 wave + 72 hf + s, s < 72
-  float q[72];
+  // this lane's query operand: [q_lat | q_pe] of its head at k = 144 wave + 36 g + s, s < 36
+  float q[36];
   {
     const size_t qrow = ((size_t)w.b * a.S + w.i) * kHeads + head;
-    const int k0 = 144 * wave + 72 * hf;
+    const int k0 = 144 * wave + 36 * g;
 #pragma unroll
-    for (int s4 = 0; s4 < 18; ++s4) {
+    for (int s4 = 0; s4 < 9; ++s4) {
       const int k = k0 + 4 * s4;  // four values on one side of the q_lat / q_pe boundary (512 = 4 x 128)
       const f32x4 v = k < kDc ? *(const f32x4*)((const float*)a.q_lat + qrow * kDc + k)
                               : *(const f32x4*)((const float*)a.q_pe + qrow * kDr + (k - kDc));
@@ -761,11 +767,9 @@ __global__ __launch_bounds__(256, 1) void decode_attn_f32_kernel(AttnArgs a) {
   }
 
   float m_run = -INFINITY, l_run = 0.f;  // of this lane's head, in log2 units
-  f32x16 o[4];                           // block b: latent 128 wave + 32 b + 8 (e/4) + 4 hf + e%4
+  f32x4 o[8];                            // block b: latent 128 wave + 16 b + 4 g + e, head l16
 #pragma unroll
-  for (int b = 0; b < 4; ++b)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) o[b][e] = 0.f;
+  for (int b = 0; b < 8; ++b) o[b] = f32x4{0.f, 0.f, 0.f, 0.f};
   MLA_LDS float* const my_p = (MLA_LDS float*)(pw + wave * kF32Tile * kF32PLd);
 
   for (int t = 0; t < ntiles; ++t) {
@@ -775,71 +779,70 @@ __global__ __launch_bounds__(256, 1) void decode_attn_f32_kernel(AttnArgs a) {
     __syncthreads();  // the tile is in LDS
     if (t + 1 < ntiles) fetch(t + 1);
 
-    // scores over this wave's k range
-    f32x16 sc;
+    // scores over this wave's k range, token blocks tb = 0, 1
 #pragma unroll
-    for (int e = 0; e < 16; ++e) sc[e] = 0.f;
-    const MLA_LDS float* arow = (const MLA_LDS float*)(tile + l32 * kF32Ld + 144 * wave + 72 * hf);
+    for (int tb = 0; tb < 2; ++tb) {
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+      const MLA_LDS float* arow = (const MLA_LDS float*)(tile + (16 * tb + l16) * kF32Ld + 144 * wave + 36 * g);
 #pragma unroll
-    for (int s4 = 0; s4 < 18; ++s4) {
-      const f32x4 av = *(const MLA_LDS f32x4*)(arow + 4 * s4);
+      for (int s4 = 0; s4 < 9; ++s4) {
+        const f32x4 av = *(const MLA_LDS f32x4*)(arow + 4 * s4);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sc = mfma32x32x2f32(av[j], q[4 * s4 + j], sc);
+        for (int j = 0; j < 4; ++j) sc = mfma16x16x4f32(av[j], q[4 * s4 + j], sc);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) spart[(wave * 8 + 4 * tb + e) * 64 + lane] = sc[e];
     }
-#pragma unroll
-    for (int e = 0; e < 16; ++e) spart[(wave * 16 + e) * 64 + lane] = sc[e];
     __syncthreads();  // every wave's partial scores
-    float z[16];
+    float z[8];
     float mt = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float v = (spart[e * 64 + lane] + spart[(16 + e) * 64 + lane]) +
-                      (spart[(32 + e) * 64 + lane] + spart[(48 + e) * 64 + lane]);
-      const int i = 8 * (e >> 2) + 4 * hf + (e & 3);  // token of element e within the tile
-      const int jn = t0 + i - w.tail;                  // draft-tree node index of that key
+    for (int e8 = 0; e8 < 8; ++e8) {
+      const float v = (spart[e8 * 64 + lane] + spart[(8 + e8) * 64 + lane]) +
+                      (spart[(16 + e8) * 64 + lane] + spart[(24 + e8) * 64 + lane]);
+      const int i = 16 * (e8 >> 2) + 4 * g + (e8 & 3);  // token of element e8 within the tile
+      const int jn = t0 + i - w.tail;                    // draft-tree node index of that key
       const bool vis = i < cnt && (!a.tree_parents || jn < 0 || (jn < 64 && ((tmask >> jn) & 1ull)));
-      z[e] = vis ? v * a.scale_log2 : -INFINITY;
-      mt = fmaxf(mt, z[e]);
+      z[e8] = vis ? v * a.scale_log2 : -INFINITY;
+      mt = fmaxf(mt, z[e8]);
     }
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
     mt = fmaxf(mt, __shfl_xor(mt, 32));
     const float m_new = fmaxf(m_run, mt);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;  // every key so far masked
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     float ls = 0.f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float pe = __builtin_amdgcn_exp2f(z[e] - m_use);  // masked keys: exp2(-inf) = 0
+    for (int e8 = 0; e8 < 8; ++e8) {
+      const float pe = __builtin_amdgcn_exp2f(z[e8] - m_use);  // masked keys: exp2(-inf) = 0
       ls += pe;
-      my_p[(8 * (e >> 2) + 4 * hf + (e & 3)) * kF32PLd + l32] = pe;
+      my_p[(16 * (e8 >> 2) + 4 * g + (e8 & 3)) * kF32PLd + l16] = pe;
     }
+    ls += __shfl_xor(ls, 16);
     ls += __shfl_xor(ls, 32);
     l_run = l_run * alpha + ls;
     m_run = m_new;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) o[b] *= alpha;
+    for (int b = 0; b < 8; ++b) o[b] *= alpha;
 
     // weighted sum: this wave's latent columns, the tile as value
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      const int k = (s & 7) + 16 * (s >> 3) + 8 * hf;
-      const float pb = my_p[k * kF32PLd + l32];
-      const MLA_LDS float* crow = (const MLA_LDS float*)(tile + k * kF32Ld + 128 * wave + l32);
+    for (int s = 0; s < 8; ++s) {
+      const int k = (s & 3) + 4 * g + 16 * (s >> 2);
+      const float pb = my_p[k * kF32PLd + l16];
+      const MLA_LDS float* crow = (const MLA_LDS float*)(tile + k * kF32Ld + 128 * wave + l16);
 #pragma unroll
-      for (int b = 0; b < 4; ++b) o[b] = mfma32x32x2f32(crow[32 * b], pb, o[b]);
+      for (int b = 0; b < 8; ++b) o[b] = mfma16x16x4f32(crow[16 * b], pb, o[b]);
     }
     __syncthreads();  // the tile, the partial scores and the probabilities are free again
   }
 
   const bool empty = l_run == 0.f;
   const float inv = empty ? 0.f : 1.0f / l_run;
-  float* orow = (float*)a.o_out + (w.out_row + head) * kDc + 128 * wave + 4 * hf;
+  float* orow = (float*)a.o_out + (w.out_row + head) * kDc + 128 * wave + 4 * g;
 #pragma unroll
-  for (int b = 0; b < 4; ++b)
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-      *(f32x4*)(orow + 32 * b + 8 * g) =
-          f32x4{o[b][4 * g] * inv, o[b][4 * g + 1] * inv, o[b][4 * g + 2] * inv, o[b][4 * g + 3] * inv};
-  if (wave == 0 && hf == 0 && a.lse_out)
+  for (int b = 0; b < 8; ++b) *(f32x4*)(orow + 16 * b) = o[b] * inv;
+  if (wave == 0 && g == 0 && a.lse_out)
     a.lse_out[w.out_row + head] = empty ? -INFINITY : (m_run + __log2f(l_run)) * 0.69314718055994531f;
 }
 

@@ -15,7 +15,7 @@ constexpr int kRow = 576;     // cached row: [c_KV | k_pe]
 constexpr int kDh = 128;      // no-RoPE head dim = value head dim
 constexpr int kPage = 64;     // tokens per cache page
 constexpr int kMaxSplitPages = 512;  // pages one attention workgroup may walk (32768 tokens)
-constexpr int kF32Heads = 32;  // heads per workgroup of the fp32 attention kernel
+constexpr int kF32Heads = 16;  // heads per workgroup of the fp32 attention kernel
 
 // Preconditions on the page table that only the device can check.  In the bounds-checked build
 // (MLA_DEBUG_BOUNDS) every kernel that walks the table tests each seq_lens entry it uses against
