@@ -15,6 +15,9 @@
 
 namespace mla {
 
+// Up to this many tokens the fp32 projections run as VALU GEMVs instead of 32-token MFMA blocks.
+constexpr int kGemvTokens = 4;
+
 // Forces the values to be complete here: every load producing them is issued before this point,
 // and the compiler cannot trickle them out one MFMA at a time.
 template <typename T>
@@ -61,6 +64,47 @@ __global__ __launch_bounds__(256) void absorb_q_f32_kernel(const void* __restric
       for (int g = 0; g < 4; ++g)
         *(f32x4*)(dst + 8 * g) = f32x4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
     }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// absorb, fp32, at most kGemvTokens tokens: one GEMV per (token, head) on the VALU.  A 32-token
+// MFMA block would be almost all padding here (31/32 of the fp32 matrix work at one token), while
+// the weight stream is the same.  Grid (4 latent blocks of 128, 128 heads), 4 waves; wave w owns
+// rows c in [128 bx + 32 w, +32).  Load k brings rows c0 + 2k (lanes 0-31) and c0 + 2k + 1 (lanes
+// 32-63), 1 KiB contiguous, and is kept in registers for every token; lane l32 holds d in
+// [4 l32, +4).  A token's 16 per-lane partial dot products are summed over the 32 lanes of each
+// half by recursive halving: at lane distance 16, 8, 4, 2 each lane keeps half of its rows and adds
+// its partner's partial sums of them, and distance 1 adds the last pair.  Lane l32 then holds row
+// c0 + 2 (l32 / 2) + hf.
+__global__ __launch_bounds__(256) void absorb_q_f32_gemv_kernel(const float* __restrict__ q_nope,
+                                                                const float* __restrict__ w_uk,
+                                                                float* __restrict__ q_lat, int tokens) {
+  const int h = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l32 = lane & 31, hf = lane >> 5;
+  const int c0 = 128 * blockIdx.x + 32 * wave;
+  const f32x4* W = (const f32x4*)(w_uk + ((size_t)h * kDc + c0 + hf) * kDh + 4 * l32);
+  f32x4 wr[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) wr[k] = W[k * (2 * kDh / 4)];  // row c0 + 2k + hf
+  for (int n = 0; n < tokens; ++n) {
+    const f32x4 qv = *(const f32x4*)(q_nope + ((size_t)n * kHeads + h) * kDh + 4 * l32);
+    float p[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      p[k] = __builtin_fmaf(wr[k][3], qv[3], __builtin_fmaf(wr[k][2], qv[2], __builtin_fmaf(wr[k][1], qv[1], wr[k][0] * qv[0])));
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) {  // partner at lane distance 2m; rows j (lower lane) or j + m
+      const bool upper = (l32 & (2 * m)) != 0;
+#pragma unroll
+      for (int j = 0; j < m; ++j) {
+        const float give = upper ? p[j] : p[j + m];
+        const float keep = upper ? p[j + m] : p[j];
+        p[j] = keep + __shfl_xor(give, 2 * m);
+      }
+    }
+    const float r = p[0] + __shfl_xor(p[0], 1);
+    if ((l32 & 1) == 0) q_lat[((size_t)n * kHeads + h) * kDc + c0 + l32 + hf] = r;
   }
 }
 
@@ -546,6 +590,53 @@ __global__ __launch_bounds__(512, 1) void merge_out_proj_kernel(const uint16_t* 
   }
 }
 
+// out-proj, fp32, at most kGemvTokens tokens: one GEMV per (token, head) on the VALU (a 32-token
+// MFMA block would be almost all padding).  Grid (2 value halves of 64, 128 heads), 4 waves; wave
+// w owns latent rows [128 w, +128), and lane group r4 = lane / 16 the 32 rows 128 w + 32 r4 + i,
+// whose 64 values of this half (256 B each, lane l16 holding values 4 l16 .. +3) stay in registers
+// for every token.  Per token a lane adds up its 32 rows weighted by o_lat (read once per lane
+// group); the four lane groups are summed by shuffles and the four waves through LDS, in a fixed
+// order.
+__global__ __launch_bounds__(256) void out_proj_f32_gemv_kernel(const float* __restrict__ o_lat,
+                                                                const float* __restrict__ w_uv,
+                                                                float* __restrict__ out, int tokens) {
+  __shared__ f32x4 part[4 * kGemvTokens * 16];  // [wave][token][l16]
+  const int h = blockIdx.y, vh = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, r4 = lane >> 4;
+  const int c0 = 128 * wave + 32 * r4;
+  const f32x4* W = (const f32x4*)(w_uv + ((size_t)h * kDc + c0) * kDh + 64 * vh + 4 * l16);
+  f32x4 wr[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) wr[i] = W[i * (kDh / 4)];  // row c0 + i
+  for (int n = 0; n < tokens; ++n) {
+    const f32x4* O = (const f32x4*)(o_lat + ((size_t)n * kHeads + h) * kDc + c0);
+    f32x4 ov[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ov[i] = O[i];
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float o = ov[i >> 2][i & 3];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(o, wr[i][e], acc[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[e] += __shfl_xor(acc[e], 16);
+      acc[e] += __shfl_xor(acc[e], 32);
+    }
+    if (r4 == 0) part[(wave * kGemvTokens + n) * 16 + l16] = acc;
+  }
+  __syncthreads();
+  const int n = lane >> 4;  // wave 0: lane 16 n + l16 sums token n's values 4 l16 .. +3
+  if (wave == 0 && n < tokens) {
+    f32x4 v = part[n * 16 + l16];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) v += part[(w * kGemvTokens + n) * 16 + l16];
+    *(f32x4*)(out + ((size_t)n * kHeads + h) * kDh + 64 * vh + 4 * l16) = v;
+  }
+}
+
 // out-proj, fp32: grid (2 value halves of 64, 128 heads), 4 waves.  The workgroup stages
 // W_UV[h][:, 64 bx .. +64) in LDS, then computes D(v x tokens) = W_UV^T x o_lat^T with the fp32
 // MFMA for every (32-value block, 32-token block) pair, round-robin over the waves.
@@ -653,6 +744,9 @@ hipError_t launch_absorb_q(const void* q_nope, const void* w_uk, void* q_lat, in
   if (bf16)
     hipLaunchKernelGGL(absorb_q_bf16_kernel, grid, dim3(256), 0, stream, (const uint16_t*)q_nope,
                        (const uint16_t*)w_uk, (uint16_t*)q_lat, tokens);
+  else if (tokens <= kGemvTokens)
+    hipLaunchKernelGGL(absorb_q_f32_gemv_kernel, grid, dim3(256), 0, stream, (const float*)q_nope,
+                       (const float*)w_uk, (float*)q_lat, tokens);
   else
     hipLaunchKernelGGL(absorb_q_f32_kernel, grid, dim3(256), 0, stream, q_nope, w_uk, q_lat, tokens);
   return hipGetLastError();
@@ -687,6 +781,9 @@ hipError_t launch_out_proj(const float* o_lat, const void* w_uv, void* out, int 
   if (bf16)
     hipLaunchKernelGGL(out_proj_bf16_kernel, dim3(2 * kHeads), dim3(256), 0, stream, o_lat,
                        (const uint16_t*)w_uv, (uint16_t*)out, tokens);
+  else if (tokens <= kGemvTokens)
+    hipLaunchKernelGGL(out_proj_f32_gemv_kernel, dim3(2, kHeads), dim3(256), 0, stream, o_lat, (const float*)w_uv,
+                       (float*)out, tokens);
   else
     hipLaunchKernelGGL(out_proj_f32_kernel, dim3(2, kHeads), dim3(256), 0, stream, o_lat, (const float*)w_uv,
                        (float*)out, tokens);

@@ -31,7 +31,7 @@ def _torch():
 
 # ------------------------------------------------------------------------------------ projections
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("tokens", [1, 33, 128])
+@pytest.mark.parametrize("tokens", [1, 2, 4, 5, 33, 128])
 def test_absorb_q(dtype, tokens):
     say("absorb_q", dtype, tokens)
     torch = _torch()
@@ -49,7 +49,7 @@ def test_absorb_q(dtype, tokens):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("tokens", [1, 33, 128])
+@pytest.mark.parametrize("tokens", [1, 2, 4, 5, 33, 128])
 def test_out_proj(dtype, tokens):
     say("out_proj", dtype, tokens)
     torch = _torch()
