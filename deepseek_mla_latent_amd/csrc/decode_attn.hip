@@ -180,34 +180,302 @@ __device__ __forceinline__ uint64_t tree_walk(int par, int S, int i) {
   return m;
 }
 
+// ---- key ranges.  With num_splits = k > 1 the grid has G = rows * k workgroups, each one key range
+// of one row (row r = b S + i).  Up to kPlanRows rows the ranges follow the rows' lengths, so that
+// a ragged batch does not leave its longest rows' workgroups walking while the others idle:
+//   P_r  = pages of the keys row r sees, capped at k * pages_per_split (all the fixed ranges cover);
+//   C    = the smallest page count with sum_r max(1, ceil(P_r / C)) <= G (C <= pages_per_split, which
+//          always fits);
+//   row r gets s_r = max(1, ceil(P_r / C)) ranges of C pages (the last one shorter, an empty row one
+//   empty range), numbered row after row: range j of row r is workgroup and partial slot first_r + j
+//   (first_r = s_0 + .. + s_{r-1}); workgroups past the last range have nothing to do.
+// Equal lengths give C = pages_per_split and s_r = k, the fixed ranges.  Above kPlanRows rows every
+// row gets the k fixed ranges of pages_per_split pages.  Every wave computes the plan itself from
+// seq_lens (wave-uniform results, no barrier): C by bisection between the bounds
+// ceil(T / G) <= C <= ceil(T / (G - rows)) (T = sum_r P_r; max(1, ceil(x)) <= x + 1 makes the upper
+// one fit), the slots by a prefix sum over the rows.
+
+// Inclusive prefix sum over each row of 16 lanes (DPP row shifts).
+__device__ __forceinline__ int row16_scan(int v, int lane) {
+  int t = __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  if ((lane & 15) >= 1) v += t;
+  t = __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  if ((lane & 15) >= 2) v += t;
+  t = __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  if ((lane & 15) >= 4) v += t;
+  t = __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  if ((lane & 15) >= 8) v += t;
+  return v;
+}
+// Sum over the wave (every lane gets it), from the row scans' last lanes.
+__device__ __forceinline__ int wave_total(int scanned) {
+  return (__builtin_amdgcn_readlane(scanned, 15) + __builtin_amdgcn_readlane(scanned, 31)) +
+         (__builtin_amdgcn_readlane(scanned, 47) + __builtin_amdgcn_readlane(scanned, 63));
+}
+// ceil(p / c) for 0 <= p < 2^22, c >= 1 (rc = 1 / c, within an ulp): the quotient from the
+// reciprocal is off by at most one, and one correction each way makes it exact.
+__device__ __forceinline__ int ceil_div_small(int p, int c, float rc) {
+  int q = (int)((float)p * rc);
+  int r = p - q * c;
+  q += (r >= c ? 1 : 0) - (r < 0 ? 1 : 0);
+  r = p - q * c;
+  return q + (r > 0 ? 1 : 0);
+}
+
+// floor(p / c) for 0 <= p < 2^22, c >= 1 (rc = 1 / c, within an ulp), corrected like ceil_div_small.
+__device__ __forceinline__ int floor_div_small(int p, int c, float rc) {
+  int q = (int)((float)p * rc);
+  const int r = p - q * c;
+  return q + (r >= c ? 1 : 0) - (r < 0 ? 1 : 0);
+}
+
+// Keys row r = b S + i sees (the decode rule: causal without a tree, else all L).
+__device__ __forceinline__ int visible_keys(const AttnArgs& a, int L, int i) {
+  int n = a.causal && !a.tree_parents ? L - a.S + i + 1 : L;
+  return n < 0 ? 0 : (n > L ? L : n);
+}
+
+struct RangePlan {
+  int r, j;          // row and key range of this workgroup
+  int first, count;  // the row's first partial slot and number of ranges
+  int chunk;         // pages per range
+  int L;             // cached tokens of the row's sequence (-1: not loaded yet)
+  bool live;         // false: past the last range
+  bool fixed;        // every row has k ranges (slot r k + j), as without the plan
+};
+
+// The common case, every row seeing the same number of keys, is recognised from scalar loads of
+// seq_lens (at most kUniformScan sequences, each row seeing its whole sequence): one round trip,
+// like the single length a workgroup loads without the plan, and a closed form after it.  They read
+// seq_lens through the constant address space (the kernel never writes it, and each launch starts
+// its scalar cache afresh), which keeps them scalar wherever they stand.
+constexpr int kUniformScan = 32;
+typedef __attribute__((address_space(4))) const int32_t const_i32;
+struct LenScan {
+  int v[kUniformScan];
+  bool on;
+};
+__device__ __forceinline__ LenScan scan_lengths(const AttnArgs& a) {
+  LenScan ls;
+  ls.on = a.num_splits > 1 && a.B * a.S <= kPlanRows && a.B <= kUniformScan &&
+          !(a.S > 1 && a.causal && !a.tree_parents);
+  if (ls.on) {
+    const_i32* sl = (const_i32*)a.seq_lens;
+    if (a.B == kUniformScan) {  // all in bounds: contiguous, so merged into wide scalar loads
+#pragma unroll
+      for (int q = 0; q < kUniformScan; ++q) ls.v[q] = sl[q];
+    } else if (a.B <= 8) {  // entries past B repeat sequence 0
+#pragma unroll
+      for (int q = 0; q < kUniformScan; ++q) ls.v[q] = sl[q < 8 && q < a.B ? q : 0];
+    } else {
+#pragma unroll
+      for (int q = 0; q < kUniformScan; ++q) ls.v[q] = sl[q < a.B ? q : 0];
+    }
+  }
+  return ls;
+}
+// The length every sequence has, or -1 (lengths differ, or no scan).
+__device__ __forceinline__ int uniform_length(const AttnArgs& a, LenScan& ls) {
+  if (!ls.on) return -1;
+  int diff = 0;
+#pragma unroll
+  for (int q = 1; q < kUniformScan; ++q) diff |= ls.v[q] ^ ls.v[0];
+  return diff == 0 ? checked_len(a.bounds, ls.v[0]) : -1;
+}
+
+// L0: the common length of all sequences when every row sees all of its keys, else -1.
+__device__ RangePlan plan_ranges(const AttnArgs& a, int g, int L0) {
+  const int rows = a.B * a.S, k = a.num_splits, pps = a.pages_per_split;
+  RangePlan p;
+  if (rows > kPlanRows) {
+    p.r = g / k;
+    p.j = g % k;
+    p.first = p.r * k;
+    p.count = k;
+    p.chunk = pps;
+    p.L = -1;
+    p.live = true;
+    p.fixed = true;
+    return p;
+  }
+  const int lane = threadIdx.x & 63;
+  const int cap = k * pps;
+  const int G = rows * k;
+  if (L0 >= 0) {  // every row sees all L0 keys: the closed form below, from P = pages of L0
+    const int pg = (L0 + kPage - 1) / kPage;
+    const int P0 = pg < cap ? pg : cap;
+    int C = (P0 + k - 1) / k;
+    C = C > 1 ? C : 1;
+    int sr = (P0 + C - 1) / C;
+    sr = sr > 1 ? sr : 1;
+    p.r = sr == k ? g / k : g / sr;
+    p.j = g - p.r * sr;
+    p.first = p.r * sr;
+    p.count = sr;
+    p.chunk = C;
+    p.live = p.r < rows;
+    p.fixed = sr == k;
+    p.L = L0;
+    return p;
+  }
+  int P[kPlanRows / 64];   // pages of keys row lane + 64 m sees, capped (-1: no such row)
+  int Ls[kPlanRows / 64];  // its sequence's cached tokens
+  int tp = 0;
+#pragma unroll
+  for (int m = 0; m < kPlanRows / 64; ++m) {
+    const int r = lane + 64 * m;
+    P[m] = -1;
+    Ls[m] = 0;
+    if (r < rows) {
+      const int b = a.S == 1 ? r : r / a.S;
+      Ls[m] = checked_len(a.bounds, a.seq_lens[b]);
+      const int n = visible_keys(a, Ls[m], r - b * a.S);
+      const int pg = (n + kPage - 1) / kPage;
+      P[m] = pg < cap ? pg : cap;
+      tp += P[m];
+    }
+  }
+  // All rows with the same page count P (the common case): C = max(1, ceil(P / k)) is the smallest
+  // with ceil(P / C) <= k, and every row gets ceil(P / C) ranges.
+  const int P0 = __builtin_amdgcn_readfirstlane(P[0]);
+  bool same = true;
+#pragma unroll
+  for (int m = 0; m < kPlanRows / 64; ++m)
+    if (64 * m < rows) same = same && __ballot(P[m] >= 0 && P[m] != P0) == 0;
+  if (__builtin_expect(same, 1)) {
+    int C = ceil_div_small(P0, k, __builtin_amdgcn_rcpf((float)k));
+    C = C > 1 ? C : 1;
+    int sr = ceil_div_small(P0, C, __builtin_amdgcn_rcpf((float)C));
+    sr = sr > 1 ? sr : 1;
+    p.r = sr == k ? g / k : floor_div_small(g, sr, __builtin_amdgcn_rcpf((float)sr));
+    p.j = g - p.r * sr;
+    p.first = p.r * sr;
+    p.count = sr;
+    p.chunk = C;
+    p.live = p.r < rows;
+    p.fixed = sr == k;
+    const int rm = p.r < rows ? p.r : 0;
+    int Lr = Ls[0];
+#pragma unroll
+    for (int m = 1; m < kPlanRows / 64; ++m)
+      if ((rm >> 6) == m) Lr = Ls[m];
+    p.L = __builtin_amdgcn_readlane(Lr, rm & 63);
+    return p;
+  }
+  const int T = wave_total(row16_scan(tp, lane));
+  auto ranges = [&](int c) {  // sum over rows of max(1, ceil(P_r / c))
+    const float rc = __builtin_amdgcn_rcpf((float)c);
+    int v = 0;
+#pragma unroll
+    for (int m = 0; m < kPlanRows / 64; ++m)
+      if (P[m] >= 0) {
+        const int q = ceil_div_small(P[m], c, rc);
+        v += q > 1 ? q : 1;
+      }
+    return wave_total(row16_scan(v, lane));
+  };
+  int lo = (T + G - 1) / G, hi = (T + (G - rows) - 1) / (G - rows);
+  lo = lo > 1 ? lo : 1;
+  hi = hi < pps ? hi : pps;
+  hi = hi > lo ? hi : lo;
+  while (lo < hi) {  // wave-uniform bisection
+    const int mid = (lo + hi) >> 1;
+    if (ranges(mid) <= G)
+      hi = mid;
+    else
+      lo = mid + 1;
+  }
+  const int C = lo;
+  const float rc = __builtin_amdgcn_rcpf((float)C);
+  p.live = false;
+  p.r = p.j = p.first = p.count = p.L = 0;
+  p.chunk = C;
+  p.fixed = true;
+  int base = 0;  // slots of the rows before this group of 64
+#pragma unroll
+  for (int m = 0; m < kPlanRows / 64; ++m) {
+    if (64 * m >= rows) break;
+    int sr = 0;
+    if (P[m] >= 0) {
+      sr = ceil_div_small(P[m], C, rc);
+      sr = sr > 1 ? sr : 1;
+    }
+    const int sc = row16_scan(sr, lane);
+    const int r15 = __builtin_amdgcn_readlane(sc, 15), r31 = __builtin_amdgcn_readlane(sc, 31),
+              r47 = __builtin_amdgcn_readlane(sc, 47), r63 = __builtin_amdgcn_readlane(sc, 63);
+    const int q16 = lane >> 4;
+    const int before = (q16 >= 1 ? r15 : 0) + (q16 >= 2 ? r31 : 0) + (q16 >= 3 ? r47 : 0);
+    const int first = base + before + sc - sr;
+    p.fixed = p.fixed && __ballot(P[m] >= 0 && sr != k) == 0;
+    const uint64_t hit = __ballot(sr > 0 && g >= first && g < first + sr);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      p.r = 64 * m + l;
+      p.first = __builtin_amdgcn_readlane(first, l);
+      p.count = __builtin_amdgcn_readlane(sr, l);
+      p.L = __builtin_amdgcn_readlane(Ls[m], l);
+      p.j = g - p.first;
+      p.live = true;
+    }
+    base += (r15 + r31) + (r47 + r63);
+  }
+  return p;
+}
+
 // Token range and output slots of one workgroup; shared by both dtypes.
 struct WorkItem {
   int b, i, split;
   int tok_begin, tok_end;  // [tok_begin, tok_end) of sequence b, page aligned at tok_begin
   int tail;                // L - S: position of the first new token (node 0 of a draft tree)
   size_t out_row;          // index of (head 0) in the o/lse output rows
+  int plan_first, plan_count;  // the row's partial slots (num_splits > 1)
+  bool live;               // false: a workgroup past the last key range
+  bool plan_fixed;         // every row's slots are r * num_splits + j (num_splits > 1)
 };
 
-__device__ __forceinline__ WorkItem make_work(const AttnArgs& a, int id) {
+// L0: as for plan_ranges.
+__device__ __forceinline__ WorkItem make_work(const AttnArgs& a, int id, int L0) {
   WorkItem w;
-  w.i = id % a.S;
-  const int rest = id / a.S;
-  w.split = rest % a.num_splits;
-  w.b = rest / a.num_splits;
-  const int L = checked_len(a.bounds, a.seq_lens[w.b]);
-  int n = a.causal && !a.tree_parents ? L - a.S + w.i + 1 : L;
-  n = n < 0 ? 0 : (n > L ? L : n);
-  const int p_begin = w.split * a.pages_per_split;
-  const int pages_L = (L + kPage - 1) / kPage;
-  int p_end = p_begin + a.pages_per_split;
-  p_end = p_end < pages_L ? p_end : pages_L;
-  w.tok_begin = p_begin * kPage;
+  int chunk = a.pages_per_split, r, L = -1;
+  w.split = 0;
+  w.plan_first = w.plan_count = 0;
+  w.live = true;
+  w.plan_fixed = true;
+  if (a.num_splits > 1) {
+    const RangePlan p = plan_ranges(a, id, L0);
+    r = p.r;
+    w.split = p.j;
+    w.plan_first = p.first;
+    w.plan_count = p.count;
+    w.live = p.live;
+    w.plan_fixed = p.fixed;
+    chunk = p.chunk;
+    L = p.L;
+  } else {
+    r = id;
+  }
+  w.i = r % a.S;
+  w.b = r / a.S;
+  if (L < 0) L = checked_len(a.bounds, a.seq_lens[w.b]);
+  const int n = visible_keys(a, L, w.i);
+  w.tok_begin = w.split * chunk * kPage;
   w.tail = L - a.S;
-  const int e = p_end * kPage;
+  const int e = (w.split + 1) * chunk * kPage;
   w.tok_end = e < n ? e : n;
-  const size_t bi = (size_t)w.b * a.S + w.i;
-  w.out_row = a.final_out ? bi * kHeads : (bi * a.num_splits + w.split) * kHeads;
+  w.out_row = a.final_out ? (size_t)r * kHeads : (size_t)(w.plan_first + w.split) * kHeads;
   return w;
+}
+
+// With num_splits > 1 the first range of every row records the row's slots for the merges (word
+// 4 + 2 r: first slot, 4 + 2 r + 1: count), and that of row 0 whether every row has the fixed
+// slots r * num_splits + j (word 0: 1 if so), so that the merges need not read the rows' entries.
+__device__ __forceinline__ void record_row_plan(const AttnArgs& a, const WorkItem& w) {
+  if (a.row_plan && w.live && w.split == 0 && threadIdx.x == 0) {
+    const int r = w.b * a.S + w.i;
+    if (r == 0) a.row_plan[0] = w.plan_fixed ? 1 : 0;
+    a.row_plan[4 + 2 * r] = w.plan_first;
+    a.row_plan[4 + 2 * r + 1] = w.plan_count;
+  }
 }
 
 template <bool kTree>
@@ -222,10 +490,15 @@ __global__ __launch_bounds__(256, 1) void decode_attn_bf16_kernel(AttnArgs a) {
   MLA_LDS int* const lds_tree = (MLA_LDS int*)(smem + kOffTree);
 
   const int id = xcd_remap(blockIdx.x, gridDim.x);
-  const WorkItem w = make_work(a, id);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int l32 = lane & 31, hf = lane >> 5;
+
+  // The rows' lengths for the key-range plan (scalar loads, before anything else).
+  LenScan lens = scan_lengths(a);
+  const WorkItem w = make_work(a, id, uniform_length(a, lens));
+  if (!w.live) return;  // past the last key range (uniform over the workgroup)
+  record_row_plan(a, w);
   // kTree: node `lane`'s parent, loaded here and walked once the query prologue has waited for its
   // loads
   const int tpar = kTree ? tree_parent_of_lane(a.tree_parents, w.b, a.S, lane) : -1;
@@ -707,11 +980,35 @@ __global__ __launch_bounds__(256, 1) void decode_attn_f32_kernel(AttnArgs a) {
   constexpr int kBlocks = kHeads / kF32Heads;
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   const int hb = id % kBlocks;
-  const WorkItem w = make_work(a, id / kBlocks);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, l16 = lane & 15, g = lane >> 4;
   const int head = kF32Heads * hb + l16;  // this lane's head (the MFMA column)
   const float* pool = (const float*)a.pool;
+
+  // this lane's query operand: [q_lat | q_pe] of its head at k = 144 wave + 36 g + s, s < 36; loaded
+  // for the row of the fixed layout while the key range is worked out, and again if the plan moves
+  // the row (a ragged batch)
+  float q[36];
+  auto load_q = [&](int row) {
+    const size_t qrow = (size_t)row * kHeads + head;
+    const int k0 = 144 * wave + 36 * g;
+#pragma unroll
+    for (int s4 = 0; s4 < 9; ++s4) {
+      const int k = k0 + 4 * s4;  // four values on one side of the q_lat / q_pe boundary (512 = 4 x 128)
+      const f32x4 v = k < kDc ? *(const f32x4*)((const float*)a.q_lat + qrow * kDc + k)
+                              : *(const f32x4*)((const float*)a.q_pe + qrow * kDr + (k - kDc));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) q[4 * s4 + j] = v[j];
+    }
+  };
+  const int piece = id / kBlocks;
+  const int row_guess = a.num_splits > 1 ? piece / a.num_splits : piece;
+  load_q(row_guess);
+  LenScan lens = scan_lengths(a);
+  const WorkItem w = make_work(a, piece, uniform_length(a, lens));
+  if (!w.live) return;  // past the last key range (uniform over the workgroup)
+  if (hb == 0) record_row_plan(a, w);
+  if (w.b * a.S + w.i != row_guess) load_q(w.b * a.S + w.i);
 
   const int ntok = w.tok_end - w.tok_begin;
   if (ntok <= 0) {  // empty key range: o = 0, lse = -inf; thread t writes 32 columns of head t / 16
@@ -750,21 +1047,6 @@ __global__ __launch_bounds__(256, 1) void decode_attn_f32_kernel(AttnArgs a) {
     }
   };
   fetch(0);
-
-  // this lane's query operand: [q_lat | q_pe] of its head at k = 144 wave + 36 g + s, s < 36
-  float q[36];
-  {
-    const size_t qrow = ((size_t)w.b * a.S + w.i) * kHeads + head;
-    const int k0 = 144 * wave + 36 * g;
-#pragma unroll
-    for (int s4 = 0; s4 < 9; ++s4) {
-      const int k = k0 + 4 * s4;  // four values on one side of the q_lat / q_pe boundary (512 = 4 x 128)
-      const f32x4 v = k < kDc ? *(const f32x4*)((const float*)a.q_lat + qrow * kDc + k)
-                              : *(const f32x4*)((const float*)a.q_pe + qrow * kDr + (k - kDc));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) q[4 * s4 + j] = v[j];
-    }
-  }
 
   float m_run = -INFINITY, l_run = 0.f;  // of this lane's head, in log2 units
   f32x4 o[8];                            // block b: latent 128 wave + 16 b + 4 g + e, head l16
@@ -889,48 +1171,59 @@ struct PartRow<uint16_t> {
 
 template <typename PartT>
 __global__ __launch_bounds__(256) void lse_merge_kernel(const PartT* __restrict__ o_part,
-                                                        const float* __restrict__ lse_part, float* __restrict__ o_lat,
+                                                        const float* __restrict__ lse_part,
+                                                        const int32_t* __restrict__ row_plan, float* __restrict__ o_lat,
                                                         float* __restrict__ lse, int num_splits) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int rh = xcd_remap(blockIdx.x, gridDim.x) * 4 + wave;  // row * kHeads + h
   const int row = rh / kHeads, h = rh % kHeads;
-  const size_t base = (size_t)row * num_splits * kHeads + h;  // split k at base + k * kHeads
-  const float* lp = lse_part + base;
-  const PartT* op = o_part + base * kDc + 8 * lane;
+  // The row's slots (first, count) come from the attention's plan.  The first partials are issued
+  // for the fixed layout (row * num_splits, num_splits) while the plan's flag loads, and issued
+  // again in the rare case that the layout differs (a ragged batch).
+  const int first_fixed = row * num_splits;
+  int first = first_fixed, nsp = num_splits;
+  if (!__builtin_amdgcn_readfirstlane(row_plan[0])) {
+    first = __builtin_amdgcn_readfirstlane(row_plan[4 + 2 * row]);
+    nsp = __builtin_amdgcn_readfirstlane(row_plan[4 + 2 * row + 1]);
+  }
   constexpr float kLog2e = 1.4426950408889634f;
-  auto lse_of = [&](int k) { return k < num_splits ? lp[(size_t)k * kHeads] : -INFINITY; };
 
   PartRow<PartT> x[8];
-  auto load_batch = [&](int kb) {  // splits kb .. kb+7 (clamped to the last one)
+  auto load_batch = [&](const PartT* op, int n, int kb) {  // splits kb .. kb+7 (clamped to the last one)
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int k = kb + j < num_splits ? kb + j : num_splits - 1;
+      const int k = kb + j < n ? kb + j : n - 1;
       x[j].load(op + (size_t)k * kHeads * kDc);
     }
   };
-  load_batch(0);  // does not depend on the weights: in flight while they are formed
+  // does not depend on the weights: in flight while they are formed
+  load_batch(o_part + ((size_t)first_fixed * kHeads + h) * kDc + 8 * lane, num_splits, 0);
+  const size_t base = (size_t)first * kHeads + h;  // split k at base + k * kHeads
+  const float* lp = lse_part + base;
+  const PartT* op = o_part + base * kDc + 8 * lane;
+  if (first != first_fixed || nsp != num_splits) load_batch(op, nsp, 0);
+  auto lse_of = [&](int k) { return k < nsp ? lp[(size_t)k * kHeads] : -INFINITY; };
   const float lse0 = lse_of(lane);
   float m = lse0;
-  for (int k0 = 64; k0 < num_splits; k0 += 64) m = fmaxf(m, lse_of(k0 + lane));
+  for (int k0 = 64; k0 < nsp; k0 += 64) m = fmaxf(m, lse_of(k0 + lane));
   m = wave_max(m);
   const float m_ref = m == -INFINITY ? 0.f : m;  // all splits empty: every weight is 0
 
   f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
   float sum = 0.f, w_lane = 0.f;
-  for (int kb = 0; kb < num_splits; kb += 8) {
+  for (int kb = 0; kb < nsp; kb += 8) {
     if ((kb & 63) == 0)  // weights of splits kb .. kb+63, one per lane (0 past the end)
       w_lane = __builtin_amdgcn_exp2f(((kb == 0 ? lse0 : lse_of(kb + lane)) - m_ref) * kLog2e);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float w = kb + j < num_splits
-                          ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_lane), (kb & 63) + j))
-                          : 0.f;
+      const float w = kb + j < nsp ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_lane), (kb & 63) + j))
+                                   : 0.f;
       sum += w;
       a0 += w * x[j].lo();
       a1 += w * x[j].hi();
     }
-    if (kb + 8 < num_splits) load_batch(kb + 8);
+    if (kb + 8 < nsp) load_batch(op, nsp, kb + 8);
   }
   const float inv = sum > 0.f ? 1.0f / sum : 0.f;
   f32x4* dst = (f32x4*)(o_lat + (size_t)rh * kDc + 8 * lane);
@@ -938,7 +1231,6 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const PartT* __restrict_
   dst[1] = a1 * inv;
   if (lane == 0 && lse) lse[rh] = m == -INFINITY ? -INFINITY : m + logf(sum);
 }
-
 hipError_t launch_decode_attn(const AttnArgs& a, int rows, hipStream_t stream) {
   forget_stale_error();
   const int nwg = rows * a.num_splits;
@@ -951,16 +1243,16 @@ hipError_t launch_decode_attn(const AttnArgs& a, int rows, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_lse_merge(const void* o_part, bool part_bf16, const float* lse_part, float* o_lat, float* lse,
-                            int rows, int num_splits, hipStream_t stream) {
+hipError_t launch_lse_merge(const void* o_part, bool part_bf16, const float* lse_part, const int32_t* row_plan,
+                            float* o_lat, float* lse, int rows, int num_splits, hipStream_t stream) {
   forget_stale_error();
   const dim3 grid(rows * (kHeads / 4));
   if (part_bf16)
     hipLaunchKernelGGL(lse_merge_kernel<uint16_t>, grid, dim3(256), 0, stream, (const uint16_t*)o_part, lse_part,
-                       o_lat, lse, num_splits);
+                       row_plan, o_lat, lse, num_splits);
   else
-    hipLaunchKernelGGL(lse_merge_kernel<float>, grid, dim3(256), 0, stream, (const float*)o_part, lse_part, o_lat,
-                       lse, num_splits);
+    hipLaunchKernelGGL(lse_merge_kernel<float>, grid, dim3(256), 0, stream, (const float*)o_part, lse_part, row_plan,
+                       o_lat, lse, num_splits);
   return hipGetLastError();
 }
 

@@ -42,26 +42,35 @@ struct AttnArgs {
                                // bf16 for the bf16 kernel, fp32 for the fp32 kernel
   float* lse_out;              // final lse (B,S,H) (may be null), or partial lse (B*S, splits, H)
   const int32_t* tree_parents;  // (B,S) draft-tree parents in [-1, j), or null (then `causal` applies)
+  // With num_splits > 1: word 0 = 1 if every row r has the fixed slots r * num_splits + j, then
+  // from word 4 (first partial slot, number of key ranges) of each row; written by the attention
+  // (range j of row r goes to slot first + j) and read by the merges; null otherwise.
+  int32_t* row_plan;
   int B, S, max_pages, pages_per_split, num_splits, causal, final_out, dtype_bf16;
   float scale;       // softmax scale
   float scale_log2;  // softmax scale * log2(e)
   Bounds bounds;
 };
 
-// decode attention over rows = B*S (b, i) pairs x num_splits page ranges
+// Key ranges with num_splits > 1: up to this many rows the ranges follow the rows' lengths (see
+// the key-range plan in decode_attn.hip); above it every row gets num_splits fixed ranges.
+constexpr int kPlanRows = 256;
+
+// decode attention over rows = B*S (b, i) pairs; rows * num_splits workgroups (x 8 for fp32)
 hipError_t launch_decode_attn(const AttnArgs& a, int rows, hipStream_t stream);
-// merge of (rows, splits, H) partials (bf16 or fp32) into o_lat (rows, H, 512) and lse (rows, H)
-// (lse may be null)
-hipError_t launch_lse_merge(const void* o_part, bool part_bf16, const float* lse_part, float* o_lat, float* lse,
-                            int rows, int num_splits, hipStream_t stream);
+// merge of the partial slots (rows * num_splits of H rows, bf16 or fp32) into o_lat (rows, H, 512)
+// and lse (rows, H) (lse may be null); row_plan gives each row's slots
+hipError_t launch_lse_merge(const void* o_part, bool part_bf16, const float* lse_part, const int32_t* row_plan,
+                            float* o_lat, float* lse, int rows, int num_splits, hipStream_t stream);
 // q_lat[n,h,:] = W_UK[h] q_nope[n,h,:] for n < tokens
 hipError_t launch_absorb_q(const void* q_nope, const void* w_uk, void* q_lat, int tokens, bool bf16,
                            hipStream_t stream);
 // out[n,h,:] = W_UV[h]^T o_lat[n,h,:] for n < tokens
 // Split merge + out-proj in one kernel (bf16 partials; W_UV bf16, or with w_fp8 the packed FP8 codes
 // and scales of launch_quantize_weight_fp8; o_lat and lse optional).
-hipError_t launch_merge_out_proj(const void* o_part, const float* lse_part, const void* w_uv, bool w_fp8, void* out,
-                                 float* o_lat, float* lse, int rows, int num_splits, hipStream_t stream);
+hipError_t launch_merge_out_proj(const void* o_part, const float* lse_part, const int32_t* row_plan, const void* w_uv,
+                                 bool w_fp8, void* out, float* o_lat, float* lse, int rows, int num_splits,
+                                 hipStream_t stream);
 hipError_t launch_out_proj(const float* o_lat, const void* w_uv, void* out, int tokens, bool bf16,
                            hipStream_t stream);
 

@@ -104,10 +104,14 @@ SplitPlan plan_splits(const mla_params* p, int requested, int cus) {
 // fp32.  The o block is a multiple of 16 bytes, so lse stays aligned.
 size_t part_elem_bytes(const mla_params* p) { return p->dtype == MLA_BF16 ? 2 : 4; }
 
+// After them the key-range plan: a 16-byte header (word 0: every row has the fixed slots), then
+// (first slot, number of ranges) per row, padded to 16 bytes.
+size_t row_plan_bytes(const mla_params* p) { return 16 + ((size_t)tokens_of(p) * 8 + 15) / 16 * 16; }
+
 size_t workspace_for(const mla_params* p, int splits) {
   if (splits <= 1) return 0;
   const size_t n = (size_t)tokens_of(p) * splits * mla::kHeads;
-  return n * mla::kDc * part_elem_bytes(p) + n * sizeof(float);
+  return n * mla::kDc * part_elem_bytes(p) + n * sizeof(float) + row_plan_bytes(p);
 }
 
 // mla_decode_attn_out_proj: with at least one 16-row block of query rows and more than one split,
@@ -120,7 +124,7 @@ bool merge_in_out_proj(const mla_params* p, int splits) { return tokens_of(p) >=
 size_t fused_workspace_for(const mla_params* p, int splits) {
   if (merge_in_out_proj(p, splits)) {
     const size_t n = (size_t)tokens_of(p) * splits * mla::kHeads;
-    return n * mla::kDc * 2 + n * sizeof(float);
+    return n * mla::kDc * 2 + n * sizeof(float) + row_plan_bytes(p);
   }
   return workspace_for(p, splits) + (size_t)tokens_of(p) * mla::kHeads * mla::kDc * sizeof(float);
 }
@@ -268,22 +272,28 @@ mla_status decode_attn_impl(const void* q_lat, const void* q_pe, const void* kv_
   if (plan.splits == 1 && !merge_in_proj) {
     a.o_out = o_lat;
     a.lse_out = lse;
+    a.row_plan = nullptr;
     a.final_out = 1;
     if (mla::launch_decode_attn(a, rows, s) != hipSuccess) return MLA_ERR_LAUNCH;
     return MLA_OK;
   }
   char* o_part = (char*)workspace;
-  float* lse_part = (float*)(o_part + (size_t)rows * plan.splits * mla::kHeads * mla::kDc * part_elem_bytes(p));
+  const size_t nslots = (size_t)rows * plan.splits * mla::kHeads;
+  float* lse_part = (float*)(o_part + nslots * mla::kDc * part_elem_bytes(p));
+  int32_t* row_plan = (int32_t*)(lse_part + nslots);
   a.o_out = o_part;
   a.lse_out = lse_part;
+  a.row_plan = row_plan;
   a.final_out = 0;
   if (mla::launch_decode_attn(a, rows, s) != hipSuccess) return MLA_ERR_LAUNCH;
   if (merge_in_proj) {
-    if (mla::launch_merge_out_proj(o_part, lse_part, w_uv, w_fp8, out, o_lat, lse, rows, plan.splits, s) != hipSuccess)
+    if (mla::launch_merge_out_proj(o_part, lse_part, row_plan, w_uv, w_fp8, out, o_lat, lse, rows, plan.splits, s) !=
+        hipSuccess)
       return MLA_ERR_LAUNCH;
     return MLA_OK;
   }
-  if (mla::launch_lse_merge(o_part, p->dtype == MLA_BF16, lse_part, o_lat, lse, rows, plan.splits, s) != hipSuccess)
+  if (mla::launch_lse_merge(o_part, p->dtype == MLA_BF16, lse_part, row_plan, o_lat, lse, rows, plan.splits, s) !=
+      hipSuccess)
     return MLA_ERR_LAUNCH;
   return MLA_OK;
 }

@@ -25,6 +25,20 @@ __device__ __forceinline__ void settle(const T& x) {
   asm volatile("" ::"v"(x));
 }
 
+// Largest of lanes 0-15's values (every lane gets it): a running maximum over the first row of 16
+// lanes by DPP row shifts, read from its last lane.
+__device__ __forceinline__ int rows16_max(int v, int lane) {
+  int t = __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  if ((lane & 15) >= 1) v = t > v ? t : v;
+  t = __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  if ((lane & 15) >= 2) v = t > v ? t : v;
+  t = __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  if ((lane & 15) >= 4) v = t > v ? t : v;
+  t = __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  if ((lane & 15) >= 8) v = t > v ? t : v;
+  return __builtin_amdgcn_readlane(v, 15);
+}
+
 // ---------------------------------------------------------------------------------------------
 // absorb, fp32: grid (4 latent blocks of 128, 128 heads), 4 waves; wave w owns 32 latent rows
 // c in [128 bx + 32 w, +32).  D(c x tokens) = W_UK[h] rows (A, straight from global) x q_nope^T
@@ -363,6 +377,7 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, 
 template <bool kFp8>
 __global__ __launch_bounds__(512, 1) void merge_out_proj_kernel(const uint16_t* __restrict__ o_part,
                                                                 const float* __restrict__ lse_part,
+                                                                const int32_t* __restrict__ row_plan,
                                                                 const void* __restrict__ w_uv,
                                                                 const float* __restrict__ w_scales,
                                                                 uint16_t* __restrict__ out, float* __restrict__ o_lat,
@@ -386,26 +401,58 @@ __global__ __launch_bounds__(512, 1) void merge_out_proj_kernel(const uint16_t* 
 
   // merge: row n = 16 blk + s16 (a row past the end reads row 16 blk, which exists, and stores nothing)
   auto row_of = [&](int blk) { return 16 * blk + s16 < rows ? 16 * blk + s16 : 16 * blk; };
-  // Batches of 4 splits (a split past the end repeats the last one with weight 0), two in flight.
+  // The slots of row n: (first, count) from the attention's plan (first + j holds its key range j);
+  // word 0 of the plan says whether every row has the fixed slots n * num_splits + j.
+  const bool plan_fixed = __builtin_amdgcn_readfirstlane(row_plan[0]) != 0;
+  auto plan_of = [&](int blk) {
+    return plan_fixed ? int2{row_of(blk) * num_splits, num_splits} : *(const int2*)(row_plan + 4 + 2 * row_of(blk));
+  };
+  // The first block's plan by scalar loads (a vector load here would be waited for together with the
+  // W_UV loads): whether all 16 rows keep the fixed layout, this lane's entry, the most ranges.
+  auto block_plan_scalar = [&](int blk, int2& mine, int& most) -> bool {
+    int e0[16], e1[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {  // all 16 loads first: one wait
+      const int n = 16 * blk + q < rows ? 16 * blk + q : 16 * blk;
+      e0[q] = __builtin_amdgcn_readfirstlane(row_plan[4 + 2 * n]);
+      e1[q] = __builtin_amdgcn_readfirstlane(row_plan[4 + 2 * n + 1]);
+    }
+    int off = 0;
+    most = 0;
+    mine = int2{e0[0], e1[0]};
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int n = 16 * blk + q < rows ? 16 * blk + q : 16 * blk;
+      off |= (e0[q] ^ (n * num_splits)) | (e1[q] ^ num_splits);
+      most = e1[q] > most ? e1[q] : most;
+      if (s16 == q) mine = int2{e0[q], e1[q]};
+    }
+    return off == 0;
+  };
+  // Batches of 4 splits (a split past the row's count repeats its last one with weight 0), two in
+  // flight.
   struct Batch {
     u32x4 x[4][2];  // [split][ks]
     float l[4];
   };
-  auto load = [&](int blk, int kb, Batch& bt) {
-    const size_t base = (size_t)row_of(blk) * num_splits * kHeads + h;  // split k at base + k * kHeads
+  auto load = [&](int2 pl, int kb, Batch& bt) {
+    const size_t base = (size_t)pl.x * kHeads + h;  // split k at base + k * kHeads
     const float* lp = lse_part + base;
     const uint16_t* op = o_part + base * kDc + c0 + 8 * g;  // + 32 ks
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int k = kb + j < num_splits ? kb + j : num_splits - 1;
-      bt.l[j] = kb + j < num_splits ? lp[(size_t)k * kHeads] : -INFINITY;
+      const int k = kb + j < pl.y ? kb + j : pl.y - 1;
+      bt.l[j] = kb + j < pl.y ? lp[(size_t)k * kHeads] : -INFINITY;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) bt.x[j][ks] = *(const u32x4*)(op + (size_t)k * kHeads * kDc + 32 * ks);
     }
   };
+  // The first block's partials go out for the fixed layout (row * num_splits, num_splits) before its
+  // plan is read; they are issued again below in the rare case that the plan differs (a ragged batch).
+  const int2 pl_fixed = {row_of(blk0) * num_splits, num_splits};
   Batch b0, b1;
-  load(blk0, 0, b0);
-  if (4 < num_splits) load(blk0, 4, b1);
+  load(pl_fixed, 0, b0);
+  if (4 < num_splits) load(pl_fixed, 4, b1);
   // W_UV[h] rows [c0, c0 + 64) after the first partials, so waiting for those does not wait for
   // W: load i covers local rows 4 i .. 4 i + 3 (16 lanes each).  Staged once for every row block of
   // the workgroup.
@@ -428,6 +475,14 @@ __global__ __launch_bounds__(512, 1) void merge_out_proj_kernel(const uint16_t* 
                                        (MLA_LDS void*)(ws + i * 1024), 16, 0, 0);
     }
   }
+  // the plan of the first block; the most ranges of its 16 rows bounds the merge loop
+  int2 pl = pl_fixed;
+  int nsp = num_splits;
+  if (!plan_fixed && !block_plan_scalar(blk0, pl, nsp)) {
+    load(pl, 0, b0);
+    if (4 < nsp) load(pl, 4, b1);
+  }
+  int2 pl_next = blk0 + 1 < blk_end ? plan_of(blk0 + 1) : pl;
   const float sw = kFp8 ? w_scales[h * 4 + (wave >> 1)] : 1.f;  // FP8: weight scale of block kb = w / 2
   // A operand of value block mb, k step ks: two transposed reads; source lane s of group g gives
   // local row 32 ks + 8 g + 4 t + s/4 and values 16 mb + 4 (s%4) .. +3 (t = 0, 1).
@@ -465,12 +520,12 @@ __global__ __launch_bounds__(512, 1) void merge_out_proj_kernel(const uint16_t* 
         }
       }
     };
-    for (int kb = 0; kb < num_splits; kb += 8) {
+    for (int kb = 0; kb < nsp; kb += 8) {
       consume(b0);
-      if (kb + 8 < num_splits) load(blk, kb + 8, b0);
-      if (kb + 4 < num_splits) {
+      if (kb + 8 < nsp) load(pl, kb + 8, b0);
+      if (kb + 4 < nsp) {
         consume(b1);
-        if (kb + 12 < num_splits) load(blk, kb + 12, b1);
+        if (kb + 12 < nsp) load(pl, kb + 12, b1);
       }
     }
     const float inv = sum > 0.f ? 1.0f / sum : 0.f;
@@ -528,10 +583,14 @@ __global__ __launch_bounds__(512, 1) void merge_out_proj_kernel(const uint16_t* 
     if (lse && live && wave == 0 && g == 0) lse[(size_t)n * kHeads + h] = m == -INFINITY ? -INFINITY : m + logf(sum);
 
     if (blk == blk0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's W rows have landed
-    // the next row block's first partials stream in during this block's products and sums
+    // the next row block's first partials stream in during this block's products and sums (its plan
+    // was loaded a block ahead)
     if (blk + 1 < blk_end) {
-      load(blk + 1, 0, b0);
-      if (4 < num_splits) load(blk + 1, 4, b1);
+      pl = pl_next;
+      nsp = plan_fixed ? num_splits : rows16_max(pl.y, lane);
+      load(pl, 0, b0);
+      if (4 < nsp) load(pl, 4, b1);
+      if (blk + 2 < blk_end) pl_next = plan_of(blk + 2);
     }
     f32x4 acc[8];
 #pragma unroll
@@ -752,8 +811,9 @@ hipError_t launch_absorb_q(const void* q_nope, const void* w_uk, void* q_lat, in
   return hipGetLastError();
 }
 
-hipError_t launch_merge_out_proj(const void* o_part, const float* lse_part, const void* w_uv, bool w_fp8, void* out,
-                                 float* o_lat, float* lse, int rows, int num_splits, hipStream_t stream) {
+hipError_t launch_merge_out_proj(const void* o_part, const float* lse_part, const int32_t* row_plan, const void* w_uv,
+                                 bool w_fp8, void* out, float* o_lat, float* lse, int rows, int num_splits,
+                                 hipStream_t stream) {
   forget_stale_error();
   // two workgroups per head (one per CU at 128 heads), each over a run of 16-row blocks, so a
   // workgroup stages its W_UV[h] slices once for all of its rows
@@ -765,11 +825,11 @@ hipError_t launch_merge_out_proj(const void* o_part, const float* lse_part, cons
   if (w_fp8) {
     const float* scales = (const float*)((const uint8_t*)w_uv + (size_t)kHeads * kDc * kDh);
     hipLaunchKernelGGL(merge_out_proj_kernel<true>, dim3((unsigned)grid), dim3(512), 0, stream,
-                       (const uint16_t*)o_part, lse_part, w_uv, scales, (uint16_t*)out, o_lat, lse, rows, num_splits,
+                       (const uint16_t*)o_part, lse_part, row_plan, w_uv, scales, (uint16_t*)out, o_lat, lse, rows, num_splits,
                        bpw);
   } else {
     hipLaunchKernelGGL(merge_out_proj_kernel<false>, dim3((unsigned)grid), dim3(512), 0, stream,
-                       (const uint16_t*)o_part, lse_part, w_uv, (const float*)nullptr, (uint16_t*)out, o_lat, lse,
+                       (const uint16_t*)o_part, lse_part, row_plan, w_uv, (const float*)nullptr, (uint16_t*)out, o_lat, lse,
                        rows, num_splits, bpw);
   }
   return hipGetLastError();

@@ -124,10 +124,15 @@ int32_t mla_decode_num_splits(const mla_params* p, int32_t num_splits);
  *                                         scaled logits
  *   workspace / workspace_bytes           scratch of at least mla_decode_workspace_bytes()
  *                                         (may be NULL when that is 0); contents are scratch
- *   num_splits                            0 = library's choice; k > 0 splits every sequence's
- *                                         keys into k contiguous page ranges, each reduced
- *                                         separately and merged by log-sum-exp. Results for a
- *                                         fixed split count are bitwise reproducible.
+ *   num_splits                            0 = library's choice; k > 1 reduces the keys in
+ *                                         B * S * k contiguous page ranges, merged per query row
+ *                                         by log-sum-exp. Up to 256 query rows the ranges follow
+ *                                         the rows' lengths: with C the smallest page count for
+ *                                         which the rows need at most B * S * k ranges of C pages
+ *                                         (at least one per row), each row is cut into ranges of
+ *                                         C pages (equal lengths give k ranges per row); above
+ *                                         256 rows every row gets k ranges. Results for a fixed
+ *                                         split count and fixed lengths are bitwise reproducible.
  * Cites: izhida answer "DeepSeek" (per head a 512-d latent and a 64-d RoPE inner product and a
  * weighted sum over the 512-d latent, per cached token) and answer "专家"; cache row of 576
  * per layer (same answer; Perplexity post, section "Одноузловое против многоузлового").
@@ -174,8 +179,9 @@ mla_status mla_out_proj(const float* o_lat, const void* w_uv, void* out, const m
 /*
  * Workspace bytes of mla_decode_attn_out_proj for this p and split request (0 for an invalid p),
  * with k = mla_decode_num_splits(p, num_splits): B * S * k * H * (d_c * 2 + 4) (the bf16 split
- * partials) when B * S >= 16 and k > 1; otherwise the call runs the separate kernels, and the
- * workspace is mla_decode_workspace_bytes(p, num_splits) plus B * S * H * d_c * 4 bytes for o_lat.
+ * partials) plus 16 + B * S * 8 rounded up to a multiple of 16 (the range plan) when B * S >= 16
+ * and k > 1; otherwise the call runs the separate kernels, and the workspace is
+ * mla_decode_workspace_bytes(p, num_splits) plus B * S * H * d_c * 4 bytes for o_lat.
  */
 size_t mla_decode_attn_out_proj_workspace_bytes(const mla_params* p, int32_t num_splits);
 

@@ -74,15 +74,21 @@ hipError_t launch_decode_attn(const AttnArgs& a, int rows, hipStream_t) {
   const size_t out_rows = a.final_out ? r : r * a.num_splits;
   touch(a.o_out, out_rows * kHeads * kDc * (a.final_out ? 4 : e));
   touch(a.lse_out, out_rows * kHeads * 4);
+  if (!a.final_out) {  // the range plan: (first slot, count) of every row
+    if (!a.row_plan) return hipErrorInvalidValue;
+    touch(a.row_plan, 16 + r * 8);
+  }
   return hipSuccess;
 }
 
-hipError_t launch_lse_merge(const void* o_part, bool part_bf16, const float* lse_part, float* o_lat, float* lse,
-                            int rows, int num_splits, hipStream_t) {
+hipError_t launch_lse_merge(const void* o_part, bool part_bf16, const float* lse_part, const int32_t* row_plan,
+                            float* o_lat, float* lse, int rows, int num_splits, hipStream_t) {
   ++g_launches[kLseMerge];
   const size_t n = (size_t)rows * num_splits * kHeads;
+  if (!row_plan) return hipErrorInvalidValue;
   touch(o_part, n * kDc * elem(part_bf16));
   touch(lse_part, n * 4);
+  touch(row_plan, 16 + (size_t)rows * 8);
   touch(o_lat, (size_t)rows * kHeads * kDc * 4);
   touch(lse, (size_t)rows * kHeads * 4);
   return hipSuccess;
@@ -98,12 +104,15 @@ hipError_t launch_absorb_q(const void* q_nope, const void* w_uk, void* q_lat, in
 
 constexpr size_t kFp8Bytes = (size_t)kHeads * kDc * kDh + (size_t)kHeads * 4 * 4;
 
-hipError_t launch_merge_out_proj(const void* o_part, const float* lse_part, const void* w_uv, bool w_fp8, void* out,
-                                 float* o_lat, float* lse, int rows, int num_splits, hipStream_t) {
+hipError_t launch_merge_out_proj(const void* o_part, const float* lse_part, const int32_t* row_plan, const void* w_uv,
+                                 bool w_fp8, void* out, float* o_lat, float* lse, int rows, int num_splits,
+                                 hipStream_t) {
   ++g_launches[kMergeOutProj];
   const size_t n = (size_t)rows * num_splits * kHeads;
+  if (!row_plan) return hipErrorInvalidValue;
   touch(o_part, n * kDc * 2);
   touch(lse_part, n * 4);
+  touch(row_plan, 16 + (size_t)rows * 8);
   touch(w_uv, w_fp8 ? kFp8Bytes : (size_t)kHeads * kDc * kDh * 2);
   touch(out, (size_t)rows * kHeads * kDh * 2);
   touch(o_lat, (size_t)rows * kHeads * kDc * 4);

@@ -78,8 +78,10 @@ def test_attention_errors():
     assert _attn(P(softmax_scale=-0.1)) == -2
     # explicit split count: workspace size is host-computable, no device query
     need = lib.mla_decode_workspace_bytes(ctypes.byref(P()), 2)
-    assert need == 2 * 1 * 2 * 128 * (512 * 2 + 4)  # bf16 partials + fp32 lse
-    assert lib.mla_decode_workspace_bytes(ctypes.byref(P(dtype=binding.MLA_F32)), 2) == 2 * 1 * 2 * 128 * (512 + 1) * 4
+    plan = 16 + 16  # the range plan: a 16-byte header, then (first slot, range count) of each of the 2 rows
+    assert need == 2 * 1 * 2 * 128 * (512 * 2 + 4) + plan  # bf16 partials + fp32 lse + range plan
+    assert lib.mla_decode_workspace_bytes(ctypes.byref(P(dtype=binding.MLA_F32)), 2) == \
+        2 * 1 * 2 * 128 * (512 + 1) * 4 + plan
     assert _attn(P(), ws=None, ws_bytes=0, splits=2) == -1
     assert _attn(P(), ws=FAKE, ws_bytes=need - 4, splits=2) == -5
     assert _attn(P(), ws=MISALIGNED, ws_bytes=need, splits=2) == -4
@@ -115,11 +117,12 @@ def test_fused_attention_out_proj_errors():
     row = 128 * (512 * 2 + 4)  # one split's bf16 partial rows and lse values of one query row
     olat = 128 * 512 * 4  # one query row of o_lat
     ws = lambda params, k: lib.mla_decode_attn_out_proj_workspace_bytes(ctypes.byref(params), k)  # noqa: E731
-    assert ws(P(batch=16), 2) == 16 * 2 * row  # merge inside the W_UV kernel
+    plan = lambda rows: 16 + (rows * 8 + 15) // 16 * 16  # noqa: E731  the range plan: header + rows, padded
+    assert ws(P(batch=16), 2) == 16 * 2 * row + plan(16)  # merge inside the W_UV kernel
     assert ws(P(batch=16), 1) == 16 * olat  # one split: the separate kernels, o_lat in the workspace
-    assert ws(P(), 2) == 2 * 2 * row + 2 * olat  # two rows: separate merge, o_lat in the workspace
+    assert ws(P(), 2) == 2 * 2 * row + plan(2) + 2 * olat  # two rows: separate merge, o_lat in the workspace
     assert ws(P(), 1) == 2 * olat
-    assert _fused(P(batch=16), ws_bytes=16 * 2 * row - 4) == -5
+    assert _fused(P(batch=16), ws_bytes=16 * 2 * row + plan(16) - 4) == -5
     assert _fused(P(dtype=binding.MLA_F32)) == -3  # bf16 only
     assert _fused(P(), {"w_uv": None}) == -1
     assert _fused(P(), {"out": None}) == -1

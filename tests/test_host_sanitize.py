@@ -57,7 +57,9 @@ def test_the_harness_reports_an_overrun(tmp_path):
     AddressSanitizer report."""
     src = tmp_path / "stubs_overrun.cpp"
     text = open(os.path.join(HERE, "stubs.cpp")).read()
-    planted = text.replace("touch(lse_part, n * 4);\n  touch(o_lat", "touch(lse_part, n * 4 + 4);\n  touch(o_lat", 1)
+    # the range plan ends the workspace of the separate merge; 16 bytes past it is past any padding
+    planted = text.replace("touch(row_plan, 16 + (size_t)rows * 8);\n  touch(o_lat",
+                           "touch(row_plan, 16 + (size_t)rows * 8 + 16);\n  touch(o_lat", 1)
     assert planted != text
     src.write_text(planted.replace('#include "../../deepseek_mla_latent_amd/csrc/kernels.h"',
                                    f'#include "{os.path.join(CSRC, "kernels.h")}"'))

@@ -76,7 +76,7 @@ def test_fused_routes():
                                        dtype=binding.MLA_BF16)
     ws = binding.mla_decode_attn_out_proj_workspace_bytes
     olat = 128 * 512 * 4
-    assert ws(mk(16), 2) == 16 * 2 * 128 * (512 * 2 + 4)
+    assert ws(mk(16), 2) == 16 * 2 * 128 * (512 * 2 + 4) + 16 + 16 * 8  # + the range plan (header, rows)
     assert ws(mk(16), 1) == 16 * olat
     assert ws(mk(15), 2) == binding.mla_decode_workspace_bytes(mk(15), 2) + 15 * olat
 
