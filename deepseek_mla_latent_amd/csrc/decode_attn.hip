@@ -189,11 +189,12 @@ __device__ __forceinline__ uint64_t tree_walk(int par, int S, int i) {
 //   row r gets s_r = max(1, ceil(P_r / C)) ranges of C pages (the last one shorter, an empty row one
 //   empty range), numbered row after row: range j of row r is workgroup and partial slot first_r + j
 //   (first_r = s_0 + .. + s_{r-1}); workgroups past the last range have nothing to do.
-// Equal lengths give C = pages_per_split and s_r = k, the fixed ranges.  Above kPlanRows rows every
-// row gets the k fixed ranges of pages_per_split pages.  Every wave computes the plan itself from
-// seq_lens (wave-uniform results, no barrier): C by bisection between the bounds
+// Rows with equal page counts P get C = max(1, ceil(P / k)) and ceil(P / C) ranges each: the k fixed
+// ranges whenever P spans them.  Above kPlanRows rows every row gets the k fixed ranges of
+// pages_per_split pages.  Every wave computes the plan itself from seq_lens (wave-uniform results,
+// no barrier): equal counts in closed form; otherwise C by bisection between the bounds
 // ceil(T / G) <= C <= ceil(T / (G - rows)) (T = sum_r P_r; max(1, ceil(x)) <= x + 1 makes the upper
-// one fit), the slots by a prefix sum over the rows.
+// one fit), and the slots by a prefix sum over the rows.
 
 // Inclusive prefix sum over each row of 16 lanes (DPP row shifts).
 __device__ __forceinline__ int row16_scan(int v, int lane) {
@@ -212,9 +213,11 @@ __device__ __forceinline__ int wave_total(int scanned) {
   return (__builtin_amdgcn_readlane(scanned, 15) + __builtin_amdgcn_readlane(scanned, 31)) +
          (__builtin_amdgcn_readlane(scanned, 47) + __builtin_amdgcn_readlane(scanned, 63));
 }
-// ceil(p / c) for 0 <= p < 2^22, c >= 1 (rc = 1 / c, within an ulp): the quotient from the
-// reciprocal is off by at most one, and one correction each way makes it exact.
+// ceil(p / c) for p >= 0, c >= 1 (rc = 1 / c, within an ulp).  Below 2^22 the quotient from the
+// reciprocal is off by at most one, and one correction each way makes it exact; larger p (not met
+// by any batch that fits a GPU's memory) take the integer division.
 __device__ __forceinline__ int ceil_div_small(int p, int c, float rc) {
+  if (p >= (1 << 22)) return (int)(((unsigned)p + (unsigned)c - 1u) / (unsigned)c);
   int q = (int)((float)p * rc);
   int r = p - q * c;
   q += (r >= c ? 1 : 0) - (r < 0 ? 1 : 0);
@@ -222,8 +225,9 @@ __device__ __forceinline__ int ceil_div_small(int p, int c, float rc) {
   return q + (r > 0 ? 1 : 0);
 }
 
-// floor(p / c) for 0 <= p < 2^22, c >= 1 (rc = 1 / c, within an ulp), corrected like ceil_div_small.
+// floor(p / c), likewise.
 __device__ __forceinline__ int floor_div_small(int p, int c, float rc) {
+  if (p >= (1 << 22)) return (int)((unsigned)p / (unsigned)c);
   int q = (int)((float)p * rc);
   const int r = p - q * c;
   return q + (r >= c ? 1 : 0) - (r < 0 ? 1 : 0);
