@@ -287,9 +287,128 @@ __device__ __forceinline__ int uniform_length(const AttnArgs& a, LenScan& ls) {
   return diff == 0 ? checked_len(a.bounds, ls.v[0]) : -1;
 }
 
+// Longest first.  With more ranges than compute units, the workgroups past the first wave start
+// as earlier ones finish, in workgroup order; ordering the ranges by decreasing length then pairs
+// the short ranges of the second wave with the compute units whose first range was short (the
+// longest-processing-time rule).  Row r's ranges are f_r = floor(P_r / C) full ranges of C pages
+// and, when C does not divide P_r (or P_r = 0), one remainder range of P_r - f_r C pages.
+// Workgroup `pos` (dispatch order) takes:
+//   pos < F = sum f_r: full range t = xcd_remap(pos, F) in row-major order, so that a row's full
+//     ranges share an XCD;
+//   F <= pos < F + R: the remainder of rank pos - F, ranks by decreasing size, ties by row;
+//   otherwise nothing.
+// Partial slots stay row-major (row r's ranges at first_r .. first_r + s_r - 1, s_r = f_r + [it
+// has a remainder]), the layout the merges read from the row table.
+__device__ __forceinline__ RangePlan plan_longest_first(const AttnArgs& a, const int* P, const int* Ls, int C,
+                                                        float rc, RangePlan p) {
+  constexpr int M = kPlanRows / 64;
+  const int rows = a.B * a.S, k = a.num_splits;
+  const int lane = threadIdx.x & 63;
+  const int pos = blockIdx.x;
+  int f[M], rem[M], sfirst[M], ffirst[M];
+  bool has[M];
+  int base_s = 0, base_f = 0;
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    f[m] = 0;
+    rem[m] = 0;
+    has[m] = false;
+    if (P[m] >= 0) {
+      f[m] = floor_div_small(P[m], C, rc);
+      rem[m] = P[m] - f[m] * C;
+      has[m] = rem[m] > 0 || P[m] == 0;
+    }
+    const int sm = f[m] + (has[m] ? 1 : 0);
+    p.fixed = p.fixed && __ballot(P[m] >= 0 && sm != k) == 0;
+    const int scs = row16_scan(sm, lane), scf = row16_scan(f[m], lane);
+    const int q16 = lane >> 4;
+    const int s15 = __builtin_amdgcn_readlane(scs, 15), s31 = __builtin_amdgcn_readlane(scs, 31),
+              s47 = __builtin_amdgcn_readlane(scs, 47), s63 = __builtin_amdgcn_readlane(scs, 63);
+    const int f15 = __builtin_amdgcn_readlane(scf, 15), f31 = __builtin_amdgcn_readlane(scf, 31),
+              f47 = __builtin_amdgcn_readlane(scf, 47), f63 = __builtin_amdgcn_readlane(scf, 63);
+    sfirst[m] = base_s + (q16 >= 1 ? s15 : 0) + (q16 >= 2 ? s31 : 0) + (q16 >= 3 ? s47 : 0) + scs - sm;
+    ffirst[m] = base_f + (q16 >= 1 ? f15 : 0) + (q16 >= 2 ? f31 : 0) + (q16 >= 3 ? f47 : 0) + scf - f[m];
+    base_s += (s15 + s31) + (s47 + s63);
+    base_f += (f15 + f31) + (f47 + f63);
+  }
+  const int F = base_f, NR = base_s;  // full ranges; all ranges
+  int r = -1, m_hit = 0, l_hit = 0, j = 0;
+  if (pos < F) {
+    const int t = xcd_remap(pos, F);
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const uint64_t hit = __ballot(f[m] > 0 && t >= ffirst[m] && t < ffirst[m] + f[m]);
+      if (hit) {
+        m_hit = m;
+        l_hit = __builtin_ctzll(hit);
+        r = 64 * m + l_hit;
+        j = t - __builtin_amdgcn_readlane(ffirst[m], l_hit);
+      }
+    }
+  } else if (pos < NR) {
+    const int q = pos - F;
+    auto count_ge = [&](int v) {  // rows whose remainder range has at least v pages
+      int c = 0;
+#pragma unroll
+      for (int m = 0; m < M; ++m) c += __builtin_popcountll(__ballot(has[m] && rem[m] >= v));
+      return c;
+    };
+    int lo = 0, hi = C - 1;  // the remainder of rank q has the largest size v with count_ge(v) > q
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (count_ge(mid) > q)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    int t = q - (lo + 1 <= C - 1 ? count_ge(lo + 1) : 0);  // rank among the rows of that size
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const bool eq = has[m] && rem[m] == lo;
+      const uint64_t mask = __ballot(eq);
+      const int c = __builtin_popcountll(mask);
+      if (r < 0 && t < c) {
+        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+        const uint64_t sel = __ballot(eq && below == t);
+        m_hit = m;
+        l_hit = __builtin_ctzll(sel);
+        r = 64 * m + l_hit;
+        j = __builtin_amdgcn_readlane(f[m], l_hit);
+      } else if (r < 0) {
+        t -= c;
+      }
+    }
+  }
+  if (r >= 0) {
+    int sf = sfirst[0], fr = f[0], L = Ls[0];
+    bool hs = has[0];
+#pragma unroll
+    for (int m = 1; m < M; ++m)
+      if (m_hit == m) {
+        sf = sfirst[m];
+        fr = f[m];
+        L = Ls[m];
+        hs = has[m];
+      }
+    p.r = r;
+    p.j = j;
+    p.first = __builtin_amdgcn_readlane(sf, l_hit);
+    p.count = __builtin_amdgcn_readlane(fr + (hs ? 1 : 0), l_hit);
+    p.L = __builtin_amdgcn_readlane(L, l_hit);
+    p.live = true;
+  }
+  (void)rows;
+  return p;
+}
+
 // L0: the common length of all sequences when every row sees all of its keys, else -1.
+// With a range budget above rows * k (set by the host only for at most kPlanRows rows), rows of
+// unequal length get up to that many ranges, dispatched longest first (see the end of this
+// function); equal rows keep the k-per-row numbering over the first rows * k workgroups.
 __device__ RangePlan plan_ranges(const AttnArgs& a, int g, int L0) {
   const int rows = a.B * a.S, k = a.num_splits, pps = a.pages_per_split;
+  const bool longest_first = a.range_budget > rows * k;
+  if (longest_first) g = (int)blockIdx.x < rows * k ? xcd_remap(blockIdx.x, rows * k) : rows * k;
   RangePlan p;
   if (rows > kPlanRows) {
     p.r = g / k;
@@ -304,7 +423,7 @@ __device__ RangePlan plan_ranges(const AttnArgs& a, int g, int L0) {
   }
   const int lane = threadIdx.x & 63;
   const int cap = k * pps;
-  const int G = rows * k;
+  const int G = longest_first ? a.range_budget : rows * k;  // ranges the rows of unequal length may take
   if (L0 >= 0) {  // every row sees all L0 keys: the closed form below, from P = pages of L0
     const int pg = (L0 + kPage - 1) / kPage;
     const int P0 = pg < cap ? pg : cap;
@@ -395,6 +514,7 @@ __device__ RangePlan plan_ranges(const AttnArgs& a, int g, int L0) {
   p.r = p.j = p.first = p.count = p.L = 0;
   p.chunk = C;
   p.fixed = true;
+  if (longest_first) return plan_longest_first(a, P, Ls, C, rc, p);
   int base = 0;  // slots of the rows before this group of 64
 #pragma unroll
   for (int m = 0; m < kPlanRows / 64; ++m) {
@@ -1237,7 +1357,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(const PartT* __restrict_
 }
 hipError_t launch_decode_attn(const AttnArgs& a, int rows, hipStream_t stream) {
   forget_stale_error();
-  const int nwg = rows * a.num_splits;
+  const int nwg = a.dtype_bf16 ? a.range_budget : rows * a.num_splits;
   if (a.dtype_bf16 && a.tree_parents)
     hipLaunchKernelGGL(decode_attn_bf16_kernel<true>, dim3(nwg), dim3(256), 0, stream, a);
   else if (a.dtype_bf16)
@@ -1248,7 +1368,8 @@ hipError_t launch_decode_attn(const AttnArgs& a, int rows, hipStream_t stream) {
 }
 
 hipError_t launch_lse_merge(const void* o_part, bool part_bf16, const float* lse_part, const int32_t* row_plan,
-                            float* o_lat, float* lse, int rows, int num_splits, hipStream_t stream) {
+                            float* o_lat, float* lse, int rows, int num_splits, int slots, hipStream_t stream) {
+  (void)slots;  // the merge reads each row's slots from row_plan
   forget_stale_error();
   const dim3 grid(rows * (kHeads / 4));
   if (part_bf16)

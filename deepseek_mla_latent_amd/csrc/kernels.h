@@ -47,6 +47,9 @@ struct AttnArgs {
   // (range j of row r goes to slot first + j) and read by the merges; null otherwise.
   int32_t* row_plan;
   int B, S, max_pages, pages_per_split, num_splits, causal, final_out, dtype_bf16;
+  // Key ranges (and partial slots, and workgroups) the plan may use: B * S * num_splits, or more
+  // when ranges of rows of unequal length are dispatched longest first (see plan_ranges)
+  int range_budget;
   float scale;       // softmax scale
   float scale_log2;  // softmax scale * log2(e)
   Bounds bounds;
@@ -56,12 +59,13 @@ struct AttnArgs {
 // the key-range plan in decode_attn.hip); above it every row gets num_splits fixed ranges.
 constexpr int kPlanRows = 256;
 
-// decode attention over rows = B*S (b, i) pairs; rows * num_splits workgroups (x 8 for fp32)
+// decode attention over rows = B*S (b, i) pairs; range_budget workgroups (bf16; at least rows *
+// num_splits), rows * num_splits * 8 for fp32
 hipError_t launch_decode_attn(const AttnArgs& a, int rows, hipStream_t stream);
-// merge of the partial slots (rows * num_splits of H rows, bf16 or fp32) into o_lat (rows, H, 512)
-// and lse (rows, H) (lse may be null); row_plan gives each row's slots
+// merge of the partial slots (`slots` of H rows, bf16 or fp32; at least rows * num_splits) into
+// o_lat (rows, H, 512) and lse (rows, H) (lse may be null); row_plan gives each row's slots
 hipError_t launch_lse_merge(const void* o_part, bool part_bf16, const float* lse_part, const int32_t* row_plan,
-                            float* o_lat, float* lse, int rows, int num_splits, hipStream_t stream);
+                            float* o_lat, float* lse, int rows, int num_splits, int slots, hipStream_t stream);
 // q_lat[n,h,:] = W_UK[h] q_nope[n,h,:] for n < tokens
 hipError_t launch_absorb_q(const void* q_nope, const void* w_uk, void* q_lat, int tokens, bool bf16,
                            hipStream_t stream);
@@ -70,7 +74,7 @@ hipError_t launch_absorb_q(const void* q_nope, const void* w_uk, void* q_lat, in
 // and scales of launch_quantize_weight_fp8; o_lat and lse optional).
 hipError_t launch_merge_out_proj(const void* o_part, const float* lse_part, const int32_t* row_plan, const void* w_uv,
                                  bool w_fp8, void* out, float* o_lat, float* lse, int rows, int num_splits,
-                                 hipStream_t stream);
+                                 int slots, hipStream_t stream);
 hipError_t launch_out_proj(const float* o_lat, const void* w_uv, void* out, int tokens, bool bf16,
                            hipStream_t stream);
 

@@ -74,6 +74,7 @@ int linear_splits(int M, int K, int N, int cus) {
 // equal page ranges and no trailing empty split.
 struct SplitPlan {
   int splits, pages_per_split;
+  int64_t slots;  // key ranges the device plan may use = partial slots = attention workgroups (bf16)
 };
 
 SplitPlan plan_splits(const mla_params* p, int requested, int cus) {
@@ -89,14 +90,25 @@ SplitPlan plan_splits(const mla_params* p, int requested, int cus) {
       if (s < 1) s = 1;
     }
   }
-  if (max_pages == 0) return {1, 1};
+  if (max_pages == 0) return {1, 1, rows};
   if (s > max_pages) s = max_pages;
   // a workgroup stages its range's page ids in LDS: at most kMaxSplitPages pages per split
   const int min_splits = (max_pages + mla::kMaxSplitPages - 1) / mla::kMaxSplitPages;
   if (s < min_splits) s = min_splits;
   const int pps = (max_pages + s - 1) / s;
   s = (max_pages + pps - 1) / pps;
-  return {s, pps};
+  // With the library's choice of splits, bf16, and 33..kPlanRows query rows, rows of unequal length
+  // may take up to 9/8 of a key range per compute unit, dispatched longest first: the eighth past
+  // the first wave fills the units whose first range was short (decode_attn.hip, plan_ranges).
+  // More, shorter ranges measured slower (each pays a workgroup's fixed cost).  Rows of equal
+  // length still use rows * s of them (the rest exit); 32 rows or fewer keep exactly rows * s
+  // workgroups.
+  int64_t slots = rows * s;
+  if (requested <= 0 && p->dtype == MLA_BF16 && s > 1 && rows > 32 && rows <= mla::kPlanRows) {
+    const int64_t want = (9 * (int64_t)cus + 7) / 8;
+    if (slots < want) slots = want;
+  }
+  return {s, pps, slots};
 }
 
 // Split partials: o (rows, splits, H, d_c) in the input dtype (bf16 partials carry 8 mantissa bits,
@@ -108,9 +120,9 @@ size_t part_elem_bytes(const mla_params* p) { return p->dtype == MLA_BF16 ? 2 : 
 // (first slot, number of ranges) per row, padded to 16 bytes.
 size_t row_plan_bytes(const mla_params* p) { return 16 + ((size_t)tokens_of(p) * 8 + 15) / 16 * 16; }
 
-size_t workspace_for(const mla_params* p, int splits) {
-  if (splits <= 1) return 0;
-  const size_t n = (size_t)tokens_of(p) * splits * mla::kHeads;
+size_t workspace_for(const mla_params* p, const SplitPlan& plan) {
+  if (plan.splits <= 1) return 0;
+  const size_t n = (size_t)plan.slots * mla::kHeads;
   return n * mla::kDc * part_elem_bytes(p) + n * sizeof(float) + row_plan_bytes(p);
 }
 
@@ -121,12 +133,12 @@ size_t workspace_for(const mla_params* p, int splits) {
 // with o_lat in the workspace after any partials when the caller wants none.
 bool merge_in_out_proj(const mla_params* p, int splits) { return tokens_of(p) >= 16 && splits > 1; }
 
-size_t fused_workspace_for(const mla_params* p, int splits) {
-  if (merge_in_out_proj(p, splits)) {
-    const size_t n = (size_t)tokens_of(p) * splits * mla::kHeads;
+size_t fused_workspace_for(const mla_params* p, const SplitPlan& plan) {
+  if (merge_in_out_proj(p, plan.splits)) {
+    const size_t n = (size_t)plan.slots * mla::kHeads;
     return n * mla::kDc * 2 + n * sizeof(float) + row_plan_bytes(p);
   }
-  return workspace_for(p, splits) + (size_t)tokens_of(p) * mla::kHeads * mla::kDc * sizeof(float);
+  return workspace_for(p, plan) + (size_t)tokens_of(p) * mla::kHeads * mla::kDc * sizeof(float);
 }
 
 // Prefill buffer: [K_nope | V] (B, H, Lp, 256) then k_pe (B, Lp, 64), bf16, Lp = max_pages * page.
@@ -196,7 +208,8 @@ int32_t mla_decode_num_splits(const mla_params* p, int32_t num_splits) {
 size_t mla_decode_workspace_bytes(const mla_params* p, int32_t num_splits) {
   const int32_t s = mla_decode_num_splits(p, num_splits);
   // more (row, split) workgroups than a grid holds: the call rejects it (MLA_ERR_SHAPE)
-  return s > 0 && tokens_of(p) * s <= 0x7fffffffLL ? workspace_for(p, s) : 0;
+  if (s <= 0 || tokens_of(p) * s > 0x7fffffffLL) return 0;
+  return workspace_for(p, plan_splits(p, num_splits, num_splits > 0 ? 1 : cu_count()));
 }
 
 }  // extern "C"
@@ -233,7 +246,7 @@ mla_status decode_attn_impl(const void* q_lat, const void* q_pe, const void* kv_
   const SplitPlan plan = plan_splits(p, num_splits, cus);
   const int64_t grid = tokens_of(p) * plan.splits * (p->dtype == MLA_BF16 ? 1 : mla::kHeads / mla::kF32Heads);
   if (grid > 0x7fffffffLL) return MLA_ERR_SHAPE;
-  const size_t need = fused ? fused_workspace_for(p, plan.splits) : workspace_for(p, plan.splits);
+  const size_t need = fused ? fused_workspace_for(p, plan) : workspace_for(p, plan);
   const bool merge_in_proj = fused && merge_in_out_proj(p, plan.splits);
   if (need > 0) {
     if (!workspace) return MLA_ERR_NULL;
@@ -241,7 +254,7 @@ mla_status decode_attn_impl(const void* q_lat, const void* q_pe, const void* kv_
     if (!aligned16(workspace)) return MLA_ERR_ALIGN;
   }
   if (fused && !merge_in_proj) {  // the separate merge and out-projection, o_lat maybe in the workspace
-    float* o = o_lat ? o_lat : (float*)((char*)workspace + workspace_for(p, plan.splits));
+    float* o = o_lat ? o_lat : (float*)((char*)workspace + workspace_for(p, plan));
     st = decode_attn_impl(q_lat, q_pe, kv_pool, block_table, seq_lens, tree_parents, o, lse, workspace,
                           workspace_bytes, num_splits, p, stream);
     if (st != MLA_OK) return st;
@@ -262,6 +275,7 @@ mla_status decode_attn_impl(const void* q_lat, const void* q_pe, const void* kv_
   a.max_pages = p->max_pages_per_seq;
   a.pages_per_split = plan.pages_per_split;
   a.num_splits = plan.splits;
+  a.range_budget = (int)plan.slots;
   a.causal = p->causal ? 1 : 0;
   a.dtype_bf16 = p->dtype == MLA_BF16;
   a.scale = p->softmax_scale;
@@ -278,7 +292,7 @@ mla_status decode_attn_impl(const void* q_lat, const void* q_pe, const void* kv_
     return MLA_OK;
   }
   char* o_part = (char*)workspace;
-  const size_t nslots = (size_t)rows * plan.splits * mla::kHeads;
+  const size_t nslots = (size_t)plan.slots * mla::kHeads;
   float* lse_part = (float*)(o_part + nslots * mla::kDc * part_elem_bytes(p));
   int32_t* row_plan = (int32_t*)(lse_part + nslots);
   a.o_out = o_part;
@@ -287,12 +301,14 @@ mla_status decode_attn_impl(const void* q_lat, const void* q_pe, const void* kv_
   a.final_out = 0;
   if (mla::launch_decode_attn(a, rows, s) != hipSuccess) return MLA_ERR_LAUNCH;
   if (merge_in_proj) {
-    if (mla::launch_merge_out_proj(o_part, lse_part, row_plan, w_uv, w_fp8, out, o_lat, lse, rows, plan.splits, s) !=
+    if (mla::launch_merge_out_proj(o_part, lse_part, row_plan, w_uv, w_fp8, out, o_lat, lse, rows, plan.splits,
+                                   (int)plan.slots, s) !=
         hipSuccess)
       return MLA_ERR_LAUNCH;
     return MLA_OK;
   }
-  if (mla::launch_lse_merge(o_part, p->dtype == MLA_BF16, lse_part, row_plan, o_lat, lse, rows, plan.splits, s) !=
+  if (mla::launch_lse_merge(o_part, p->dtype == MLA_BF16, lse_part, row_plan, o_lat, lse, rows, plan.splits,
+                            (int)plan.slots, s) !=
       hipSuccess)
     return MLA_ERR_LAUNCH;
   return MLA_OK;
@@ -323,7 +339,8 @@ mla_status mla_decode_attn_tree(const void* q_lat, const void* q_pe, const void*
 
 size_t mla_decode_attn_out_proj_workspace_bytes(const mla_params* p, int32_t num_splits) {
   const int32_t s = mla_decode_num_splits(p, num_splits);
-  return s > 0 && tokens_of(p) * s <= 0x7fffffffLL ? fused_workspace_for(p, s) : 0;
+  if (s <= 0 || tokens_of(p) * s > 0x7fffffffLL) return 0;
+  return fused_workspace_for(p, plan_splits(p, num_splits, num_splits > 0 ? 1 : cu_count()));
 }
 
 mla_status mla_decode_attn_out_proj(const void* q_lat, const void* q_pe, const void* kv_pool,

@@ -813,7 +813,8 @@ hipError_t launch_absorb_q(const void* q_nope, const void* w_uk, void* q_lat, in
 
 hipError_t launch_merge_out_proj(const void* o_part, const float* lse_part, const int32_t* row_plan, const void* w_uv,
                                  bool w_fp8, void* out, float* o_lat, float* lse, int rows, int num_splits,
-                                 hipStream_t stream) {
+                                 int slots, hipStream_t stream) {
+  (void)slots;  // the merge reads each row's slots from row_plan
   forget_stale_error();
   // two workgroups per head (one per CU at 128 heads), each over a run of 16-row blocks, so a
   // workgroup stages its W_UV[h] slices once for all of its rows

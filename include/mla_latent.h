@@ -131,8 +131,14 @@ int32_t mla_decode_num_splits(const mla_params* p, int32_t num_splits);
  *                                         which the rows need at most B * S * k ranges of C pages
  *                                         (at least one per row), each row is cut into ranges of
  *                                         C pages (equal lengths give k ranges per row); above
- *                                         256 rows every row gets k ranges. Results for a fixed
- *                                         split count and fixed lengths are bitwise reproducible.
+ *                                         256 rows every row gets k ranges. With num_splits = 0,
+ *                                         bf16 and 33..256 query rows, the bound is
+ *                                         R = max(B * S * k, ceil(9/8 * compute units)) ranges
+ *                                         instead, and rows of unequal length are cut to fill it,
+ *                                         run longest first (the ranges past the first wave of
+ *                                         one per compute unit fill the units that finish early).
+ *                                         Results for a fixed split count and fixed lengths are
+ *                                         bitwise reproducible.
  * Cites: izhida answer "DeepSeek" (per head a 512-d latent and a 64-d RoPE inner product and a
  * weighted sum over the 512-d latent, per cached token) and answer "专家"; cache row of 576
  * per layer (same answer; Perplexity post, section "Одноузловое против многоузлового").
@@ -178,9 +184,10 @@ mla_status mla_out_proj(const float* o_lat, const void* w_uv, void* out, const m
 
 /*
  * Workspace bytes of mla_decode_attn_out_proj for this p and split request (0 for an invalid p),
- * with k = mla_decode_num_splits(p, num_splits): B * S * k * H * (d_c * 2 + 4) (the bf16 split
- * partials) plus 16 + B * S * 8 rounded up to a multiple of 16 (the range plan) when B * S >= 16
- * and k > 1; otherwise the call runs the separate kernels, and the workspace is
+ * with k = mla_decode_num_splits(p, num_splits) and R the range bound of mla_decode_attn (B * S * k
+ * unless the library's own choice allows more): R * H * (d_c * 2 + 4) (the bf16 split partials)
+ * plus 16 + B * S * 8 rounded up to a multiple of 16 (the range plan) when B * S >= 16 and k > 1;
+ * otherwise the call runs the separate kernels, and the workspace is
  * mla_decode_workspace_bytes(p, num_splits) plus B * S * H * d_c * 4 bytes for o_lat.
  */
 size_t mla_decode_attn_out_proj_workspace_bytes(const mla_params* p, int32_t num_splits);

@@ -71,7 +71,8 @@ hipError_t launch_decode_attn(const AttnArgs& a, int rows, hipStream_t) {
   touch(a.block_table, (size_t)a.B * a.max_pages * 4);
   if (a.tree_parents) touch(a.tree_parents, (size_t)a.B * a.S * 4);
   if (a.bounds.num_pages > 0) touch(a.pool, (size_t)a.bounds.num_pages * kPage * kRow * e);
-  const size_t out_rows = a.final_out ? r : r * a.num_splits;
+  if (!a.final_out && (size_t)a.range_budget < r * a.num_splits) return hipErrorInvalidValue;
+  const size_t out_rows = a.final_out ? r : (size_t)a.range_budget;
   touch(a.o_out, out_rows * kHeads * kDc * (a.final_out ? 4 : e));
   touch(a.lse_out, out_rows * kHeads * 4);
   if (!a.final_out) {  // the range plan: (first slot, count) of every row
@@ -82,9 +83,10 @@ hipError_t launch_decode_attn(const AttnArgs& a, int rows, hipStream_t) {
 }
 
 hipError_t launch_lse_merge(const void* o_part, bool part_bf16, const float* lse_part, const int32_t* row_plan,
-                            float* o_lat, float* lse, int rows, int num_splits, hipStream_t) {
+                            float* o_lat, float* lse, int rows, int num_splits, int slots, hipStream_t) {
   ++g_launches[kLseMerge];
-  const size_t n = (size_t)rows * num_splits * kHeads;
+  if (slots < rows * num_splits) return hipErrorInvalidValue;
+  const size_t n = (size_t)slots * kHeads;
   if (!row_plan) return hipErrorInvalidValue;
   touch(o_part, n * kDc * elem(part_bf16));
   touch(lse_part, n * 4);
@@ -106,9 +108,10 @@ constexpr size_t kFp8Bytes = (size_t)kHeads * kDc * kDh + (size_t)kHeads * 4 * 4
 
 hipError_t launch_merge_out_proj(const void* o_part, const float* lse_part, const int32_t* row_plan, const void* w_uv,
                                  bool w_fp8, void* out, float* o_lat, float* lse, int rows, int num_splits,
-                                 hipStream_t) {
+                                 int slots, hipStream_t) {
   ++g_launches[kMergeOutProj];
-  const size_t n = (size_t)rows * num_splits * kHeads;
+  if (slots < rows * num_splits) return hipErrorInvalidValue;
+  const size_t n = (size_t)slots * kHeads;
   if (!row_plan) return hipErrorInvalidValue;
   touch(o_part, n * kDc * 2);
   touch(lse_part, n * 4);

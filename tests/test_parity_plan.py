@@ -32,8 +32,9 @@ def _cdiv(a, b):
     return -(-a // b)
 
 
-def plan_reference(x, k, causal=True):
-    """(first, count) per row and the chunk C, from the plan's definition."""
+def plan_reference(x, k, causal=True, budget=None):
+    """(first, count) per row and the chunk C, from the plan's definition (budget: the ranges the
+    rows may take, rows * k unless the library allows more)."""
     w = x.workload
     S = w.q_len
     rows = w.batch * S
@@ -47,17 +48,18 @@ def plan_reference(x, k, causal=True):
         pages.append(min(_cdiv(n, PAGE), k * pps))
     if rows > 256:
         return [(r * k, k) for r in range(rows)], pps
-    G = rows * k
+    G = rows * k if budget is None else budget
     C = next(c for c in range(1, pps + 1) if sum(max(1, _cdiv(p, c)) for p in pages) <= G)
     counts = [max(1, _cdiv(p, C)) for p in pages]
     firsts = np.concatenate([[0], np.cumsum(counts)[:-1]]).astype(int)
     return list(zip(firsts.tolist(), counts)), C
 
 
-def _table(ws, x, k, elem):
-    """The plan after the partials: header word 0 (1: every row has k fixed slots), then the rows."""
+def _table(ws, x, k, elem, slots=None):
+    """The plan after the partials (`slots` of them, rows * k by default): header word 0 (1: every
+    row has k fixed slots), then the rows."""
     rows = x.workload.batch * x.workload.q_len
-    off = rows * k * 128 * (512 * elem + 4)
+    off = (rows * k if slots is None else slots) * 128 * (512 * elem + 4)
     t = ws.view(-1).view(__import__("torch").int32)[off // 4: off // 4 + 4 + 2 * rows].cpu().numpy()
     entries = [(int(t[4 + 2 * r]), int(t[4 + 2 * r + 1])) for r in range(rows)]
     assert int(t[0]) == int(entries == [(r * k, k) for r in range(rows)])
@@ -183,3 +185,80 @@ def test_plan_in_the_fused_merge():
     for name, e in errs.items():
         assert e <= tol_for(x), name
     check_lse(lse, want["lse"], tol_for(x))
+
+
+def _longest_first_budget(rows, k):
+    """Ranges the library lets rows of unequal length take with its own split choice (bf16): 9/8 of
+    one per compute unit for 33..256 query rows, when rows * k is fewer."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    want = -(-9 * cus // 8)
+    return want if 32 < rows <= 256 and k > 1 and rows * k < want else rows * k
+
+
+@pytest.mark.parametrize("route", ["separate merge", "merge in out-projection"])
+def test_plan_longest_first(route):
+    """128 ragged rows with the library's split choice: more ranges than compute units, dispatched
+    longest first.  Every row's slots and count match the plan restated here with the larger budget;
+    every range is computed exactly once (workspace and outputs start as NaN, so a range left out
+    shows); outputs match the oracle and a second call is bitwise equal."""
+    import torch
+    rng = np.random.default_rng(5)
+    lens = rng.integers(1, 2200, size=128).astype(np.int32)
+    lens[[7, 40, 99]] = 0          # empty rows: one empty range each, dispatched last
+    lens[[3, 4, 5]] = 640          # equal remainders (ties broken by row)
+    lens[60] = 4096                # a long row with several full ranges
+    say("plan: longest first, 128 ragged rows,", route)
+    w = gen.small_workload(len(lens), 1, cache_len=1, dtype="bf16", paged=True)
+    x = gen.generate(w, 43, poison_unused=True, seq_lens=lens)
+    q_lat_bits, _ = gen.generate_latent(w, 44)
+    d = to_device(x)
+    p = params_for(x)
+    k = binding.mla_decode_num_splits(p, 0)
+    budget = _longest_first_budget(len(lens), k)
+    fused = route != "separate merge"
+
+    def run():
+        o = torch.full((w.batch, 1, 128, 512), float("nan"), device="cuda")
+        lse = torch.full((w.batch, 1, 128), float("nan"), device="cuda")
+        if fused:
+            nb = binding.mla_decode_attn_out_proj_workspace_bytes(p, 0)
+            ws = torch.full((nb // 4,), float("nan"), device="cuda")
+            out = torch.full((w.batch, 1, 128, 128), float("nan"), device="cuda").to(torch.bfloat16)
+            binding.mla_decode_attn_out_proj(device_array(q_lat_bits, True), d["q_pe"], d["pool"], d["block_table"],
+                                             d["seq_lens"], None, d["w_uv"], out, o, lse, ws, 0, p)
+        else:
+            nb = binding.mla_decode_workspace_bytes(p, 0)
+            ws = torch.full((nb // 4,), float("nan"), device="cuda")
+            out = None
+            binding.mla_decode_attn(device_array(q_lat_bits, True), d["q_pe"], d["pool"], d["block_table"],
+                                    d["seq_lens"], o, lse, ws, 0, p)
+        torch.cuda.synchronize()
+        return ws, o, lse, out
+
+    ws, o, lse, out = run()
+    want_plan, C = plan_reference(x, k, budget=budget)
+    nranges = sum(c for _, c in want_plan)
+    say("  k", k, "budget", budget, "chunk", C, "ranges", nranges)
+    assert budget > len(lens) * k  # the larger budget is in force on this device
+    assert nranges > len(lens) * k  # and the plan uses it: a second wave of ranges
+    assert _table(ws, x, k, 2, slots=budget) == want_plan
+    q, want = _oracle(x, q_lat_bits, True)
+    o_h, lse_h = to_host(o), to_host(lse)
+    assert not np.isnan(o_h).any() and not np.isnan(lse_h).any()
+    err = rel_err(o_h, want["o_lat"])
+    check_lse(lse_h, want["lse"], tol_for(x))
+    check_softmax_mass(q, x.f32("q_pe"), x.f32("pool"), x.block_table, x.seq_lens, lse_h,
+                       sample_rows(want["lse"], seed=45), softmax_scale=w.softmax_scale, tol=tol_for(x))
+    errs = {"o_lat": err}
+    if fused:
+        out_h = to_host(out)
+        assert not np.isnan(out_h).any()
+        errs["out"] = rel_err(out_h, ref.out_proj_reference(want["o_lat"], x.f32("w_uv")))
+    say("  rel errs", errs)
+    for name, e in errs.items():
+        assert e <= tol_for(x), name
+    _, o2, lse2, out2 = run()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    if fused:
+        assert torch.equal(out, out2)
