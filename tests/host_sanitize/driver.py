@@ -75,7 +75,8 @@ def params(**kw):
     return binding.make_params(**kw)
 
 
-def case_decode(batch, q_len, max_seq_len, splits, dtype, num_pages=0, tree=False, cus=256):
+def case_decode(batch, q_len, max_seq_len, splits, dtype, num_pages=0, tree=False, cus=256, slots=None):
+    """slots: the partial slots the workspace must hold (checked against its size when given)."""
     lib.san_set_cus(cus)
     e = 2 if dtype == binding.MLA_BF16 else 4
     p = params(batch=batch, q_len=q_len, max_seq_len=max_seq_len, dtype=dtype, num_pages=num_pages)
@@ -86,6 +87,8 @@ def case_decode(batch, q_len, max_seq_len, splits, dtype, num_pages=0, tree=Fals
     bt, ln = table(batch, pages, num_pages), lens(batch, max_seq_len)
     o, lse = buf(rows * H * DC * 4), buf(rows * H * 4)
     nbytes = lib.mla_decode_workspace_bytes(ctypes.byref(p), splits)
+    if slots is not None:  # partials (bf16 or fp32 rows of 512, fp32 lse) and the (first, count) table
+        assert nbytes == slots * H * (DC * e + 4) + 16 + (rows * 8 + 15) // 16 * 16, (nbytes, slots)
     ws = buf(nbytes)
     before = counts()
     if tree:
@@ -209,6 +212,12 @@ if __name__ == "__main__":
         case_projections(3, dt)
     case_decode(1, 1, PAGE * 512 * 2 + 1, 0, binding.MLA_BF16)  # more pages than one workgroup stages
     case_decode(64, 2, 16386, 0, binding.MLA_BF16, cus=304)
+    # 33..256 rows, bf16, the library's split count: up to ceil(9/8 * CUs) ranges (longest first)
+    case_decode(128, 1, 8192, 0, binding.MLA_BF16, cus=256, slots=288)
+    case_decode(128, 1, 8192, 2, binding.MLA_BF16, cus=256, slots=256)  # split count given: rows * k
+    case_decode(128, 1, 8192, 0, binding.MLA_F32, cus=256, slots=256)   # fp32: rows * k
+    case_decode(32, 1, 4096, 0, binding.MLA_BF16, cus=256, slots=256)   # 32 rows: rows * k
+    case_decode(100, 1, 8192, 0, binding.MLA_BF16, cus=256, slots=300)  # rows * k = 300 >= 288
     case_decode(2, 8, 4104, 2, binding.MLA_BF16, tree=True)
     case_decode(2, 8, 4104, 0, binding.MLA_BF16, tree=True, cus=1)
     case_fused(16, 1, 700, 2, False)
@@ -216,6 +225,7 @@ if __name__ == "__main__":
     case_fused(2, 1, 700, 2, False)
     case_fused(2, 1, 700, 1, False)
     case_fused(32, 1, 4096, 0, True)
+    case_fused(128, 1, 8192, 0, True)  # the merge in the W_UV kernel over 288 partial slots
     for args in ((16, 1, 700, 2, False), (2, 1, 700, 2, True), (32, 1, 4096, 0, True), (4, 1, 300, 1, False)):
         case_fused(*args, fp8=True)
     case_prefill(2, 96, 160, 0)
