@@ -262,3 +262,57 @@ def test_plan_longest_first(route):
     assert torch.equal(o, o2) and torch.equal(lse, lse2)
     if fused:
         assert torch.equal(out, out2)
+
+
+hypothesis = pytest.importorskip("hypothesis")
+from hypothesis import HealthCheck, given, settings  # noqa: E402
+from hypothesis import strategies as st  # noqa: E402
+
+
+@st.composite
+def _ragged_batches(draw):
+    # query-row counts where rows * k stays below 9/8 of 256 compute units (k = ceil(256 / rows)), so
+    # the larger budget applies: 64 or 70 sequences of 2 query tokens, 86..90 or 128..140 of one
+    batch, q_len = draw(st.sampled_from([(64, 2), (70, 2), (86, 1), (90, 1), (128, 1), (140, 1)]))
+    kinds = draw(st.lists(st.sampled_from(["empty", "short", "mid", "long", "long"]), min_size=batch,
+                          max_size=batch))
+    span = {"empty": (0, 0), "short": (1, 200), "mid": (200, 1200), "long": (1200, 2600)}
+    lens = [draw(st.integers(*span[k])) for k in kinds]
+    return dict(batch=batch, q_len=q_len, lens=lens, seed=draw(st.integers(0, 2**31 - 1)))
+
+
+@settings(max_examples=8, deadline=None, derandomize=True, suppress_health_check=list(HealthCheck))
+@given(case=_ragged_batches())
+def test_plan_longest_first_drawn(case):
+    """Drawn ragged batches of 64..140 sequences (S = 1 or 2, causal; empty, short and long rows)
+    with the library's split count: the slot table matches the plan restated with the library's
+    range budget, every range is computed (NaN-filled workspace and outputs), and o_lat and lse match
+    the oracle on every row."""
+    import torch
+    say("plan: drawn ragged batch", {k: v for k, v in case.items() if k != "lens"}, "rows",
+        case["batch"] * case["q_len"])
+    w = gen.small_workload(case["batch"], case["q_len"], cache_len=1, dtype="bf16", paged=True)
+    lens = np.maximum(np.array(case["lens"], np.int32), 0)
+    x = gen.generate(w, case["seed"] % 100000, poison_unused=True, seq_lens=lens)
+    q_lat_bits, _ = gen.generate_latent(w, case["seed"] % 100000 + 1)
+    d = to_device(x)
+    p = params_for(x)
+    k = binding.mla_decode_num_splits(p, 0)
+    rows = case["batch"] * case["q_len"]
+    budget = _longest_first_budget(rows, k)
+    nb = binding.mla_decode_workspace_bytes(p, 0)
+    ws = torch.full((max(nb, 16) // 4,), float("nan"), device="cuda")
+    o = torch.full((w.batch, w.q_len, 128, 512), float("nan"), device="cuda")
+    lse = torch.full((w.batch, w.q_len, 128), float("nan"), device="cuda")
+    binding.mla_decode_attn(device_array(q_lat_bits, True), d["q_pe"], d["pool"], d["block_table"], d["seq_lens"],
+                            o, lse, ws if nb else None, 0, p)
+    torch.cuda.synchronize()
+    if k > 1:
+        want_plan, C = plan_reference(x, k, budget=budget)
+        say("  k", k, "budget", budget, "chunk", C, "ranges", sum(c for _, c in want_plan))
+        assert _table(ws, x, k, 2, slots=budget) == want_plan
+    q, want = _oracle(x, q_lat_bits, True)
+    o_h, lse_h = to_host(o), to_host(lse)
+    assert not np.isnan(o_h).any() and not np.isnan(lse_h).any()
+    assert rel_err(o_h, want["o_lat"]) <= tol_for(x)
+    check_lse(lse_h, want["lse"], tol_for(x))
