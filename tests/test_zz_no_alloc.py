@@ -42,15 +42,18 @@ def _same(a, b):
     return all(torch.equal(u, v) for u, v in zip(a, b))
 
 
-@pytest.mark.parametrize("route", ["merge in out-projection", "separate kernels"])
+@pytest.mark.parametrize("route", ["merge in out-projection", "separate kernels", "longest first"])
 def test_static_scratch_matches_workspace_call(route):
     import torch
     # 24 query rows and auto splits take the merge inside the W_UV kernel; 6 rows take the
-    # separate kernels (o_lat in the scratch when not asked for; asked for here)
-    big_b, small_b = (24, 17) if route == "merge in out-projection" else (6, 3)
+    # separate kernels (o_lat in the scratch when not asked for; asked for here); 128 and 90 ragged
+    # rows take more key ranges than compute units (the longest-first plan: more partial slots)
+    big_b, small_b = {"merge in out-projection": (24, 17), "separate kernels": (6, 3),
+                      "longest first": (128, 90)}[route]
+    hi = 2000 if route == "longest first" else 900
     cases = []
     for B, seed in ((big_b, 31), (small_b, 32)):
-        w = gen.small_workload(B, 1, ragged=(40, 900), dtype="bf16", paged=True)
+        w = gen.small_workload(B, 1, ragged=(40, hi), dtype="bf16", paged=True)
         x = gen.generate(w, seed, poison_unused=True)
         q_lat, _ = gen.generate_latent(w, seed + 100)
         cases.append((x, q_lat))
