@@ -302,7 +302,7 @@ __device__ __forceinline__ int uniform_length(const AttnArgs& a, LenScan& ls) {
 __device__ __forceinline__ RangePlan plan_longest_first(const AttnArgs& a, const int* P, const int* Ls, int C,
                                                         float rc, RangePlan p) {
   constexpr int M = kPlanRows / 64;
-  const int rows = a.B * a.S, k = a.num_splits;
+  const int k = a.num_splits;
   const int lane = threadIdx.x & 63;
   const int pos = blockIdx.x;
   int f[M], rem[M], sfirst[M], ffirst[M];
@@ -397,7 +397,6 @@ __device__ __forceinline__ RangePlan plan_longest_first(const AttnArgs& a, const
     p.L = __builtin_amdgcn_readlane(L, l_hit);
     p.live = true;
   }
-  (void)rows;
   return p;
 }
 
