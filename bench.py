@@ -1,10 +1,11 @@
 #!/usr/bin/env python3
 """Absorbed-MLA decode throughput on one MI355X.
 
-One step = one pass of the whole decode path over one batch, for one layer: with bf16 weights
+One step = one pass of the whole decode path over one batch, for one layer:
 mla_absorb_q -> mla_decode_attn_out_proj (split-K attention, then the log-sum-exp merge of the
-splits fused with W_UV), with --fp8-projections the FP8 forms of both calls (mla_absorb_q_fp8 ->
-mla_decode_attn_out_proj_fp8); with fp32 or --unfused mla_absorb_q -> mla_decode_attn
+splits fused with W_UV; in fp32, for a few query rows, fused with the out-projection's dot
+products), with --fp8-projections the FP8 forms of both calls (mla_absorb_q_fp8 ->
+mla_decode_attn_out_proj_fp8); with --unfused mla_absorb_q -> mla_decode_attn
 (split-K attention + merge) -> mla_out_proj.  Default workload: batch 32
 sequences x 1 query token, 128 heads, d_c 512, d_R 64, d_h 128, 4096 cached tokens each (bf16,
 contiguous cache = identity page table).  Inputs are seeded synthetic data already resident in HBM.
@@ -592,7 +593,7 @@ def main():
         return torch.from_numpy(a).to(dev)
 
     fp8 = bool(args.fp8_projections)
-    fused = x.is_bf16 and not args.unfused  # attention + merge/W_UV in one call
+    fused = not args.unfused  # attention + merge/W_UV in one call
     costs = accounting.path_costs(x.seq_lens, w.q_len, dt, tree=parents, fused=fused)
     per_replica = sum(c.bytes for c in costs)
     R = args.replicas or max(2, math.ceil(2 * MALL_BYTES / per_replica) + 1)

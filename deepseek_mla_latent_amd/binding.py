@@ -388,18 +388,17 @@ class DecodeBuffers:
         self.o_lat = torch.empty((B, S, H, params.kv_lora_rank), dtype=torch.float32, device=device)
         self.lse = torch.empty((B, S, H), dtype=torch.float32, device=device)
         self.out = torch.empty((B, S, H, params.head_dim), dtype=dt, device=device)
-        ws = mla_decode_workspace_bytes(params, num_splits)
-        if params.dtype == MLA_BF16:  # room for the fused route too
-            ws = max(ws, mla_decode_attn_out_proj_workspace_bytes(params, num_splits))
+        ws = max(mla_decode_workspace_bytes(params, num_splits),  # room for the fused route too
+                 mla_decode_attn_out_proj_workspace_bytes(params, num_splits))
         self.workspace = torch.empty(max(ws, 16) // 4 + 4, dtype=torch.float32, device=device) if ws else None
 
     def run(self, q_nope, q_pe, w_uk, w_uv, kv_pool, block_table, seq_lens, stream=None, fp8: bool = False,
             tree_parents=None, fused: bool = False, latent_outputs: bool = True):
         """The three calls; with ``fp8`` the weights are packed FP8 weights and the two projections
         run block-quantised (mla_absorb_q_fp8 / mla_out_proj_fp8); with ``tree_parents`` (B, S)
-        int32 the attention is the tree-masked verify (mla_decode_attn_tree).  With ``fused`` (bf16
-        weights) the attention and the out-projection are one call, mla_decode_attn_out_proj, which
-        writes o_lat and lse only with ``latent_outputs``."""
+        int32 the attention is the tree-masked verify (mla_decode_attn_tree).  With ``fused`` the
+        attention and the out-projection are one call, mla_decode_attn_out_proj, which writes o_lat
+        and lse only with ``latent_outputs``."""
         p = self.params
         (mla_absorb_q_fp8 if fp8 else mla_absorb_q)(q_nope, w_uk, self.q_lat, p, stream)
         if fused:

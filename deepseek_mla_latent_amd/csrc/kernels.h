@@ -77,6 +77,12 @@ hipError_t launch_merge_out_proj(const void* o_part, const float* lse_part, cons
                                  int slots, hipStream_t stream);
 hipError_t launch_out_proj(const float* o_lat, const void* w_uv, void* out, int tokens, bool bf16,
                            hipStream_t stream);
+// fp32, at most kGemvMergeTokens query rows: the split merge (fp32 partials, `slots` of them, each
+// row's from row_plan) inside the out-projection GEMV; o_lat and lse optional
+constexpr int kGemvMergeTokens = 4;
+hipError_t launch_merge_out_proj_f32(const float* o_part, const float* lse_part, const int32_t* row_plan,
+                                     const float* w_uv, float* out, float* o_lat, float* lse, int tokens, int num_splits,
+                                     int slots, hipStream_t stream);
 
 // Prefill in multi-head form (bf16).  kv (B,H,Lp,256) = [K_nope | V] per head and token and
 // kpe (B,Lp,64) = the shared RoPE key, Lp = max_pages * 64; rows from seq_lens[b] up to the end of

@@ -130,14 +130,22 @@ size_t workspace_for(const mla_params* p, const SplitPlan& plan) {
 // the merge runs inside the W_UV kernel, which reads the bf16 partials.  With fewer rows most of
 // that kernel's lanes would idle while each walks every split, and with one split there is no
 // merge to save (the attention writes o_lat itself), so the call then takes the separate kernels,
-// with o_lat in the workspace after any partials when the caller wants none.
-bool merge_in_out_proj(const mla_params* p, int splits) { return tokens_of(p) >= 16 && splits > 1; }
+// with o_lat in the workspace after any partials when the caller wants none.  In fp32, with at most
+// kGemvMergeTokens query rows and more than one split, the merge runs inside the out-projection
+// GEMV (fp32 partials), which saves the separate merge launch.
+bool merge_in_out_proj(const mla_params* p, int splits) {
+  return p->dtype == MLA_BF16 && tokens_of(p) >= 16 && splits > 1;
+}
+bool merge_in_gemv(const mla_params* p, int splits) {
+  return p->dtype == MLA_F32 && tokens_of(p) <= mla::kGemvMergeTokens && splits > 1;
+}
 
 size_t fused_workspace_for(const mla_params* p, const SplitPlan& plan) {
   if (merge_in_out_proj(p, plan.splits)) {
     const size_t n = (size_t)plan.slots * mla::kHeads;
     return n * mla::kDc * 2 + n * sizeof(float) + row_plan_bytes(p);
   }
+  if (merge_in_gemv(p, plan.splits)) return workspace_for(p, plan);
   return workspace_for(p, plan) + (size_t)tokens_of(p) * mla::kHeads * mla::kDc * sizeof(float);
 }
 
@@ -173,7 +181,7 @@ const char* mla_status_str(mla_status s) {
     case MLA_OK: return "MLA_OK";
     case MLA_ERR_NULL: return "MLA_ERR_NULL: a required pointer is NULL";
     case MLA_ERR_SHAPE: return "MLA_ERR_SHAPE: a size is out of range";
-    case MLA_ERR_DTYPE: return "MLA_ERR_DTYPE: dtype not supported by this call (MLA_F32 or MLA_BF16; prefill and the fused decode call: MLA_BF16 only)";
+    case MLA_ERR_DTYPE: return "MLA_ERR_DTYPE: dtype not supported by this call (MLA_F32 or MLA_BF16; prefill and the FP8 calls: MLA_BF16 only)";
     case MLA_ERR_ALIGN: return "MLA_ERR_ALIGN: pointers must be 16-byte aligned";
     case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace too small";
     case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: only H=128, d_c=512, d_R=64, d_h=128, page 64";
@@ -229,7 +237,7 @@ mla_status decode_attn_impl(const void* q_lat, const void* q_pe, const void* kv_
   if (num_splits < 0) return MLA_ERR_SHAPE;
   const int max_pages = pages_of(p);
   if (p->max_pages_per_seq < max_pages) return MLA_ERR_SHAPE;
-  if (fused && p->dtype != MLA_BF16) return MLA_ERR_DTYPE;
+  if (fused && w_fp8 && p->dtype != MLA_BF16) return MLA_ERR_DTYPE;
   if (tokens_of(p) == 0) return MLA_OK;
   if (!q_lat || !q_pe || !seq_lens || (!fused && !o_lat)) return MLA_ERR_NULL;
   if (fused && (!w_uv || !out)) return MLA_ERR_NULL;
@@ -248,18 +256,20 @@ mla_status decode_attn_impl(const void* q_lat, const void* q_pe, const void* kv_
   if (grid > 0x7fffffffLL) return MLA_ERR_SHAPE;
   const size_t need = fused ? fused_workspace_for(p, plan) : workspace_for(p, plan);
   const bool merge_in_proj = fused && merge_in_out_proj(p, plan.splits);
+  const bool merge_gemv = fused && merge_in_gemv(p, plan.splits);
   if (need > 0) {
     if (!workspace) return MLA_ERR_NULL;
     if (workspace_bytes < need) return MLA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return MLA_ERR_ALIGN;
   }
-  if (fused && !merge_in_proj) {  // the separate merge and out-projection, o_lat maybe in the workspace
+  if (fused && !merge_in_proj && !merge_gemv) {  // the separate merge and out-projection, o_lat maybe in the workspace
     float* o = o_lat ? o_lat : (float*)((char*)workspace + workspace_for(p, plan));
     st = decode_attn_impl(q_lat, q_pe, kv_pool, block_table, seq_lens, tree_parents, o, lse, workspace,
                           workspace_bytes, num_splits, p, stream);
     if (st != MLA_OK) return st;
     const hipError_t e = w_fp8 ? mla::launch_out_proj_fp8(o, w_uv, out, (int)tokens_of(p), (hipStream_t)stream)
-                               : mla::launch_out_proj(o, w_uv, out, (int)tokens_of(p), true, (hipStream_t)stream);
+                               : mla::launch_out_proj(o, w_uv, out, (int)tokens_of(p), p->dtype == MLA_BF16,
+                                                      (hipStream_t)stream);
     return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH;
   }
 
@@ -304,6 +314,12 @@ mla_status decode_attn_impl(const void* q_lat, const void* q_pe, const void* kv_
     if (mla::launch_merge_out_proj(o_part, lse_part, row_plan, w_uv, w_fp8, out, o_lat, lse, rows, plan.splits,
                                    (int)plan.slots, s) !=
         hipSuccess)
+      return MLA_ERR_LAUNCH;
+    return MLA_OK;
+  }
+  if (merge_gemv) {
+    if (mla::launch_merge_out_proj_f32((const float*)o_part, lse_part, row_plan, (const float*)w_uv, (float*)out,
+                                       o_lat, lse, rows, plan.splits, (int)plan.slots, s) != hipSuccess)
       return MLA_ERR_LAUNCH;
     return MLA_OK;
   }

@@ -17,6 +17,7 @@ namespace mla {
 
 // Up to this many tokens the fp32 projections run as VALU GEMVs instead of 32-token MFMA blocks.
 constexpr int kGemvTokens = 4;
+static_assert(kGemvMergeTokens == kGemvTokens, "the merging GEMV takes as many rows as the plain one");
 
 // Forces the values to be complete here: every load producing them is issued before this point,
 // and the compiler cannot trickle them out one MFMA at a time.
@@ -696,6 +697,109 @@ __global__ __launch_bounds__(256) void out_proj_f32_gemv_kernel(const float* __r
   }
 }
 
+// Split merge + out-proj, fp32, at most kGemvTokens query rows: out_proj_f32_gemv_kernel's grid,
+// waves and dot products, with o_lat formed in the kernel from the attention's fp32 split partials
+// instead of read from memory (the separate lse_merge_kernel launch is saved; at one query row it
+// is much of a step's fixed cost).  Row n's ranges are slots first .. first + count - 1 of the row
+// table (first = n * num_splits, count = num_splits when word 0 says every row keeps those).
+// The merge comes first and uses all 256 threads: thread t takes latent columns 2t, 2t + 1 of
+// head h and loads them from eight splits at a time together with their lse values, so the
+// partials of a row arrive in one round trip beside the W_UV rows; o = sum_k w_k o_k / sum_k w_k,
+// w_k = e^(lse_k - max_k lse_k) (all splits empty: o = 0, lse = -inf), the merge of
+// "【笔记】MLA矩阵吸收分析" §三.2 step 1 over key ranges, with the maximum taken per batch of eight.  The merged
+// rows go to LDS for the dot products; the workgroups of value half 0 also write o_lat and lse
+// when asked for.
+__global__ __launch_bounds__(256) void merge_out_proj_f32_gemv_kernel(const float* __restrict__ o_part,
+                                                                      const float* __restrict__ lse_part,
+                                                                      const int32_t* __restrict__ row_plan,
+                                                                      const float* __restrict__ w_uv,
+                                                                      float* __restrict__ out, float* __restrict__ o_lat,
+                                                                      float* __restrict__ lse, int tokens,
+                                                                      int num_splits) {
+  __shared__ f32x4 part[4 * kGemvTokens * 16];              // [wave][token][l16]
+  __shared__ __attribute__((aligned(16))) float om[kGemvTokens * kDc];  // merged rows
+  const int h = blockIdx.y, vh = blockIdx.x;
+  const int t = threadIdx.x;
+  const int wave = t >> 6, lane = t & 63, l16 = lane & 15, r4 = lane >> 4;
+  const int c0 = 128 * wave + 32 * r4;
+  const f32x4* W = (const f32x4*)(w_uv + ((size_t)h * kDc + c0) * kDh + 64 * vh + 4 * l16);
+  f32x4 wr[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) wr[i] = W[i * (kDh / 4)];  // row c0 + i
+  const bool fixed = __builtin_amdgcn_readfirstlane(row_plan[0]) != 0;
+  constexpr float kLog2e = 1.4426950408889634f;
+  for (int n = 0; n < tokens; ++n) {
+    const int first = fixed ? n * num_splits : __builtin_amdgcn_readfirstlane(row_plan[4 + 2 * n]);
+    const int cnt = fixed ? num_splits : __builtin_amdgcn_readfirstlane(row_plan[4 + 2 * n + 1]);
+    const float* lp = lse_part + (size_t)first * kHeads + h;  // split k at lp[k * kHeads]
+    const float* op = o_part + ((size_t)first * kHeads + h) * kDc + 2 * t;  // split k at op[k * kHeads * kDc]
+    // eight splits' lse values and partials in flight at once; the running maximum is raised per
+    // batch (the sums rescaled with it), so a row's loads need no round trip before them
+    float m = -INFINITY, a0 = 0.f, a1 = 0.f, sum = 0.f;
+    for (int kb = 0; kb < cnt; kb += 8) {
+      float l[8];
+      float2 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int k = kb + j < cnt ? kb + j : cnt - 1;
+        l[j] = lp[(size_t)k * kHeads];
+        v[j] = *(const float2*)(op + (size_t)k * kHeads * kDc);
+      }
+      float mb = m;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mb = kb + j < cnt ? fmaxf(mb, l[j]) : mb;
+      const float sc = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - mb) * kLog2e);
+      a0 *= sc;
+      a1 *= sc;
+      sum *= sc;
+      m = mb;
+      const float m_ref = m == -INFINITY ? 0.f : m;  // all splits so far empty: every weight is 0
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float w = kb + j < cnt ? __builtin_amdgcn_exp2f((l[j] - m_ref) * kLog2e) : 0.f;
+        sum += w;
+        a0 = __builtin_fmaf(w, v[j].x, a0);
+        a1 = __builtin_fmaf(w, v[j].y, a1);
+      }
+    }
+    const float inv = sum > 0.f ? 1.0f / sum : 0.f;
+    const float2 o2 = {a0 * inv, a1 * inv};
+    *(float2*)(om + n * kDc + 2 * t) = o2;
+    if (vh == 0) {
+      if (o_lat) *(float2*)(o_lat + ((size_t)n * kHeads + h) * kDc + 2 * t) = o2;
+      if (lse && t == 0) lse[(size_t)n * kHeads + h] = m == -INFINITY ? -INFINITY : m + logf(sum);
+    }
+  }
+  __syncthreads();  // the merged rows are in LDS
+  for (int n = 0; n < tokens; ++n) {
+    const f32x4* O = (const f32x4*)(om + n * kDc + c0);
+    f32x4 ov[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ov[i] = O[i];
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float o = ov[i >> 2][i & 3];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(o, wr[i][e], acc[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[e] += __shfl_xor(acc[e], 16);
+      acc[e] += __shfl_xor(acc[e], 32);
+    }
+    if (r4 == 0) part[(wave * kGemvTokens + n) * 16 + l16] = acc;
+  }
+  __syncthreads();
+  const int n = lane >> 4;  // wave 0: lane 16 n + l16 sums token n's values 4 l16 .. +3
+  if (wave == 0 && n < tokens) {
+    f32x4 v = part[n * 16 + l16];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) v += part[(w * kGemvTokens + n) * 16 + l16];
+    *(f32x4*)(out + ((size_t)n * kHeads + h) * kDh + 64 * vh + 4 * l16) = v;
+  }
+}
+
 // out-proj, fp32: grid (2 value halves of 64, 128 heads), 4 waves.  The workgroup stages
 // W_UV[h][:, 64 bx .. +64) in LDS, then computes D(v x tokens) = W_UV^T x o_lat^T with the fp32
 // MFMA for every (32-value block, 32-token block) pair, round-robin over the waves.
@@ -833,6 +937,18 @@ hipError_t launch_merge_out_proj(const void* o_part, const float* lse_part, cons
                        (const uint16_t*)o_part, lse_part, row_plan, w_uv, (const float*)nullptr, (uint16_t*)out, o_lat, lse,
                        rows, num_splits, bpw);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_out_proj_f32(const float* o_part, const float* lse_part, const int32_t* row_plan,
+                                     const float* w_uv, float* out, float* o_lat, float* lse, int tokens, int num_splits,
+                                     int slots, hipStream_t stream) {
+  (void)slots;  // the merge reads each row's slots from row_plan
+  forget_stale_error();
+  if (tokens <= 0) return hipSuccess;
+  if (tokens > kGemvTokens) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(merge_out_proj_f32_gemv_kernel, dim3(2, kHeads), dim3(256), 0, stream, o_part, lse_part, row_plan,
+                     w_uv, out, o_lat, lse, tokens, num_splits);
   return hipGetLastError();
 }
 

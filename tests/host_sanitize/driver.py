@@ -23,7 +23,7 @@ lib.san_set_cus.argtypes = [ctypes.c_int]
 libc = ctypes.CDLL(None)
 libc.posix_memalign.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t, ctypes.c_size_t]
 KINDS = dict(attn=0, lse_merge=1, absorb=2, merge_out_proj=3, out_proj=4, kv_up=5, prefill=6, linear=7, quant=8,
-             absorb_fp8=9, out_proj_fp8=10, rope=11)
+             absorb_fp8=9, out_proj_fp8=10, rope=11, merge_out_proj_f32=12)
 H, DC, DR, DH, PAGE, ROW = 128, 512, 64, 128, 64, 576
 INT32_MAX = 2 ** 31 - 1
 
@@ -109,14 +109,15 @@ def case_decode(batch, q_len, max_seq_len, splits, dtype, num_pages=0, tree=Fals
     print(f"decode B={batch} S={q_len} L={max_seq_len} splits={splits}->{n_split} dtype={dtype} tree={tree} ok")
 
 
-def case_fused(batch, q_len, max_seq_len, splits, latent_outputs, fp8=False):
+def case_fused(batch, q_len, max_seq_len, splits, latent_outputs, fp8=False, dtype=binding.MLA_BF16):
     lib.san_set_cus(256)
-    p = params(batch=batch, q_len=q_len, max_seq_len=max_seq_len)
+    p = params(batch=batch, q_len=q_len, max_seq_len=max_seq_len, dtype=dtype)
+    e = 2 if dtype == binding.MLA_BF16 else 4
     rows = batch * q_len
-    q_lat, q_pe, pool = buf(rows * H * DC * 2), buf(rows * H * DR * 2), buf(PAGE * ROW * 2)
+    q_lat, q_pe, pool = buf(rows * H * DC * e), buf(rows * H * DR * e), buf(PAGE * ROW * e)
     bt, ln = table(batch, p.max_pages_per_seq, 1), lens(batch, max_seq_len)
-    w_uv = buf(lib.mla_fp8_weight_bytes() if fp8 else H * DC * DH * 2)
-    out = buf(rows * H * DH * 2)
+    w_uv = buf(lib.mla_fp8_weight_bytes() if fp8 else H * DC * DH * e)
+    out = buf(rows * H * DH * e)
     o = buf(rows * H * DC * 4) if latent_outputs else None
     lse = buf(rows * H * 4) if latent_outputs else None
     nbytes = lib.mla_decode_attn_out_proj_workspace_bytes(ctypes.byref(p), splits)
@@ -127,9 +128,13 @@ def case_fused(batch, q_len, max_seq_len, splits, latent_outputs, fp8=False):
                 None)
     expect(code, f"fused B={batch} S={q_len} splits={splits} fp8={fp8}")
     assert launched("attn", before) == 1
-    assert launched("merge_out_proj", before) + launched("out_proj_fp8" if fp8 else "out_proj", before) == 1
-    print(f"fused B={batch} S={q_len} L={max_seq_len} splits={splits} latent={latent_outputs} fp8={fp8} ok "
-          f"(merge in W_UV: {launched('merge_out_proj', before)})")
+    assert launched("merge_out_proj", before) + launched("merge_out_proj_f32", before) + \
+        launched("out_proj_fp8" if fp8 else "out_proj", before) == 1
+    if dtype == binding.MLA_F32 and rows <= 4 and lib.mla_decode_num_splits(ctypes.byref(p), splits) > 1:
+        assert launched("merge_out_proj_f32", before) == 1 and launched("lse_merge", before) == 0
+    print(f"fused B={batch} S={q_len} L={max_seq_len} splits={splits} latent={latent_outputs} fp8={fp8} "
+          f"dtype={dtype} ok (merge in W_UV: {launched('merge_out_proj', before)}, "
+          f"in the fp32 GEMV: {launched('merge_out_proj_f32', before)})")
 
 
 def case_projections(tokens, dtype):
@@ -226,6 +231,9 @@ if __name__ == "__main__":
     case_fused(2, 1, 700, 1, False)
     case_fused(32, 1, 4096, 0, True)
     case_fused(128, 1, 8192, 0, True)  # the merge in the W_UV kernel over 288 partial slots
+    for args in ((1, 1, 512, 0, False), (1, 1, 512, 0, True), (2, 2, 700, 3, True), (1, 1, 300, 1, True),
+                 (6, 1, 700, 0, False)):  # fp32: the merge in the GEMV (<= 4 rows), else separate kernels
+        case_fused(*args, dtype=binding.MLA_F32)
     for args in ((16, 1, 700, 2, False), (2, 1, 700, 2, True), (32, 1, 4096, 0, True), (4, 1, 300, 1, False)):
         case_fused(*args, fp8=True)
     case_prefill(2, 96, 160, 0)

@@ -19,7 +19,7 @@ namespace {
 int g_cus = 256;
 long g_launches[16];
 enum Kind { kAttn, kLseMerge, kAbsorb, kMergeOutProj, kOutProj, kKvUp, kPrefill, kLinear, kQuant, kAbsorbFp8,
-            kOutProjFp8, kRope, kKinds };
+            kOutProjFp8, kRope, kMergeOutProjF32, kKinds };
 
 volatile unsigned char g_sink;
 
@@ -128,6 +128,22 @@ hipError_t launch_out_proj(const float* o_lat, const void* w_uv, void* out, int 
   touch(o_lat, (size_t)tokens * kHeads * kDc * 4);
   touch(w_uv, (size_t)kHeads * kDc * kDh * elem(bf16));
   touch(out, (size_t)tokens * kHeads * kDh * elem(bf16));
+  return hipSuccess;
+}
+
+hipError_t launch_merge_out_proj_f32(const float* o_part, const float* lse_part, const int32_t* row_plan,
+                                     const float* w_uv, float* out, float* o_lat, float* lse, int tokens, int num_splits,
+                                     int slots, hipStream_t) {
+  ++g_launches[kMergeOutProjF32];
+  if (tokens > kGemvMergeTokens || slots < tokens * num_splits || !row_plan) return hipErrorInvalidValue;
+  const size_t n = (size_t)slots * kHeads;
+  touch(o_part, n * kDc * 4);
+  touch(lse_part, n * 4);
+  touch(row_plan, 16 + (size_t)tokens * 8);
+  touch(w_uv, (size_t)kHeads * kDc * kDh * 4);
+  touch(out, (size_t)tokens * kHeads * kDh * 4);
+  touch(o_lat, (size_t)tokens * kHeads * kDc * 4);
+  touch(lse, (size_t)tokens * kHeads * 4);
   return hipSuccess;
 }
 

@@ -123,7 +123,9 @@ def test_fused_attention_out_proj_errors():
     assert ws(P(), 2) == 2 * 2 * row + plan(2) + 2 * olat  # two rows: separate merge, o_lat in the workspace
     assert ws(P(), 1) == 2 * olat
     assert _fused(P(batch=16), ws_bytes=16 * 2 * row + plan(16) - 4) == -5
-    assert _fused(P(dtype=binding.MLA_F32)) == -3  # bf16 only
+    row32 = 128 * (512 * 4 + 4)  # fp32 partial rows and lse values
+    assert ws(P(dtype=binding.MLA_F32), 2) == 2 * 2 * row32 + plan(2)  # fp32, <= 4 rows: merge in the GEMV
+    assert ws(P(dtype=binding.MLA_F32, batch=6), 2) == 6 * 2 * row32 + plan(6) + 6 * olat  # separate kernels
     assert _fused(P(), {"w_uv": None}) == -1
     assert _fused(P(), {"out": None}) == -1
     assert _fused(P(), {"q_lat": None}) == -1
@@ -232,6 +234,9 @@ def test_fp8_errors():
         assert fn(FAKE, FAKE, MISALIGNED, ctypes.byref(P()), None) == -4
         assert fn(FAKE, FAKE, FAKE, ctypes.byref(P(head_dim=64)), None) == -6
         assert fn(FAKE, FAKE, FAKE, ctypes.byref(P(batch=0)), None) == 0
+    # the fused FP8 call takes bf16 activations only (the plain fused call also takes fp32)
+    assert lib.mla_decode_attn_out_proj_fp8(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, None, FAKE, 1 << 30,
+                                            2, ctypes.byref(P(dtype=binding.MLA_F32)), None) == -3
 
 
 def _run_py(code):

@@ -237,17 +237,17 @@ def test_end_to_end_small_mtp_all_heads():
 
 
 # ------------------------------------------------------------------------------------ boundary
-@pytest.mark.parametrize("variant", ["causal", "tree", "fp8", "fused", "fused fp8"])
+@pytest.mark.parametrize("variant", ["causal", "tree", "fp8", "fused", "fused fp8", "fused fp32"])
 def test_graph_capture_replays_match_eager(variant):
     """The step's calls captured in one HIP graph; replays interleaved with eager work all match the
     eager run bit for bit (decode as is, with a draft-tree mask, with the FP8 projections, and the
     fused attention + merge/W_UV call in bf16 and FP8 at 16 rows, where the merge runs inside the
-    W_UV kernel)."""
+    W_UV kernel, and in fp32 at 2 rows, where it runs inside the out-projection's dot products)."""
     say("graph capture", variant)
     torch = _torch()
     S = 4 if variant == "tree" else 1
-    B = 16 if variant.startswith("fused") else 4
-    w = gen.small_workload(B, S, ragged=(200, 700), dtype="bf16", paged=True)
+    B = 2 if variant == "fused fp32" else (16 if variant.startswith("fused") else 4)
+    w = gen.small_workload(B, S, ragged=(200, 700), dtype="f32" if variant.endswith("fp32") else "bf16", paged=True)
     x = gen.generate(w, 23, poison_unused=True)
     d = to_device(x)
     p = params_for(x, causal=variant != "tree")

@@ -28,9 +28,10 @@ def _run_fused(x, q_lat_bits, splits, causal=True, parents=None, latent=True):
     d = to_device(x)
     p = params_for(x, causal=causal)
     w = x.workload
-    q_lat = device_array(q_lat_bits, True)
+    q_lat = device_array(q_lat_bits, x.is_bf16)
     par = None if parents is None else torch.from_numpy(np.ascontiguousarray(parents, dtype=np.int32)).cuda()
-    out = torch.full((w.batch, w.q_len, 128, 128), float("nan"), device="cuda").to(torch.bfloat16)
+    out = torch.full((w.batch, w.q_len, 128, 128), float("nan"), device="cuda").to(
+        torch.bfloat16 if x.is_bf16 else torch.float32)
     o = torch.full((w.batch, w.q_len, 128, 512), float("nan"), device="cuda") if latent else None
     lse = torch.full((w.batch, w.q_len, 128), float("nan"), device="cuda") if latent else None
     ws_bytes = binding.mla_decode_attn_out_proj_workspace_bytes(p, splits)
@@ -43,7 +44,8 @@ def _run_fused(x, q_lat_bits, splits, causal=True, parents=None, latent=True):
 
 def _check(x, q_lat_bits, splits, causal=True, parents=None):
     out, o, lse = _run_fused(x, q_lat_bits, splits, causal, parents)
-    want = ref.latent_attention_reference(gen.bf16_bits_to_f32(q_lat_bits), x.f32("q_pe"), x.f32("pool"),
+    q = gen.bf16_bits_to_f32(q_lat_bits) if x.is_bf16 else q_lat_bits
+    want = ref.latent_attention_reference(q, x.f32("q_pe"), x.f32("pool"),
                                           x.block_table, x.seq_lens, softmax_scale=x.workload.softmax_scale,
                                           causal=causal, tree=parents)
     want_out = ref.out_proj_reference(want["o_lat"], x.f32("w_uv"))
@@ -54,7 +56,7 @@ def _check(x, q_lat_bits, splits, causal=True, parents=None):
     for k, e in errs.items():
         assert e <= tol_for(x), k
     check_lse(lse, want["lse"], tol_for(x))
-    check_softmax_mass(gen.bf16_bits_to_f32(q_lat_bits), x.f32("q_pe"), x.f32("pool"), x.block_table, x.seq_lens, lse,
+    check_softmax_mass(q, x.f32("q_pe"), x.f32("pool"), x.block_table, x.seq_lens, lse,
                        sample_rows(want["lse"]), softmax_scale=x.workload.softmax_scale, tol=tol_for(x),
                        causal=causal, tree=parents)
     bare, _, _ = _run_fused(x, q_lat_bits, splits, causal, parents, latent=False)
@@ -113,6 +115,27 @@ def test_fused_many_splits():
     for splits in (24, 47):
         say("fused splits", splits)
         _check(x, q_lat, splits)
+
+
+@pytest.mark.parametrize("B,S,splits", [(1, 1, 0), (3, 1, 0), (2, 2, 3), (1, 1, 1), (6, 1, 0)])
+def test_fused_fp32(B, S, splits):
+    """fp32 (bar 1e-4): with at most 4 query rows and several splits the merge of the fp32 partials
+    runs inside the out-projection's dot products; one split, or more rows, take the separate
+    kernels."""
+    say("fused fp32 B", B, "S", S, "splits", splits)
+    w = gen.small_workload(B, S, ragged=(40, 700), dtype="f32", paged=True)
+    x = gen.generate(w, 50 + 10 * B + S, poison_unused=True)
+    q_lat, _ = gen.generate_latent(w, 70 + B)
+    _check(x, q_lat, splits)
+
+
+def test_fused_fp32_tiny_full_size():
+    """The tiny fp32 workload (1 row, 512 cached tokens, contiguous) through the fused call, every
+    head."""
+    say("fused fp32 tiny_fp32")
+    x = gen.generate_named("tiny_fp32", poison_unused=True)
+    q_lat, _ = gen.generate_latent(x.workload, 71)
+    _check(x, q_lat, 0)
 
 
 @pytest.mark.parametrize("S,splits", [(8, 0), (8, 3), (64, 1)])
