@@ -366,6 +366,19 @@ __global__ __launch_bounds__(256, 1) void out_proj_bf16_kernel(const float* __re
 //     (ks, value block), the wave's sums scaled by the row's activation scale times the weight
 //     scale of block kb before the waves' sums meet.
 constexpr int kMopRows = 16;
+// Direct-to-LDS load of 16 bytes per lane (lane l's bytes at LDS lds + 16 l) from a wave-uniform
+// base plus a per-lane byte offset, issued from asm: with the builtin the compiler waits for every
+// outstanding vector-memory load before each later LDS read it cannot prove disjoint from the
+// loaded bytes, which would also retire the next row block's partials loading in the background.
+// The loads are awaited explicitly (before the first row block's products).
+__device__ __forceinline__ void mop_dma16(const void* base, uint32_t voff, const MLA_LDS char* lds) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  const uint64_t sbase = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
+                         (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+               "s"(__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds))
+               : "memory");
+}
 __device__ __forceinline__ int mop_swz(int c) { return (c & 3) | (((c >> 3) & 1) << 2); }
 __device__ __forceinline__ int mop_swz8(int v) { return (v >> 2) & 3; }
 
@@ -463,8 +476,7 @@ __global__ __launch_bounds__(512, 1) void merge_out_proj_kernel(const uint16_t* 
     for (int i = 0; i < 8; ++i) {
       const int v = 16 * i + (lane >> 2);
       const int u = (lane & 3) ^ mop_swz8(v);
-      __builtin_amdgcn_global_load_lds((const MLA_GLOBAL void*)(src + (size_t)v * kDc + u * 16),
-                                       (MLA_LDS void*)(ws + i * 1024), 16, 0, 0);
+      mop_dma16(src, (uint32_t)(v * kDc + u * 16), ws + i * 1024);
     }
   } else {
     const char* src = (const char*)((const uint16_t*)w_uv + ((size_t)h * kDc + c0) * kDh);
@@ -472,8 +484,7 @@ __global__ __launch_bounds__(512, 1) void merge_out_proj_kernel(const uint16_t* 
     for (int i = 0; i < 16; ++i) {
       const int c = 4 * i + g, u = s16;
       const int us = 2 * ((u >> 1) ^ mop_swz(c)) + (u & 1);
-      __builtin_amdgcn_global_load_lds((const MLA_GLOBAL void*)(src + (size_t)c * kDh * 2 + us * 16),
-                                       (MLA_LDS void*)(ws + i * 1024), 16, 0, 0);
+      mop_dma16(src, (uint32_t)(c * kDh * 2 + us * 16), ws + i * 1024);
     }
   }
   // the plan of the first block; the most ranges of its 16 rows bounds the merge loop
@@ -591,7 +602,9 @@ __global__ __launch_bounds__(512, 1) void merge_out_proj_kernel(const uint16_t* 
       nsp = plan_fixed ? num_splits : rows16_max(pl.y, lane);
       load(pl, 0, b0);
       if (4 < nsp) load(pl, 4, b1);
-      if (blk + 2 < blk_end) pl_next = plan_of(blk + 2);
+      // from the table, unconditionally (past the end: the last block's entry again, unused), so
+      // that nothing uses the loaded entry before the next row block
+      pl_next = *(const int2*)(row_plan + 4 + 2 * row_of(blk + 2 < blk_end ? blk + 2 : blk_end - 1));
     }
     f32x4 acc[8];
 #pragma unroll
